@@ -1,0 +1,273 @@
+"""Pins for the oracle's ops: each is checked against something other than its
+own formula -- f64 central differences for every backward, closed forms,
+invariants, hand-worked values, brute-force loops and library/table values.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import fd, ops
+from oracle.numerics import round_bf16, bf16_to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(1234)
+
+
+def rnd(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+def check_fd(f_out, bwd_grads, inputs, W, tol=1e-6):
+    """For each input k, compare bwd_grads[k] with the central difference of
+    L = sum(W * f_out(*inputs)) w.r.t. inputs[k]."""
+    L = fd.weighted_loss(W)
+    for k, x in enumerate(inputs):
+        def f(xk, k=k):
+            args = list(inputs)
+            args[k] = xk
+            return L(f_out(*args))
+        num = fd.numeric_grad(f, x)
+        ana = np.asarray(bwd_grads[k], dtype=np.float64)
+        scale = max(1.0, float(np.max(np.abs(num))))
+        assert np.max(np.abs(ana - num)) <= tol * scale, (k, np.max(np.abs(ana - num)))
+
+
+# ------------------------------------------------------------------ matmul
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_matmul_brute_force_and_fd(ta, tb):
+    M, K, N = 3, 4, 5
+    A = rnd(K, M) if ta else rnd(M, K)
+    B = rnd(N, K) if tb else rnd(K, N)
+    alpha = 0.75
+    C = ops.matmul(A, B, alpha, ta, tb)
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                a = A[k][i] if ta else A[i][k]
+                b = B[j][k] if tb else B[k][j]
+                s += a * b
+            assert abs(C[i, j] - alpha * s) < 1e-12
+    W = rnd(M, N)
+    dA, dB = ops.matmul_bwd(W, A, B, alpha, ta, tb)
+    check_fd(lambda a, b: ops.matmul(a, b, alpha, ta, tb), [dA, dB], [A, B], W)
+
+
+def test_matmul_batched_matches_per_batch_loop():
+    A, B = rnd(2, 3, 4, 5), rnd(2, 3, 5, 6)
+    C = ops.matmul(A, B, 2.0, False, False)
+    for i in range(2):
+        for j in range(3):
+            ref = [[2.0 * sum(A[i, j, r, k] * B[i, j, k, c] for k in range(5)) for c in range(6)]
+                   for r in range(4)]
+            np.testing.assert_allclose(C[i, j], ref, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------- add / mul / scale
+def test_add_mul_scale_fd():
+    a, b, W = rnd(3, 4), rnd(3, 4), rnd(3, 4)
+    check_fd(ops.add, ops.add_bwd(W), [a, b], W)
+    check_fd(ops.mul, ops.mul_bwd(W, a, b), [a, b], W)
+    check_fd(lambda x: ops.scale(x, -1.7), [ops.scale_bwd(W, -1.7)], [a], W)
+    assert ops.mul([[2.0]], [[3.0]])[0, 0] == 6.0
+    assert ops.add([[2.0]], [[3.0]])[0, 0] == 5.0
+
+
+def test_add_bias_fd_and_loop():
+    x, bias, W = rnd(5, 3), rnd(3), rnd(5, 3)
+    dx, db = ops.add_bias_bwd(W)
+    check_fd(ops.add_bias, [dx, db], [x, bias], W)
+    for c in range(3):
+        assert abs(db[c] - sum(W[r][c] for r in range(5))) < 1e-12
+        for r in range(5):
+            assert ops.add_bias(x, bias)[r, c] == x[r, c] + bias[c]
+
+
+# ------------------------------------------------------------- rms_norm
+def test_rms_norm_worked_value():
+    y, ir = ops.rms_norm([[3.0, 4.0]], [1.0, 2.0], 0.0)
+    # mean(x^2) = 12.5
+    assert abs(ir[0] - 1.0 / math.sqrt(12.5)) < 1e-15
+    np.testing.assert_allclose(y[0], [3.0 / math.sqrt(12.5), 8.0 / math.sqrt(12.5)], rtol=1e-15)
+
+
+@pytest.mark.parametrize("eps", [1e-5, 0.3])
+def test_rms_norm_fd_and_invariants(eps):
+    x, gamma, W = rnd(4, 6), 1.0 + 0.1 * rnd(6), rnd(4, 6)
+    y, ir = ops.rms_norm(x, gamma, eps)
+    dx, dg = ops.rms_norm_bwd(W, x, gamma, ir)
+    check_fd(lambda a, g: ops.rms_norm(a, g, eps)[0], [dx, dg], [x, gamma], W)
+    ms = np.mean(x * x, axis=1)
+    rms_of_normed = np.sqrt(np.mean((y / gamma) ** 2, axis=1))
+    np.testing.assert_allclose(rms_of_normed, np.sqrt(ms / (ms + eps)), rtol=1e-13)
+
+
+def test_rms_norm_scale_invariance_gives_orthogonal_grad():
+    # eps = 0: y(c*x) = y(x)  =>  sum_c x*dx = 0 on every row
+    x, gamma, W = rnd(5, 7), rnd(7), rnd(5, 7)
+    _, ir = ops.rms_norm(x, gamma, 0.0)
+    dx, _ = ops.rms_norm_bwd(W, x, gamma, ir)
+    assert np.max(np.abs(np.sum(x * dx, axis=1))) < 1e-12
+
+
+# ----------------------------------------------------------- layer_norm
+def test_layer_norm_worked_value():
+    y, mu, rstd = ops.layer_norm([[1.0, 2.0, 3.0, 4.0]], [1.0] * 4, [0.0] * 4, 0.0)
+    assert mu[0] == 2.5 and abs(rstd[0] - 1.0 / math.sqrt(1.25)) < 1e-15
+    np.testing.assert_allclose(y[0], np.array([-1.5, -0.5, 0.5, 1.5]) / math.sqrt(1.25), rtol=1e-14)
+
+
+@pytest.mark.parametrize("eps", [1e-5, 0.5])
+def test_layer_norm_fd_and_invariants(eps):
+    x, g, b, W = rnd(4, 6), 1 + 0.1 * rnd(6), 0.1 * rnd(6), rnd(4, 6)
+    y, mu, rs = ops.layer_norm(x, g, b, eps)
+    dx, dg, db = ops.layer_norm_bwd(W, x, g, mu, rs)
+    check_fd(lambda a, gg, bb: ops.layer_norm(a, gg, bb, eps)[0], [dx, dg, db], [x, g, b], W)
+    xhat = (y - b) / g
+    assert np.max(np.abs(np.mean(xhat, axis=1))) < 1e-13
+    var = np.var(x, axis=1)
+    np.testing.assert_allclose(np.mean(xhat ** 2, axis=1), var / (var + eps), rtol=1e-12)
+    # shift invariance: the gradient rows sum to zero, even with eps
+    assert np.max(np.abs(np.sum(dx, axis=1))) < 1e-12
+    np.testing.assert_allclose(db, W.sum(axis=0), rtol=1e-14)
+
+
+# --------------------------------------------------------------- softmax
+def test_softmax_worked_values():
+    y = ops.softmax([[0.0, math.log(2.0), math.log(3.0)]])
+    np.testing.assert_allclose(y[0], [1 / 6, 2 / 6, 3 / 6], rtol=1e-14)
+    y = ops.softmax([[0.0, math.log(4.0)]], alpha=0.5)       # softmax([0, ln 2])
+    np.testing.assert_allclose(y[0], [1 / 3, 2 / 3], rtol=1e-14)
+    np.testing.assert_allclose(ops.softmax(np.full((2, 5), 3.3)), np.full((2, 5), 0.2), rtol=1e-15)
+
+
+@pytest.mark.parametrize("alpha,causal", [(1.0, False), (0.125, False), (1.0, True), (0.5, True)])
+def test_softmax_fd_and_invariants(alpha, causal):
+    R, C, S = 6, 4, 4
+    x, W = rnd(R, C, scale=2.0), rnd(R, C)
+    y = ops.softmax(x, alpha, causal, S)
+    np.testing.assert_allclose(y.sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(ops.softmax(x + 7.0, alpha, causal, S), y, rtol=1e-12)
+    dx = ops.softmax_bwd(W, y, alpha)
+    assert np.max(np.abs(dx.sum(axis=1))) < 1e-13
+    check_fd(lambda a: ops.softmax(a, alpha, causal, S), [dx], [x], W)
+    if causal:
+        for r in range(R):
+            q = r % S
+            assert np.all(y[r, q + 1:] == 0.0) and np.all(dx[r, q + 1:] == 0.0)
+            np.testing.assert_allclose(y[r, :q + 1], ops.softmax(x[r:r + 1, :q + 1], alpha)[0], rtol=1e-14)
+        np.testing.assert_array_equal(y[0], [1.0, 0.0, 0.0, 0.0])
+
+
+# --------------------------------------------------------- cross_entropy
+def test_cross_entropy_worked_value():
+    L, lse, loss_row = ops.cross_entropy([[0.0, math.log(2.0), math.log(3.0)]], [2])
+    assert abs(lse[0] - math.log(6.0)) < 1e-15
+    assert abs(L - math.log(2.0)) < 1e-15          # -log(3/6)
+    d = ops.cross_entropy_bwd(1.0, [[0.0, math.log(2.0), math.log(3.0)]], [2], lse)
+    np.testing.assert_allclose(d[0], [1 / 6, 2 / 6, 3 / 6 - 1], rtol=1e-14)
+
+
+@pytest.mark.parametrize("V", [64, 4096, 50257, 128256])
+def test_cross_entropy_constant_logits_is_log_vocab(V):
+    # every class equally likely: L = ln V (math.log as the library routine)
+    L, _, _ = ops.cross_entropy(np.full((2, V), -1.25), [0, V - 1])
+    assert abs(L - math.log(V)) < 1e-12
+
+
+def test_cross_entropy_fd_and_invariants():
+    R, V = 4, 7
+    x, t = rnd(R, V, scale=2.0), np.array([0, 6, 3, 3])
+    L, lse, loss_row = ops.cross_entropy(x, t)
+    assert L >= 0 and np.all(loss_row >= 0)
+    g = -0.6
+    dx = ops.cross_entropy_bwd(g, x, t, lse)
+    assert np.max(np.abs(dx.sum(axis=1))) < 1e-14
+    num = fd.numeric_grad(lambda a: g * ops.cross_entropy(a, t)[0], x)
+    assert np.max(np.abs(num - dx)) < 1e-8
+
+
+def test_cross_entropy_bad_target_is_nan_row():
+    x = rnd(3, 5)
+    L, lse, loss_row = ops.cross_entropy(x, [1, 5, -1])
+    assert math.isnan(L) and not math.isnan(loss_row[0]) and math.isnan(loss_row[1]) and math.isnan(loss_row[2])
+    dx = ops.cross_entropy_bwd(1.0, x, [1, 5, -1], lse)
+    assert np.all(np.isfinite(dx[0])) and np.all(np.isnan(dx[1])) and np.all(np.isnan(dx[2]))
+
+
+# ------------------------------------------------------ silu / swiglu / gelu
+def test_silu_gelu_values():
+    assert ops.silu([0.0])[0] == 0.0 and ops.silu_bwd([1.0], [0.0])[0] == 0.5
+    assert abs(ops.silu([1.0])[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert ops.gelu([0.0])[0] == 0.0 and ops.gelu_bwd([1.0], [0.0])[0] == 0.5
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "normal_cdf_table.txt")) if l.strip() and l[0] != "#"]
+    for xs, phis in rows:
+        xv, phi = float(xs), float(phis)
+        assert abs(ops.normal_cdf([xv])[0] - phi) < 1e-14
+        assert abs(ops.gelu([xv])[0] - xv * phi) < 1e-14
+    from scipy.stats import norm
+    xs = np.linspace(-6, 6, 101)
+    np.testing.assert_allclose(ops.normal_cdf(xs), norm.cdf(xs), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(ops.normal_pdf(xs), norm.pdf(xs), rtol=1e-13)
+
+
+def test_silu_swiglu_gelu_fd():
+    x, g, u, W = rnd(3, 5, scale=2.0), rnd(3, 5, scale=2.0), rnd(3, 5), rnd(3, 5)
+    check_fd(ops.silu, [ops.silu_bwd(W, x)], [x], W)
+    check_fd(ops.gelu, [ops.gelu_bwd(W, x)], [x], W)
+    check_fd(ops.swiglu, list(ops.swiglu_bwd(W, g, u)), [g, u], W)
+    np.testing.assert_allclose(ops.swiglu(g, np.ones_like(g)), ops.silu(g), rtol=1e-15)
+
+
+# ------------------------------------------------------------------ rope
+def test_rope_pairing_direction_and_angles():
+    # head_dim 4, base 4: theta_{pos,0} = pos, theta_{pos,1} = pos/2
+    x = np.zeros((3, 4)); x[:, 0] = 1.0
+    y = ops.rope(x, 4, 4.0, 3)
+    for pos in range(3):
+        np.testing.assert_allclose(y[pos], [math.cos(pos), 0.0, math.sin(pos), 0.0], atol=1e-15)
+    x = np.zeros((3, 4)); x[:, 1] = 1.0
+    y = ops.rope(x, 4, 4.0, 3)
+    for pos in range(3):
+        np.testing.assert_allclose(y[pos], [0.0, math.cos(pos / 2), 0.0, math.sin(pos / 2)], atol=1e-15)
+    # the page's backward formula on d = e_{i+h}: dx_i = sin, dx_{i+h} = cos
+    d = np.zeros((3, 4)); d[:, 2] = 1.0
+    dx = ops.rope_bwd(d, 4, 4.0, 3)
+    for pos in range(3):
+        np.testing.assert_allclose(dx[pos], [math.sin(pos), 0.0, math.cos(pos), 0.0], atol=1e-15)
+
+
+def test_rope_is_complex_rotation_for_head_dim_2():
+    R = 7
+    x = rnd(R, 6)                          # three heads of width 2
+    y = ops.rope(x, 2, 10000.0, R)
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * np.arange(R))[:, None]
+    np.testing.assert_allclose(y[:, 0::2], z.real, atol=1e-14)
+    np.testing.assert_allclose(y[:, 1::2], z.imag, atol=1e-14)
+
+
+def test_rope_orthogonal_identity_at_zero_and_fd():
+    Dh, R, S = 8, 6, 4
+    x, W = rnd(R, 2 * Dh), rnd(R, 2 * Dh)
+    y = ops.rope(x, Dh, 10000.0, S)
+    np.testing.assert_array_equal(y[0], x[0])                  # pos 0
+    np.testing.assert_array_equal(y[S], x[S])                  # pos wraps to 0
+    h = Dh // 2
+    for hd in range(2):
+        a = x[:, hd * Dh:hd * Dh + h] ** 2 + x[:, hd * Dh + h:(hd + 1) * Dh] ** 2
+        b = y[:, hd * Dh:hd * Dh + h] ** 2 + y[:, hd * Dh + h:(hd + 1) * Dh] ** 2
+        np.testing.assert_allclose(a, b, rtol=1e-13)
+    np.testing.assert_allclose(ops.rope_bwd(y, Dh, 10000.0, S), x, atol=1e-14)
+    check_fd(lambda a: ops.rope(a, Dh, 10000.0, S), [ops.rope_bwd(W, Dh, 10000.0, S)], [x], W)
+
+
+# ----------------------------------------------------------- accumulate
+def test_grad_accumulate_and_bf16_rounding():
+    a, b = rnd(3, 3), rnd(3, 3)
+    np.testing.assert_array_equal(ops.grad_accumulate(a, b), a + b)
+    # bf16 rounding: 1 + 2^-8 is a tie between 1 and 1+2^-7 -> even (1.0)
+    np.testing.assert_array_equal(round_bf16([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9]),
+                                  [1.0, 1.0 + 2 ** -6, 1.0])
+    np.testing.assert_array_equal(bf16_to_f64(np.array([0x3F80, 0xC000], dtype=np.uint16)), [1.0, -2.0])
