@@ -1,0 +1,196 @@
+// Device helpers shared by the HIP kernels of libxt (gfx950, wave64).
+//
+// Storage types: f32 and bf16 (carried as uint16_t bit patterns, the upper
+// half of an IEEE binary32).  All arithmetic is f32.  Global traffic moves
+// in 16-byte packs (4 f32 or 8 bf16) so every wave issues 1 KiB per
+// global_load_dwordx4 / global_store_dwordx4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xt {
+
+typedef uint16_t bf16_t;
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Accumulating add that the compiler may not fuse with a preceding multiply:
+// a gradient contribution is rounded to f32 first, then added (one rounding
+// per push, in push order).
+__device__ __forceinline__ float acc_add(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+// ---------------------------------------------------------------- type traits
+template <typename T> struct io;
+
+template <> struct io<float> {
+  static constexpr int VEC = 4;               // elements per 16-byte pack
+  __device__ static __forceinline__ float ld(const float* p) { return *p; }
+  __device__ static __forceinline__ void st(float* p, float v) { *p = v; }
+  __device__ static __forceinline__ void unpack(const uint4& q, float* f) {
+    f[0] = __uint_as_float(q.x); f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z); f[3] = __uint_as_float(q.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+template <> struct io<bf16_t> {
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  __device__ static __forceinline__ void st(bf16_t* p, float v) { *p = (bf16_t)f2bf(v); }
+  __device__ static __forceinline__ void unpack(const uint4& q, float* f) {
+    f[0] = __uint_as_float(q.x << 16); f[1] = __uint_as_float(q.x & 0xffff0000u);
+    f[2] = __uint_as_float(q.y << 16); f[3] = __uint_as_float(q.y & 0xffff0000u);
+    f[4] = __uint_as_float(q.z << 16); f[5] = __uint_as_float(q.z & 0xffff0000u);
+    f[6] = __uint_as_float(q.w << 16); f[7] = __uint_as_float(q.w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(f2bf(f[0]) | (f2bf(f[1]) << 16), f2bf(f[2]) | (f2bf(f[3]) << 16),
+                      f2bf(f[4]) | (f2bf(f[5]) << 16), f2bf(f[6]) | (f2bf(f[7]) << 16));
+  }
+};
+
+// Load VEC elements starting at column c0 of a row (valid columns < n):
+// a full in-bounds pack is one 16-byte load; a partial pack is read
+// element by element with the missing lanes set to `fill`.
+template <typename T>
+__device__ __forceinline__ void load_pack(const T* row, int64_t c0, int64_t n, float* f, float fill) {
+  constexpr int V = io<T>::VEC;
+  if (c0 + V <= n) {
+    io<T>::unpack(*reinterpret_cast<const uint4*>(row + c0), f);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) f[k] = (c0 + k < n) ? io<T>::ld(row + c0 + k) : fill;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_pack(T* row, int64_t c0, int64_t n, const float* f) {
+  constexpr int V = io<T>::VEC;
+  if (c0 + V <= n) {
+    *reinterpret_cast<uint4*>(row + c0) = io<T>::pack(f);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (c0 + k < n) io<T>::st(row + c0 + k, f[k]);
+  }
+}
+
+// Store with optional in-place accumulation (dst += v, one rounding).
+template <typename T>
+__device__ __forceinline__ void store_pack_acc(T* row, int64_t c0, int64_t n, float* f, bool acc) {
+  if (acc) {
+    float o[io<T>::VEC];
+    load_pack<T>(row, c0, n, o, 0.f);
+#pragma unroll
+    for (int k = 0; k < io<T>::VEC; ++k) f[k] = acc_add(o[k], f[k]);
+  }
+  store_pack<T>(row, c0, n, f);
+}
+
+// --------------------------------------------------------------- reductions
+// Butterfly over the 64 lanes: every lane ends with the same bits (each level
+// adds the same two operands in both lanes), so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Sum over a group of RW consecutive waves of the block (one row per group).
+// Every thread of the block must call it (it contains barriers when RW > 1).
+// `lds` holds one float per wave of the block.
+template <int RW>
+__device__ __forceinline__ float group_sum(float v, float* lds) {
+  v = wave_sum(v);
+  if constexpr (RW == 1) {
+    return v;
+  } else {
+    const int w = threadIdx.x / WAVE;
+    const int g0 = (w / RW) * RW;
+    __syncthreads();
+    if ((threadIdx.x % WAVE) == 0) lds[w] = v;
+    __syncthreads();
+    float s = lds[g0];
+#pragma unroll
+    for (int i = 1; i < RW; ++i) s += lds[g0 + i];
+    return s;
+  }
+}
+
+template <int RW>
+__device__ __forceinline__ float group_max(float v, float* lds) {
+  v = wave_max(v);
+  if constexpr (RW == 1) {
+    return v;
+  } else {
+    const int w = threadIdx.x / WAVE;
+    const int g0 = (w / RW) * RW;
+    __syncthreads();
+    if ((threadIdx.x % WAVE) == 0) lds[w] = v;
+    __syncthreads();
+    float s = lds[g0];
+#pragma unroll
+    for (int i = 1; i < RW; ++i) s = fmaxf(s, lds[g0 + i]);
+    return s;
+  }
+}
+
+// Two sums over the group with one pair of barriers.  `lds` holds two
+// floats per wave of the block.
+template <int RW>
+__device__ __forceinline__ void group_sum2(float& a, float& b, float* lds) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if constexpr (RW > 1) {
+    const int w = threadIdx.x / WAVE;
+    const int g0 = (w / RW) * RW;
+    __syncthreads();
+    if ((threadIdx.x % WAVE) == 0) { lds[2 * w] = a; lds[2 * w + 1] = b; }
+    __syncthreads();
+    a = lds[2 * g0];
+    b = lds[2 * g0 + 1];
+#pragma unroll
+    for (int i = 1; i < RW; ++i) { a += lds[2 * (g0 + i)]; b += lds[2 * (g0 + i) + 1]; }
+  }
+}
+
+// Load n (multiple of 4, <= 8) f32 values starting at column c0 of a f32
+// vector of length `len` (gamma/beta/bias); missing entries read as 0.
+template <int N>
+__device__ __forceinline__ void load_f32s(const float* p, int64_t c0, int64_t len, float* f) {
+  if (c0 + N <= len && (((uintptr_t)(p + c0)) & 15) == 0) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+      float4 q = *reinterpret_cast<const float4*>(p + c0 + k);
+      f[k] = q.x; f[k + 1] = q.y; f[k + 2] = q.z; f[k + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) f[k] = (c0 + k < len) ? p[c0 + k] : 0.f;
+  }
+}
+
+}  // namespace xt

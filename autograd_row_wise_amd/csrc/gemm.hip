@@ -1,0 +1,249 @@
+// Matmul forward and backward on the matrix cores (MFMA) of gfx950.
+//
+// [AE] op-backward table row "matmul": C = A@B, dA = d@B^T, dB = A^T@d.
+// All three are one kernel, C (+)= alpha * op(A) op(B), with op() the
+// identity or the transpose of the stored operand; batches (attention
+// heads) run along gridDim.z with two-level element strides.
+//
+// Tiling: a 256-thread block (4 waves, 2 x 2) computes a 128 x 128 tile of C;
+// each wave owns 64 x 64 = 2 x 2 MFMA 32x32 accumulators.  K advances in
+// tiles of BK staged in LDS as [row][k] for both operands (k contiguous), so
+// every MFMA operand is one or two 16-byte LDS reads per lane.  The next K
+// tile is fetched into registers while the current one is multiplied (LDS
+// double buffer, one barrier per K tile).
+//   bf16: v_mfma_f32_32x32x16_bf16, BK = 32 (two MFMA steps of 16).
+//   f32 : v_mfma_f32_32x32x2_f32, BK = 16; lane l supplies k = 8*(l/32)+j to
+//         the j-th of eight MFMAs (a permutation of the summation order).
+// Accumulation is f32; the epilogue scales by alpha, optionally adds the
+// existing C, and rounds once to C's dtype.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace xt {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int BM = 128, BN = 128, NT = 256;
+
+template <typename TA> struct gcfg;
+template <> struct gcfg<bf16_t> { static constexpr int BK = 32, PAD = 8; };
+template <> struct gcfg<float> { static constexpr int BK = 16, PAD = 4; };
+
+// Registers holding one thread's share of a BM x BK (or BN x BK) tile.
+// Non-transposed storage ([rows][K], k contiguous): each thread moves
+// 16-byte chunks along k.  Transposed storage ([K][rows]): chunks along rows,
+// scattered into the [row][k] LDS layout.
+template <typename TA, bool KCONTIG>
+struct TileLoader {
+  static constexpr int BK = gcfg<TA>::BK;
+  static constexpr int V = 16 / sizeof(TA);                    // elements per chunk
+  static constexpr int CHUNKS = BM * BK / V;                   // chunks per tile
+  static constexpr int PER_T = CHUNKS / NT;                    // chunks per thread
+  uint4 r[PER_T];
+
+  // g: operand base (batch applied); rows_total: M or N; K; ld: storage ld
+  __device__ __forceinline__ void load(const TA* g, int64_t ld, int64_t row0, int64_t rows_total,
+                                       int64_t k0, int64_t K, bool full) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = i * NT + threadIdx.x;
+      int row, kk;
+      if (KCONTIG) { row = c / (BK / V); kk = (c % (BK / V)) * V; }
+      else { kk = c / (BM / V); row = (c % (BM / V)) * V; }
+      const int64_t gr = row0 + row, gk = k0 + kk;
+      if (full) {
+        const TA* p = KCONTIG ? g + gr * ld + gk : g + gk * ld + gr;
+        r[i] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        TA tmp[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int64_t rr = KCONTIG ? gr : gr + j, kq = KCONTIG ? gk + j : gk;
+          tmp[j] = (rr < rows_total && kq < K) ? g[KCONTIG ? rr * ld + kq : kq * ld + rr] : (TA)0;
+        }
+        r[i] = *reinterpret_cast<const uint4*>(tmp);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(TA* lds) const {
+    constexpr int LDK = BK + gcfg<TA>::PAD;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int c = i * NT + threadIdx.x;
+      if (KCONTIG) {
+        const int row = c / (BK / V), kk = (c % (BK / V)) * V;
+        *reinterpret_cast<uint4*>(lds + row * LDK + kk) = r[i];
+      } else {
+        const int kk = c / (BM / V), row = (c % (BM / V)) * V;
+        const TA* v = reinterpret_cast<const TA*>(&r[i]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) lds[(row + j) * LDK + kk] = v[j];
+      }
+    }
+  }
+};
+
+template <typename TA>
+__device__ __forceinline__ void mfma_tile(const TA* As, const TA* Bs, int wm, int wn,
+                                          f32x16_t (&acc)[2][2]) {
+  constexpr int BK = gcfg<TA>::BK, LDK = BK + gcfg<TA>::PAD;
+  const int l = threadIdx.x % WAVE;
+  const int lr = l % 32, lk = (l / 32) * 8;
+  if constexpr (sizeof(TA) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = *reinterpret_cast<const bf16x8_t*>(As + (wm + t * 32 + lr) * LDK + ks + lk);
+        b[t] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn + t * 32 + lr) * LDK + ks + lk);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  } else {
+    float a[2][8], b[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float4* pa = reinterpret_cast<const float4*>(As + (wm + t * 32 + lr) * LDK + lk);
+      const float4* pb = reinterpret_cast<const float4*>(Bs + (wn + t * 32 + lr) * LDK + lk);
+      const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+      a[t][0] = a0.x; a[t][1] = a0.y; a[t][2] = a0.z; a[t][3] = a0.w;
+      a[t][4] = a1.x; a[t][5] = a1.y; a[t][6] = a1.z; a[t][7] = a1.w;
+      b[t][0] = b0.x; b[t][1] = b0.y; b[t][2] = b0.z; b[t][3] = b0.w;
+      b[t][4] = b1.x; b[t][5] = b1.y; b[t][6] = b1.z; b[t][7] = b1.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][k], b[j][k], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <typename TA, typename TC, bool TRANS_A, bool TRANS_B>
+__global__ __launch_bounds__(NT) void gemm_k(
+    const TA* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
+    const TA* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
+    TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c) {
+  constexpr int BK = gcfg<TA>::BK, LDK = BK + gcfg<TA>::PAD;
+  __shared__ __align__(16) TA As[2][BM * LDK];
+  __shared__ __align__(16) TA Bs[2][BN * LDK];
+
+  const int64_t z = blockIdx.z, b0 = z / nb1, b1 = z % nb1;
+  A += b0 * sa0 + b1 * sa1;
+  B += b0 * sb0 + b1 * sb1;
+  C += b0 * sc0 + b1 * sc1;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int w = threadIdx.x / WAVE;
+  const int wm = (w / 2) * 64, wn = (w % 2) * 64;
+
+  // A as [M][K] is k-contiguous unless transposed; B as [K][N] is k-contiguous
+  // only when transposed ([N][K] storage).
+  TileLoader<TA, !TRANS_A> la;
+  TileLoader<TA, TRANS_B> lb;
+  const bool fullMN = (m0 + BM <= M) && (n0 + BN <= N);
+  const bool alA = (((uintptr_t)A) & 15) == 0 && ((lda * (int64_t)sizeof(TA)) & 15) == 0;
+  const bool alB = (((uintptr_t)B) & 15) == 0 && ((ldb * (int64_t)sizeof(TA)) & 15) == 0;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int64_t nk = (K + BK - 1) / BK;
+  if (nk > 0) {
+    bool full = fullMN && BK <= K && alA && alB;
+    la.load(A, lda, m0, M, 0, K, full);
+    lb.load(B, ldb, n0, N, 0, K, full);
+    la.store(As[0]);
+    lb.store(Bs[0]);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        const int64_t k0 = (kt + 1) * BK;
+        full = fullMN && (k0 + BK <= K) && alA && alB;
+        la.load(A, lda, m0, M, k0, K, full);
+        lb.load(B, ldb, n0, N, k0, K, full);
+      }
+      mfma_tile<TA>(As[cur], Bs[cur], wm, wn, acc);
+      if (more) {
+        la.store(As[cur ^ 1]);
+        lb.store(Bs[cur ^ 1]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue: 32x32 accumulator layout -- lane l, register q holds
+  // row 8*(q/4) + 4*(l/32) + q%4, column l%32 of the tile
+  const int l = threadIdx.x % WAVE;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm + i * 32 + 8 * (q / 4) + 4 * (l / 32) + (q % 4);
+        const int64_t col = n0 + wn + j * 32 + (l % 32);
+        if (row < M && col < N) {
+          TC* p = C + row * ldc + col;
+          float v = alpha * acc[i][j][q];
+          if (acc_c) v = acc_add(io<TC>::ld(p), v);
+          io<TC>::st(p, v);
+        }
+      }
+}
+
+template <typename TA, typename TC>
+hipError_t gemm_go(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
+                   float alpha, bool acc, hipStream_t s) {
+  const int64_t M = C.rows, N = C.cols;
+  const int64_t K = ta ? A.rows : A.cols;
+  const int64_t nb0 = C.nb[0], nb1 = C.nb[1];
+  if (M == 0 || N == 0 || nb0 * nb1 == 0) return hipSuccess;
+  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)(nb0 * nb1));
+  const TA* a = (const TA*)A.data;
+  const TA* b = (const TA*)B.data;
+  TC* c = (TC*)C.data;
+#define XT_GEMM_LAUNCH(TA_, TB_)                                                              \
+  gemm_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
+                                               B.sb[1], c, C.ld, C.sb[0], C.sb[1], M, N, K,  \
+                                               nb1, alpha, acc ? 1 : 0)
+  if (!ta && !tb) XT_GEMM_LAUNCH(false, false);
+  else if (!ta && tb) XT_GEMM_LAUNCH(false, true);
+  else if (ta && !tb) XT_GEMM_LAUNCH(true, false);
+  else XT_GEMM_LAUNCH(true, true);
+#undef XT_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
+                       const xt_tensor& C, float alpha, bool acc, hipStream_t s) {
+  if (A.dtype == XT_BF16) {
+    return C.dtype == XT_BF16 ? gemm_go<bf16_t, bf16_t>(A, ta, B, tb, C, alpha, acc, s)
+                              : gemm_go<bf16_t, float>(A, ta, B, tb, C, alpha, acc, s);
+  }
+  return C.dtype == XT_BF16 ? gemm_go<float, bf16_t>(A, ta, B, tb, C, alpha, acc, s)
+                            : gemm_go<float, float>(A, ta, B, tb, C, alpha, acc, s);
+}
+
+}  // namespace xt

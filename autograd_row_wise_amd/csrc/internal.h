@@ -1,0 +1,100 @@
+// Internal launch interface between the C ABI (abi.cpp) and the kernels.
+// Every launcher enqueues on `stream`, returns hipSuccess or the launch
+// error, and assumes the ABI layer has already validated shapes, dtypes,
+// alignment and workspace size.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/xt.h"
+
+namespace xt {
+
+// --- row-wise reductions (rowwise.hip) ---------------------------------
+// Plan of a row-resident launch: RW waves share one row, each thread keeps
+// NV 16-byte packs of it in registers; rows longer than the register
+// capacity, or rows that are not 16-byte aligned, use the generic path.
+struct RowPlan {
+  bool fast;        // register-resident vector path
+  int rw, nv;       // waves per row, packs per thread
+  int block;        // threads per block
+  int grid;         // blocks
+  int groups;       // rows in flight per block (block / (64*rw))
+};
+
+enum RowKind { RK_RMS_FWD, RK_RMS_BWD, RK_LN_FWD, RK_LN_BWD, RK_SM_FWD, RK_SM_BWD };
+
+RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned);
+// Workspace (bytes) of the parameter-gradient partials of a row backward.
+size_t row_bwd_workspace(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned);
+
+hipError_t launch_rms_fwd(const xt_tensor& x, const float* gamma, const xt_tensor& y,
+                          const xt_tensor& inv_rms, float eps, hipStream_t s);
+hipError_t launch_rms_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
+                          const xt_tensor& inv_rms, const xt_tensor* dx, bool acc_dx,
+                          float* dgamma, bool acc_dgamma, void* ws, hipStream_t s);
+hipError_t launch_ln_fwd(const xt_tensor& x, const float* gamma, const float* beta,
+                         const xt_tensor& y, const xt_tensor& mean, const xt_tensor& rstd,
+                         float eps, hipStream_t s);
+hipError_t launch_ln_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
+                         const xt_tensor& mean, const xt_tensor& rstd,
+                         const xt_tensor* dx, bool acc_dx, float* dgamma, bool acc_dgamma,
+                         float* dbeta, bool acc_dbeta, void* ws, hipStream_t s);
+hipError_t launch_softmax_fwd(const xt_tensor& x, const xt_tensor& y, float alpha,
+                              int causal, int seq_len, hipStream_t s);
+hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx,
+                              bool acc, float alpha, hipStream_t s);
+
+// Column sums: out[c] (+)= sum_r d[r, c]  (add_bias backward).
+size_t colsum_workspace(int dtype, int64_t R, int64_t C);
+hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, hipStream_t s);
+
+// --- cross entropy (ce.hip) --------------------------------------------
+hipError_t launch_ce_fwd(const xt_tensor& logits, const int32_t* targets, int64_t ld_t,
+                         float* L, float* lse, int64_t ld_lse, float* loss_row,
+                         int64_t ld_loss, hipStream_t s);
+hipError_t launch_ce_bwd(const float* dL, const xt_tensor& logits, const int32_t* targets,
+                         int64_t ld_t, const float* lse, int64_t ld_lse,
+                         const xt_tensor& dlogits, bool acc, hipStream_t s);
+
+// --- elementwise (elementwise.hip) ---------------------------------------
+enum EwOp {
+  EW_ADD, EW_MUL, EW_SCALE, EW_ADD_BIAS, EW_SILU, EW_GELU, EW_SWIGLU,
+  EW_COPY_SCALED,              // out0 (+)= alpha * in0
+  EW_MUL_BWD,                  // out0 (+)= d*b, out1 (+)= d*a
+  EW_SILU_BWD, EW_GELU_BWD, EW_SWIGLU_BWD,
+  EW_ACCUMULATE                // out0 += in0 (dtypes may differ)
+};
+struct EwArgs {
+  const xt_tensor* in[3];
+  const xt_tensor* out[2];     // NULL = not wanted
+  uint32_t acc;                // bit k: out[k] +=
+  float alpha;
+  const float* colvec;         // ADD_BIAS: bias[C]
+};
+hipError_t launch_ew(EwOp op, const EwArgs& a, hipStream_t s);
+
+// --- dropout (elementwise.hip) -------------------------------------------
+// keep iff (splitmix64(seed ^ i*gamma) >> 40) >= thr, thr = ceil(p * 2^24).
+hipError_t launch_dropout_fwd(const xt_tensor& x, const xt_tensor& y, const xt_tensor* mask,
+                              uint32_t thr, float scale, uint64_t seed, hipStream_t s);
+hipError_t launch_dropout_mask_only(const xt_tensor& mask, uint32_t thr, uint64_t seed,
+                                    hipStream_t s);
+hipError_t launch_dropout_bwd(const xt_tensor& d, const xt_tensor& mask, const xt_tensor& dx,
+                              bool acc, float scale, hipStream_t s);
+
+// --- rope (rope.hip) ------------------------------------------------------
+hipError_t launch_rope(const xt_tensor& x, const xt_tensor& y, bool acc, int head_dim,
+                       float base, int seq_len, bool inverse, hipStream_t s);
+
+// --- matmul (gemm.hip) ----------------------------------------------------
+// C (+)= alpha * op(A) op(B), batched over nb[0] x nb[1].
+hipError_t launch_gemm(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
+                       const xt_tensor& C, float alpha, bool acc, hipStream_t s);
+
+// --- misc -------------------------------------------------------------------
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+}  // namespace xt

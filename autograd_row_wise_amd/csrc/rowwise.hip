@@ -1,0 +1,939 @@
+// Row-wise reductions: rms_norm, layer_norm and softmax, forward and backward,
+// plus the fixed-order column reductions that finish parameter gradients.
+//
+// [AE] "RMSNorm" paragraph, op-backward table rows "softmax" and the
+// "Softmax 反向推导"; [BP] k_layernorm_fwd/k_layernorm_bwd, "Sparade
+// tensorer" (mean and variance saved by the forward) and "En baklängeskärnas
+// uppgift" (one launch yields grad_input and the parameter gradient).
+//
+// Fast path: a row is held in registers by a group of RW waves (RW = 1, 4 or
+// 16), each thread keeping NV 16-byte packs, so x (and d) are read from HBM
+// exactly once per op.  Reductions are wave butterflies then a fixed-order
+// LDS combine: results do not depend on scheduling.  Backward kernels run one
+// 1024-thread block per CU; each thread accumulates the parameter-gradient
+// terms of its own columns over the block's rows, the groups of a block are
+// folded in LDS in group order, and one partial row per block goes to the
+// workspace.  A separate pass sums the partial rows in block order.
+//
+// Generic path (rows that do not fit in registers or are not 16-byte
+// aligned): one 256-thread block per row, several passes over global memory.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace xt {
+
+namespace {
+
+constexpr int BWD_BLOCK = 1024;
+constexpr int BWD_GRID_MAX = 256;     // one backward block per CU
+constexpr int FWD_GRID_MAX = 4096;
+constexpr int GEN_BLOCK = 256;
+
+__device__ __forceinline__ float fast_exp(float t) {
+  return __builtin_amdgcn_exp2f(t * 1.4426950408889634f);
+}
+
+template <typename T> __device__ __forceinline__ const T* row_ptr(const void* p, int64_t r, int64_t ld) {
+  return reinterpret_cast<const T*>(p) + r * ld;
+}
+template <typename T> __device__ __forceinline__ T* row_ptr_w(void* p, int64_t r, int64_t ld) {
+  return reinterpret_cast<T*>(p) + r * ld;
+}
+
+// ===================================================================== RMS
+template <typename T, int RW, int NV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
+    const void* __restrict__ x, int64_t ldx, const float* __restrict__ gamma,
+    void* __restrict__ y, int64_t ldy, float* __restrict__ ir, int64_t ldir,
+    int64_t R, int64_t C, float eps, float invC) {
+  constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
+  __shared__ float lds[BLOCK / WAVE];
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  float gam[NV][V];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
+    const int64_t r = base + g;
+    const bool active = r < R;
+    float v[NV][V];
+    float ss = 0.f;
+    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      if (active && c0 < C) load_pack<T>(xr, c0, C, v[j], 0.f);
+      else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) v[j][k] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) ss += v[j][k] * v[j][k];
+    }
+    ss = group_sum<RW>(ss, lds);
+    const float irv = rsqrtf(ss * invC + eps);
+    if (active) {
+      T* yr = row_ptr_w<T>(y, r, ldy);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t c0 = (int64_t)(j * G + gl) * V;
+        if (c0 < C) {
+          float o[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) o[k] = v[j][k] * irv * gam[j][k];
+          store_pack<T>(yr, c0, C, o);
+        }
+      }
+      if (gl == 0) ir[r * ldir] = irv;
+    }
+  }
+}
+
+// Folds the per-group parameter partials of a block (NG groups, fixed group
+// order) into LDS and writes one partial row (NP vectors of C) per block.
+template <int NV, int V, int G, int NG, int NP, int BLOCK>
+__device__ __forceinline__ void fold_partials(float (&pp)[NP][NV][V], float* red, float* part,
+                                              int64_t C) {
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  for (int gi = 0; gi < NG; ++gi) {
+    if (g == gi) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const int64_t c = (int64_t)(j * G + gl) * V + k;
+            if (c < C) red[q * C + c] = (gi == 0) ? pp[q][j][k] : red[q * C + c] + pp[q][j][k];
+          }
+    }
+    __syncthreads();
+  }
+  float* out = part + (int64_t)blockIdx.x * NP * C;
+  for (int64_t c = threadIdx.x; c < NP * C; c += BLOCK) out[c] = red[c];
+}
+
+template <typename T, int RW, int NV>
+__global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
+    const void* __restrict__ d, int64_t ldd, const void* __restrict__ x, int64_t ldx,
+    const float* __restrict__ gamma, const float* __restrict__ ir, int64_t ldir,
+    void* __restrict__ dx, int64_t lddx, int acc_dx, float* __restrict__ part,
+    int64_t R, int64_t C, float invC, int64_t rpb) {
+  constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BWD_BLOCK / G;
+  extern __shared__ float red[];               // C floats
+  __shared__ float lds[BWD_BLOCK / WAVE];
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  float gam[NV][V], pp[1][NV][V];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+#pragma unroll
+    for (int k = 0; k < V; ++k) pp[0][j][k] = 0.f;
+  }
+  const int64_t start = (int64_t)blockIdx.x * rpb;
+  const int64_t end = min(R, start + rpb);
+  for (int64_t base = start; base < end; base += NG) {
+    const int64_t r = base + g;
+    const bool active = r < end;
+    const T* dr = row_ptr<T>(d, active ? r : 0, ldd);
+    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    float dv[NV][V], xv[NV][V];
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      if (active && c0 < C) {
+        load_pack<T>(dr, c0, C, dv[j], 0.f);
+        load_pack<T>(xr, c0, C, xv[j], 0.f);
+      } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) { dv[j][k] = 0.f; xv[j][k] = 0.f; }
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) dot += dv[j][k] * gam[j][k] * xv[j][k];
+    }
+    dot = group_sum<RW>(dot, lds);
+    if (active) {
+      const float irv = ir[r * ldir];
+      const float c1 = irv * irv * irv * invC * dot;
+      T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t c0 = (int64_t)(j * G + gl) * V;
+        if (c0 < C) {
+          float o[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            o[k] = irv * (dv[j][k] * gam[j][k]) - xv[j][k] * c1;
+            pp[0][j][k] += dv[j][k] * xv[j][k] * irv;
+          }
+          if (dxr) store_pack_acc<T>(dxr, c0, C, o, acc_dx != 0);
+        }
+      }
+    }
+  }
+  if (part) fold_partials<NV, V, G, NG, 1, BWD_BLOCK>(pp, red, part, C);
+}
+
+// ================================================================ LayerNorm
+template <typename T, int RW, int NV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
+    const void* __restrict__ x, int64_t ldx, const float* __restrict__ gamma,
+    const float* __restrict__ beta, void* __restrict__ y, int64_t ldy,
+    float* __restrict__ mean, int64_t ldm, float* __restrict__ rstd, int64_t ldr,
+    int64_t R, int64_t C, float eps, float invC) {
+  constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
+  __shared__ float lds[BLOCK / WAVE];
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  float gam[NV][V], bet[NV][V];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+    load_f32s<V>(beta, (int64_t)(j * G + gl) * V, C, bet[j]);
+  }
+  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
+    const int64_t r = base + g;
+    const bool active = r < R;
+    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    float v[NV][V];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      if (active && c0 < C) load_pack<T>(xr, c0, C, v[j], 0.f);
+      else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) v[j][k] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) s += v[j][k];
+    }
+    const float mu = group_sum<RW>(s, lds) * invC;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float t = v[j][k] - mu;
+        if ((int64_t)(j * G + gl) * V + k < C) q += t * t;
+      }
+    const float var = group_sum<RW>(q, lds) * invC;
+    const float rs = rsqrtf(var + eps);
+    if (active) {
+      T* yr = row_ptr_w<T>(y, r, ldy);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t c0 = (int64_t)(j * G + gl) * V;
+        if (c0 < C) {
+          float o[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) o[k] = (v[j][k] - mu) * rs * gam[j][k] + bet[j][k];
+          store_pack<T>(yr, c0, C, o);
+        }
+      }
+      if (gl == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
+    }
+  }
+}
+
+template <typename T, int RW, int NV>
+__global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
+    const void* __restrict__ d, int64_t ldd, const void* __restrict__ x, int64_t ldx,
+    const float* __restrict__ gamma, const float* __restrict__ mean, int64_t ldm,
+    const float* __restrict__ rstd, int64_t ldr, void* __restrict__ dx, int64_t lddx,
+    int acc_dx, float* __restrict__ part, int64_t R, int64_t C, float invC, int64_t rpb) {
+  constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BWD_BLOCK / G;
+  extern __shared__ float red[];               // 2C floats
+  __shared__ float lds[2 * BWD_BLOCK / WAVE];
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  float gam[NV][V], pp[2][NV][V];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+#pragma unroll
+    for (int k = 0; k < V; ++k) { pp[0][j][k] = 0.f; pp[1][j][k] = 0.f; }
+  }
+  const int64_t start = (int64_t)blockIdx.x * rpb;
+  const int64_t end = min(R, start + rpb);
+  for (int64_t base = start; base < end; base += NG) {
+    const int64_t r = base + g;
+    const bool active = r < end;
+    const T* dr = row_ptr<T>(d, active ? r : 0, ldd);
+    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    const float mu = active ? mean[r * ldm] : 0.f;
+    const float rs = active ? rstd[r * ldr] : 0.f;
+    float dv[NV][V], xh[NV][V];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      if (active && c0 < C) {
+        load_pack<T>(dr, c0, C, dv[j], 0.f);
+        load_pack<T>(xr, c0, C, xh[j], 0.f);
+      } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) { dv[j][k] = 0.f; xh[j][k] = 0.f; }
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const bool ok = c0 + k < C;
+        xh[j][k] = ok ? (xh[j][k] - mu) * rs : 0.f;
+        const float gv = dv[j][k] * gam[j][k];
+        s1 += gv;
+        s2 += gv * xh[j][k];
+      }
+    }
+    group_sum2<RW>(s1, s2, lds);
+    if (active) {
+      const float a = s1 * invC, b = s2 * invC;
+      T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t c0 = (int64_t)(j * G + gl) * V;
+        if (c0 < C) {
+          float o[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            o[k] = rs * (dv[j][k] * gam[j][k] - a - xh[j][k] * b);
+            pp[0][j][k] += dv[j][k] * xh[j][k];
+            pp[1][j][k] += dv[j][k];
+          }
+          if (dxr) store_pack_acc<T>(dxr, c0, C, o, acc_dx != 0);
+        }
+      }
+    }
+  }
+  if (part) fold_partials<NV, V, G, NG, 2, BWD_BLOCK>(pp, red, part, C);
+}
+
+// ================================================================== softmax
+template <typename T, int RW, int NV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
+    const void* __restrict__ x, int64_t ldx, void* __restrict__ y, int64_t ldy,
+    int64_t R, int64_t C, float alpha, int causal, int seq_len) {
+  constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
+  __shared__ float lds[BLOCK / WAVE];
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const float NEG_INF = -__builtin_inff();
+  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
+    const int64_t r = base + g;
+    const bool active = r < R;
+    const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;   // valid columns
+    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    float v[NV][V];
+    float m = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      if (active && c0 < C) load_pack<T>(xr, c0, C, v[j], 0.f);
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        v[j][k] = (active && c0 + k < lim) ? alpha * v[j][k] : NEG_INF;
+        m = fmaxf(m, v[j][k]);
+      }
+    }
+    m = group_max<RW>(m, lds);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        v[j][k] = fast_exp(v[j][k] - m);        // masked: exp(-inf) = 0
+        s += v[j][k];
+      }
+    s = group_sum<RW>(s, lds);
+    const float inv = 1.0f / s;
+    if (active) {
+      T* yr = row_ptr_w<T>(y, r, ldy);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t c0 = (int64_t)(j * G + gl) * V;
+        if (c0 < C) {
+          float o[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) o[k] = v[j][k] * inv;
+          store_pack<T>(yr, c0, C, o);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int RW, int NV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
+    const void* __restrict__ d, int64_t ldd, const void* __restrict__ y, int64_t ldy,
+    void* __restrict__ dx, int64_t lddx, int acc, int64_t R, int64_t C, float alpha) {
+  constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
+  __shared__ float lds[BLOCK / WAVE];
+  const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
+    const int64_t r = base + g;
+    const bool active = r < R;
+    const T* dr = row_ptr<T>(d, active ? r : 0, ldd);
+    const T* yr = row_ptr<T>(y, active ? r : 0, ldy);
+    float dv[NV][V], yv[NV][V];
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      if (active && c0 < C) {
+        load_pack<T>(dr, c0, C, dv[j], 0.f);
+        load_pack<T>(yr, c0, C, yv[j], 0.f);
+      } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) { dv[j][k] = 0.f; yv[j][k] = 0.f; }
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) dot += dv[j][k] * yv[j][k];
+    }
+    dot = group_sum<RW>(dot, lds);
+    if (active) {
+      T* dxr = row_ptr_w<T>(dx, r, lddx);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t c0 = (int64_t)(j * G + gl) * V;
+        if (c0 < C) {
+          float o[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) o[k] = alpha * yv[j][k] * (dv[j][k] - dot);
+          store_pack_acc<T>(dxr, c0, C, o, acc != 0);
+        }
+      }
+    }
+  }
+}
+
+// =============================================================== generic path
+// One 256-thread block per row, element-wise loads, several passes.
+template <typename T> __device__ __forceinline__ float gl1(const void* p, int64_t r, int64_t ld, int64_t c) {
+  return io<T>::ld(reinterpret_cast<const T*>(p) + r * ld + c);
+}
+template <typename T> __device__ __forceinline__ void gs1(void* p, int64_t r, int64_t ld, int64_t c, float v, bool acc) {
+  T* q = reinterpret_cast<T*>(p) + r * ld + c;
+  io<T>::st(q, acc ? acc_add(io<T>::ld(q), v) : v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void rms_fwd_gen(
+    const void* x, int64_t ldx, const float* gamma, void* y, int64_t ldy, float* ir, int64_t ldir,
+    int64_t R, int64_t C, float eps, float invC) {
+  __shared__ float lds[GEN_BLOCK / WAVE];
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    float ss = 0.f;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) { const float v = gl1<T>(x, r, ldx, c); ss += v * v; }
+    ss = group_sum<GEN_BLOCK / WAVE>(ss, lds);
+    const float irv = rsqrtf(ss * invC + eps);
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) gs1<T>(y, r, ldy, c, gl1<T>(x, r, ldx, c) * irv * gamma[c], false);
+    if (threadIdx.x == 0) ir[r * ldir] = irv;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void rms_bwd_gen(
+    const void* d, int64_t ldd, const void* x, int64_t ldx, const float* gamma, const float* ir,
+    int64_t ldir, void* dx, int64_t lddx, int acc, int64_t R, int64_t C, float invC) {
+  __shared__ float lds[GEN_BLOCK / WAVE];
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    float dot = 0.f;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) dot += gl1<T>(d, r, ldd, c) * gamma[c] * gl1<T>(x, r, ldx, c);
+    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds);
+    const float irv = ir[r * ldir];
+    const float c1 = irv * irv * irv * invC * dot;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
+      gs1<T>(dx, r, lddx, c, irv * (gl1<T>(d, r, ldd, c) * gamma[c]) - gl1<T>(x, r, ldx, c) * c1, acc != 0);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void ln_fwd_gen(
+    const void* x, int64_t ldx, const float* gamma, const float* beta, void* y, int64_t ldy,
+    float* mean, int64_t ldm, float* rstd, int64_t ldr, int64_t R, int64_t C, float eps, float invC) {
+  __shared__ float lds[GEN_BLOCK / WAVE];
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    float s = 0.f;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) s += gl1<T>(x, r, ldx, c);
+    const float mu = group_sum<GEN_BLOCK / WAVE>(s, lds) * invC;
+    float q = 0.f;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) { const float t = gl1<T>(x, r, ldx, c) - mu; q += t * t; }
+    const float rs = rsqrtf(group_sum<GEN_BLOCK / WAVE>(q, lds) * invC + eps);
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
+      gs1<T>(y, r, ldy, c, (gl1<T>(x, r, ldx, c) - mu) * rs * gamma[c] + beta[c], false);
+    if (threadIdx.x == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void ln_bwd_gen(
+    const void* d, int64_t ldd, const void* x, int64_t ldx, const float* gamma, const float* mean,
+    int64_t ldm, const float* rstd, int64_t ldr, void* dx, int64_t lddx, int acc, int64_t R,
+    int64_t C, float invC) {
+  __shared__ float lds[2 * GEN_BLOCK / WAVE];
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const float mu = mean[r * ldm], rs = rstd[r * ldr];
+    float s1 = 0.f, s2 = 0.f;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
+      const float gv = gl1<T>(d, r, ldd, c) * gamma[c];
+      s1 += gv;
+      s2 += gv * (gl1<T>(x, r, ldx, c) - mu) * rs;
+    }
+    group_sum2<GEN_BLOCK / WAVE>(s1, s2, lds);
+    const float a = s1 * invC, b = s2 * invC;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
+      const float xh = (gl1<T>(x, r, ldx, c) - mu) * rs;
+      gs1<T>(dx, r, lddx, c, rs * (gl1<T>(d, r, ldd, c) * gamma[c] - a - xh * b), acc != 0);
+    }
+  }
+}
+
+// Parameter-gradient partials of the generic path: block b sums its row
+// chunk for each column (threads stride over columns).  kind 0: d*x*ir
+// (rms_norm dgamma); kind 1: d*xhat and d (layer_norm dgamma, dbeta).
+template <typename T, int KIND>
+__global__ __launch_bounds__(GEN_BLOCK) void norm_partials_gen(
+    const void* d, int64_t ldd, const void* x, int64_t ldx, const float* st0, int64_t ld0,
+    const float* st1, int64_t ld1, float* part, int64_t R, int64_t C, int64_t rpb) {
+  const int64_t start = (int64_t)blockIdx.x * rpb, end = min(R, start + rpb);
+  constexpr int NP = KIND == 0 ? 1 : 2;
+  float* out = part + (int64_t)blockIdx.x * NP * C;
+  for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
+    float a = 0.f, b = 0.f;
+    for (int64_t r = start; r < end; ++r) {
+      const float dv = gl1<T>(d, r, ldd, c), xv = gl1<T>(x, r, ldx, c);
+      if (KIND == 0) a += dv * xv * st0[r * ld0];
+      else { a += dv * (xv - st0[r * ld0]) * st1[r * ld1]; b += dv; }
+    }
+    out[c] = a;
+    if (KIND == 1) out[C + c] = b;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void sm_fwd_gen(
+    const void* x, int64_t ldx, void* y, int64_t ldy, int64_t R, int64_t C, float alpha,
+    int causal, int seq_len) {
+  __shared__ float lds[GEN_BLOCK / WAVE];
+  const float NEG_INF = -__builtin_inff();
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;
+    float m = NEG_INF;
+    for (int64_t c = threadIdx.x; c < lim; c += GEN_BLOCK) m = fmaxf(m, alpha * gl1<T>(x, r, ldx, c));
+    m = group_max<GEN_BLOCK / WAVE>(m, lds);
+    float s = 0.f;
+    for (int64_t c = threadIdx.x; c < lim; c += GEN_BLOCK) s += fast_exp(alpha * gl1<T>(x, r, ldx, c) - m);
+    const float inv = 1.0f / group_sum<GEN_BLOCK / WAVE>(s, lds);
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
+      gs1<T>(y, r, ldy, c, c < lim ? fast_exp(alpha * gl1<T>(x, r, ldx, c) - m) * inv : 0.f, false);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void sm_bwd_gen(
+    const void* d, int64_t ldd, const void* y, int64_t ldy, void* dx, int64_t lddx, int acc,
+    int64_t R, int64_t C, float alpha) {
+  __shared__ float lds[GEN_BLOCK / WAVE];
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    float dot = 0.f;
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) dot += gl1<T>(d, r, ldd, c) * gl1<T>(y, r, ldy, c);
+    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds);
+    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
+      const float yv = gl1<T>(y, r, ldy, c);
+      gs1<T>(dx, r, lddx, c, alpha * yv * (gl1<T>(d, r, ldd, c) - dot), acc != 0);
+    }
+  }
+}
+
+// ============================================================ column sums
+// Second pass: out[c] (+)= sum_b part[b*stride + c] over b = 0..P-1 in a
+// fixed order (wave w takes b = w, w+16, ..., then the 16 wave sums are
+// added in wave order).  64 columns per block.
+__global__ __launch_bounds__(1024) void fold_columns(const float* __restrict__ part, int64_t P,
+                                                    int64_t stride, int64_t C,
+                                                    float* __restrict__ out, int acc) {
+  __shared__ float lds[16][64];
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const int64_t c = (int64_t)blockIdx.x * 64 + l;
+  float s = 0.f;
+  if (c < C)
+    for (int64_t b = w; b < P; b += 16) s += part[b * stride + c];
+  lds[w][l] = s;
+  __syncthreads();
+  if (w == 0 && c < C) {
+    float t = lds[0][l];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) t += lds[i][l];
+    out[c] = acc ? acc_add(out[c], t) : t;
+  }
+}
+
+// First pass of a plain column sum (add_bias backward): a 1024-thread block
+// holds TPC threads per row (one 16-byte pack each) and 1024/TPC row phases;
+// block (bx, by) covers packs [bx*TPC, ...) of rows [by*rpb, ...).  The row
+// phases are folded in LDS in phase order; one partial row per block row.
+template <typename T>
+__global__ __launch_bounds__(1024) void colsum_partials(
+    const void* __restrict__ d, int64_t ldd, int64_t R, int64_t C, int tpc, int64_t rpb,
+    float* __restrict__ part) {
+  constexpr int V = io<T>::VEC;
+  extern __shared__ float red[];                 // tpc * V floats
+  const int ph = threadIdx.x / tpc, t = threadIdx.x % tpc, nph = 1024 / tpc;
+  const int64_t c0 = ((int64_t)blockIdx.x * tpc + t) * V;
+  const int64_t start = (int64_t)blockIdx.y * rpb, end = min(R, start + rpb);
+  float a[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) a[k] = 0.f;
+  if (c0 < C) {
+    int64_t r = start + ph;
+    for (; r + 3 * nph < end; r += 4 * nph) {
+      float v0[V], v1[V], v2[V], v3[V];
+      load_pack<T>(row_ptr<T>(d, r, ldd), c0, C, v0, 0.f);
+      load_pack<T>(row_ptr<T>(d, r + nph, ldd), c0, C, v1, 0.f);
+      load_pack<T>(row_ptr<T>(d, r + 2 * nph, ldd), c0, C, v2, 0.f);
+      load_pack<T>(row_ptr<T>(d, r + 3 * nph, ldd), c0, C, v3, 0.f);
+#pragma unroll
+      for (int k = 0; k < V; ++k) a[k] += v0[k] + v1[k] + v2[k] + v3[k];
+    }
+    for (; r < end; r += nph) {
+      float v0[V];
+      load_pack<T>(row_ptr<T>(d, r, ldd), c0, C, v0, 0.f);
+#pragma unroll
+      for (int k = 0; k < V; ++k) a[k] += v0[k];
+    }
+  }
+  for (int p = 0; p < nph; ++p) {
+    if (ph == p)
+#pragma unroll
+      for (int k = 0; k < V; ++k) red[t * V + k] = (p == 0) ? a[k] : red[t * V + k] + a[k];
+    __syncthreads();
+  }
+  float* out = part + (int64_t)blockIdx.y * C;
+  for (int i = threadIdx.x; i < tpc * V; i += 1024) {
+    const int64_t c = (int64_t)blockIdx.x * tpc * V + i;
+    if (c < C) out[c] = red[i];
+  }
+}
+
+// Generic first pass for rows that are not 16-byte aligned: block y sums
+// its row chunk for every column (threads stride over columns).
+template <typename T>
+__global__ __launch_bounds__(GEN_BLOCK) void colsum_partials_gen(
+    const void* __restrict__ d, int64_t ldd, int64_t R, int64_t C, int64_t rpb,
+    float* __restrict__ part) {
+  const int64_t start = (int64_t)blockIdx.y * rpb, end = min(R, start + rpb);
+  for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
+    float a = 0.f;
+    for (int64_t r = start; r < end; ++r) a += gl1<T>(d, r, ldd, c);
+    part[(int64_t)blockIdx.y * C + c] = a;
+  }
+}
+
+__global__ void fill_f32_k(float* p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// ============================================================== dispatching
+int pick_rw(int rw_idx) { return rw_idx == 0 ? 1 : (rw_idx == 1 ? 4 : 16); }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_bwd(RowKind k) { return k == RK_RMS_BWD || k == RK_LN_BWD; }
+
+}  // namespace
+
+RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
+  RowPlan p{};
+  const int V = dtype == XT_F32 ? 4 : 8;
+  const int emax = is_bwd(kind) ? 16 : 32;
+  const int nvmax = emax / V;
+  const int64_t packs = cdiv(C, V);
+  p.fast = false;
+  if (aligned && C > 0) {
+    for (int i = 0; i < 3 && !p.fast; ++i) {
+      const int rw = pick_rw(i);
+      const int64_t need = cdiv(packs, (int64_t)WAVE * rw);
+      int nv = 1;
+      while (nv < need) nv *= 2;
+      if (nv <= nvmax && nv <= 8) { p.fast = true; p.rw = rw; p.nv = nv; }
+    }
+    // backward folds parameter partials in LDS: keep them within 64 KiB
+    const int np = kind == RK_LN_BWD ? 2 : 1;
+    if (is_bwd(kind) && (int64_t)np * C * 4 > 65536) p.fast = false;
+  }
+  if (p.fast) {
+    p.block = is_bwd(kind) ? BWD_BLOCK : (p.rw == 16 ? 1024 : 256);
+    p.groups = p.block / (WAVE * p.rw);
+    const int64_t gmax = is_bwd(kind) ? BWD_GRID_MAX : FWD_GRID_MAX;
+    p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(R, p.groups), gmax));
+  } else {
+    p.rw = 4; p.nv = 0; p.block = GEN_BLOCK; p.groups = 1;
+    p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(R, is_bwd(kind) ? BWD_GRID_MAX : FWD_GRID_MAX));
+  }
+  return p;
+}
+
+size_t row_bwd_workspace(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
+  if (R <= 0 || C <= 0) return 0;
+  const RowPlan p = plan_rows(kind, dtype, R, C, aligned);
+  const int np = kind == RK_LN_BWD ? 2 : 1;
+  return (size_t)p.grid * np * C * sizeof(float);
+}
+
+#define XT_ROW_SWITCH(T, P, ...)                                               \
+  do {                                                                       \
+    const int rw_ = (P).rw, nv_ = (P).nv;                                    \
+    if (rw_ == 1 && nv_ == 1) { constexpr int RW = 1, NV = 1; __VA_ARGS__; }        \
+    else if (rw_ == 1 && nv_ == 2) { constexpr int RW = 1, NV = 2; __VA_ARGS__; }   \
+    else if (rw_ == 1 && nv_ == 4) { constexpr int RW = 1, NV = 4; __VA_ARGS__; }   \
+    else if (rw_ == 1 && nv_ == 8) { constexpr int RW = 1, NV = 8; __VA_ARGS__; }   \
+    else if (rw_ == 4 && nv_ == 1) { constexpr int RW = 4, NV = 1; __VA_ARGS__; }   \
+    else if (rw_ == 4 && nv_ == 2) { constexpr int RW = 4, NV = 2; __VA_ARGS__; }   \
+    else if (rw_ == 4 && nv_ == 4) { constexpr int RW = 4, NV = 4; __VA_ARGS__; }   \
+    else if (rw_ == 4 && nv_ == 8) { constexpr int RW = 4, NV = 8; __VA_ARGS__; }   \
+    else if (rw_ == 16 && nv_ == 1) { constexpr int RW = 16, NV = 1; __VA_ARGS__; } \
+    else if (rw_ == 16 && nv_ == 2) { constexpr int RW = 16, NV = 2; __VA_ARGS__; } \
+    else if (rw_ == 16 && nv_ == 4) { constexpr int RW = 16, NV = 4; __VA_ARGS__; } \
+    else if (rw_ == 16 && nv_ == 8) { constexpr int RW = 16, NV = 8; __VA_ARGS__; } \
+    else return hipErrorInvalidValue;                                        \
+  } while (0)
+
+static bool aligned16(const xt_tensor& t) {
+  const int es = t.dtype == XT_F32 ? 4 : 2;
+  return (((uintptr_t)t.data) & 15) == 0 && ((t.ld * es) & 15) == 0;
+}
+
+template <typename T>
+static hipError_t rms_fwd_t(const xt_tensor& x, const float* gamma, const xt_tensor& y,
+                            const xt_tensor& ir, float eps, hipStream_t s) {
+  const int64_t R = x.rows, C = x.cols;
+  const float invC = 1.0f / (float)C;
+  const RowPlan p = plan_rows(RK_RMS_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
+  if (p.fast) {
+    XT_ROW_SWITCH(T, p, {
+      if (p.block == 256)
+        rms_fwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
+      else
+        rms_fwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
+    });
+  } else {
+    rms_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_fwd(const xt_tensor& x, const float* gamma, const xt_tensor& y,
+                          const xt_tensor& inv_rms, float eps, hipStream_t s) {
+  if (x.rows == 0) return hipSuccess;
+  return x.dtype == XT_F32 ? rms_fwd_t<float>(x, gamma, y, inv_rms, eps, s)
+                           : rms_fwd_t<bf16_t>(x, gamma, y, inv_rms, eps, s);
+}
+
+template <typename T>
+static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* gamma,
+                            const xt_tensor& ir, const xt_tensor* dx, bool acc_dx, float* dgamma,
+                            bool acc_dg, void* ws, hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  const float invC = 1.0f / (float)C;
+  const bool al = aligned16(d) && aligned16(x) && (!dx || aligned16(*dx));
+  const RowPlan p = plan_rows(RK_RMS_BWD, d.dtype, R, C, al);
+  float* part = dgamma ? (float*)ws : nullptr;
+  const int64_t rpb = cdiv(R, p.grid);
+  if (p.fast) {
+    const size_t shm = dgamma ? (size_t)C * sizeof(float) : 0;
+    XT_ROW_SWITCH(T, p, {
+      rms_bwd_fast<T, RW, NV><<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
+                                                             dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC, rpb);
+    });
+  } else {
+    if (dx)
+      rms_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld, dx->data, dx->ld, acc_dx, R, C, invC);
+    if (dgamma)
+      norm_partials_gen<T, 0><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)ir.data, ir.ld, nullptr, 0, part, R, C, rpb);
+  }
+  if (dgamma) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, C, C, dgamma, acc_dg);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
+                          const xt_tensor& inv_rms, const xt_tensor* dx, bool acc_dx,
+                          float* dgamma, bool acc_dgamma, void* ws, hipStream_t s) {
+  if (d.rows == 0) return hipSuccess;
+  return d.dtype == XT_F32 ? rms_bwd_t<float>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, s)
+                           : rms_bwd_t<bf16_t>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, s);
+}
+
+template <typename T>
+static hipError_t ln_fwd_t(const xt_tensor& x, const float* gamma, const float* beta,
+                           const xt_tensor& y, const xt_tensor& mean, const xt_tensor& rstd,
+                           float eps, hipStream_t s) {
+  const int64_t R = x.rows, C = x.cols;
+  const float invC = 1.0f / (float)C;
+  const RowPlan p = plan_rows(RK_LN_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
+  if (p.fast) {
+    XT_ROW_SWITCH(T, p, {
+      if (p.block == 256)
+        ln_fwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
+      else
+        ln_fwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
+    });
+  } else {
+    ln_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_fwd(const xt_tensor& x, const float* gamma, const float* beta,
+                         const xt_tensor& y, const xt_tensor& mean, const xt_tensor& rstd,
+                         float eps, hipStream_t s) {
+  if (x.rows == 0) return hipSuccess;
+  return x.dtype == XT_F32 ? ln_fwd_t<float>(x, gamma, beta, y, mean, rstd, eps, s)
+                           : ln_fwd_t<bf16_t>(x, gamma, beta, y, mean, rstd, eps, s);
+}
+
+template <typename T>
+static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* gamma,
+                           const xt_tensor& mean, const xt_tensor& rstd, const xt_tensor* dx,
+                           bool acc_dx, float* dgamma, bool acc_dg, float* dbeta, bool acc_db,
+                           void* ws, hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  const float invC = 1.0f / (float)C;
+  const bool al = aligned16(d) && aligned16(x) && (!dx || aligned16(*dx));
+  const RowPlan p = plan_rows(RK_LN_BWD, d.dtype, R, C, al);
+  const bool want_p = dgamma || dbeta;
+  float* part = want_p ? (float*)ws : nullptr;
+  const int64_t rpb = cdiv(R, p.grid);
+  if (p.fast) {
+    const size_t shm = want_p ? (size_t)2 * C * sizeof(float) : 0;
+    XT_ROW_SWITCH(T, p, {
+      ln_bwd_fast<T, RW, NV><<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
+                                                            (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr, dx ? dx->ld : 0,
+                                                            acc_dx, part, R, C, invC, rpb);
+    });
+  } else {
+    if (dx)
+      ln_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
+                                                 (const float*)rstd.data, rstd.ld, dx->data, dx->ld, acc_dx, R, C, invC);
+    if (want_p)
+      norm_partials_gen<T, 1><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)mean.data, mean.ld,
+                                                           (const float*)rstd.data, rstd.ld, part, R, C, rpb);
+  }
+  if (dgamma) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, 2 * C, C, dgamma, acc_dg);
+  if (dbeta) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part + C, p.grid, 2 * C, C, dbeta, acc_db);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
+                         const xt_tensor& mean, const xt_tensor& rstd,
+                         const xt_tensor* dx, bool acc_dx, float* dgamma, bool acc_dgamma,
+                         float* dbeta, bool acc_dbeta, void* ws, hipStream_t s) {
+  if (d.rows == 0) return hipSuccess;
+  return d.dtype == XT_F32
+             ? ln_bwd_t<float>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, s)
+             : ln_bwd_t<bf16_t>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, s);
+}
+
+template <typename T>
+static hipError_t sm_fwd_t(const xt_tensor& x, const xt_tensor& y, float alpha, int causal,
+                           int seq_len, hipStream_t s) {
+  const int64_t R = x.rows, C = x.cols;
+  const RowPlan p = plan_rows(RK_SM_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
+  if (p.fast) {
+    XT_ROW_SWITCH(T, p, {
+      if (p.block == 256)
+        sm_fwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
+      else
+        sm_fwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
+    });
+  } else {
+    sm_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_fwd(const xt_tensor& x, const xt_tensor& y, float alpha,
+                              int causal, int seq_len, hipStream_t s) {
+  if (x.rows == 0) return hipSuccess;
+  return x.dtype == XT_F32 ? sm_fwd_t<float>(x, y, alpha, causal, seq_len, s)
+                           : sm_fwd_t<bf16_t>(x, y, alpha, causal, seq_len, s);
+}
+
+template <typename T>
+static hipError_t sm_bwd_t(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx, bool acc,
+                           float alpha, hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  const RowPlan p = plan_rows(RK_SM_BWD, d.dtype, R, C, aligned16(d) && aligned16(y) && aligned16(dx));
+  if (p.fast) {
+    XT_ROW_SWITCH(T, p, {
+      if (p.block == 256)
+        sm_bwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
+      else
+        sm_bwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
+    });
+  } else {
+    sm_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx,
+                              bool acc, float alpha, hipStream_t s) {
+  if (d.rows == 0) return hipSuccess;
+  return d.dtype == XT_F32 ? sm_bwd_t<float>(d, y, dx, acc, alpha, s)
+                           : sm_bwd_t<bf16_t>(d, y, dx, acc, alpha, s);
+}
+
+// Column-sum geometry shared by the workspace query and the launch.
+struct ColsumPlan { int tpc; unsigned gx, gy; int64_t rpb; };
+
+static ColsumPlan colsum_plan(int dtype, int64_t R, int64_t C) {
+  const int V = dtype == XT_F32 ? 4 : 8;
+  const int64_t packs = cdiv(C, V);
+  int tpc = 64;
+  while (tpc < packs && tpc < 1024) tpc *= 2;
+  ColsumPlan p;
+  p.tpc = tpc;
+  p.gx = (unsigned)cdiv(packs, tpc);
+  const int64_t gy_max = std::max<int64_t>(1, 256 / (int64_t)p.gx);
+  p.gy = (unsigned)std::max<int64_t>(1, std::min<int64_t>(gy_max, cdiv(R, 1024 / tpc)));
+  p.rpb = cdiv(R, p.gy);
+  return p;
+}
+
+size_t colsum_workspace(int dtype, int64_t R, int64_t C) {
+  if (R <= 0 || C <= 0) return 0;
+  return (size_t)colsum_plan(dtype, R, C).gy * C * sizeof(float);
+}
+
+hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  if (C == 0) return hipSuccess;
+  if (R == 0) {
+    if (!acc) fill_f32_k<<<(unsigned)cdiv(C, 256), 256, 0, s>>>(out, C, 0.f);
+    return hipGetLastError();
+  }
+  const ColsumPlan p = colsum_plan(d.dtype, R, C);
+  float* part = (float*)ws;
+  const bool al = aligned16(d);
+  const int V = d.dtype == XT_F32 ? 4 : 8;
+  if (al) {
+    const size_t shm = (size_t)p.tpc * V * sizeof(float);
+    if (d.dtype == XT_F32)
+      colsum_partials<float><<<dim3(p.gx, p.gy), 1024, shm, s>>>(d.data, d.ld, R, C, p.tpc, p.rpb, part);
+    else
+      colsum_partials<bf16_t><<<dim3(p.gx, p.gy), 1024, shm, s>>>(d.data, d.ld, R, C, p.tpc, p.rpb, part);
+  } else {
+    if (d.dtype == XT_F32)
+      colsum_partials_gen<float><<<dim3(1, p.gy), GEN_BLOCK, 0, s>>>(d.data, d.ld, R, C, p.rpb, part);
+    else
+      colsum_partials_gen<bf16_t><<<dim3(1, p.gy), GEN_BLOCK, 0, s>>>(d.data, d.ld, R, C, p.rpb, part);
+  }
+  fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.gy, C, C, out, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  fill_f32_k<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 4096), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace xt

@@ -1,0 +1,250 @@
+/*
+ * xt.h -- C ABI of libxt.so: forward kernels, hand-derived backward kernels
+ * and a reverse-mode tape for the row-wise ops of a small transformer, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [AE] xtrain design document "Phase: Autograd Engine + Op Backward"
+ *        (docs/03-autograd-engine.md) -- sections "Module Layout",
+ *        "Tape 设计", "梯度累加（扇出求和）", the op-backward table
+ *        "各算子 backward 数学", the RMSNorm / RoPE / Softmax / Cross-entropy
+ *        derivations, "Attention 用组合".
+ *   [BP] "Träna en språkmodell: Backprop i anpassad CUDA" -- the kernel-pair
+ *        table "Varje Forward-op Får En Backward-tvilling",
+ *        "En baklängeskärnas uppgift", "Sparade tensorer",
+ *        "Ackumulation över mikrobatcher".
+ *   [DO] xtrain design document "Phase T18: Dropout (device RNG + mask)"
+ *        (docs/17-dropout.md) -- "Module Layout" (dropout_mask_apply /
+ *        dropout_apply_mask), "RNG：counter-based", "dropout 节点的 backward".
+ *
+ * Conventions for every entry point
+ *   - All calls are made from the host.  Kernels are enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream) and the call returns without
+ *     synchronising.  Device buffers must stay alive until the stream has
+ *     passed the kernels.
+ *   - Every pointer inside an xt_tensor is a DEVICE pointer owned by the
+ *     caller.  The op entry points allocate nothing and keep no pointer
+ *     after they return.  Workspace is caller-provided (xt_workspace_bytes).
+ *   - Argument, shape, dtype and workspace problems are detected on the
+ *     host before anything is launched: the call returns a nonzero
+ *     xt_status and launches nothing.  xt_last_error() then holds a
+ *     thread-local text naming the problem.  A failed launch returns
+ *     XT_ERR_HIP.  No C++ exception crosses this ABI.
+ *   - Data-dependent problems are not detected on the host: a
+ *     cross-entropy target outside [0, cols) gives that row a NaN loss and
+ *     a NaN gradient row (so the mean loss is NaN).
+ *   - Rows = 0 is a valid no-op.  Every function is re-entrant.
+ */
+#ifndef XT_H
+#define XT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XT_OK = 0,
+  XT_ERR_INVALID_ARG = 1,   /* null pointer, bad parameter value, bad count */
+  XT_ERR_SHAPE = 2,         /* shapes do not agree, ld < cols, ...          */
+  XT_ERR_DTYPE = 3,         /* dtype combination not supported              */
+  XT_ERR_UNSUPPORTED = 4,   /* valid request this build does not implement  */
+  XT_ERR_WORKSPACE = 5,     /* workspace missing or too small               */
+  XT_ERR_HIP = 6,           /* a HIP runtime call or launch failed          */
+  XT_ERR_ALLOC = 7          /* the tape's allocator callback returned NULL  */
+} xt_status;
+
+typedef enum { XT_F32 = 0, XT_BF16 = 1, XT_I32 = 2, XT_U8 = 3 } xt_dtype;
+
+/*
+ * A caller-owned device view, row-major: element (r, c) of batch (i, j)
+ * lives at data + i*sb[0] + j*sb[1] + r*ld + c  (all in elements).
+ * Unbatched views use nb = {1, 1}, sb = {0, 0}; only MATMUL reads nb/sb.
+ * bf16 is the upper half of an IEEE binary32 (round-to-nearest-even).
+ */
+typedef struct {
+  void*   data;
+  int32_t dtype;        /* xt_dtype */
+  int32_t reserved;     /* must be 0 */
+  int64_t rows, cols;
+  int64_t ld;           /* >= cols */
+  int64_t nb[2];        /* batch extents */
+  int64_t sb[2];        /* batch strides */
+} xt_tensor;
+
+typedef enum {
+  XT_OP_MATMUL = 0,        /* C = alpha * op(A) op(B)                      */
+  XT_OP_ADD = 1,           /* y = a + b                                    */
+  XT_OP_MUL = 2,           /* y = a * b (elementwise)                      */
+  XT_OP_SCALE = 3,         /* y = alpha * x                                */
+  XT_OP_ADD_BIAS = 4,      /* y[r,c] = x[r,c] + bias[c]                    */
+  XT_OP_RMS_NORM = 5,      /* y = x * inv_rms * gamma                      */
+  XT_OP_LAYER_NORM = 6,    /* y = (x - mean) * rstd * gamma + beta         */
+  XT_OP_SOFTMAX = 7,       /* y = softmax(alpha * x) per row (+ causal)    */
+  XT_OP_CROSS_ENTROPY = 8, /* L = mean_r(lse_r - x[r, t_r])                */
+  XT_OP_SILU = 9,          /* y = x * sigmoid(x)                           */
+  XT_OP_SWIGLU = 10,       /* y = silu(g) * u                              */
+  XT_OP_GELU = 11,         /* y = x * Phi(x) (exact, erf form)             */
+  XT_OP_ROPE = 12,         /* rotate-half rotary embedding                 */
+  XT_OP_DROPOUT = 13,      /* counter-based inverted dropout               */
+  XT_OP_COUNT = 14
+} xt_op;
+
+typedef struct {
+  float    eps;        /* RMS_NORM, LAYER_NORM: added to the mean square /
+                          variance inside the square root (e.g. 1e-5)        */
+  float    alpha;      /* SCALE factor; SOFTMAX pre-scale; MATMUL scale      */
+  int32_t  causal;     /* SOFTMAX: 1 = column c > (row mod seq_len) excluded  */
+  int32_t  seq_len;    /* SOFTMAX causal and ROPE: position = row mod seq_len */
+  int32_t  head_dim;   /* ROPE: even head width; cols must be a multiple     */
+  float    rope_base;  /* ROPE: theta(pos, i) = pos * base^(-2i/head_dim)    */
+  float    p;          /* DROPOUT: drop probability, 0 <= p < 1              */
+  int32_t  reserved0;  /* must be 0 */
+  uint64_t seed;       /* DROPOUT: 64-bit counter-RNG seed                   */
+  int32_t  trans_a;    /* MATMUL: read A transposed                          */
+  int32_t  trans_b;    /* MATMUL: read B transposed                          */
+} xt_params;
+
+/*
+ * Per-op tensor lists (in = inputs, out = out[0] result + saved tensors,
+ * din = one gradient per input; a din with data == NULL is not computed).
+ *
+ *  op            in                 out (fwd)                    din (bwd)
+ *  MATMUL        A, B               C                            dA, dB
+ *  ADD           a, b               y                            da, db
+ *  MUL           a, b               y                            da, db
+ *  SCALE         x                  y                            dx
+ *  ADD_BIAS      x, bias[1,C] f32   y                            dx, dbias
+ *  RMS_NORM      x, gamma[1,C] f32  y, inv_rms[R,1] f32          dx, dgamma
+ *  LAYER_NORM    x, gamma, beta     y, mean[R,1], rstd[R,1] f32  dx, dgamma, dbeta
+ *  SOFTMAX       x                  y (y is also what bwd saves) dx
+ *  CROSS_ENTROPY logits, targets    L[1,1], lse[R,1], loss_row[R,1] (all f32)
+ *                [R,1] i32                                       dlogits (+ a
+ *                                                                NULL slot for targets)
+ *  SILU, GELU    x                  y                            dx
+ *  SWIGLU        g, u               y                            dg, du
+ *  ROPE          x                  y                            dx
+ *  DROPOUT       x                  y, mask[R,C] u8 (1 = keep)   dx
+ *
+ * Backward "saved" lists: MATMUL none (reads in); RMS_NORM {inv_rms};
+ * LAYER_NORM {mean, rstd}; SOFTMAX {y}; CROSS_ENTROPY {lse}; DROPOUT {mask};
+ * every other op none.  `dout` is the gradient of out[0] (for
+ * CROSS_ENTROPY: a device f32[1,1] holding dL).
+ *
+ * dtypes: activations, their gradients and matmul operands are f32 or bf16
+ * (all of one op's activation tensors share one dtype, except MATMUL's
+ * outputs/gradients which may each be f32 or bf16); arithmetic is f32.
+ * gamma/beta/bias and their gradients, and all row statistics, are f32.
+ */
+
+/* Bytes of workspace xt_op_fwd (is_bwd = 0) or xt_op_bwd (is_bwd = 1) needs
+ * for these inputs; 0 if none.  Ops that need workspace: the backward of
+ * RMS_NORM, LAYER_NORM and ADD_BIAS (per-block partial parameter
+ * gradients, summed by a fixed-order second pass). */
+size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm,
+                          const xt_tensor* in, int n_in);
+
+/* Forward of `op`: reads in[0..n_in), writes out[0..n_out).
+ *   [AE] op-backward table (forward column) for matmul, add, mul, add_bias,
+ *   scale, rms_norm, silu, swiglu, rope, softmax, cross_entropy; [BP] kernel
+ *   pairs for layer_norm, the GELU MLP and the residual add; [DO] for
+ *   dropout (the mask is written to out[1]).
+ * CROSS_ENTROPY writes L = (1/R) sum_r loss_row[r] by a fixed-order second
+ * pass, so results are bitwise reproducible. */
+xt_status xt_op_fwd(xt_op op, const xt_params* prm,
+                    const xt_tensor* in, int n_in,
+                    const xt_tensor* out, int n_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of `op`: given dout, the forward inputs and the saved tensors,
+ * writes each wanted din[k].  Bit k of `accumulate` selects din[k] += grad
+ * (one rounding into din's dtype) instead of din[k] = grad -- [BP]
+ * "Ackumulation över mikrobatcher" (backward kernels add into the gradient
+ * buffers) and [AE] "梯度累加" (fan-out sums).  Parameter gradients of
+ * RMS_NORM / LAYER_NORM / ADD_BIAS come out of the same launch as dx as
+ * per-block partials ([BP] "En baklängeskärnas uppgift"), then a
+ * fixed-order second pass sums them: results are bitwise reproducible.
+ * Two din entries must not alias each other or any input. */
+xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
+                    const xt_tensor* in, int n_in,
+                    const xt_tensor* saved, int n_saved,
+                    const xt_tensor* din, int n_din, uint32_t accumulate,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* dst += src elementwise, in place (f32 arithmetic, one rounding into dst's
+ * dtype).  dst and src have the same shape; dtypes may differ.
+ * [AE] "梯度累加（扇出求和）": the accumulate of push_grad. */
+xt_status xt_grad_accumulate(const xt_tensor* dst, const xt_tensor* src, void* stream);
+
+/* Writes the u8 dropout mask (1 = keep) of a tensor of mask's shape:
+ * element (r, c) uses counter i = r*cols + c; keep iff
+ * (splitmix64(seed ^ i*0x9E3779B97F4A7C15) >> 40) * 2^-24 >= p (f32).
+ * [DO] "RNG：counter-based".  0 <= p < 1, mask dtype XT_U8. */
+xt_status xt_dropout_mask(const xt_tensor* mask, float p, uint64_t seed, void* stream);
+
+const char* xt_status_str(xt_status s);
+const char* xt_last_error(void);    /* thread-local detail of the last failure */
+int         xt_abi_version(void);   /* 1 */
+
+/* ------------------------------------------------------------------------
+ * Tape: define-by-run reverse mode over the ops above.
+ * [AE] "Tape 设计": each op records a node (parents + what its backward
+ * needs); backward() builds a post-order DFS topological order from the
+ * loss (deduplicated by node), seeds the one-element loss with 1 and visits
+ * the order in reverse; [AE] "梯度累加": every contribution that reaches a
+ * node is summed, also when one op uses the same node twice (mul(x, x)
+ * pushes twice; the node is visited once).
+ *
+ * Memory: the tape allocates node values, saved tensors, gradients and
+ * workspace only through the caller's callbacks (alloc(ctx, bytes, stream)
+ * returns a device pointer or NULL; free(ctx, ptr, stream) releases it in
+ * stream order).  Leaf values are caller views; they must outlive the tape.
+ * Gradients of leaves accumulate across backward() calls until
+ * xt_tape_zero_grad ([BP] "Ackumulation över mikrobatcher").
+ * Functions returning xt_var return a negative value -(xt_status) on error.
+ * A tape is not thread-safe.
+ * ---------------------------------------------------------------------- */
+typedef struct xt_tape xt_tape;
+typedef int64_t xt_var;
+typedef void* (*xt_alloc_fn)(void* ctx, size_t bytes, void* stream);
+typedef void  (*xt_free_fn)(void* ctx, void* ptr, void* stream);
+
+xt_tape*  xt_tape_create(xt_alloc_fn alloc, xt_free_fn free_fn, void* ctx, void* stream);
+void      xt_tape_destroy(xt_tape* t);
+/* A leaf over a caller view (not copied).  requires_grad = 0 for inputs that
+ * get no gradient (e.g. cross-entropy targets). */
+xt_var    xt_tape_leaf(xt_tape* t, const xt_tensor* value, int requires_grad);
+/* Record one op on the parents (in the op's input order); the result is a
+ * fresh dense tensor of the op's output shape (MATMUL with batch extents:
+ * [nb0, nb1, M, N] contiguous). */
+xt_var    xt_tape_apply(xt_tape* t, xt_op op, const xt_params* prm,
+                        const xt_var* parents, int n_parents);
+/* As xt_tape_apply, but the output is laid out by `layout` (data ignored;
+ * rows, cols, ld, nb, sb, dtype used) in a fresh buffer spanning it -- e.g.
+ * a batched attention product written straight into a [B*S, H*Dh] matrix. */
+xt_var    xt_tape_apply_layout(xt_tape* t, xt_op op, const xt_params* prm,
+                               const xt_var* parents, int n_parents,
+                               const xt_tensor* layout);
+/* A node that re-reads `parent`'s buffer through another layout that covers
+ * the same elements exactly once (e.g. [B*S, H*Dh] as B x H heads of
+ * [S, Dh]).  Its gradient is the parent's gradient seen through the layout.
+ * layout->data is an element offset into the parent buffer (cast to a
+ * pointer, usually 0). */
+xt_var    xt_tape_view(xt_tape* t, xt_var parent, const xt_tensor* layout);
+xt_status xt_tape_value(xt_tape* t, xt_var v, xt_tensor* out_view);
+/* Extra forward outputs of a node (RMS_NORM inv_rms, CROSS_ENTROPY lse and
+ * loss_row, DROPOUT mask, ...): index k of the op's out list, k >= 1. */
+xt_status xt_tape_saved(xt_tape* t, xt_var v, int k, xt_tensor* out_view);
+/* Reverse pass from a one-element loss (seeded with 1). */
+xt_status xt_tape_backward(xt_tape* t, xt_var loss);
+/* View of v's gradient; data == NULL if no gradient reached v. */
+xt_status xt_tape_grad(xt_tape* t, xt_var v, xt_tensor* out_view);
+xt_status xt_tape_zero_grad(xt_tape* t);
+int64_t   xt_tape_num_nodes(const xt_tape* t);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XT_H */
