@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxt.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built: run `python -m autograd_row_wise_amd.build` "
+        f"{LIB_PATH} is not built: run `python autograd_row_wise_amd/build.py` "
         "(or __graft_entry__.build()); there is no non-HIP fallback")
 
 lib = C.CDLL(LIB_PATH)
@@ -96,6 +96,8 @@ lib.xt_tape_saved.restype = C.c_int
 lib.xt_tape_saved.argtypes = [C.c_void_p, C.c_int64, C.c_int, _TP]
 lib.xt_tape_backward.restype = C.c_int
 lib.xt_tape_backward.argtypes = [C.c_void_p, C.c_int64]
+lib.xt_tape_backward_seeded.restype = C.c_int
+lib.xt_tape_backward_seeded.argtypes = [C.c_void_p, C.c_int64, _TP]
 lib.xt_tape_zero_grad.restype = C.c_int
 lib.xt_tape_zero_grad.argtypes = [C.c_void_p]
 lib.xt_tape_num_nodes.restype = C.c_int64
@@ -298,6 +300,9 @@ class Tape:
 
     def backward(self, loss: int) -> None:
         _check(lib.xt_tape_backward(self.h, loss), "xt_tape_backward")
+
+    def backward_seeded(self, out: int, dout: Tensor) -> None:
+        _check(lib.xt_tape_backward_seeded(self.h, out, C.byref(dout)), "xt_tape_backward_seeded")
 
     def zero_grad(self) -> None:
         _check(lib.xt_tape_zero_grad(self.h), "xt_tape_zero_grad")

@@ -1,6 +1,6 @@
 """Build libxt.so (HIP kernels + C ABI + tape) for gfx950 with hipcc.
 
-    python -m autograd_row_wise_amd.build          # writes autograd_row_wise_amd/libxt.so
+    python autograd_row_wise_amd/build.py      # writes autograd_row_wise_amd/libxt.so
 
 Every source is compiled every time (in parallel), then linked.  The packed
 FP32 target feature is turned off for all device code (hipcc's host pass

@@ -67,25 +67,31 @@ __global__ __launch_bounds__(CE_BLOCK) void ce_fwd_k(
       else s += exp2_(t - m);
     };
     for (int64_t c = threadIdx.x; c < head; c += CE_BLOCK) push(io<T>::ld(row + c));
-    // aligned body: two packs per thread per iteration
-    int64_t p = threadIdx.x;
-    for (; p + CE_BLOCK < bp; p += 2 * CE_BLOCK) {
-      float a[V], b[V];
-      io<T>::unpack(reinterpret_cast<const uint4*>(body)[p], a);
-      io<T>::unpack(reinterpret_cast<const uint4*>(body)[p + CE_BLOCK], b);
-      float pm = a[0];
+    // aligned body: four packs per thread in flight per iteration
+    const uint4* bq = reinterpret_cast<const uint4*>(body);
+    int p = threadIdx.x;
+    const int bpi = (int)bp;
+    for (; p + 3 * CE_BLOCK < bpi; p += 4 * CE_BLOCK) {
+      float a[4][V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) pm = fmaxf(pm, fmaxf(a[k], b[k]));
+      for (int u = 0; u < 4; ++u) io<T>::unpack(bq[p + u * CE_BLOCK], a[u]);
+      float pm = a[0][0];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < V; ++k) pm = fmaxf(pm, a[u][k]);
       const float t = pm * LOG2E;
       if (t > m) { s *= exp2_(m - t); m = t; }
       float acc = 0.f;
 #pragma unroll
-      for (int k = 0; k < V; ++k) acc += exp2_(fmaf(a[k], LOG2E, -m)) + exp2_(fmaf(b[k], LOG2E, -m));
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < V; ++k) acc += exp2_(fmaf(a[u][k], LOG2E, -m));
       s += acc;
     }
-    for (; p < bp; p += CE_BLOCK) {
+    for (; p < bpi; p += CE_BLOCK) {
       float a[V];
-      io<T>::unpack(reinterpret_cast<const uint4*>(body)[p], a);
+      io<T>::unpack(bq[p], a);
       float pm = a[0];
 #pragma unroll
       for (int k = 1; k < V; ++k) pm = fmaxf(pm, a[k]);
@@ -142,50 +148,69 @@ __global__ __launch_bounds__(CE_BLOCK) void ce_bwd_k(
     const int32_t* __restrict__ tgt, int64_t ldt, const float* __restrict__ lse, int64_t ldl,
     void* __restrict__ dx, int64_t lddx, int acc, int64_t R, int64_t V_) {
   constexpr int V = io<T>::VEC;
+  constexpr int U = 4;                         // packs in flight per thread
   const float scale = dL[0] / (float)R;
+  const int n = (int)V_;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const T* row = reinterpret_cast<const T*>(logits) + r * ld;
     T* orow = reinterpret_cast<T*>(dx) + r * lddx;
     const int32_t t = tgt[r * ldt];
-    const bool ok = t >= 0 && t < V_;
+    const bool ok = t >= 0 && t < n;
+    // p = exp(x - lse) = 2^(x*log2e - lse*log2e); a bad target poisons the row
     const float nl = ok ? lse[r * ldl] * LOG2E : __builtin_nanf("");
-    auto val = [&](float x, int64_t c) {
+    auto val = [&](float x, int c) {
       const float p = exp2_(fmaf(x, LOG2E, -nl));
       return (c == t ? p - 1.f : p) * scale;
     };
-    int64_t head, bp;
-    split_row<T>(row, V_, head, bp);
+    auto put = [&](int c) {
+      const float v = val(io<T>::ld(row + c), c);
+      io<T>::st(orow + c, acc ? acc_add(io<T>::ld(orow + c), v) : v);
+    };
+    int64_t head64, bp64;
+    split_row<T>(row, V_, head64, bp64);
+    const int head = (int)head64, bp = (int)bp64;
     if (((((uintptr_t)row) ^ ((uintptr_t)orow)) & 15) != 0) {      // misaligned pair: scalar row
-      for (int64_t c = threadIdx.x; c < V_; c += CE_BLOCK) {
-        const float v = val(io<T>::ld(row + c), c);
-        io<T>::st(orow + c, acc ? acc_add(io<T>::ld(orow + c), v) : v);
-      }
+      for (int c = threadIdx.x; c < n; c += CE_BLOCK) put(c);
       continue;
     }
-    for (int64_t c = threadIdx.x; c < head; c += CE_BLOCK) {
-      const float v = val(io<T>::ld(row + c), c);
-      io<T>::st(orow + c, acc ? acc_add(io<T>::ld(orow + c), v) : v);
-    }
+    for (int c = threadIdx.x; c < head; c += CE_BLOCK) put(c);
     const uint4* body = reinterpret_cast<const uint4*>(row + head);
     uint4* obody = reinterpret_cast<uint4*>(orow + head);
-    for (int64_t p = threadIdx.x; p < bp; p += CE_BLOCK) {
-      float a[V];
-      io<T>::unpack(body[p], a);
-      const int64_t c0 = head + p * V;
+    // packs p, p+B, ..., p+(U-1)B: all loads are issued before any store
+    for (int p0 = threadIdx.x; p0 < bp; p0 += U * CE_BLOCK) {
+      uint4 q[U], o[U];
 #pragma unroll
-      for (int k = 0; k < V; ++k) a[k] = val(a[k], c0 + k);
-      if (acc) {
-        float o[V];
-        io<T>::unpack(obody[p], o);
-#pragma unroll
-        for (int k = 0; k < V; ++k) a[k] = acc_add(o[k], a[k]);
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * CE_BLOCK;
+        if (p < bp) {
+          q[u] = body[p];
+          if (acc) o[u] = obody[p];
+        }
       }
-      obody[p] = io<T>::pack(a);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * CE_BLOCK;
+        if (p >= bp) break;
+        float a[V];
+        io<T>::unpack(q[u], a);
+#pragma unroll
+        for (int k = 0; k < V; ++k) a[k] = exp2_(fmaf(a[k], LOG2E, -nl)) * scale;
+        const int c0 = head + p * V;
+        if ((unsigned)(t - c0) < (unsigned)V) {     // this pack holds the target column
+#pragma unroll
+          for (int k = 0; k < V; ++k)
+            if (c0 + k == t) a[k] = (exp2_(fmaf(io<T>::ld(row + t), LOG2E, -nl)) - 1.f) * scale;
+        }
+        if (acc) {
+          float b[V];
+          io<T>::unpack(o[u], b);
+#pragma unroll
+          for (int k = 0; k < V; ++k) a[k] = acc_add(b[k], a[k]);
+        }
+        obody[p] = io<T>::pack(a);
+      }
     }
-    for (int64_t c = head + bp * V + threadIdx.x; c < V_; c += CE_BLOCK) {
-      const float v = val(io<T>::ld(row + c), c);
-      io<T>::st(orow + c, acc ? acc_add(io<T>::ld(orow + c), v) : v);
-    }
+    for (int c = head + bp * V + threadIdx.x; c < n; c += CE_BLOCK) put(c);
   }
 }
 

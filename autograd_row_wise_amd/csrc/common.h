@@ -18,12 +18,17 @@ constexpr int WAVE = 64;
 // ---------------------------------------------------------------- bf16 <-> f32
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Round-to-nearest-even, NaN kept quiet.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two f32 -> packed bf16 pair (low = a), round-to-nearest-even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f2bf(float f) { return f2bf2(f, 0.f) & 0xffffu; }
 
 // Accumulating add that the compiler may not fuse with a preceding multiply:
 // a gradient contribution is rounded to f32 first, then added (one rounding
@@ -61,8 +66,7 @@ template <> struct io<bf16_t> {
     f[6] = __uint_as_float(q.w << 16); f[7] = __uint_as_float(q.w & 0xffff0000u);
   }
   __device__ static __forceinline__ uint4 pack(const float* f) {
-    return make_uint4(f2bf(f[0]) | (f2bf(f[1]) << 16), f2bf(f[2]) | (f2bf(f[3]) << 16),
-                      f2bf(f[4]) | (f2bf(f[5]) << 16), f2bf(f[6]) | (f2bf(f[7]) << 16));
+    return make_uint4(f2bf2(f[0], f[1]), f2bf2(f[2], f[3]), f2bf2(f[4], f[5]), f2bf2(f[6], f[7]));
   }
 };
 
@@ -91,6 +95,37 @@ __device__ __forceinline__ void store_pack(T* row, int64_t c0, int64_t n, const 
       if (c0 + k < n) io<T>::st(row + c0 + k, f[k]);
   }
 }
+
+// Raw 16-byte pack at column c0 (valid columns < n); a partial pack is read
+// element by element with zero fill.  Callers mask columns >= n themselves
+// where zero is not neutral.
+template <typename T>
+__device__ __forceinline__ uint4 load_raw(const T* row, int64_t c0, int64_t n) {
+  constexpr int V = io<T>::VEC;
+  if (c0 + V <= n) return *reinterpret_cast<const uint4*>(row + c0);
+  T tmp[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) tmp[k] = (c0 + k < n) ? row[c0 + k] : (T)0;
+  return *reinterpret_cast<const uint4*>(tmp);
+}
+
+// A row slice held as raw packs: pack j of group lane gl covers columns
+// [(j*G + gl)*VEC, +VEC).
+template <typename T, int NV, int G>
+struct RowPacks {
+  uint4 q[NV];
+  __device__ __forceinline__ void load(const T* row, int gl, int64_t C, bool active) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c0 = (int64_t)(j * G + gl) * io<T>::VEC;
+      q[j] = (active && c0 < C) ? load_raw<T>(row, c0, C) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void unpack(float (&f)[NV][io<T>::VEC]) const {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) io<T>::unpack(q[j], f[j]);
+  }
+};
 
 // Store with optional in-place accumulation (dst += v, one rounding).
 template <typename T>

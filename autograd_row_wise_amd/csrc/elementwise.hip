@@ -91,32 +91,74 @@ struct EwK {
 
 // T: activation/output dtype; TS: dtype of in[0] (only differs for the
 // accumulate, whose source may be f32 or bf16).
-template <typename T, typename TS, int OP>
+// Raw storage of N elements of type TS (one or two 16-byte packs, or 8 bytes).
+template <typename TS, int N>
+struct RawN {
+  static constexpr int WORDS = (N * (int)sizeof(TS) + 15) / 16;
+  uint4 w[WORDS];
+  __device__ __forceinline__ void load(const TS* row, int64_t c0, int64_t C) {
+    if (c0 + N <= C) {
+      if constexpr (N * sizeof(TS) == 8) {
+        const uint2 q = *reinterpret_cast<const uint2*>(row + c0);
+        w[0] = make_uint4(q.x, q.y, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) w[i] = reinterpret_cast<const uint4*>(row + c0)[i];
+      }
+    } else {
+      TS tmp[WORDS * 16 / sizeof(TS)];
+#pragma unroll
+      for (int k = 0; k < N; ++k) tmp[k] = (c0 + k < C) ? row[c0 + k] : (TS)0;
+#pragma unroll
+      for (int i = 0; i < WORDS; ++i) w[i] = reinterpret_cast<const uint4*>(tmp)[i];
+    }
+  }
+  __device__ __forceinline__ void unpack(float* f) const {
+    if constexpr (N * sizeof(TS) == 8) {
+      f[0] = __uint_as_float(w[0].x << 16); f[1] = __uint_as_float(w[0].x & 0xffff0000u);
+      f[2] = __uint_as_float(w[0].y << 16); f[3] = __uint_as_float(w[0].y & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WORDS; ++i) io<TS>::unpack(w[i], f + i * io<TS>::VEC);
+    }
+  }
+};
+
+// ACC: bit o set = out[o] is accumulated into (compile-time, so the old
+// values occupy registers only when needed).  The EW_UNROLL packs of a
+// thread are all loaded (raw) before any is computed or stored.
+template <typename T, typename TS, int OP, int ACC>
 __global__ __launch_bounds__(EW_BLOCK) void ew_vec_k(EwK a) {
   constexpr int V = io<T>::VEC, NI = n_in<OP>(), NO = n_out<OP>();
   const int64_t ppr = (a.C + V - 1) / V;
   for (int64_t r = blockIdx.y; r < a.R; r += gridDim.y) {
     for (int64_t pb = (int64_t)blockIdx.x * EW_BLOCK * EW_UNROLL; pb < ppr; pb += (int64_t)gridDim.x * EW_BLOCK * EW_UNROLL) {
+      RawN<TS, V> in0[EW_UNROLL];
+      RawN<T, V> inr[EW_UNROLL][NI > 1 ? NI - 1 : 1];
+      RawN<T, V> old[EW_UNROLL][(ACC != 0) ? NO : 1];
+#pragma unroll
+      for (int u = 0; u < EW_UNROLL; ++u) {
+        const int64_t p = pb + u * EW_BLOCK + threadIdx.x;
+        if (p >= ppr) continue;
+        const int64_t c0 = p * V;
+        in0[u].load(reinterpret_cast<const TS*>(a.in[0]) + r * a.ldi[0], c0, a.C);
+#pragma unroll
+        for (int i = 1; i < NI; ++i) inr[u][i - 1].load(reinterpret_cast<const T*>(a.in[i]) + r * a.ldi[i], c0, a.C);
+        if constexpr (ACC != 0) {
+#pragma unroll
+          for (int o = 0; o < NO; ++o)
+            if (((ACC >> o) & 1) && a.out[o]) old[u][o].load(reinterpret_cast<const T*>(a.out[o]) + r * a.ldo[o], c0, a.C);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < EW_UNROLL; ++u) {
         const int64_t p = pb + u * EW_BLOCK + threadIdx.x;
         if (p >= ppr) break;
         const int64_t c0 = p * V;
-        const bool full = c0 + V <= a.C;
         float vin[3][V], vout[2][V];
+        in0[u].unpack(vin[0]);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i == 0 && !__is_same(TS, T)) {
-            const TS* row = reinterpret_cast<const TS*>(a.in[0]) + r * a.ldi[0];
-            if (full) load_n<TS, V>(row + c0, vin[0]);
-            else
-#pragma unroll
-              for (int k = 0; k < V; ++k) vin[0][k] = c0 + k < a.C ? io<TS>::ld(row + c0 + k) : 0.f;
-          } else {
-            const T* row = reinterpret_cast<const T*>(a.in[i]) + r * a.ldi[i];
-            load_pack<T>(row, c0, a.C, vin[i], 0.f);
-          }
-        }
+        for (int i = 1; i < NI; ++i) inr[u][i - 1].unpack(vin[i]);
         float colv[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) colv[k] = 0.f;
@@ -138,8 +180,16 @@ __global__ __launch_bounds__(EW_BLOCK) void ew_vec_k(EwK a) {
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
           if (!a.out[o]) continue;
+          if constexpr (ACC != 0) {
+            if ((ACC >> o) & 1) {
+              float ov[V];
+              old[u][o].unpack(ov);
+#pragma unroll
+              for (int k = 0; k < V; ++k) vout[o][k] = acc_add(ov[k], vout[o][k]);
+            }
+          }
           T* row = reinterpret_cast<T*>(a.out[o]) + r * a.ldo[o];
-          store_pack_acc<T>(row, c0, a.C, vout[o], (OP == EW_ACCUMULATE) || ((a.acc >> o) & 1u));
+          store_pack<T>(row, c0, a.C, vout[o]);
         }
       }
     }
@@ -182,83 +232,103 @@ __device__ __forceinline__ uint32_t splitmix_top24(uint64_t key) {
   return (uint32_t)(z >> 40);
 }
 
+__device__ __forceinline__ void unpack_mask(const uint8_t* mr, int64_t c0, int64_t C, int V, bool vec,
+                                            uint8_t* m) {
+  if (vec && V == 8 && c0 + 8 <= C) {
+    const uint2 q = *reinterpret_cast<const uint2*>(mr);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { m[k] = (q.x >> (8 * k)) & 0xff; m[k + 4] = (q.y >> (8 * k)) & 0xff; }
+  } else if (vec && V == 4 && c0 + 4 <= C) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(mr);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m[k] = (q >> (8 * k)) & 0xff;
+  } else {
+    for (int k = 0; k < V; ++k) m[k] = c0 + k < C ? mr[k] : 0;
+  }
+}
+
+__device__ __forceinline__ void store_mask(uint8_t* mr, int64_t c0, int64_t C, int V, bool vec,
+                                           const uint8_t* m) {
+  if (vec && V == 8 && c0 + 8 <= C) {
+    uint2 q;
+    q.x = m[0] | (m[1] << 8) | (m[2] << 16) | ((uint32_t)m[3] << 24);
+    q.y = m[4] | (m[5] << 8) | (m[6] << 16) | ((uint32_t)m[7] << 24);
+    *reinterpret_cast<uint2*>(mr) = q;
+  } else if (vec && V == 4 && c0 + 4 <= C) {
+    *reinterpret_cast<uint32_t*>(mr) = m[0] | (m[1] << 8) | (m[2] << 16) | ((uint32_t)m[3] << 24);
+  } else {
+    for (int k = 0; k < V; ++k) if (c0 + k < C) mr[k] = m[k];
+  }
+}
+
 // MODE 0: forward (y, optional mask); MODE 1: mask only; MODE 2: backward
-// (dx = mask ? d*scale : 0).
-template <typename T, int MODE, bool VEC>
+// (dx = mask ? d*scale : 0).  Each thread handles DU packs per iteration,
+// issuing every load before any store.
+constexpr int DU = EW_UNROLL;
+template <typename T, int MODE, bool VEC, bool ACC>
 __global__ __launch_bounds__(EW_BLOCK) void dropout_k(
     const void* __restrict__ x, int64_t ldx, void* __restrict__ y, int64_t ldy,
-    uint8_t* __restrict__ mask, int64_t ldm, int acc, int64_t R, int64_t C, int64_t Clog,
+    uint8_t* __restrict__ mask, int64_t ldm, int64_t R, int64_t C, int64_t Clog,
     int64_t r0log, uint32_t thr, float scale, uint64_t seed) {
   constexpr int V = VEC ? io<T>::VEC : 1;
   const int64_t ppr = (C + V - 1) / V;
   for (int64_t r = blockIdx.y; r < R; r += gridDim.y) {
-    for (int64_t p = (int64_t)blockIdx.x * EW_BLOCK + threadIdx.x; p < ppr; p += (int64_t)gridDim.x * EW_BLOCK) {
-      const int64_t c0 = p * V;
-      const bool full = c0 + V <= C;
-      float v[V];
-      uint8_t m[V];
-      if (MODE == 2) {
-        const uint8_t* mr = mask + r * ldm + c0;
-        if constexpr (V == 8) {
-          if (full) { const uint2 q = *reinterpret_cast<const uint2*>(mr);
+    for (int64_t pb = (int64_t)blockIdx.x * EW_BLOCK * DU; pb < ppr; pb += (int64_t)gridDim.x * EW_BLOCK * DU) {
+      uint4 xq[DU], oq[ACC ? DU : 1];
+      uint8_t m[DU][V];
+      // every load first
 #pragma unroll
-            for (int k = 0; k < 4; ++k) { m[k] = (q.x >> (8 * k)) & 0xff; m[k + 4] = (q.y >> (8 * k)) & 0xff; }
-          } else {
-#pragma unroll
-            for (int k = 0; k < V; ++k) m[k] = c0 + k < C ? mr[k] : 0;
-          }
-        } else if constexpr (V == 4) {
-          if (full) { const uint32_t q = *reinterpret_cast<const uint32_t*>(mr);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) m[k] = (q >> (8 * k)) & 0xff;
-          } else {
-#pragma unroll
-            for (int k = 0; k < V; ++k) m[k] = c0 + k < C ? mr[k] : 0;
-          }
-        } else {
-          m[0] = mr[0];
+      for (int u = 0; u < DU; ++u) {
+        const int64_t p = pb + u * EW_BLOCK + threadIdx.x;
+        if (p >= ppr) continue;
+        const int64_t c0 = p * V;
+        if (MODE != 1) {
+          const T* xr = reinterpret_cast<const T*>(x) + r * ldx;
+          if constexpr (VEC) xq[u] = load_raw<T>(xr, c0, C);
+          else xq[u].x = __float_as_uint(io<T>::ld(xr + c0));
         }
-      } else {
-        // counter of element (r, c): logical row-major index of the tensor
-        const int64_t i0 = ((r0log + r) * Clog) + c0;   // host flattens so that Clog*r + c is the index
-        uint64_t kg = (uint64_t)i0 * GOLDEN;
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          m[k] = splitmix_top24(seed ^ kg) >= thr ? 1 : 0;
-          kg += GOLDEN;
+        if (MODE == 2) {
+          unpack_mask(mask + r * ldm + c0, c0, C, V, VEC, m[u]);
+          if constexpr (ACC) {
+            const T* yr = reinterpret_cast<const T*>(y) + r * ldy;
+            if constexpr (VEC) oq[u] = load_raw<T>(yr, c0, C);
+            else oq[u].x = __float_as_uint(io<T>::ld(yr + c0));
+          }
         }
       }
-      if (MODE != 1) {
-        const T* xr = reinterpret_cast<const T*>(x) + r * ldx;
-        if constexpr (VEC) load_pack<T>(xr, c0, C, v, 0.f);
-        else v[0] = io<T>::ld(xr + c0);
 #pragma unroll
-        for (int k = 0; k < V; ++k) v[k] = m[k] ? v[k] * scale : 0.f;
-        T* yr = reinterpret_cast<T*>(y) + r * ldy;
-        if constexpr (VEC) store_pack_acc<T>(yr, c0, C, v, MODE == 2 && acc);
-        else io<T>::st(yr + c0, (MODE == 2 && acc) ? acc_add(io<T>::ld(yr + c0), v[0]) : v[0]);
-      }
-      if (MODE != 2 && mask) {
-        uint8_t* mr = mask + r * ldm + c0;
-        if constexpr (V == 8) {
-          if (full) {
-            uint2 q;
-            q.x = m[0] | (m[1] << 8) | (m[2] << 16) | ((uint32_t)m[3] << 24);
-            q.y = m[4] | (m[5] << 8) | (m[6] << 16) | ((uint32_t)m[7] << 24);
-            *reinterpret_cast<uint2*>(mr) = q;
-          } else {
+      for (int u = 0; u < DU; ++u) {
+        const int64_t p = pb + u * EW_BLOCK + threadIdx.x;
+        if (p >= ppr) break;
+        const int64_t c0 = p * V;
+        if (MODE != 2) {
+          // counter of element (r, c): logical row-major index r*Clog + c
+          const int64_t i0 = ((r0log + r) * Clog) + c0;
+          uint64_t kg = (uint64_t)i0 * GOLDEN;
 #pragma unroll
-            for (int k = 0; k < V; ++k) if (c0 + k < C) mr[k] = m[k];
+          for (int k = 0; k < V; ++k) {
+            m[u][k] = splitmix_top24(seed ^ kg) >= thr ? 1 : 0;
+            kg += GOLDEN;
           }
-        } else if constexpr (V == 4) {
-          if (full) *reinterpret_cast<uint32_t*>(mr) = m[0] | (m[1] << 8) | (m[2] << 16) | ((uint32_t)m[3] << 24);
-          else {
-#pragma unroll
-            for (int k = 0; k < V; ++k) if (c0 + k < C) mr[k] = m[k];
-          }
-        } else {
-          mr[0] = m[0];
         }
+        if (MODE != 1) {
+          float v[V];
+          if constexpr (VEC) io<T>::unpack(xq[u], v);
+          else v[0] = __uint_as_float(xq[u].x);
+#pragma unroll
+          for (int k = 0; k < V; ++k) v[k] = m[u][k] ? v[k] * scale : 0.f;
+          if constexpr (ACC) {
+            float o[V];
+            if constexpr (VEC) io<T>::unpack(oq[u], o);
+            else o[0] = __uint_as_float(oq[u].x);
+#pragma unroll
+            for (int k = 0; k < V; ++k) v[k] = acc_add(o[k], v[k]);
+          }
+          T* yr = reinterpret_cast<T*>(y) + r * ldy;
+          if constexpr (VEC) store_pack<T>(yr, c0, C, v);
+          else io<T>::st(yr + c0, v[0]);
+        }
+        if (MODE != 2 && mask) store_mask(mask + r * ldm + c0, c0, C, V, VEC, m[u]);
       }
     }
   }
@@ -306,7 +376,12 @@ hipError_t ew_go(const EwArgs& e, hipStream_t s) {
   }
   constexpr int V = io<T>::VEC;
   if (al) {
-    ew_vec_k<T, TS, OP><<<ew_grid(a.R, a.C, V, true), EW_BLOCK, 0, s>>>(a);
+    const dim3 grid = ew_grid(a.R, a.C, V, true);
+    const unsigned accb = (OP == EW_ACCUMULATE) ? 1u : (a.acc & ((1u << NO) - 1u));
+    if (accb == 0) ew_vec_k<T, TS, OP, 0><<<grid, EW_BLOCK, 0, s>>>(a);
+    else if (accb == 1) ew_vec_k<T, TS, OP, 1><<<grid, EW_BLOCK, 0, s>>>(a);
+    else if (accb == 2) ew_vec_k<T, TS, OP, (NO > 1 ? 2 : 1)><<<grid, EW_BLOCK, 0, s>>>(a);
+    else ew_vec_k<T, TS, OP, (NO > 1 ? 3 : 1)><<<grid, EW_BLOCK, 0, s>>>(a);
   } else {
     ew_scalar_k<T, TS, OP><<<ew_grid(a.R, a.C, 1, false), EW_BLOCK, 0, s>>>(a);
   }
@@ -361,14 +436,15 @@ static hipError_t dropout_go(const xt_tensor* x, const xt_tensor* y, const xt_te
   bool vec = (!x || (((uintptr_t)x->data & 15) == 0 && ((ldx * es(x->dtype)) & 15) == 0)) &&
              (!y || (((uintptr_t)y->data & 15) == 0 && ((ldy * es(y->dtype)) & 15) == 0)) &&
              (!mask || (((uintptr_t)mask->data & (V - 1)) == 0 && (ldm % V) == 0));
-  const dim3 grid = ew_grid(Rw, Cw, vec ? V : 1, false);
+  const dim3 grid = ew_grid(Rw, Cw, vec ? V : 1, true);     // DU == EW_UNROLL packs per thread
   const void* xp = x ? x->data : nullptr;
   void* yp = y ? y->data : nullptr;
   uint8_t* mp = mask ? (uint8_t*)mask->data : nullptr;
-  if (vec)
-    dropout_k<T, MODE, true><<<grid, EW_BLOCK, 0, s>>>(xp, ldx, yp, ldy, mp, ldm, acc, Rw, Cw, Clw, 0, thr, scale, seed);
-  else
-    dropout_k<T, MODE, false><<<grid, EW_BLOCK, 0, s>>>(xp, ldx, yp, ldy, mp, ldm, acc, Rw, Cw, Clw, 0, thr, scale, seed);
+#define XT_DROP(VEC_, ACC_) \
+  dropout_k<T, MODE, VEC_, ACC_><<<grid, EW_BLOCK, 0, s>>>(xp, ldx, yp, ldy, mp, ldm, Rw, Cw, Clw, 0, thr, scale, seed)
+  if (vec) { if (acc) XT_DROP(true, true); else XT_DROP(true, false); }
+  else { if (acc) XT_DROP(false, true); else XT_DROP(false, false); }
+#undef XT_DROP
   return hipGetLastError();
 }
 

@@ -45,37 +45,50 @@ __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t
     __syncthreads();
     const T* xr = reinterpret_cast<const T*>(x) + r * ldx;
     T* yr = reinterpret_cast<T*>(y) + r * ldy;
-    for (int64_t w = threadIdx.x; w < items; w += RB) {
-      const int64_t h = w / per_head, vi = w % per_head;
-      const int64_t ca = h * head_dim + vi * V, cb = ca + half;
-      float a[V], b[V], ya[V], yb[V];
-      if constexpr (VEC) {
-        io<T>::unpack(*reinterpret_cast<const uint4*>(xr + ca), a);
-        io<T>::unpack(*reinterpret_cast<const uint4*>(xr + cb), b);
-      } else {
-        a[0] = io<T>::ld(xr + ca);
-        b[0] = io<T>::ld(xr + cb);
-      }
+    // two work items per thread, both loaded before either is stored
+    for (int64_t w0 = threadIdx.x; w0 < items; w0 += 2 * RB) {
+      float a[2][V], b[2][V], oa[2][V], ob[2][V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) {
-        const int i = (int)(vi * V + k);
-        const float c = cs[i], s = cs[half + i];
-        ya[k] = a[k] * c - b[k] * s;
-        yb[k] = a[k] * s + b[k] * c;
-      }
-      if constexpr (VEC) {
-        if (acc) {
-          float oa[V], ob[V];
-          io<T>::unpack(*reinterpret_cast<const uint4*>(yr + ca), oa);
-          io<T>::unpack(*reinterpret_cast<const uint4*>(yr + cb), ob);
-#pragma unroll
-          for (int k = 0; k < V; ++k) { ya[k] = acc_add(oa[k], ya[k]); yb[k] = acc_add(ob[k], yb[k]); }
+      for (int u = 0; u < 2; ++u) {
+        const int64_t w = w0 + u * RB;
+        if (w >= items) continue;
+        const int64_t h = w / per_head, vi = w % per_head;
+        const int64_t ca = h * head_dim + vi * V, cb = ca + half;
+        if constexpr (VEC) {
+          io<T>::unpack(*reinterpret_cast<const uint4*>(xr + ca), a[u]);
+          io<T>::unpack(*reinterpret_cast<const uint4*>(xr + cb), b[u]);
+          if (acc) {
+            io<T>::unpack(*reinterpret_cast<const uint4*>(yr + ca), oa[u]);
+            io<T>::unpack(*reinterpret_cast<const uint4*>(yr + cb), ob[u]);
+          }
+        } else {
+          a[u][0] = io<T>::ld(xr + ca);
+          b[u][0] = io<T>::ld(xr + cb);
+          if (acc) { oa[u][0] = io<T>::ld(yr + ca); ob[u][0] = io<T>::ld(yr + cb); }
         }
-        *reinterpret_cast<uint4*>(yr + ca) = io<T>::pack(ya);
-        *reinterpret_cast<uint4*>(yr + cb) = io<T>::pack(yb);
-      } else {
-        io<T>::st(yr + ca, acc ? acc_add(io<T>::ld(yr + ca), ya[0]) : ya[0]);
-        io<T>::st(yr + cb, acc ? acc_add(io<T>::ld(yr + cb), yb[0]) : yb[0]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t w = w0 + u * RB;
+        if (w >= items) break;
+        const int64_t h = w / per_head, vi = w % per_head;
+        const int64_t ca = h * head_dim + vi * V, cb = ca + half;
+        float ya[V], yb[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          const int i = (int)(vi * V + k);
+          const float c = cs[i], sn = cs[half + i];
+          ya[k] = a[u][k] * c - b[u][k] * sn;
+          yb[k] = a[u][k] * sn + b[u][k] * c;
+          if (acc) { ya[k] = acc_add(oa[u][k], ya[k]); yb[k] = acc_add(ob[u][k], yb[k]); }
+        }
+        if constexpr (VEC) {
+          *reinterpret_cast<uint4*>(yr + ca) = io<T>::pack(ya);
+          *reinterpret_cast<uint4*>(yr + cb) = io<T>::pack(yb);
+        } else {
+          io<T>::st(yr + ca, ya[0]);
+          io<T>::st(yr + cb, yb[0]);
+        }
       }
     }
   }

@@ -42,6 +42,11 @@ template <typename T> __device__ __forceinline__ T* row_ptr_w(void* p, int64_t r
   return reinterpret_cast<T*>(p) + r * ld;
 }
 
+// Every fast kernel walks its rows with the next row's packs already in
+// flight: they are loaded (raw, 16 bytes each) before the current row's
+// reductions and stores, so HBM latency overlaps the barrier phase and no
+// load waits behind a store it might alias.
+
 // ===================================================================== RMS
 template <typename T, int RW, int NV, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
@@ -51,26 +56,24 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int64_t stride = (int64_t)gridDim.x * NG;
   float gam[NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
-  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
-    const int64_t r = base + g;
+  RowPacks<T, NV, G> cur, nxt;
+  int64_t base = (int64_t)blockIdx.x * NG;
+  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, C, base + g < R);
+  for (; base < R; base += stride) {
+    const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
+    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, C, rn < R);
     float v[NV][V];
+    cur.unpack(v);
     float ss = 0.f;
-    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t c0 = (int64_t)(j * G + gl) * V;
-      if (active && c0 < C) load_pack<T>(xr, c0, C, v[j], 0.f);
-      else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) v[j][k] = 0.f;
-      }
+    for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) ss += v[j][k] * v[j][k];
-    }
     ss = group_sum<RW>(ss, lds);
     const float irv = rsqrtf(ss * invC + eps);
     if (active) {
@@ -87,6 +90,7 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
       }
       if (gl == 0) ir[r * ldir] = irv;
     }
+    cur = nxt;
   }
 }
 
@@ -133,26 +137,27 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
   }
   const int64_t start = (int64_t)blockIdx.x * rpb;
   const int64_t end = min(R, start + rpb);
+  RowPacks<T, NV, G> cd, cx, nd, nx;
+  {
+    const int64_t r = start + g;
+    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, C, r < end);
+    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, C, r < end);
+  }
   for (int64_t base = start; base < end; base += NG) {
-    const int64_t r = base + g;
+    const int64_t r = base + g, rn = base + NG + g;
     const bool active = r < end;
-    const T* dr = row_ptr<T>(d, active ? r : 0, ldd);
-    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    if (base + NG < end) {
+      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, C, rn < end);
+      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, C, rn < end);
+    }
     float dv[NV][V], xv[NV][V];
+    cd.unpack(dv);
+    cx.unpack(xv);
     float dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t c0 = (int64_t)(j * G + gl) * V;
-      if (active && c0 < C) {
-        load_pack<T>(dr, c0, C, dv[j], 0.f);
-        load_pack<T>(xr, c0, C, xv[j], 0.f);
-      } else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) { dv[j][k] = 0.f; xv[j][k] = 0.f; }
-      }
+    for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) dot += dv[j][k] * gam[j][k] * xv[j][k];
-    }
     dot = group_sum<RW>(dot, lds);
     if (active) {
       const float irv = ir[r * ldir];
@@ -172,6 +177,8 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
         }
       }
     }
+    cd = nd;
+    cx = nx;
   }
   if (part) fold_partials<NV, V, G, NG, 1, BWD_BLOCK>(pp, red, part, C);
 }
@@ -186,29 +193,27 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int64_t stride = (int64_t)gridDim.x * NG;
   float gam[NV][V], bet[NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
     load_f32s<V>(beta, (int64_t)(j * G + gl) * V, C, bet[j]);
   }
-  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
-    const int64_t r = base + g;
+  RowPacks<T, NV, G> cur, nxt;
+  int64_t base = (int64_t)blockIdx.x * NG;
+  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, C, base + g < R);
+  for (; base < R; base += stride) {
+    const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
-    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, C, rn < R);
     float v[NV][V];
+    cur.unpack(v);
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t c0 = (int64_t)(j * G + gl) * V;
-      if (active && c0 < C) load_pack<T>(xr, c0, C, v[j], 0.f);
-      else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) v[j][k] = 0.f;
-      }
+    for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) s += v[j][k];
-    }
     const float mu = group_sum<RW>(s, lds) * invC;
     float q = 0.f;
 #pragma unroll
@@ -234,6 +239,7 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
       }
       if (gl == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
     }
+    cur = nxt;
   }
 }
 
@@ -256,25 +262,28 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
   }
   const int64_t start = (int64_t)blockIdx.x * rpb;
   const int64_t end = min(R, start + rpb);
+  RowPacks<T, NV, G> cd, cx, nd, nx;
+  {
+    const int64_t r = start + g;
+    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, C, r < end);
+    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, C, r < end);
+  }
   for (int64_t base = start; base < end; base += NG) {
-    const int64_t r = base + g;
+    const int64_t r = base + g, rn = base + NG + g;
     const bool active = r < end;
-    const T* dr = row_ptr<T>(d, active ? r : 0, ldd);
-    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
+    if (base + NG < end) {
+      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, C, rn < end);
+      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, C, rn < end);
+    }
     const float mu = active ? mean[r * ldm] : 0.f;
     const float rs = active ? rstd[r * ldr] : 0.f;
     float dv[NV][V], xh[NV][V];
+    cd.unpack(dv);
+    cx.unpack(xh);
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int64_t c0 = (int64_t)(j * G + gl) * V;
-      if (active && c0 < C) {
-        load_pack<T>(dr, c0, C, dv[j], 0.f);
-        load_pack<T>(xr, c0, C, xh[j], 0.f);
-      } else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) { dv[j][k] = 0.f; xh[j][k] = 0.f; }
-      }
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         const bool ok = c0 + k < C;
@@ -303,6 +312,8 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
         }
       }
     }
+    cd = nd;
+    cx = nx;
   }
   if (part) fold_partials<NV, V, G, NG, 2, BWD_BLOCK>(pp, red, part, C);
 }
@@ -316,17 +327,21 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const float NEG_INF = -__builtin_inff();
-  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
-    const int64_t r = base + g;
+  const int64_t stride = (int64_t)gridDim.x * NG;
+  RowPacks<T, NV, G> cur, nxt;
+  int64_t base = (int64_t)blockIdx.x * NG;
+  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, C, base + g < R);
+  for (; base < R; base += stride) {
+    const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
+    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, C, rn < R);
     const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;   // valid columns
-    const T* xr = row_ptr<T>(x, active ? r : 0, ldx);
     float v[NV][V];
+    cur.unpack(v);
     float m = NEG_INF;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int64_t c0 = (int64_t)(j * G + gl) * V;
-      if (active && c0 < C) load_pack<T>(xr, c0, C, v[j], 0.f);
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         v[j][k] = (active && c0 + k < lim) ? alpha * v[j][k] : NEG_INF;
@@ -357,6 +372,7 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
         }
       }
     }
+    cur = nxt;
   }
 }
 
@@ -367,26 +383,29 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
-  for (int64_t base = (int64_t)blockIdx.x * NG; base < R; base += (int64_t)gridDim.x * NG) {
+  const int64_t stride = (int64_t)gridDim.x * NG;
+  RowPacks<T, NV, G> cd, cy, nd, ny;
+  int64_t base = (int64_t)blockIdx.x * NG;
+  {
     const int64_t r = base + g;
+    cd.load(row_ptr<T>(d, r < R ? r : 0, ldd), gl, C, r < R);
+    cy.load(row_ptr<T>(y, r < R ? r : 0, ldy), gl, C, r < R);
+  }
+  for (; base < R; base += stride) {
+    const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
-    const T* dr = row_ptr<T>(d, active ? r : 0, ldd);
-    const T* yr = row_ptr<T>(y, active ? r : 0, ldy);
+    if (base + stride < R) {
+      nd.load(row_ptr<T>(d, rn < R ? rn : 0, ldd), gl, C, rn < R);
+      ny.load(row_ptr<T>(y, rn < R ? rn : 0, ldy), gl, C, rn < R);
+    }
     float dv[NV][V], yv[NV][V];
+    cd.unpack(dv);
+    cy.unpack(yv);
     float dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t c0 = (int64_t)(j * G + gl) * V;
-      if (active && c0 < C) {
-        load_pack<T>(dr, c0, C, dv[j], 0.f);
-        load_pack<T>(yr, c0, C, yv[j], 0.f);
-      } else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) { dv[j][k] = 0.f; yv[j][k] = 0.f; }
-      }
+    for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) dot += dv[j][k] * yv[j][k];
-    }
     dot = group_sum<RW>(dot, lds);
     if (active) {
       T* dxr = row_ptr_w<T>(dx, r, lddx);
@@ -401,6 +420,8 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
         }
       }
     }
+    cd = nd;
+    cy = ny;
   }
 }
 

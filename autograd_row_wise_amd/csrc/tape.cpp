@@ -299,16 +299,17 @@ xt_status xt_tape_zero_grad(xt_tape* t) {
   return XT_OK;
 }
 
-xt_status xt_tape_backward(xt_tape* t, xt_var loss) {
-  if (!valid_var(t, loss)) return XT_ERR_INVALID_ARG;
-  Node& L = t->nodes[loss];
-  if (L.value.rows * L.value.cols * L.value.nb[0] * L.value.nb[1] != 1 || L.value.dtype != XT_F32)
-    return XT_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+// Shared reverse walk: `seed` writes the gradient of `out` once its buffer exists.
+template <typename Seed>
+xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
   // post-order DFS (iterative), each node once
   std::vector<xt_var> order;
   std::vector<char> state(t->nodes.size(), 0);     // 0 new, 1 open, 2 done
-  std::vector<std::pair<xt_var, size_t>> stack{{loss, 0}};
-  state[loss] = 1;
+  std::vector<std::pair<xt_var, size_t>> stack{{out, 0}};
+  state[out] = 1;
   while (!stack.empty()) {
     auto& top = stack.back();
     const Node& n = t->nodes[top.first];
@@ -325,13 +326,11 @@ xt_status xt_tape_backward(xt_tape* t, xt_var loss) {
   // accumulating until xt_tape_zero_grad
   for (xt_var v : order)
     if (!t->nodes[v].leaf) t->nodes[v].grad_live = false;
-  if (L.leaf) return XT_OK;
-  xt_status s = ensure_grad(t, loss);
+  xt_status s = ensure_grad(t, out);
   if (s != XT_OK) return s;
-  if (xt::launch_fill_f32((float*)t->nodes[grad_owner(t, loss)].grad.data + 0, 1, 1.0f, t->stream) != hipSuccess)
-    return XT_ERR_HIP;
-  set_grad_live(t, loss);
-
+  s = seed(t->nodes[out].grad, grad_live(t, out));
+  if (s != XT_OK) return s;
+  set_grad_live(t, out);
   for (auto it = order.rbegin(); it != order.rend(); ++it) {
     const xt_var v = *it;
     Node& n = t->nodes[v];
@@ -381,6 +380,34 @@ xt_status xt_tape_backward(xt_tape* t, xt_var loss) {
     if (s != XT_OK) return s;
   }
   return XT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+xt_status xt_tape_backward(xt_tape* t, xt_var loss) {
+  if (!valid_var(t, loss)) return XT_ERR_INVALID_ARG;
+  const Node& L = t->nodes[loss];
+  if (L.value.rows * L.value.cols * L.value.nb[0] * L.value.nb[1] != 1 || L.value.dtype != XT_F32)
+    return XT_ERR_SHAPE;
+  return reverse_pass(t, loss, [&](const xt_tensor& g, bool live) -> xt_status {
+    (void)live;
+    return xt::launch_fill_f32((float*)g.data, 1, 1.0f, t->stream) == hipSuccess ? XT_OK : XT_ERR_HIP;
+  });
+}
+
+xt_status xt_tape_backward_seeded(xt_tape* t, xt_var out, const xt_tensor* dout) {
+  if (!valid_var(t, out) || !dout) return XT_ERR_INVALID_ARG;
+  const Node& n = t->nodes[out];
+  if (dout->rows != n.value.rows || dout->cols != n.value.cols || dout->nb[0] != 1 ||
+      dout->nb[1] != 1 || n.value.nb[0] != 1 || n.value.nb[1] != 1)
+    return XT_ERR_SHAPE;                 // unbatched outputs only
+  if (dout->dtype != n.value.dtype || !dout->data) return XT_ERR_DTYPE;
+  return reverse_pass(t, out, [&](const xt_tensor& g, bool live) -> xt_status {
+    // grad(out) (+)= dout: a leaf keeps accumulating across passes
+    xt::EwArgs e{{dout, nullptr, nullptr}, {&g, nullptr}, live && t->nodes[out].leaf ? 1u : 0u, 1.f, nullptr};
+    return xt::launch_ew(xt::EW_SCALE, e, t->stream) == hipSuccess ? XT_OK : XT_ERR_HIP;
+  });
 }
 
 }  // extern "C"

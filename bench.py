@@ -1,0 +1,457 @@
+#!/usr/bin/env python3
+"""Throughput of the row-wise autograd hot path on one MI355X.
+
+One step = one forward+backward pass of every op of the hot path over one
+batch of synthetic input, each at the shape its workload names:
+  * GPT-2-small-shaped f32 (batch 8 x seq 1024, d 768): layer_norm, GELU
+    MLP (hidden 3072: both GEMMs fwd+bwd and the GELU), residual add,
+    cross-entropy over vocab 50257 (logits ~ N(0, 2));
+  * bf16, 16384 rows x d 4096: rms_norm, SwiGLU gate/up 16384 x 11008, rope
+    32 heads x 128, residual dropout p=0.1 at the two sites
+    (seeds 42^0^0xA77, 42^0^0xF70), fan-out grad accumulate;
+  * bf16 stress: cross-entropy 32768 x 128256 (logits ~ N(0, 3)), softmax
+    32768 x 32768, dbias column sum over 65536 x 4096, matmul backward of
+    8192 x 4096 x 4096;
+  * the tiny transformer block (batch 4, seq 256, d 256, 4 x 64 heads,
+    SwiGLU 688, vocab 4096, f32) recorded on the tape, fwd+bwd.
+Inputs are drawn on the GPU before timing (torch's seeded generator).
+
+`value` is the step's algorithmic HBM bytes / step time (GB/s): what the
+method must read and write, not what the caches move.  Per-op figures
+(bytes, time from HIP events on the launch stream, GB/s or TFLOP/s,
+fraction of peak) are in `ops`; `roofline` is for the op with the largest
+share of step time.  `cpu_baseline` is the CPU oracle on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", nargs="*", default=None, help="run only ops whose name starts with one of these")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ops-json", default=None, help="also write the per-op table to this file")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+class Entry:
+    def __init__(self, name, workload, dtype, kind, fn, nbytes=0, flops=0, rows=0):
+        self.name, self.workload, self.dtype, self.kind = name, workload, dtype, kind
+        self.fn, self.bytes, self.flops, self.rows = fn, nbytes, flops, rows
+        self.times_ms = []
+
+
+def build_entries(only):
+    import torch
+    import autograd_row_wise_amd as xt
+    from autograd_row_wise_amd import block as xb
+    from synth import device_normal, device_uniform_int
+
+    V, P = xt.view, xt.params
+    E = []
+    want = (lambda n: True) if not only else (lambda n: any(n.startswith(o) for o in only))
+
+    def empty(shape, dt):
+        return torch.empty(shape, dtype={"f32": torch.float32, "bf16": torch.bfloat16, "u8": torch.uint8}[dt],
+                           device="cuda")
+
+    def ws(op, prm, ins):
+        n = xt.xt_workspace_bytes(op, 1, prm, ins)
+        if not n:
+            return None, 0
+        buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+        keep.append(buf)
+        return buf.data_ptr(), n
+
+    keep = []
+    nullslot = lambda t: (lambda v: (setattr(v, "data", None), v)[1])(V(t))  # noqa: E731
+
+    # Each workload is built in its own function so the op closures bind
+    # that workload's tensors.
+    def c3():
+        nonlocal keep
+        W3 = "gpt2s-f32 8x1024x768"
+        R3, D3, H3, V3 = 8192, 768, 3072, 50257
+        if any(want(n) for n in ("c3.ln", "c3.gelu", "c3.add", "c3.ce", "c3.mlp")):
+            x = device_normal((R3, D3), 3, "x")
+            d = device_normal((R3, D3), 3, "dout")
+            gam = device_normal((D3,), 3, "gamma", 1.0, 0.1)
+            bet = device_normal((D3,), 3, "beta", 0.0, 0.1)
+            y, mu, rs = empty((R3, D3), "f32"), empty((R3, 1), "f32"), empty((R3, 1), "f32")
+            dx, dg, db = empty((R3, D3), "f32"), empty((D3,), "f32"), empty((D3,), "f32")
+            pln = P(eps=1e-5)
+            keep += [x, d, gam, bet, y, mu, rs, dx, dg, db]
+            N = R3 * D3
+            if want("c3.ln"):
+                E.append(Entry("c3.ln.fwd", W3, "f32", "hbm", lambda: xt.xt_op_fwd(
+                    xt.OP.LAYER_NORM, pln, [V(x), V(gam), V(bet)], [V(y), V(mu), V(rs)]), 2 * 4 * N + 8 * R3, rows=R3))
+                wp, wn = ws(xt.OP.LAYER_NORM, pln, [V(x), V(gam), V(bet)])
+                E.append(Entry("c3.ln.bwd", W3, "f32", "hbm", lambda: xt.xt_op_bwd(
+                    xt.OP.LAYER_NORM, pln, V(d), [V(x), V(gam), V(bet)], [V(mu), V(rs)], [V(dx), V(dg), V(db)], 0, wp, wn),
+                    3 * 4 * N + 8 * R3, rows=R3))
+            if want("c3.add"):
+                r2 = empty((R3, D3), "f32")
+                keep.append(r2)
+                E.append(Entry("c3.add.fwd", W3, "f32", "hbm", lambda: xt.xt_op_fwd(
+                    xt.OP.ADD, P(), [V(x), V(d)], [V(r2)]), 3 * 4 * N, rows=R3))
+            if want("c3.gelu") or want("c3.mlp"):
+                hpre = device_normal((R3, H3), 3, "g")
+                hd = device_normal((R3, H3), 3, "d2")
+                hy, hdx = empty((R3, H3), "f32"), empty((R3, H3), "f32")
+                keep += [hpre, hd, hy, hdx]
+                NH = R3 * H3
+                if want("c3.gelu"):
+                    E.append(Entry("c3.gelu.fwd", W3, "f32", "hbm", lambda: xt.xt_op_fwd(
+                        xt.OP.GELU, P(), [V(hpre)], [V(hy)]), 2 * 4 * NH, rows=R3))
+                    E.append(Entry("c3.gelu.bwd", W3, "f32", "hbm", lambda: xt.xt_op_bwd(
+                        xt.OP.GELU, P(), V(hd), [V(hpre)], [], [V(hdx)]), 3 * 4 * NH, rows=R3))
+                if want("c3.mlp"):
+                    w1 = device_normal((D3, H3), 3, "w1", 0.0, 0.02)
+                    w2 = device_normal((H3, D3), 3, "w2", 0.0, 0.02)
+                    dw1, dw2 = empty((D3, H3), "f32"), empty((H3, D3), "f32")
+                    o1, o2, dxa = empty((R3, H3), "f32"), empty((R3, D3), "f32"), empty((R3, D3), "f32")
+                    dh = empty((R3, H3), "f32")
+                    keep += [w1, w2, dw1, dw2, o1, o2, dxa, dh]
+                    f1 = 2 * R3 * D3 * H3
+                    b1 = 4 * (R3 * D3 + D3 * H3 + R3 * H3)
+                    E.append(Entry("c3.mlp1.fwd", W3, "f32", "mfma", lambda: xt.xt_op_fwd(
+                        xt.OP.MATMUL, P(), [V(x), V(w1)], [V(o1)]), b1, f1, R3))
+                    E.append(Entry("c3.mlp1.bwd", W3, "f32", "mfma", lambda: xt.xt_op_bwd(
+                        xt.OP.MATMUL, P(), V(hd), [V(x), V(w1)], [], [V(dxa), V(dw1)]), 2 * b1, 2 * f1, R3))
+                    E.append(Entry("c3.mlp2.fwd", W3, "f32", "mfma", lambda: xt.xt_op_fwd(
+                        xt.OP.MATMUL, P(), [V(hy), V(w2)], [V(o2)]), b1, f1, R3))
+                    E.append(Entry("c3.mlp2.bwd", W3, "f32", "mfma", lambda: xt.xt_op_bwd(
+                        xt.OP.MATMUL, P(), V(d), [V(hy), V(w2)], [], [V(dh), V(dw2)]), 2 * b1, 2 * f1, R3))
+            if want("c3.ce"):
+                lg = device_normal((R3, V3), 3, "logits", 0.0, 2.0)
+                tg = device_uniform_int((R3, 1), 0, V3, 3, "targets")
+                L, lse, lr = empty((1, 1), "f32"), empty((R3, 1), "f32"), empty((R3, 1), "f32")
+                dL = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+                dlg = empty((R3, V3), "f32")
+                keep += [lg, tg, L, lse, lr, dL, dlg]
+                E.append(Entry("c3.ce.fwd", W3, "f32", "hbm", lambda: xt.xt_op_fwd(
+                    xt.OP.CROSS_ENTROPY, P(), [V(lg), V(tg)], [V(L), V(lse), V(lr)]), 4 * R3 * V3 + 16 * R3, rows=R3))
+                E.append(Entry("c3.ce.bwd", W3, "f32", "hbm", lambda: xt.xt_op_bwd(
+                    xt.OP.CROSS_ENTROPY, P(), V(dL), [V(lg), V(tg)], [V(lse)], [V(dlg), nullslot(tg)]),
+                    2 * 4 * R3 * V3 + 8 * R3, rows=R3))
+
+    def c4():
+        nonlocal keep
+        W4 = "bf16 16384x4096"
+        R4, D4, F4 = 16384, 4096, 11008
+        N4 = R4 * D4
+        if any(want(n) for n in ("c4.",)):
+            x = device_normal((R4, D4), 4, "x", dtype="bf16")
+            d = device_normal((R4, D4), 4, "dout", dtype="bf16")
+            keep += [x, d]
+            if want("c4.rms"):
+                gam = device_normal((D4,), 4, "gamma", 1.0, 0.1)
+                y, ir, dx, dg = empty((R4, D4), "bf16"), empty((R4, 1), "f32"), empty((R4, D4), "bf16"), empty((D4,), "f32")
+                keep += [gam, y, ir, dx, dg]
+                prm = P(eps=1e-5)
+                E.append(Entry("c4.rms.fwd", W4, "bf16", "hbm", lambda: xt.xt_op_fwd(
+                    xt.OP.RMS_NORM, prm, [V(x), V(gam)], [V(y), V(ir)]), 2 * 2 * N4 + 4 * R4, rows=R4))
+                wp, wn = ws(xt.OP.RMS_NORM, prm, [V(x), V(gam)])
+                E.append(Entry("c4.rms.bwd", W4, "bf16", "hbm", lambda: xt.xt_op_bwd(
+                    xt.OP.RMS_NORM, prm, V(d), [V(x), V(gam)], [V(ir)], [V(dx), V(dg)], 0, wp, wn),
+                    3 * 2 * N4 + 4 * R4, rows=R4))
+            if want("c4.swiglu"):
+                g = device_normal((R4, F4), 4, "g", dtype="bf16")
+                u = device_normal((R4, F4), 4, "u", dtype="bf16")
+                dd = device_normal((R4, F4), 4, "d2", dtype="bf16")
+                yy, dgg, duu = empty((R4, F4), "bf16"), empty((R4, F4), "bf16"), empty((R4, F4), "bf16")
+                keep += [g, u, dd, yy, dgg, duu]
+                NF = R4 * F4
+                E.append(Entry("c4.swiglu.fwd", W4, "bf16", "hbm", lambda: xt.xt_op_fwd(
+                    xt.OP.SWIGLU, P(), [V(g), V(u)], [V(yy)]), 3 * 2 * NF, rows=R4))
+                E.append(Entry("c4.swiglu.bwd", W4, "bf16", "hbm", lambda: xt.xt_op_bwd(
+                    xt.OP.SWIGLU, P(), V(dd), [V(g), V(u)], [], [V(dgg), V(duu)]), 5 * 2 * NF, rows=R4))
+            if want("c4.rope"):
+                ry, rdx = empty((R4, D4), "bf16"), empty((R4, D4), "bf16")
+                keep += [ry, rdx]
+                prm_r = P(head_dim=128, seq_len=4096, rope_base=10000.0)
+                E.append(Entry("c4.rope.fwd", W4, "bf16", "hbm", lambda: xt.xt_op_fwd(
+                    xt.OP.ROPE, prm_r, [V(x)], [V(ry)]), 2 * 2 * N4, rows=R4))
+                E.append(Entry("c4.rope.bwd", W4, "bf16", "hbm", lambda: xt.xt_op_bwd(
+                    xt.OP.ROPE, prm_r, V(d), [V(x)], [], [V(rdx)]), 2 * 2 * N4, rows=R4))
+            if want("c4.dropout"):
+                for site, const in (("attn", 0xA77), ("ffn", 0xF70)):
+                    prm_d = P(p=0.1, seed=42 ^ 0 ^ const)
+                    dy, dm, ddx = empty((R4, D4), "bf16"), empty((R4, D4), "u8"), empty((R4, D4), "bf16")
+                    keep += [dy, dm, ddx]
+                    E.append(Entry(f"c4.dropout.{site}.fwd", W4, "bf16", "hbm",
+                                   (lambda prm_d=prm_d, dy=dy, dm=dm: xt.xt_op_fwd(
+                                       xt.OP.DROPOUT, prm_d, [V(x)], [V(dy), V(dm)])), 2 * 2 * N4 + N4, rows=R4))
+                    E.append(Entry(f"c4.dropout.{site}.bwd", W4, "bf16", "hbm",
+                                   (lambda prm_d=prm_d, dm=dm, ddx=ddx: xt.xt_op_bwd(
+                                       xt.OP.DROPOUT, prm_d, V(d), [V(x)], [V(dm)], [V(ddx)])), 2 * 2 * N4 + N4, rows=R4))
+            if want("c4.accumulate"):
+                dres = device_normal((R4, D4), 4, "resid", dtype="bf16")
+                keep.append(dres)
+                E.append(Entry("c4.accumulate", W4, "bf16", "hbm", lambda: xt.xt_grad_accumulate(V(dres), V(d)),
+                               3 * 2 * N4, rows=R4))
+
+    def c5():
+        nonlocal keep
+        W5 = "bf16 stress"
+        if want("c5.ce"):
+            R5, V5 = 32768, 128256
+            lg = device_normal((R5, V5), 5, "logits", 0.0, 3.0, dtype="bf16")
+            tg = device_uniform_int((R5, 1), 0, V5, 5, "targets")
+            L, lse, lr = empty((1, 1), "f32"), empty((R5, 1), "f32"), empty((R5, 1), "f32")
+            dL = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+            dlg = empty((R5, V5), "bf16")
+            keep += [lg, tg, L, lse, lr, dL, dlg]
+            E.append(Entry("c5.ce.fwd", W5, "bf16", "hbm", lambda: xt.xt_op_fwd(
+                xt.OP.CROSS_ENTROPY, P(), [V(lg), V(tg)], [V(L), V(lse), V(lr)]), 2 * R5 * V5 + 16 * R5, rows=R5))
+            E.append(Entry("c5.ce.bwd", W5, "bf16", "hbm", lambda: xt.xt_op_bwd(
+                xt.OP.CROSS_ENTROPY, P(), V(dL), [V(lg), V(tg)], [V(lse)], [V(dlg), nullslot(tg)]),
+                2 * 2 * R5 * V5 + 8 * R5, rows=R5))
+        if want("c5.softmax"):
+            R5 = C5 = 32768
+            sx = device_normal((R5, C5), 5, "x", dtype="bf16")
+            sd = device_normal((R5, C5), 5, "dout", dtype="bf16")
+            sy, sdx = empty((R5, C5), "bf16"), empty((R5, C5), "bf16")
+            keep += [sx, sd, sy, sdx]
+            NS = R5 * C5
+            E.append(Entry("c5.softmax.fwd", W5, "bf16", "hbm", lambda: xt.xt_op_fwd(
+                xt.OP.SOFTMAX, P(), [V(sx)], [V(sy)]), 2 * 2 * NS, rows=R5))
+            E.append(Entry("c5.softmax.bwd", W5, "bf16", "hbm", lambda: xt.xt_op_bwd(
+                xt.OP.SOFTMAX, P(), V(sd), [V(sx)], [V(sy)], [V(sdx)]), 3 * 2 * NS, rows=R5))
+        if want("c5.dbias"):
+            RB, CB = 65536, 4096
+            bd = device_normal((RB, CB), 5, "d3", dtype="bf16")
+            bx = torch.empty((RB, CB), dtype=torch.bfloat16, device="cuda")   # shape only (not read)
+            bias = torch.zeros((CB,), dtype=torch.float32, device="cuda")
+            dbias = empty((CB,), "f32")
+            keep += [bd, bx, bias, dbias]
+            wp, wn = ws(xt.OP.ADD_BIAS, P(), [V(bd), V(bias)])
+            E.append(Entry("c5.dbias", W5, "bf16", "hbm", lambda: xt.xt_op_bwd(
+                xt.OP.ADD_BIAS, P(), V(bd), [V(bx), V(bias)], [], [nullslot(bx), V(dbias)], 0, wp, wn),
+                2 * RB * CB + 4 * CB, rows=RB))
+        if want("c5.gemm"):
+            M, K, N = 8192, 4096, 4096
+            A = device_normal((M, K), 5, "a", dtype="bf16")
+            B = device_normal((K, N), 5, "b", 0.0, 0.02, dtype="bf16")
+            Dg = device_normal((M, N), 5, "dout", dtype="bf16")
+            dA, dB = empty((M, K), "bf16"), empty((K, N), "f32")
+            keep += [A, B, Dg, dA, dB]
+            fl = 2 * M * N * K
+            E.append(Entry("c5.gemm.bwd_dA", W5, "bf16", "mfma", lambda: xt.xt_op_bwd(
+                xt.OP.MATMUL, P(), V(Dg), [V(A), V(B)], [], [V(dA), nullslot(B)]), 2 * (M * N + N * K + M * K), fl, M))
+            E.append(Entry("c5.gemm.bwd_dB", W5, "bf16", "mfma", lambda: xt.xt_op_bwd(
+                xt.OP.MATMUL, P(), V(Dg), [V(A), V(B)], [], [nullslot(A), V(dB)]),
+                2 * (M * K + M * N) + 4 * K * N, fl, M))
+
+    def c2():
+        nonlocal keep
+        if want("c2.block"):
+            shp = xb.BlockShape(B=4, S=256, H=4, Dh=64, hidden=688, vocab=4096)
+            Wt = {}
+            for k, s in xb.WEIGHT_SHAPES(shp).items():
+                Wt[k] = (torch.ones(s, dtype=torch.float32, device="cuda") if k.startswith("g")
+                         else device_normal(s, 2, k, 0.0, 0.02))
+            bx2 = device_normal((shp.B * shp.S, shp.D), 2, "x")
+            bt2 = device_uniform_int((shp.B * shp.S, 1), 0, shp.vocab, 2, "targets")
+            keep += list(Wt.values()) + [bx2, bt2]
+            holder = {}
+
+            def run_block():
+                if "tape" in holder:
+                    holder["tape"].close()
+                t = xt.Tape()
+                w = xb.leaves(t, Wt)
+                loss = xb.block(t, w, t.leaf(V(bx2)), t.leaf(V(bt2), requires_grad=False), shp, xt.DT.F32)
+                t.backward(loss)
+                holder["tape"] = t
+            # GEMM flops of one fwd+bwd (for the record; the block is launch/cache bound)
+            T, D = shp.B * shp.S, shp.D
+            fl = 2 * T * D * D * 4 + 2 * T * D * shp.hidden * 3 + 2 * T * D * shp.vocab \
+                + 2 * 2 * shp.B * shp.H * shp.S * shp.S * shp.Dh
+            E.append(Entry("c2.block.fwdbwd", "tiny block 4x256x256 f32", "f32", "block", run_block, 0, 3 * fl,
+                           shp.B * shp.S))
+    c3()
+    c4()
+    c5()
+    c2()
+    return E, keep
+
+
+# --------------------------------------------------------------------------
+def cpu_baseline(frac_rows=1 / 256):
+    """The oracle (numpy f64, single thread) on the first `frac_rows` of the
+    rows of every memory-bound op of the step; returns GB/s over the sample's
+    algorithmic bytes."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ops, rng
+    import synth
+
+    def rows(R):
+        return max(1, int(R * frac_rows))
+
+    jobs = []   # (name, bytes, fn)
+    R = rows(8192)
+    x = synth.host_normal((R, 768), 3, "x").astype(np.float64)
+    g = synth.host_normal((768,), 3, "gamma", 1.0, 0.1).astype(np.float64)
+    b = synth.host_normal((768,), 3, "beta", 0.0, 0.1).astype(np.float64)
+    d = synth.host_normal((R, 768), 3, "dout").astype(np.float64)
+    N = R * 768
+    jobs.append(("ln", (5 * 4 * N + 16 * R), lambda: ops.layer_norm_bwd(d, x, g, *ops.layer_norm(x, g, b, 1e-5)[1:])))
+    h = synth.host_normal((R, 3072), 3, "g").astype(np.float64)
+    jobs.append(("gelu", 5 * 4 * R * 3072, lambda: (ops.gelu(h), ops.gelu_bwd(h, h))))
+    lg = synth.host_normal((R, 50257), 3, "logits", 0.0, 2.0).astype(np.float64)
+    t = synth.host_uniform_int((R,), 0, 50257, 3, "targets")
+    jobs.append(("ce3", 3 * 4 * R * 50257, lambda: ops.cross_entropy_bwd(1.0, lg, t, ops.cross_entropy(lg, t)[1])))
+    R4 = rows(16384)
+    x4 = synth.host_normal((R4, 4096), 4, "x").astype(np.float64)
+    g4 = synth.host_normal((4096,), 4, "gamma", 1.0, 0.1).astype(np.float64)
+    d4 = synth.host_normal((R4, 4096), 4, "dout").astype(np.float64)
+    N4 = R4 * 4096
+    jobs.append(("rms", 5 * 2 * N4, lambda: ops.rms_norm_bwd(d4, x4, g4, ops.rms_norm(x4, g4, 1e-5)[1])))
+    jobs.append(("rope", 4 * 2 * N4, lambda: (ops.rope(x4, 128, 10000.0, 4096), ops.rope_bwd(d4, 128, 10000.0, 4096))))
+    jobs.append(("dropout", 2 * (2 * 2 * N4 + N4), lambda: rng.dropout_bwd(d4, rng.dropout(x4, 0.1, 42 ^ 0xA77)[1], 0.1)))
+    sg = synth.host_normal((R4, 11008), 4, "g").astype(np.float64)
+    jobs.append(("swiglu", 8 * 2 * R4 * 11008, lambda: (ops.swiglu(sg, sg), ops.swiglu_bwd(sg, sg, sg))))
+    R5 = rows(32768)
+    sx = synth.host_normal((R5, 32768), 5, "x").astype(np.float64)
+    jobs.append(("softmax", 5 * 2 * R5 * 32768, lambda: ops.softmax_bwd(sx, ops.softmax(sx))))
+    lg5 = synth.host_normal((R5, 128256), 5, "logits", 0.0, 3.0).astype(np.float64)
+    t5 = synth.host_uniform_int((R5,), 0, 128256, 5, "targets")
+    jobs.append(("ce5", 3 * 2 * R5 * 128256, lambda: ops.cross_entropy_bwd(1.0, lg5, t5, ops.cross_entropy(lg5, t5)[1])))
+    total_b, total_t = 0, 0.0
+    with threadpool_limits(limits=1):
+        for name, nb, fn in jobs:
+            t0 = time.perf_counter()
+            fn()
+            total_t += time.perf_counter() - t0
+            total_b += nb
+    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"numpy f64 oracle, fwd+bwd of layer_norm, gelu, cross_entropy (both vocabularies), rms_norm, "
+                      f"rope, dropout, swiglu, softmax on the first 1/{int(round(1 / frac_rows))} of each op's rows; "
+                      f"{total_b / 1e9:.2f} GB algorithmic in {total_t:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (collectives are out of scope); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    entries, keep = build_entries(args.only)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(record):
+        for e in entries:
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                e.fn()
+                b.record(stream)
+                e._ev = (a, b)
+            else:
+                e.fn()
+        if record:
+            return [(e, e._ev) for e in entries]
+        return None
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        evs.append(step(True))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for rec in evs:
+        for e, (a, b) in rec:
+            e.times_ms.append(a.elapsed_time(b))
+    wall_ms = (t1 - t0) * 1e3 / max(args.steps, 1)
+
+    total_bytes = sum(e.bytes for e in entries)
+    ops_out = []
+    for e in entries:
+        ms = sum(e.times_ms) / len(e.times_ms)
+        rec = {"op": e.name, "workload": e.workload, "dtype": e.dtype, "ms": round(ms, 5)}
+        if e.kind == "hbm":
+            gbps = e.bytes / (ms * 1e-3) / 1e9
+            rec.update(bytes=e.bytes, GBps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
+                       rows_per_s=round(e.rows / (ms * 1e-3), 1))
+        elif e.kind == "mfma":
+            tf = e.flops / (ms * 1e-3) / 1e12
+            rec.update(flops=e.flops, TFLOPs=round(tf, 2), frac=round(tf / MFMA_PEAK_TFLOPS[e.dtype], 4),
+                       bytes=e.bytes)
+        else:
+            rec.update(flops=e.flops, TFLOPs=round(e.flops / (ms * 1e-3) / 1e12, 3), note="tape-driven, cache-resident")
+        ops_out.append(rec)
+    dom = max(entries, key=lambda e: sum(e.times_ms)) if entries else None
+    roof = None
+    if dom is not None:
+        ms = sum(dom.times_ms) / len(dom.times_ms)
+        if dom.kind == "mfma":
+            ach = dom.flops / (ms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS[dom.dtype]
+            roof = {"bound": "mfma", "kernel": dom.name, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": None}
+        else:
+            ach = dom.bytes / (ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": dom.name, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+    hbm_entries = [e for e in entries if e.kind == "hbm"]
+    hbm_ms = sum(sum(e.times_ms) / len(e.times_ms) for e in hbm_entries)
+    hbm_bytes = sum(e.bytes for e in hbm_entries)
+    out = {
+        "metric": "fwd+bwd achieved HBM GB/s (fraction of peak) per op; rows/s at d=768..4096",
+        "value": round(total_bytes / (wall_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32+bf16", "data": "synthetic",
+        "config": {"workload": "hot-path suite: every op fwd+bwd at the gpt2s-f32 8x1024x768, bf16 16384x4096 and "
+                               "bf16-stress shapes, plus the tiny transformer block on the tape",
+                   "parallelism": "none (1 GPU)"},
+        "memory_bound_GBps": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1) if hbm_ms else None,
+        "memory_bound_frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if hbm_ms else None,
+        "roofline": roof,
+        "cpu_baseline": None,
+        "ops": ops_out,
+    }
+    if args.ops_json:
+        with open(args.ops_json, "w") as f:
+            json.dump(ops_out, f, indent=1)
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline()
+        except Exception as ex:  # the baseline is reported, never required
+            out["cpu_baseline"] = {"error": repr(ex)}
+    del keep
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -239,6 +239,10 @@ xt_status xt_tape_value(xt_tape* t, xt_var v, xt_tensor* out_view);
 xt_status xt_tape_saved(xt_tape* t, xt_var v, int k, xt_tensor* out_view);
 /* Reverse pass from a one-element loss (seeded with 1). */
 xt_status xt_tape_backward(xt_tape* t, xt_var loss);
+/* Reverse pass from any node, seeded with the caller's upstream gradient
+ * `dout` (out's shape and dtype; unbatched): the vector-Jacobian product
+ * of [AE] "验证方法" (L = sum(W * out) gives dOut = W). */
+xt_status xt_tape_backward_seeded(xt_tape* t, xt_var out, const xt_tensor* dout);
 /* View of v's gradient; data == NULL if no gradient reached v. */
 xt_status xt_tape_grad(xt_tape* t, xt_var v, xt_tensor* out_view);
 xt_status xt_tape_zero_grad(xt_tape* t);

@@ -8,6 +8,7 @@ import numpy as np
 
 from oracle import fd
 from oracle.tape import Tape
+from oracle_block import block_loss
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -91,51 +92,6 @@ def test_composed_attention_fd():
     np.testing.assert_allclose(t.value(out), p @ V, rtol=1e-13)
 
 
-def block_loss(params, x0, targets, B, S, H, Dh, V, hidden, p_drop=0.0, seed=0):
-    """Small pre-norm block: h = x + Wo*attn(rope(Wq n), rope(Wk n), Wv n),
-    h = h + Wd*swiglu(Wg n, Wu n), logits = rms(h) Wout, mean CE."""
-    t = Tape()
-    P = {k: t.leaf(v) for k, v in params.items()}
-    x = t.leaf(x0)
-    D = H * Dh
-    n1 = t.rms_norm(x, P["g1"], 1e-5)
-    q = t.rope(t.matmul(n1, P["wq"]), Dh, 10000.0, S)
-    k = t.rope(t.matmul(n1, P["wk"]), Dh, 10000.0, S)
-    v = t.matmul(n1, P["wv"])
-    heads = []
-    for b in range(B):
-        for hh in range(H):
-            sl = (slice(b * S, (b + 1) * S), slice(hh * Dh, (hh + 1) * Dh))
-            qs, ks, vs = (t._push(t.value(z)[sl], [z], (lambda d, z=z, sl=sl: [_scatter(t.value(z).shape, sl, d)]))
-                          for z in (q, k, v))
-            heads.append(((b, hh), _attention(t, qs, ks, vs, S, Dh)))
-    cat = _concat(t, heads, B, S, H, Dh)
-    h = t.add(x, t.dropout(t.matmul(cat, P["wo"]), p_drop, seed))
-    n2 = t.rms_norm(h, P["g2"], 1e-5)
-    m = t.matmul(t.swiglu(t.matmul(n2, P["wg"]), t.matmul(n2, P["wu"])), P["wd"])
-    h2 = t.add(h, t.dropout(m, p_drop, seed + 1))
-    logits = t.matmul(t.rms_norm(h2, P["g3"], 1e-5), P["wout"])
-    return t, P, x, t.cross_entropy(logits, targets)
-
-
-def _scatter(shape, sl, d):
-    z = np.zeros(shape)
-    z[sl] = d
-    return z
-
-
-def _concat(t, heads, B, S, H, Dh):
-    shape = (B * S, H * Dh)
-    val = np.zeros(shape)
-    sls = []
-    for (b, hh), node in heads:
-        sl = (slice(b * S, (b + 1) * S), slice(hh * Dh, (hh + 1) * Dh))
-        val[sl] = t.value(node)
-        sls.append(sl)
-    nodes = [n for _, n in heads]
-    return t._push(val, nodes, lambda d: [d[sl] for sl in sls])
-
-
 def test_block_fd_on_sampled_entries():
     B, S, H, Dh, V, hidden = 2, 4, 2, 4, 11, 6
     D = H * Dh
@@ -148,14 +104,14 @@ def test_block_fd_on_sampled_entries():
     x0 = g.standard_normal((B * S, D))
     targets = g.integers(0, V, size=B * S)
     for p_drop in (0.0, 0.2):
-        t, P, x, L = block_loss(params, x0, targets, B, S, H, Dh, V, hidden, p_drop, 11)
+        t, P, x, L = block_loss(params, x0, targets, B, S, H, Dh, p_drop, 11)
         t.backward(L)
         for name in ("wq", "wk", "wo", "wd", "g1", "wout"):
             for idx in [(0,) * params[name].ndim, tuple(s - 1 for s in params[name].shape)]:
                 def f(eps):
                     pp = {k: v.copy() for k, v in params.items()}
                     pp[name][idx] += eps
-                    tt, _, _, LL = block_loss(pp, x0, targets, B, S, H, Dh, V, hidden, p_drop, 11)
+                    tt, _, _, LL = block_loss(pp, x0, targets, B, S, H, Dh, p_drop, 11)
                     return float(tt.value(LL)[0])
                 num = (f(1e-6) - f(-1e-6)) / 2e-6
                 assert abs(t.grad(P[name])[idx] - num) <= 1e-6 * max(1.0, abs(num)), (name, idx)
@@ -164,7 +120,7 @@ def test_block_fd_on_sampled_entries():
         def fx(eps):
             xx = x0.copy()
             xx[idx] += eps
-            tt, _, _, LL = block_loss(params, xx, targets, B, S, H, Dh, V, hidden, p_drop, 11)
+            tt, _, _, LL = block_loss(params, xx, targets, B, S, H, Dh, p_drop, 11)
             return float(tt.value(LL)[0])
         num = (fx(1e-6) - fx(-1e-6)) / 2e-6
         assert abs(t.grad(x)[idx] - num) <= 1e-6 * max(1.0, abs(num))
