@@ -128,9 +128,12 @@ xt_status check_matmul(const xt_params* prm, const xt_tensor* A, const xt_tensor
   return XT_OK;
 }
 
-size_t row_ws_bound(int np, int64_t R, int64_t C) {
+// Partial-gradient workspace of a row backward: the larger of the
+// register-resident and the generic plan (alignment is not known when the
+// caller asks), exactly what the launch will use.
+size_t row_ws_bound(RowKind kind, int dtype, int64_t R, int64_t C) {
   if (R <= 0 || C <= 0) return 0;
-  return (size_t)std::min<int64_t>(R, 256) * np * C * sizeof(float);
+  return std::max(row_bwd_workspace(kind, dtype, R, C, true), row_bwd_workspace(kind, dtype, R, C, false));
 }
 
 }  // namespace
@@ -160,8 +163,8 @@ size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm, const xt_t
   if (!is_bwd || !in || n_in < 1) return 0;
   const int64_t R = in[0].rows, C = in[0].cols;
   switch (op) {
-    case XT_OP_RMS_NORM: return row_ws_bound(1, R, C);
-    case XT_OP_LAYER_NORM: return row_ws_bound(2, R, C);
+    case XT_OP_RMS_NORM: return row_ws_bound(RK_RMS_BWD, in[0].dtype, R, C);
+    case XT_OP_LAYER_NORM: return row_ws_bound(RK_LN_BWD, in[0].dtype, R, C);
     case XT_OP_ADD_BIAS: return colsum_workspace(in[0].dtype, R, C);
     default: return 0;
   }
@@ -385,7 +388,7 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
       if (wanted(din, n_din, 1)) {
         XT_TRY(check_param_vec(&din[1], dout->cols, "dbias"));
         if (ws_bytes < ws_need || (ws_need && !ws)) return fail(XT_ERR_WORKSPACE, "add_bias backward needs %zu workspace bytes", ws_need);
-        XT_TRY(hip_status(launch_colsum(*dout, (float*)din[1].data, acc(1), ws, s), "add_bias dbias"));
+        XT_TRY(hip_status(launch_colsum(*dout, (float*)din[1].data, acc(1), ws, ws_bytes, s), "add_bias dbias"));
       }
       return XT_OK;
     }
@@ -424,7 +427,8 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
       if (!dx && !dg) return XT_OK;
       if (dg && (ws_bytes < ws_need || (ws_need && !ws))) return fail(XT_ERR_WORKSPACE, "rms_norm backward needs %zu workspace bytes", ws_need);
       xt_tensor ir = saved[0]; ir.ld = ld_of(saved[0]);
-      return hip_status(launch_rms_bwd(*dout, in[0], (const float*)in[1].data, ir, dx, acc(0), dg, acc(1), ws, s), "rms_norm backward");
+      return hip_status(launch_rms_bwd(*dout, in[0], (const float*)in[1].data, ir, dx, acc(0), dg, acc(1), ws, ws_bytes, s),
+                        "rms_norm backward");
     }
     case XT_OP_LAYER_NORM: {
       XT_TRY(need(3, 2, 3));
@@ -443,7 +447,8 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
       if ((dg || db) && (ws_bytes < ws_need || (ws_need && !ws))) return fail(XT_ERR_WORKSPACE, "layer_norm backward needs %zu workspace bytes", ws_need);
       xt_tensor mu = saved[0], rs = saved[1];
       mu.ld = ld_of(saved[0]); rs.ld = ld_of(saved[1]);
-      return hip_status(launch_ln_bwd(*dout, in[0], (const float*)in[1].data, mu, rs, dx, acc(0), dg, acc(1), db, acc(2), ws, s),
+      return hip_status(launch_ln_bwd(*dout, in[0], (const float*)in[1].data, mu, rs, dx, acc(0), dg, acc(1), db, acc(2), ws,
+                                      ws_bytes, s),
                         "layer_norm backward");
     }
     case XT_OP_SOFTMAX: {

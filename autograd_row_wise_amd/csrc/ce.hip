@@ -74,7 +74,7 @@ __global__ __launch_bounds__(CE_BLOCK) void ce_fwd_k(
     for (; p + 3 * CE_BLOCK < bpi; p += 4 * CE_BLOCK) {
       float a[4][V];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) io<T>::unpack(bq[p + u * CE_BLOCK], a[u]);
+      for (int u = 0; u < 4; ++u) io<T>::unpack(ld_nt(bq + p + u * CE_BLOCK), a[u]);
       float pm = a[0][0];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(CE_BLOCK) void ce_fwd_k(
     }
     for (; p < bpi; p += CE_BLOCK) {
       float a[V];
-      io<T>::unpack(bq[p], a);
+      io<T>::unpack(ld_nt(bq + p), a);
       float pm = a[0];
 #pragma unroll
       for (int k = 1; k < V; ++k) pm = fmaxf(pm, a[k]);
@@ -142,75 +142,62 @@ __global__ __launch_bounds__(1024) void ce_mean_k(const float* __restrict__ loss
   if (threadIdx.x == 0) L[0] = R > 0 ? (float)(part[0] / (double)R) : __builtin_nanf("");
 }
 
+// Backward: a 2-D grid, block (x, y) writes the x-th run of CE_BLOCK
+// 16-byte packs of row y (one pack per thread, the pattern that streams
+// fastest), block 0 also the scalar head and the last block the tail.
 template <typename T>
 __global__ __launch_bounds__(CE_BLOCK) void ce_bwd_k(
     const float* __restrict__ dL, const void* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ tgt, int64_t ldt, const float* __restrict__ lse, int64_t ldl,
     void* __restrict__ dx, int64_t lddx, int acc, int64_t R, int64_t V_) {
   constexpr int V = io<T>::VEC;
-  constexpr int U = 4;                         // packs in flight per thread
   const float scale = dL[0] / (float)R;
   const int n = (int)V_;
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+  for (int64_t r = blockIdx.y; r < R; r += gridDim.y) {
     const T* row = reinterpret_cast<const T*>(logits) + r * ld;
     T* orow = reinterpret_cast<T*>(dx) + r * lddx;
     const int32_t t = tgt[r * ldt];
     const bool ok = t >= 0 && t < n;
     // p = exp(x - lse) = 2^(x*log2e - lse*log2e); a bad target poisons the row
     const float nl = ok ? lse[r * ldl] * LOG2E : __builtin_nanf("");
-    auto val = [&](float x, int c) {
-      const float p = exp2_(fmaf(x, LOG2E, -nl));
-      return (c == t ? p - 1.f : p) * scale;
-    };
     auto put = [&](int c) {
-      const float v = val(io<T>::ld(row + c), c);
+      const float p = exp2_(fmaf(io<T>::ld(row + c), LOG2E, -nl));
+      const float v = (c == t ? p - 1.f : p) * scale;
       io<T>::st(orow + c, acc ? acc_add(io<T>::ld(orow + c), v) : v);
     };
     int64_t head64, bp64;
     split_row<T>(row, V_, head64, bp64);
     const int head = (int)head64, bp = (int)bp64;
-    if (((((uintptr_t)row) ^ ((uintptr_t)orow)) & 15) != 0) {      // misaligned pair: scalar row
-      for (int c = threadIdx.x; c < n; c += CE_BLOCK) put(c);
+    const int x = blockIdx.x, nx = gridDim.x;
+    if (((((uintptr_t)row) ^ ((uintptr_t)orow)) & 15) != 0) {      // misaligned pair: scalar
+      for (int c = x * CE_BLOCK + threadIdx.x; c < n; c += nx * CE_BLOCK) put(c);
       continue;
     }
-    for (int c = threadIdx.x; c < head; c += CE_BLOCK) put(c);
+    if (x == 0)
+      for (int c = threadIdx.x; c < head; c += CE_BLOCK) put(c);
+    if (x == nx - 1)
+      for (int c = head + bp * V + threadIdx.x; c < n; c += CE_BLOCK) put(c);
     const uint4* body = reinterpret_cast<const uint4*>(row + head);
     uint4* obody = reinterpret_cast<uint4*>(orow + head);
-    // packs p, p+B, ..., p+(U-1)B: all loads are issued before any store
-    for (int p0 = threadIdx.x; p0 < bp; p0 += U * CE_BLOCK) {
-      uint4 q[U], o[U];
+    for (int p = x * CE_BLOCK + threadIdx.x; p < bp; p += nx * CE_BLOCK) {
+      float a[V];
+      io<T>::unpack(ld_nt(body + p), a);
+      float b[V];
+      if (acc) io<T>::unpack(ld_nt(obody + p), b);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + u * CE_BLOCK;
-        if (p < bp) {
-          q[u] = body[p];
-          if (acc) o[u] = obody[p];
-        }
+      for (int k = 0; k < V; ++k) a[k] = exp2_(fmaf(a[k], LOG2E, -nl)) * scale;
+      const int c0 = head + p * V;
+      if ((unsigned)(t - c0) < (unsigned)V) {     // this pack holds the target column
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+          if (c0 + k == t) a[k] = (exp2_(fmaf(io<T>::ld(row + t), LOG2E, -nl)) - 1.f) * scale;
       }
+      if (acc) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = p0 + u * CE_BLOCK;
-        if (p >= bp) break;
-        float a[V];
-        io<T>::unpack(q[u], a);
-#pragma unroll
-        for (int k = 0; k < V; ++k) a[k] = exp2_(fmaf(a[k], LOG2E, -nl)) * scale;
-        const int c0 = head + p * V;
-        if ((unsigned)(t - c0) < (unsigned)V) {     // this pack holds the target column
-#pragma unroll
-          for (int k = 0; k < V; ++k)
-            if (c0 + k == t) a[k] = (exp2_(fmaf(io<T>::ld(row + t), LOG2E, -nl)) - 1.f) * scale;
-        }
-        if (acc) {
-          float b[V];
-          io<T>::unpack(o[u], b);
-#pragma unroll
-          for (int k = 0; k < V; ++k) a[k] = acc_add(b[k], a[k]);
-        }
-        obody[p] = io<T>::pack(a);
+        for (int k = 0; k < V; ++k) a[k] = acc_add(b[k], a[k]);
       }
+      st_nt(obody + p, io<T>::pack(a));
     }
-    for (int c = head + bp * V + threadIdx.x; c < n; c += CE_BLOCK) put(c);
   }
 }
 
@@ -237,10 +224,14 @@ hipError_t launch_ce_bwd(const float* dL, const xt_tensor& x, const int32_t* tar
                          const xt_tensor& dx, bool acc, hipStream_t s) {
   const int64_t R = x.rows, V_ = x.cols;
   if (R == 0) return hipSuccess;
+  // x blocks per row: enough CE_BLOCK-pack runs to cover the aligned body
+  const int V = x.dtype == XT_F32 ? 4 : 8;
+  const int64_t nx = std::max<int64_t>(1, (V_ / V + CE_BLOCK - 1) / CE_BLOCK);
+  const dim3 grid((unsigned)nx, (unsigned)std::min<int64_t>(R, 65535));
   if (x.dtype == XT_F32)
-    ce_bwd_k<float><<<ce_grid(R), CE_BLOCK, 0, s>>>(dL, x.data, x.ld, targets, ld_t, lse, ld_lse, dx.data, dx.ld, acc, R, V_);
+    ce_bwd_k<float><<<grid, CE_BLOCK, 0, s>>>(dL, x.data, x.ld, targets, ld_t, lse, ld_lse, dx.data, dx.ld, acc, R, V_);
   else
-    ce_bwd_k<bf16_t><<<ce_grid(R), CE_BLOCK, 0, s>>>(dL, x.data, x.ld, targets, ld_t, lse, ld_lse, dx.data, dx.ld, acc, R, V_);
+    ce_bwd_k<bf16_t><<<grid, CE_BLOCK, 0, s>>>(dL, x.data, x.ld, targets, ld_t, lse, ld_lse, dx.data, dx.ld, acc, R, V_);
   return hipGetLastError();
 }
 

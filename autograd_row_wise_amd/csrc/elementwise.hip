@@ -19,7 +19,7 @@ namespace xt {
 namespace {
 
 constexpr int EW_BLOCK = 256;
-constexpr int EW_UNROLL = 4;
+constexpr int EW_UNROLL = 1;   // one pack per thread over a full grid (see common.h)
 
 // ---- loading N elements of type T as f32 (aligned, in bounds) --------------
 template <typename T, int N>
@@ -103,7 +103,7 @@ struct RawN {
         w[0] = make_uint4(q.x, q.y, 0, 0);
       } else {
 #pragma unroll
-        for (int i = 0; i < WORDS; ++i) w[i] = reinterpret_cast<const uint4*>(row + c0)[i];
+        for (int i = 0; i < WORDS; ++i) w[i] = ld_nt(reinterpret_cast<const uint4*>(row + c0) + i);
       }
     } else {
       TS tmp[WORDS * 16 / sizeof(TS)];
@@ -344,12 +344,12 @@ bool aligned(const xt_tensor* t) {
 }
 
 dim3 ew_grid(int64_t R, int64_t C, int V, bool vec) {
+  // one thread per pack (vec) or per element, every pack covered in one pass
   const int64_t ppr = vec ? cdiv(C, V) : C;
   const int64_t per_block = vec ? (int64_t)EW_BLOCK * EW_UNROLL : EW_BLOCK;
-  int64_t gx = std::min<int64_t>(cdiv(ppr, per_block), 8192);
-  int64_t gy = std::min<int64_t>(R, std::max<int64_t>(1, 8192 / gx));
-  gy = std::min<int64_t>(gy, 65535);
-  return dim3((unsigned)std::max<int64_t>(gx, 1), (unsigned)std::max<int64_t>(gy, 1));
+  const int64_t gx = std::min<int64_t>(cdiv(ppr, per_block), 0x7fffffff);
+  const int64_t gy = std::min<int64_t>(std::max<int64_t>(R, 1), 65535);
+  return dim3((unsigned)std::max<int64_t>(gx, 1), (unsigned)gy);
 }
 
 template <typename T, typename TS, int OP>

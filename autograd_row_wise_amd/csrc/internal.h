@@ -32,16 +32,18 @@ size_t row_bwd_workspace(RowKind kind, int dtype, int64_t R, int64_t C, bool ali
 
 hipError_t launch_rms_fwd(const xt_tensor& x, const float* gamma, const xt_tensor& y,
                           const xt_tensor& inv_rms, float eps, hipStream_t s);
+// Backward launchers never write past ws_bytes: the block count is clamped so
+// the per-block partial rows fit the workspace they are given.
 hipError_t launch_rms_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                           const xt_tensor& inv_rms, const xt_tensor* dx, bool acc_dx,
-                          float* dgamma, bool acc_dgamma, void* ws, hipStream_t s);
+                          float* dgamma, bool acc_dgamma, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_ln_fwd(const xt_tensor& x, const float* gamma, const float* beta,
                          const xt_tensor& y, const xt_tensor& mean, const xt_tensor& rstd,
                          float eps, hipStream_t s);
 hipError_t launch_ln_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                          const xt_tensor& mean, const xt_tensor& rstd,
                          const xt_tensor* dx, bool acc_dx, float* dgamma, bool acc_dgamma,
-                         float* dbeta, bool acc_dbeta, void* ws, hipStream_t s);
+                         float* dbeta, bool acc_dbeta, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_softmax_fwd(const xt_tensor& x, const xt_tensor& y, float alpha,
                               int causal, int seq_len, hipStream_t s);
 hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx,
@@ -49,7 +51,7 @@ hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_t
 
 // Column sums: out[c] (+)= sum_r d[r, c]  (add_bias backward).
 size_t colsum_workspace(int dtype, int64_t R, int64_t C);
-hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, hipStream_t s);
+hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, size_t ws_bytes, hipStream_t s);
 
 // --- cross entropy (ce.hip) --------------------------------------------
 hipError_t launch_ce_fwd(const xt_tensor& logits, const int32_t* targets, int64_t ld_t,

@@ -55,11 +55,11 @@ __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t
         const int64_t h = w / per_head, vi = w % per_head;
         const int64_t ca = h * head_dim + vi * V, cb = ca + half;
         if constexpr (VEC) {
-          io<T>::unpack(*reinterpret_cast<const uint4*>(xr + ca), a[u]);
-          io<T>::unpack(*reinterpret_cast<const uint4*>(xr + cb), b[u]);
+          io<T>::unpack(ld_nt(xr + ca), a[u]);
+          io<T>::unpack(ld_nt(xr + cb), b[u]);
           if (acc) {
-            io<T>::unpack(*reinterpret_cast<const uint4*>(yr + ca), oa[u]);
-            io<T>::unpack(*reinterpret_cast<const uint4*>(yr + cb), ob[u]);
+            io<T>::unpack(ld_nt(yr + ca), oa[u]);
+            io<T>::unpack(ld_nt(yr + cb), ob[u]);
           }
         } else {
           a[u][0] = io<T>::ld(xr + ca);
@@ -83,8 +83,8 @@ __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t
           if (acc) { ya[k] = acc_add(oa[u][k], ya[k]); yb[k] = acc_add(ob[u][k], yb[k]); }
         }
         if constexpr (VEC) {
-          *reinterpret_cast<uint4*>(yr + ca) = io<T>::pack(ya);
-          *reinterpret_cast<uint4*>(yr + cb) = io<T>::pack(yb);
+          st_nt(yr + ca, io<T>::pack(ya));
+          st_nt(yr + cb, io<T>::pack(yb));
         } else {
           io<T>::st(yr + ca, ya[0]);
           io<T>::st(yr + cb, yb[0]);

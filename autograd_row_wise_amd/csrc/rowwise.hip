@@ -26,8 +26,8 @@ namespace xt {
 
 namespace {
 
-constexpr int BWD_BLOCK = 1024;
-constexpr int BWD_GRID_MAX = 256;     // one backward block per CU
+constexpr int BWD_BLOCK = 512;       // 8 waves: up to 256 VGPRs per thread, no spills
+constexpr int BWD_GRID_MAX = 512;     // two backward blocks per CU
 constexpr int FWD_GRID_MAX = 4096;
 constexpr int GEN_BLOCK = 256;
 
@@ -40,6 +40,19 @@ template <typename T> __device__ __forceinline__ const T* row_ptr(const void* p,
 }
 template <typename T> __device__ __forceinline__ T* row_ptr_w(void* p, int64_t r, int64_t ld) {
   return reinterpret_cast<T*>(p) + r * ld;
+}
+
+// Whole 16-byte pack store with optional accumulation (row width is a
+// multiple of the pack width on the register-resident path).
+template <typename T>
+__device__ __forceinline__ void store_full(T* p, float* f, bool acc) {
+  if (acc) {
+    float o[io<T>::VEC];
+    io<T>::unpack(ld_nt(p), o);
+#pragma unroll
+    for (int k = 0; k < io<T>::VEC; ++k) f[k] = acc_add(o[k], f[k]);
+  }
+  st_nt(p, io<T>::pack(f));
 }
 
 // Every fast kernel walks its rows with the next row's packs already in
@@ -56,17 +69,18 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   const int64_t stride = (int64_t)gridDim.x * NG;
   float gam[NV][V];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+  for (int j = 0; j < NV; ++j) load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
   RowPacks<T, NV, G> cur, nxt;
   int64_t base = (int64_t)blockIdx.x * NG;
-  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, C, base + g < R);
+  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
   for (; base < R; base += stride) {
     const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
-    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, C, rn < R);
+    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float v[NV][V];
     cur.unpack(v);
     float ss = 0.f;
@@ -80,12 +94,12 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
       T* yr = row_ptr_w<T>(y, r, ldy);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int64_t c0 = (int64_t)(j * G + gl) * V;
-        if (c0 < C) {
+        const int c0 = (j * G + gl) * V;
+        if (c0 < Ci) {
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) o[k] = v[j][k] * irv * gam[j][k];
-          store_pack<T>(yr, c0, C, o);
+          st_nt(yr + c0, io<T>::pack(o));
         }
       }
       if (gl == 0) ir[r * ldir] = irv;
@@ -100,6 +114,7 @@ template <int NV, int V, int G, int NG, int NP, int BLOCK>
 __device__ __forceinline__ void fold_partials(float (&pp)[NP][NV][V], float* red, float* part,
                                               int64_t C) {
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   for (int gi = 0; gi < NG; ++gi) {
     if (g == gi) {
 #pragma unroll
@@ -108,7 +123,7 @@ __device__ __forceinline__ void fold_partials(float (&pp)[NP][NV][V], float* red
         for (int j = 0; j < NV; ++j)
 #pragma unroll
           for (int k = 0; k < V; ++k) {
-            const int64_t c = (int64_t)(j * G + gl) * V + k;
+            const int c = (j * G + gl) * V + k;
             if (c < C) red[q * C + c] = (gi == 0) ? pp[q][j][k] : red[q * C + c] + pp[q][j][k];
           }
     }
@@ -128,10 +143,11 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
   extern __shared__ float red[];               // C floats
   __shared__ float lds[BWD_BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   float gam[NV][V], pp[1][NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+    load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
 #pragma unroll
     for (int k = 0; k < V; ++k) pp[0][j][k] = 0.f;
   }
@@ -140,15 +156,15 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
   RowPacks<T, NV, G> cd, cx, nd, nx;
   {
     const int64_t r = start + g;
-    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, C, r < end);
-    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, C, r < end);
+    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
+    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
   }
   for (int64_t base = start; base < end; base += NG) {
     const int64_t r = base + g, rn = base + NG + g;
     const bool active = r < end;
     if (base + NG < end) {
-      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, C, rn < end);
-      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, C, rn < end);
+      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
+      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
     }
     float dv[NV][V], xv[NV][V];
     cd.unpack(dv);
@@ -165,15 +181,15 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
       T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int64_t c0 = (int64_t)(j * G + gl) * V;
-        if (c0 < C) {
+        const int c0 = (j * G + gl) * V;
+        if (c0 < Ci) {
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) {
             o[k] = irv * (dv[j][k] * gam[j][k]) - xv[j][k] * c1;
             pp[0][j][k] += dv[j][k] * xv[j][k] * irv;
           }
-          if (dxr) store_pack_acc<T>(dxr, c0, C, o, acc_dx != 0);
+          if (dxr) store_full<T>(dxr + c0, o, acc_dx != 0);
         }
       }
     }
@@ -193,20 +209,21 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   const int64_t stride = (int64_t)gridDim.x * NG;
   float gam[NV][V], bet[NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
-    load_f32s<V>(beta, (int64_t)(j * G + gl) * V, C, bet[j]);
+    load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
+    load_f32s<V, int>(beta, (j * G + gl) * V, Ci, bet[j]);
   }
   RowPacks<T, NV, G> cur, nxt;
   int64_t base = (int64_t)blockIdx.x * NG;
-  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, C, base + g < R);
+  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
   for (; base < R; base += stride) {
     const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
-    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, C, rn < R);
+    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float v[NV][V];
     cur.unpack(v);
     float s = 0.f;
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         const float t = v[j][k] - mu;
-        if ((int64_t)(j * G + gl) * V + k < C) q += t * t;
+        if ((j * G + gl) * V + k < Ci) q += t * t;
       }
     const float var = group_sum<RW>(q, lds) * invC;
     const float rs = rsqrtf(var + eps);
@@ -229,12 +246,12 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
       T* yr = row_ptr_w<T>(y, r, ldy);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int64_t c0 = (int64_t)(j * G + gl) * V;
-        if (c0 < C) {
+        const int c0 = (j * G + gl) * V;
+        if (c0 < Ci) {
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) o[k] = (v[j][k] - mu) * rs * gam[j][k] + bet[j][k];
-          store_pack<T>(yr, c0, C, o);
+          st_nt(yr + c0, io<T>::pack(o));
         }
       }
       if (gl == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
@@ -253,10 +270,11 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
   extern __shared__ float red[];               // 2C floats
   __shared__ float lds[2 * BWD_BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   float gam[NV][V], pp[2][NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V>(gamma, (int64_t)(j * G + gl) * V, C, gam[j]);
+    load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
 #pragma unroll
     for (int k = 0; k < V; ++k) { pp[0][j][k] = 0.f; pp[1][j][k] = 0.f; }
   }
@@ -265,15 +283,15 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
   RowPacks<T, NV, G> cd, cx, nd, nx;
   {
     const int64_t r = start + g;
-    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, C, r < end);
-    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, C, r < end);
+    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
+    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
   }
   for (int64_t base = start; base < end; base += NG) {
     const int64_t r = base + g, rn = base + NG + g;
     const bool active = r < end;
     if (base + NG < end) {
-      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, C, rn < end);
-      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, C, rn < end);
+      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
+      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
     }
     const float mu = active ? mean[r * ldm] : 0.f;
     const float rs = active ? rstd[r * ldr] : 0.f;
@@ -283,10 +301,10 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      const int c0 = (j * G + gl) * V;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
-        const bool ok = c0 + k < C;
+        const bool ok = c0 + k < Ci;
         xh[j][k] = ok ? (xh[j][k] - mu) * rs : 0.f;
         const float gv = dv[j][k] * gam[j][k];
         s1 += gv;
@@ -299,8 +317,8 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
       T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int64_t c0 = (int64_t)(j * G + gl) * V;
-        if (c0 < C) {
+        const int c0 = (j * G + gl) * V;
+        if (c0 < Ci) {
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) {
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
             pp[0][j][k] += dv[j][k] * xh[j][k];
             pp[1][j][k] += dv[j][k];
           }
-          if (dxr) store_pack_acc<T>(dxr, c0, C, o, acc_dx != 0);
+          if (dxr) store_full<T>(dxr + c0, o, acc_dx != 0);
         }
       }
     }
@@ -326,22 +344,23 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   const float NEG_INF = -__builtin_inff();
   const int64_t stride = (int64_t)gridDim.x * NG;
   RowPacks<T, NV, G> cur, nxt;
   int64_t base = (int64_t)blockIdx.x * NG;
-  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, C, base + g < R);
+  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
   for (; base < R; base += stride) {
     const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
-    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, C, rn < R);
-    const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;   // valid columns
+    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
+    const int lim = causal ? (int)min(C, (int64_t)(r % seq_len) + 1) : Ci;   // valid columns
     float v[NV][V];
     cur.unpack(v);
     float m = NEG_INF;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int64_t c0 = (int64_t)(j * G + gl) * V;
+      const int c0 = (j * G + gl) * V;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         v[j][k] = (active && c0 + k < lim) ? alpha * v[j][k] : NEG_INF;
@@ -363,12 +382,12 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
       T* yr = row_ptr_w<T>(y, r, ldy);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int64_t c0 = (int64_t)(j * G + gl) * V;
-        if (c0 < C) {
+        const int c0 = (j * G + gl) * V;
+        if (c0 < Ci) {
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) o[k] = v[j][k] * inv;
-          store_pack<T>(yr, c0, C, o);
+          st_nt(yr + c0, io<T>::pack(o));
         }
       }
     }
@@ -383,20 +402,21 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
+  const int Ci = (int)C;
   const int64_t stride = (int64_t)gridDim.x * NG;
   RowPacks<T, NV, G> cd, cy, nd, ny;
   int64_t base = (int64_t)blockIdx.x * NG;
   {
     const int64_t r = base + g;
-    cd.load(row_ptr<T>(d, r < R ? r : 0, ldd), gl, C, r < R);
-    cy.load(row_ptr<T>(y, r < R ? r : 0, ldy), gl, C, r < R);
+    cd.load(row_ptr<T>(d, r < R ? r : 0, ldd), gl, Ci, r < R);
+    cy.load(row_ptr<T>(y, r < R ? r : 0, ldy), gl, Ci, r < R);
   }
   for (; base < R; base += stride) {
     const int64_t r = base + g, rn = base + stride + g;
     const bool active = r < R;
     if (base + stride < R) {
-      nd.load(row_ptr<T>(d, rn < R ? rn : 0, ldd), gl, C, rn < R);
-      ny.load(row_ptr<T>(y, rn < R ? rn : 0, ldy), gl, C, rn < R);
+      nd.load(row_ptr<T>(d, rn < R ? rn : 0, ldd), gl, Ci, rn < R);
+      ny.load(row_ptr<T>(y, rn < R ? rn : 0, ldy), gl, Ci, rn < R);
     }
     float dv[NV][V], yv[NV][V];
     cd.unpack(dv);
@@ -411,12 +431,12 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
       T* dxr = row_ptr_w<T>(dx, r, lddx);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int64_t c0 = (int64_t)(j * G + gl) * V;
-        if (c0 < C) {
+        const int c0 = (j * G + gl) * V;
+        if (c0 < Ci) {
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) o[k] = alpha * yv[j][k] * (dv[j][k] - dot);
-          store_pack_acc<T>(dxr, c0, C, o, acc != 0);
+          store_full<T>(dxr + c0, o, acc != 0);
         }
       }
     }
@@ -653,35 +673,51 @@ __global__ void fill_f32_k(float* p, int64_t n, float v) {
 }
 
 // ============================================================== dispatching
-int pick_rw(int rw_idx) { return rw_idx == 0 ? 1 : (rw_idx == 1 ? 4 : 16); }
-
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_bwd(RowKind k) { return k == RK_RMS_BWD || k == RK_LN_BWD; }
+
+// Register-resident shapes each kind may use: waves per row, block size and
+// the largest packs-per-thread for f32 / bf16.  The limits keep every
+// selectable instantiation free of register spills (checked in the gfx950
+// ISA): 1024-thread blocks cap a thread at 128 VGPRs, 512-thread blocks at
+// 256, and the kernels hold the current and the prefetched row.
+struct RowShape { int rw, block, nv_f32, nv_bf16; };
+
+int row_shapes(RowKind k, const RowShape** out) {
+  static const RowShape fwd[] = {{1, 256, 8, 4}, {4, 256, 8, 4}, {8, 512, 8, 8}};
+  static const RowShape lnf[] = {{1, 256, 8, 4}, {4, 256, 8, 4}, {8, 512, 8, 4}};
+  static const RowShape smb[] = {{1, 256, 8, 4}, {4, 256, 8, 4}, {16, 1024, 4, 4}};
+  static const RowShape bwd[] = {{1, BWD_BLOCK, 4, 2}, {4, BWD_BLOCK, 4, 2}, {8, BWD_BLOCK, 4, 2}};
+  if (k == RK_SM_BWD) *out = smb;
+  else if (is_bwd(k)) *out = bwd;
+  else if (k == RK_LN_FWD) *out = lnf;
+  else *out = fwd;
+  return 3;
+}
 
 }  // namespace
 
 RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
   RowPlan p{};
   const int V = dtype == XT_F32 ? 4 : 8;
-  const int emax = is_bwd(kind) ? 16 : 32;
-  const int nvmax = emax / V;
   const int64_t packs = cdiv(C, V);
   p.fast = false;
-  if (aligned && C > 0) {
-    for (int i = 0; i < 3 && !p.fast; ++i) {
-      const int rw = pick_rw(i);
-      const int64_t need = cdiv(packs, (int64_t)WAVE * rw);
+  if (aligned && C > 0 && C % V == 0) {
+    const RowShape* sh;
+    const int n = row_shapes(kind, &sh);
+    for (int i = 0; i < n && !p.fast; ++i) {
+      const int64_t need = cdiv(packs, (int64_t)WAVE * sh[i].rw);
       int nv = 1;
       while (nv < need) nv *= 2;
-      if (nv <= nvmax && nv <= 8) { p.fast = true; p.rw = rw; p.nv = nv; }
+      const int nvmax = dtype == XT_F32 ? sh[i].nv_f32 : sh[i].nv_bf16;
+      if (nv <= nvmax) { p.fast = true; p.rw = sh[i].rw; p.nv = nv; p.block = sh[i].block; }
     }
     // backward folds parameter partials in LDS: keep them within 64 KiB
     const int np = kind == RK_LN_BWD ? 2 : 1;
     if (is_bwd(kind) && (int64_t)np * C * 4 > 65536) p.fast = false;
   }
   if (p.fast) {
-    p.block = is_bwd(kind) ? BWD_BLOCK : (p.rw == 16 ? 1024 : 256);
     p.groups = p.block / (WAVE * p.rw);
     const int64_t gmax = is_bwd(kind) ? BWD_GRID_MAX : FWD_GRID_MAX;
     p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(R, p.groups), gmax));
@@ -699,23 +735,28 @@ size_t row_bwd_workspace(RowKind kind, int dtype, int64_t R, int64_t C, bool ali
   return (size_t)p.grid * np * C * sizeof(float);
 }
 
-#define XT_ROW_SWITCH(T, P, ...)                                               \
-  do {                                                                       \
-    const int rw_ = (P).rw, nv_ = (P).nv;                                    \
-    if (rw_ == 1 && nv_ == 1) { constexpr int RW = 1, NV = 1; __VA_ARGS__; }        \
-    else if (rw_ == 1 && nv_ == 2) { constexpr int RW = 1, NV = 2; __VA_ARGS__; }   \
-    else if (rw_ == 1 && nv_ == 4) { constexpr int RW = 1, NV = 4; __VA_ARGS__; }   \
-    else if (rw_ == 1 && nv_ == 8) { constexpr int RW = 1, NV = 8; __VA_ARGS__; }   \
-    else if (rw_ == 4 && nv_ == 1) { constexpr int RW = 4, NV = 1; __VA_ARGS__; }   \
-    else if (rw_ == 4 && nv_ == 2) { constexpr int RW = 4, NV = 2; __VA_ARGS__; }   \
-    else if (rw_ == 4 && nv_ == 4) { constexpr int RW = 4, NV = 4; __VA_ARGS__; }   \
-    else if (rw_ == 4 && nv_ == 8) { constexpr int RW = 4, NV = 8; __VA_ARGS__; }   \
-    else if (rw_ == 16 && nv_ == 1) { constexpr int RW = 16, NV = 1; __VA_ARGS__; } \
-    else if (rw_ == 16 && nv_ == 2) { constexpr int RW = 16, NV = 2; __VA_ARGS__; } \
-    else if (rw_ == 16 && nv_ == 4) { constexpr int RW = 16, NV = 4; __VA_ARGS__; } \
-    else if (rw_ == 16 && nv_ == 8) { constexpr int RW = 16, NV = 8; __VA_ARGS__; } \
-    else return hipErrorInvalidValue;                                        \
+// Dispatch over the (RW, NV, BLOCK) shapes plan_rows can return.
+#define XT_ROW_CASE(RW_, NV_, B_, ...) \
+  else if (p.rw == RW_ && p.nv == NV_ && p.block == B_) { constexpr int RW = RW_, NV = NV_, BLOCK = B_; (void)BLOCK; __VA_ARGS__; }
+#define XT_ROW_SWITCH_FWD(...) \
+  do { \
+    if (false) {} \
+    XT_ROW_CASE(1, 1, 256, __VA_ARGS__) XT_ROW_CASE(1, 2, 256, __VA_ARGS__) XT_ROW_CASE(1, 4, 256, __VA_ARGS__) XT_ROW_CASE(1, 8, 256, __VA_ARGS__) XT_ROW_CASE(4, 1, 256, __VA_ARGS__) XT_ROW_CASE(4, 2, 256, __VA_ARGS__) XT_ROW_CASE(4, 4, 256, __VA_ARGS__) XT_ROW_CASE(4, 8, 256, __VA_ARGS__) XT_ROW_CASE(8, 1, 512, __VA_ARGS__) XT_ROW_CASE(8, 2, 512, __VA_ARGS__) XT_ROW_CASE(8, 4, 512, __VA_ARGS__) XT_ROW_CASE(8, 8, 512, __VA_ARGS__) \
+    else return hipErrorInvalidValue; \
   } while (0)
+#define XT_ROW_SWITCH_SMB(...) \
+  do { \
+    if (false) {} \
+    XT_ROW_CASE(1, 1, 256, __VA_ARGS__) XT_ROW_CASE(1, 2, 256, __VA_ARGS__) XT_ROW_CASE(1, 4, 256, __VA_ARGS__) XT_ROW_CASE(1, 8, 256, __VA_ARGS__) XT_ROW_CASE(4, 1, 256, __VA_ARGS__) XT_ROW_CASE(4, 2, 256, __VA_ARGS__) XT_ROW_CASE(4, 4, 256, __VA_ARGS__) XT_ROW_CASE(4, 8, 256, __VA_ARGS__) XT_ROW_CASE(16, 1, 1024, __VA_ARGS__) XT_ROW_CASE(16, 2, 1024, __VA_ARGS__) XT_ROW_CASE(16, 4, 1024, __VA_ARGS__) XT_ROW_CASE(16, 8, 1024, __VA_ARGS__) \
+    else return hipErrorInvalidValue; \
+  } while (0)
+#define XT_ROW_SWITCH_BWD(...) \
+  do { \
+    if (false) {} \
+    XT_ROW_CASE(1, 1, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(1, 2, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(1, 4, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(4, 1, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(4, 2, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(4, 4, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(8, 1, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(8, 2, BWD_BLOCK, __VA_ARGS__) XT_ROW_CASE(8, 4, BWD_BLOCK, __VA_ARGS__) \
+    else return hipErrorInvalidValue; \
+  } while (0)
+
 
 static bool aligned16(const xt_tensor& t) {
   const int es = t.dtype == XT_F32 ? 4 : 2;
@@ -729,12 +770,8 @@ static hipError_t rms_fwd_t(const xt_tensor& x, const float* gamma, const xt_ten
   const float invC = 1.0f / (float)C;
   const RowPlan p = plan_rows(RK_RMS_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
   if (p.fast) {
-    XT_ROW_SWITCH(T, p, {
-      if (p.block == 256)
-        rms_fwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
-      else
-        rms_fwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
-    });
+    XT_ROW_SWITCH_FWD(
+        rms_fwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC));
   } else {
     rms_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
   }
@@ -748,22 +785,30 @@ hipError_t launch_rms_fwd(const xt_tensor& x, const float* gamma, const xt_tenso
                            : rms_fwd_t<bf16_t>(x, gamma, y, inv_rms, eps, s);
 }
 
+// Largest block count whose partial rows (np vectors of C floats) fit ws_bytes.
+static RowPlan clamp_to_workspace(RowPlan p, int np, int64_t C, size_t ws_bytes, bool want) {
+  if (!want) return p;
+  const int64_t fit = (int64_t)(ws_bytes / ((size_t)np * C * sizeof(float)));
+  if (fit < p.grid) p.grid = (int)fit;
+  return p;
+}
+
 template <typename T>
 static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                             const xt_tensor& ir, const xt_tensor* dx, bool acc_dx, float* dgamma,
-                            bool acc_dg, void* ws, hipStream_t s) {
+                            bool acc_dg, void* ws, size_t ws_bytes, hipStream_t s) {
   const int64_t R = d.rows, C = d.cols;
   const float invC = 1.0f / (float)C;
   const bool al = aligned16(d) && aligned16(x) && (!dx || aligned16(*dx));
-  const RowPlan p = plan_rows(RK_RMS_BWD, d.dtype, R, C, al);
+  const RowPlan p = clamp_to_workspace(plan_rows(RK_RMS_BWD, d.dtype, R, C, al), 1, C, ws_bytes, dgamma != nullptr);
+  if (p.grid < 1) return hipErrorInvalidValue;
   float* part = dgamma ? (float*)ws : nullptr;
   const int64_t rpb = cdiv(R, p.grid);
   if (p.fast) {
     const size_t shm = dgamma ? (size_t)C * sizeof(float) : 0;
-    XT_ROW_SWITCH(T, p, {
+    XT_ROW_SWITCH_BWD(
       rms_bwd_fast<T, RW, NV><<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
-                                                             dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC, rpb);
-    });
+                                                             dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC, rpb));
   } else {
     if (dx)
       rms_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld, dx->data, dx->ld, acc_dx, R, C, invC);
@@ -776,10 +821,10 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
 
 hipError_t launch_rms_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                           const xt_tensor& inv_rms, const xt_tensor* dx, bool acc_dx,
-                          float* dgamma, bool acc_dgamma, void* ws, hipStream_t s) {
+                          float* dgamma, bool acc_dgamma, void* ws, size_t ws_bytes, hipStream_t s) {
   if (d.rows == 0) return hipSuccess;
-  return d.dtype == XT_F32 ? rms_bwd_t<float>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, s)
-                           : rms_bwd_t<bf16_t>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, s);
+  return d.dtype == XT_F32 ? rms_bwd_t<float>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, ws_bytes, s)
+                           : rms_bwd_t<bf16_t>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, ws_bytes, s);
 }
 
 template <typename T>
@@ -790,12 +835,8 @@ static hipError_t ln_fwd_t(const xt_tensor& x, const float* gamma, const float* 
   const float invC = 1.0f / (float)C;
   const RowPlan p = plan_rows(RK_LN_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
   if (p.fast) {
-    XT_ROW_SWITCH(T, p, {
-      if (p.block == 256)
-        ln_fwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
-      else
-        ln_fwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
-    });
+    XT_ROW_SWITCH_FWD(
+        ln_fwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC));
   } else {
     ln_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
   }
@@ -814,21 +855,21 @@ template <typename T>
 static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                            const xt_tensor& mean, const xt_tensor& rstd, const xt_tensor* dx,
                            bool acc_dx, float* dgamma, bool acc_dg, float* dbeta, bool acc_db,
-                           void* ws, hipStream_t s) {
+                           void* ws, size_t ws_bytes, hipStream_t s) {
   const int64_t R = d.rows, C = d.cols;
   const float invC = 1.0f / (float)C;
   const bool al = aligned16(d) && aligned16(x) && (!dx || aligned16(*dx));
-  const RowPlan p = plan_rows(RK_LN_BWD, d.dtype, R, C, al);
   const bool want_p = dgamma || dbeta;
+  const RowPlan p = clamp_to_workspace(plan_rows(RK_LN_BWD, d.dtype, R, C, al), 2, C, ws_bytes, want_p);
+  if (p.grid < 1) return hipErrorInvalidValue;
   float* part = want_p ? (float*)ws : nullptr;
   const int64_t rpb = cdiv(R, p.grid);
   if (p.fast) {
     const size_t shm = want_p ? (size_t)2 * C * sizeof(float) : 0;
-    XT_ROW_SWITCH(T, p, {
+    XT_ROW_SWITCH_BWD(
       ln_bwd_fast<T, RW, NV><<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
                                                             (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr, dx ? dx->ld : 0,
-                                                            acc_dx, part, R, C, invC, rpb);
-    });
+                                                            acc_dx, part, R, C, invC, rpb));
   } else {
     if (dx)
       ln_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
@@ -845,11 +886,11 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
 hipError_t launch_ln_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                          const xt_tensor& mean, const xt_tensor& rstd,
                          const xt_tensor* dx, bool acc_dx, float* dgamma, bool acc_dgamma,
-                         float* dbeta, bool acc_dbeta, void* ws, hipStream_t s) {
+                         float* dbeta, bool acc_dbeta, void* ws, size_t ws_bytes, hipStream_t s) {
   if (d.rows == 0) return hipSuccess;
   return d.dtype == XT_F32
-             ? ln_bwd_t<float>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, s)
-             : ln_bwd_t<bf16_t>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, s);
+             ? ln_bwd_t<float>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, ws_bytes, s)
+             : ln_bwd_t<bf16_t>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, ws_bytes, s);
 }
 
 template <typename T>
@@ -858,12 +899,8 @@ static hipError_t sm_fwd_t(const xt_tensor& x, const xt_tensor& y, float alpha, 
   const int64_t R = x.rows, C = x.cols;
   const RowPlan p = plan_rows(RK_SM_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
   if (p.fast) {
-    XT_ROW_SWITCH(T, p, {
-      if (p.block == 256)
-        sm_fwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
-      else
-        sm_fwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
-    });
+    XT_ROW_SWITCH_FWD(
+        sm_fwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len));
   } else {
     sm_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
   }
@@ -883,12 +920,8 @@ static hipError_t sm_bwd_t(const xt_tensor& d, const xt_tensor& y, const xt_tens
   const int64_t R = d.rows, C = d.cols;
   const RowPlan p = plan_rows(RK_SM_BWD, d.dtype, R, C, aligned16(d) && aligned16(y) && aligned16(dx));
   if (p.fast) {
-    XT_ROW_SWITCH(T, p, {
-      if (p.block == 256)
-        sm_bwd_fast<T, RW, NV, 256><<<p.grid, 256, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
-      else
-        sm_bwd_fast<T, RW, NV, 1024><<<p.grid, 1024, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
-    });
+    XT_ROW_SWITCH_SMB(
+        sm_bwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha));
   } else {
     sm_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
   }
@@ -924,14 +957,18 @@ size_t colsum_workspace(int dtype, int64_t R, int64_t C) {
   return (size_t)colsum_plan(dtype, R, C).gy * C * sizeof(float);
 }
 
-hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, hipStream_t s) {
+hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, size_t ws_bytes, hipStream_t s) {
   const int64_t R = d.rows, C = d.cols;
   if (C == 0) return hipSuccess;
   if (R == 0) {
     if (!acc) fill_f32_k<<<(unsigned)cdiv(C, 256), 256, 0, s>>>(out, C, 0.f);
     return hipGetLastError();
   }
-  const ColsumPlan p = colsum_plan(d.dtype, R, C);
+  ColsumPlan p = colsum_plan(d.dtype, R, C);
+  // never write more partial rows than the workspace holds
+  const int64_t fit = (int64_t)(ws_bytes / ((size_t)C * sizeof(float)));
+  if (fit < 1) return hipErrorInvalidValue;
+  if ((int64_t)p.gy > fit) { p.gy = (unsigned)fit; p.rpb = cdiv(R, p.gy); }
   float* part = (float*)ws;
   const bool al = aligned16(d);
   const int V = d.dtype == XT_F32 ? 4 : 8;

@@ -268,11 +268,12 @@ def rope_angles(positions, head_dim: int, base: float) -> np.ndarray:
     return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
 
 
-def _rope(x, head_dim, base, seq_len, sign):
+def _rope(x, head_dim, base, seq_len, sign, positions=None):
     X = _f(x)
     R, C = X.shape
     half = head_dim // 2
-    th = rope_angles(np.arange(R) % seq_len, head_dim, base)       # [R, half]
+    pos = np.arange(R) % seq_len if positions is None else np.asarray(positions)
+    th = rope_angles(pos, head_dim, base)                          # [R, half]
     c, s = np.cos(th), sign * np.sin(th)
     Xh = X.reshape(R, C // head_dim, head_dim)
     a, b = Xh[:, :, :half], Xh[:, :, half:]
@@ -281,12 +282,14 @@ def _rope(x, head_dim, base, seq_len, sign):
     return np.concatenate([ya, yb], axis=2).reshape(R, C)
 
 
-def rope(x, head_dim: int, base: float, seq_len: int):
-    return _rope(x, head_dim, base, seq_len, +1.0)
+def rope(x, head_dim: int, base: float, seq_len: int, positions=None):
+    """``positions`` (one per row) overrides row mod seq_len, e.g. for a
+    sample of rows taken out of a longer batch."""
+    return _rope(x, head_dim, base, seq_len, +1.0, positions)
 
 
-def rope_bwd(d, head_dim: int, base: float, seq_len: int):
-    return _rope(d, head_dim, base, seq_len, -1.0)
+def rope_bwd(d, head_dim: int, base: float, seq_len: int, positions=None):
+    return _rope(d, head_dim, base, seq_len, -1.0, positions)
 
 
 # --------------------------------------------------------------------------

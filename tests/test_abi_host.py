@@ -104,5 +104,12 @@ def test_workspace_query_is_host_only():
     assert xt.xt_workspace_bytes(xt.OP.SILU, 1, xt.params(), [shape(8, 64)]) == 0
     assert xt.xt_workspace_bytes(xt.OP.RMS_NORM, 0, xt.params(), [shape(8, 64)]) == 0
     assert xt.xt_workspace_bytes(xt.OP.RMS_NORM, 1, xt.params(), [shape(8, 64)]) == 8 * 64 * 4
-    assert xt.xt_workspace_bytes(xt.OP.LAYER_NORM, 1, xt.params(), [shape(8192, 768)]) == 256 * 2 * 768 * 4
-    assert xt.xt_workspace_bytes(xt.OP.ADD_BIAS, 1, xt.params(), [shape(65536, 4096, xt.DT.BF16)]) > 0
+    # partial-gradient workspaces are whole partial rows (np vectors of C
+    # floats), at most one per block and never more blocks than rows
+    for op, np_, R, C, dt in [(xt.OP.LAYER_NORM, 2, 8192, 768, xt.DT.F32), (xt.OP.RMS_NORM, 1, 16384, 4096, xt.DT.BF16),
+                              (xt.OP.RMS_NORM, 1, 1024, 256, xt.DT.F32), (xt.OP.LAYER_NORM, 2, 5, 3001, xt.DT.BF16)]:
+        w = xt.xt_workspace_bytes(op, 1, xt.params(), [shape(R, C, dt)])
+        row = np_ * C * 4
+        assert w > 0 and w % row == 0 and w // row <= min(R, 512), (op, R, C, w)
+    w = xt.xt_workspace_bytes(xt.OP.ADD_BIAS, 1, xt.params(), [shape(65536, 4096, xt.DT.BF16)])
+    assert w > 0 and w % (4096 * 4) == 0

@@ -260,6 +260,9 @@ def test_rope_orthogonal_identity_at_zero_and_fd():
         b = y[:, hd * Dh:hd * Dh + h] ** 2 + y[:, hd * Dh + h:(hd + 1) * Dh] ** 2
         np.testing.assert_allclose(a, b, rtol=1e-13)
     np.testing.assert_allclose(ops.rope_bwd(y, Dh, 10000.0, S), x, atol=1e-14)
+    # explicit positions select the same rotation as the row index would
+    rows = np.array([5, 2, 3])
+    np.testing.assert_array_equal(ops.rope(x[rows], Dh, 10000.0, S, positions=rows % S), y[rows])
     check_fd(lambda a: ops.rope(a, Dh, 10000.0, S), [ops.rope_bwd(W, Dh, 10000.0, S)], [x], W)
 
 
