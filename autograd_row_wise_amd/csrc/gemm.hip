@@ -211,9 +211,264 @@ __global__ __launch_bounds__(NT) void gemm_k(
       }
 }
 
+// ==========================================================================
+// Large-tile kernel for aligned problems (every tile full, K a multiple of
+// BK, 16-byte aligned operands).
+//
+//   bf16: 256 x 256 block tile, BK = 64, 4 waves (2 x 2) of 128 x 128, each
+//         wave 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16.
+//   f32 : 128 x 128 block tile, BK = 32, 4 waves of 64 x 64, 2 x 2
+//         accumulators of v_mfma_f32_32x32x2_f32.
+//
+// Both operands sit in LDS as [row][k] (k contiguous) rows of 128 bytes =
+// eight 16-byte chunks; chunk c of row r is stored at chunk c ^ (r & 7) so
+// the lanes of an MFMA fragment read (32 consecutive rows, one chunk)
+// spread over all banks without padding.  Operands stored transposed in
+// HBM ([K][rows]) are read as 8 x 8 (bf16) or 4 x 4 (f32) blocks with
+// 16-byte loads and transposed in registers (v_perm_b32 for bf16) before
+// the 16-byte LDS stores.  The next K tile is fetched into registers while
+// the current one is multiplied.  Tiles are ordered so that each of the 8
+// XCDs (blocks are dealt to XCDs round-robin) owns whole rows of tiles and
+// reuses their A panels in its own L2.
+// ==========================================================================
+template <typename TA> struct big;
+template <> struct big<bf16_t> { static constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4; };
+template <> struct big<float> { static constexpr int BM = 128, BN = 128, BK = 32, TM = 2, TN = 2; };
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+// 8 x 8 bf16 transpose: in[k] holds m = 0..7 of row k; out[m] holds k = 0..7.
+__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&out)[8]) {
+  const uint32_t* w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = reinterpret_cast<const uint32_t*>(&in[k]);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(w[2 * j + 1][m >> 1], w[2 * j][m >> 1], sel);
+    out[m] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// One thread's share of a BM x BK operand tile, staged in registers.
+template <typename TA, int ROWS, bool KCONTIG>
+struct BigLoader {
+  static constexpr int BK = big<TA>::BK;
+  static constexpr int V = 16 / sizeof(TA);                 // elements per chunk
+  static constexpr int PER_T = ROWS * 8 / NT;               // 16-byte chunks per thread
+  uint4 r[PER_T];
+
+  __device__ __forceinline__ void load(const TA* g, int64_t ld, int64_t row0, int64_t k0) {
+    if constexpr (KCONTIG) {
+      // chunk i of thread t: row t/8 + i*(NT/8), k chunk t%8 (coalesced rows)
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        const int row = threadIdx.x / 8 + i * (NT / 8), c = threadIdx.x % 8;
+        r[i] = ld_nt_ro(g + (row0 + row) * ld + k0 + c * V);
+      }
+    } else {
+      // one V x V block: k rows kb*V.., rows mb*V..  (PER_T == V)
+      constexpr int MB = ROWS / V;
+      const int kb = threadIdx.x / MB, mb = threadIdx.x % MB;
+#pragma unroll
+      for (int i = 0; i < V; ++i) r[i] = ld_nt_ro(g + (k0 + kb * V + i) * ld + row0 + mb * V);
+    }
+  }
+
+  __device__ __forceinline__ void store(TA* lds) const {
+    uint4* L = reinterpret_cast<uint4*>(lds);
+    if constexpr (KCONTIG) {
+#pragma unroll
+      for (int i = 0; i < PER_T; ++i) {
+        const int row = threadIdx.x / 8 + i * (NT / 8), c = threadIdx.x % 8;
+        L[swz(row, c)] = r[i];
+      }
+    } else {
+      constexpr int MB = ROWS / V;
+      const int kb = threadIdx.x / MB, mb = threadIdx.x % MB;
+      uint4 t[V];
+      if constexpr (V == 8) {
+        transpose8x8_bf16(reinterpret_cast<const uint4(&)[8]>(r), reinterpret_cast<uint4(&)[8]>(t));
+      } else {
+        // 4 x 4 f32: r[k] = (m0..m3) of k row; t[m] = (k0..k3)
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) t[m] = make_uint4(w0[m], w1[m], w2[m], w3[m]);
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) L[swz(mb * V + j, kb)] = t[j];
+    }
+  }
+
+  // plain (cached) 16-byte load: operand panels are re-read by other blocks
+  __device__ static __forceinline__ uint4 ld_nt_ro(const TA* p) { return *reinterpret_cast<const uint4*>(p); }
+};
+
+template <typename TA, typename TC, bool TRANS_A, bool TRANS_B>
+__global__ __launch_bounds__(NT) void gemm_big_k(
+    const TA* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
+    const TA* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
+    TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c) {
+  constexpr int BM_ = big<TA>::BM, BN_ = big<TA>::BN, BK_ = big<TA>::BK, TM = big<TA>::TM, TN = big<TA>::TN;
+  __shared__ __align__(16) TA As[BM_ * BK_];
+  __shared__ __align__(16) TA Bs[BN_ * BK_];
+
+  const int64_t z = blockIdx.z, b0 = z / nb1, b1 = z % nb1;
+  A += b0 * sa0 + b1 * sa1;
+  B += b0 * sb0 + b1 * sb1;
+  C += b0 * sc0 + b1 * sc1;
+  // XCD-aware tile order: block g runs on XCD g % 8; give each XCD a
+  // contiguous run of tiles (whole tile rows when they divide evenly)
+  const int tiles_n = (int)(N / BN_);
+  const int tiles = (int)(M / BM_) * tiles_n;
+  const int g = blockIdx.x;
+  const int t = (tiles % 8 == 0) ? (g % 8) * (tiles / 8) + g / 8 : g;
+  const int64_t m0 = (int64_t)(t / tiles_n) * BM_, n0 = (int64_t)(t % tiles_n) * BN_;
+
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const int wm = (w / 2) * (BM_ / 2), wn = (w % 2) * (BN_ / 2);
+  BigLoader<TA, BM_, !TRANS_A> la;
+  BigLoader<TA, BN_, TRANS_B> lb;
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int nk = (int)(K / BK_);
+  la.load(A, lda, m0, 0);
+  lb.load(B, ldb, n0, 0);
+  const uint4* LA = reinterpret_cast<const uint4*>(As);
+  const uint4* LB = reinterpret_cast<const uint4*>(Bs);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(As);
+    lb.store(Bs);
+    __syncthreads();
+    if (kt + 1 < nk) {                      // next tile in flight during the MFMAs
+      la.load(A, lda, m0, (int64_t)(kt + 1) * BK_);
+      lb.load(B, ldb, n0, (int64_t)(kt + 1) * BK_);
+    }
+    const int lr = l % 32, lh = l / 32;
+    if constexpr (sizeof(TA) == 2) {
+#pragma unroll
+      for (int s = 0; s < BK_ / 16; ++s) {
+        bf16x8_t a[TM], b[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm + i * 32 + lr;
+          a[i] = __builtin_bit_cast(bf16x8_t, LA[swz(row, 2 * s + lh)]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = wn + j * 32 + lr;
+          b[j] = __builtin_bit_cast(bf16x8_t, LB[swz(row, 2 * s + lh)]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < BK_ / 16; ++s) {
+        // lane l supplies k = 16*s + 8*(l/32) + j to the j-th MFMA
+        float a[TM][8], b[TN][8];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm + i * 32 + lr;
+          const uint4 q0 = LA[swz(row, 4 * s + 2 * lh)], q1 = LA[swz(row, 4 * s + 2 * lh + 1)];
+          a[i][0] = __uint_as_float(q0.x); a[i][1] = __uint_as_float(q0.y);
+          a[i][2] = __uint_as_float(q0.z); a[i][3] = __uint_as_float(q0.w);
+          a[i][4] = __uint_as_float(q1.x); a[i][5] = __uint_as_float(q1.y);
+          a[i][6] = __uint_as_float(q1.z); a[i][7] = __uint_as_float(q1.w);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = wn + j * 32 + lr;
+          const uint4 q0 = LB[swz(row, 4 * s + 2 * lh)], q1 = LB[swz(row, 4 * s + 2 * lh + 1)];
+          b[j][0] = __uint_as_float(q0.x); b[j][1] = __uint_as_float(q0.y);
+          b[j][2] = __uint_as_float(q0.z); b[j][3] = __uint_as_float(q0.w);
+          b[j][4] = __uint_as_float(q1.x); b[j][5] = __uint_as_float(q1.y);
+          b[j][6] = __uint_as_float(q1.z); b[j][7] = __uint_as_float(q1.w);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][k], b[j][k], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm + i * 32 + 8 * (q / 4) + 4 * (l / 32) + (q % 4);
+        const int64_t col = n0 + wn + j * 32 + (l % 32);
+        TC* p = C + row * ldc + col;
+        float v = alpha * acc[i][j][q];
+        if (acc_c) v = acc_add(io<TC>::ld(p), v);
+        io<TC>::st(p, v);
+      }
+}
+
+template <typename TA, typename TC>
+hipError_t gemm_small(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
+                      float alpha, bool acc, hipStream_t s);
+
+template <typename TA>
+bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C) {
+  const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
+  const int64_t e = 16 / sizeof(TA);
+  auto al = [&](const xt_tensor& t) {
+    return (((uintptr_t)t.data) & 15) == 0 && t.ld % e == 0 && t.sb[0] % e == 0 && t.sb[1] % e == 0;
+  };
+  return M % big<TA>::BM == 0 && N % big<TA>::BN == 0 && K % big<TA>::BK == 0 && K > 0 && al(A) && al(B);
+}
+
 template <typename TA, typename TC>
 hipError_t gemm_go(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
                    float alpha, bool acc, hipStream_t s) {
+  if (C.rows > 0 && C.cols > 0 && C.nb[0] * C.nb[1] > 0 && big_ok<TA>(A, ta, B, tb, C)) {
+    const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
+    const int64_t nb1 = C.nb[1];
+    dim3 grid((unsigned)((M / big<TA>::BM) * (N / big<TA>::BN)), 1, (unsigned)(C.nb[0] * nb1));
+    const TA* a = (const TA*)A.data;
+    const TA* b = (const TA*)B.data;
+    TC* c = (TC*)C.data;
+#define XT_BIG(TA_, TB_)                                                                           \
+    gemm_big_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
+                                                     B.sb[1], c, C.ld, C.sb[0], C.sb[1], M, N, K, \
+                                                     nb1, alpha, acc ? 1 : 0)
+    if (!ta && !tb) XT_BIG(false, false);
+    else if (!ta && tb) XT_BIG(false, true);
+    else if (ta && !tb) XT_BIG(true, false);
+    else XT_BIG(true, true);
+#undef XT_BIG
+    return hipGetLastError();
+  }
+  return gemm_small<TA, TC>(A, ta, B, tb, C, alpha, acc, s);
+}
+
+template <typename TA, typename TC>
+hipError_t gemm_small(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
+                      float alpha, bool acc, hipStream_t s) {
   const int64_t M = C.rows, N = C.cols;
   const int64_t K = ta ? A.rows : A.cols;
   const int64_t nb0 = C.nb[0], nb1 = C.nb[1];
