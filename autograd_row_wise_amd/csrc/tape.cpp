@@ -65,19 +65,38 @@ struct Node {
 
 }  // namespace
 
+// Device memory of a tape comes from the caller's allocator in slabs of at
+// least SLAB bytes; values, saved tensors, gradients and workspace are
+// carved from them with 256-byte alignment and live until the tape is
+// destroyed.  One allocator callback serves many tensors, which keeps the
+// per-op host cost of recording and of backward low.
 struct xt_tape {
+  static constexpr size_t SLAB = size_t(64) << 20;
+  static constexpr size_t ALIGN = 256;
   xt_alloc_fn alloc;
   xt_free_fn release;
   void* ctx;
   hipStream_t stream;
   std::vector<Node> nodes;
-  std::vector<void*> owned;      // every buffer the tape allocated
+  std::vector<void*> owned;      // every slab the tape allocated
+  char* cur = nullptr;           // bump region of the newest slab
+  size_t left = 0;
   std::string err;
 
   void* get(size_t bytes) {
-    if (bytes == 0) bytes = 16;
-    void* p = alloc(ctx, bytes, (void*)stream);
-    if (p) owned.push_back(p);
+    bytes = (bytes + ALIGN - 1) / ALIGN * ALIGN;
+    if (bytes == 0) bytes = ALIGN;
+    if (bytes > left) {
+      const size_t n = bytes > SLAB ? bytes : SLAB;
+      void* p = alloc(ctx, n, (void*)stream);
+      if (!p) return nullptr;
+      owned.push_back(p);
+      cur = static_cast<char*>(p);
+      left = n;
+    }
+    void* p = cur;
+    cur += bytes;
+    left -= bytes;
     return p;
   }
 };
@@ -343,7 +362,7 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
     const size_t wsb = xt_workspace_bytes(n.op, 1, &n.prm, in_vals.data(), np);
     void* ws = nullptr;
     if (wsb) {
-      ws = t->alloc(t->ctx, wsb, (void*)t->stream);
+      ws = t->get(wsb);
       if (!ws) return XT_ERR_ALLOC;
     }
     // Backward calls: each call serves a set of parent positions whose nodes
@@ -376,7 +395,6 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
       if (s != XT_OK) break;
       for (xt_var q : used) set_grad_live(t, q);
     }
-    if (ws) t->release(t->ctx, ws, (void*)t->stream);
     if (s != XT_OK) return s;
   }
   return XT_OK;

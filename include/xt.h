@@ -197,10 +197,12 @@ int         xt_abi_version(void);   /* 1 */
  * node is summed, also when one op uses the same node twice (mul(x, x)
  * pushes twice; the node is visited once).
  *
- * Memory: the tape allocates node values, saved tensors, gradients and
- * workspace only through the caller's callbacks (alloc(ctx, bytes, stream)
- * returns a device pointer or NULL; free(ctx, ptr, stream) releases it in
- * stream order).  Leaf values are caller views; they must outlive the tape.
+ * Memory: the tape takes device memory only from the caller's callbacks
+ * (alloc(ctx, bytes, stream) returns a device pointer or NULL; free(ctx,
+ * ptr, stream) releases it in stream order), in slabs of 64 MiB or more
+ * that it sub-allocates (256-byte aligned) for node values, saved tensors,
+ * gradients and backward workspace; everything is released by
+ * xt_tape_destroy.  Leaf values are caller views; they must outlive the tape.
  * Gradients of leaves accumulate across backward() calls until
  * xt_tape_zero_grad ([BP] "Ackumulation över mikrobatcher").
  * Functions returning xt_var return a negative value -(xt_status) on error.
