@@ -136,6 +136,31 @@ size_t row_ws_bound(RowKind kind, int dtype, int64_t R, int64_t C) {
   return std::max(row_bwd_workspace(kind, dtype, R, C, true), row_bwd_workspace(kind, dtype, R, C, false));
 }
 
+// Split-K workspace of the matmul forward (C = op(A) op(B)) or of the two
+// backward products (dA, dB run one after the other and share it).  The
+// upstream gradient is not among the inputs: a pointer-less stand-in of its
+// shape makes the plan assume the larger of the two kernels' needs.
+size_t matmul_ws(const xt_params* prm, const xt_tensor* in, int n_in, int is_bwd) {
+  if (!prm || n_in < 2) return 0;
+  const xt_tensor &A = in[0], &B = in[1];
+  const bool ta = prm->trans_a != 0, tb = prm->trans_b != 0;
+  const int64_t M = ta ? A.cols : A.rows, K = ta ? A.rows : A.cols, N = tb ? B.rows : B.cols;
+  const int64_t nb0 = std::max(A.nb[0], B.nb[0]), nb1 = std::max(A.nb[1], B.nb[1]), nb = nb0 * nb1;
+  if (!is_bwd) return gemm_workspace(A, ta, B, tb, M, N, nb);
+  xt_tensor D{};
+  D.dtype = A.dtype;
+  D.rows = M;
+  D.cols = N;
+  D.ld = N;
+  D.nb[0] = nb0;
+  D.nb[1] = nb1;
+  D.sb[0] = nb1 * M * N;
+  D.sb[1] = M * N;
+  const size_t wa = !ta ? gemm_workspace(D, false, B, !tb, M, K, nb) : gemm_workspace(B, tb, D, true, K, M, nb);
+  const size_t wb = !tb ? gemm_workspace(A, !ta, D, false, K, N, nb) : gemm_workspace(D, true, A, ta, N, K, nb);
+  return std::max(wa, wb);
+}
+
 }  // namespace
 
 extern "C" {
@@ -159,8 +184,9 @@ const char* xt_last_error(void) { return g_err.c_str(); }
 int xt_abi_version(void) { return 1; }
 
 size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm, const xt_tensor* in, int n_in) {
-  (void)prm;
-  if (!is_bwd || !in || n_in < 1) return 0;
+  if (!in || n_in < 1) return 0;
+  if (op == XT_OP_MATMUL) return matmul_ws(prm, in, n_in, is_bwd);
+  if (!is_bwd) return 0;
   const int64_t R = in[0].rows, C = in[0].cols;
   switch (op) {
     case XT_OP_RMS_NORM: return row_ws_bound(RK_RMS_BWD, in[0].dtype, R, C);
@@ -172,7 +198,6 @@ size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm, const xt_t
 
 xt_status xt_op_fwd(xt_op op, const xt_params* prm, const xt_tensor* in, int n_in,
                     const xt_tensor* out, int n_out, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   if (!prm) return fail(XT_ERR_INVALID_ARG, "null params");
   if (!in || !out) return fail(XT_ERR_INVALID_ARG, "null tensor list");
   hipStream_t s = (hipStream_t)stream;
@@ -186,7 +211,8 @@ xt_status xt_op_fwd(xt_op op, const xt_params* prm, const xt_tensor* in, int n_i
       XT_TRY(need(2, 1));
       int64_t M, N, K;
       XT_TRY(check_matmul(prm, &in[0], &in[1], &out[0], &M, &N, &K));
-      return hip_status(launch_gemm(in[0], prm->trans_a != 0, in[1], prm->trans_b != 0, out[0], prm->alpha, false, s), "matmul");
+      return hip_status(launch_gemm(in[0], prm->trans_a != 0, in[1], prm->trans_b != 0, out[0], prm->alpha, false,
+                                    ws, ws_bytes, s), "matmul");
     }
     case XT_OP_ADD:
     case XT_OP_MUL: {
@@ -332,8 +358,8 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
         for (int i = 0; i < 2; ++i) if (dA.nb[i] != D.nb[i]) return fail(XT_ERR_SHAPE, "dA batch extents must match the output's");
         hipError_t e;
         // stored dA: !ta -> d op(B)^T ; ta -> op(B) d^T
-        if (!ta) e = launch_gemm(D, false, B, !tb, dA, prm->alpha, acc(0), s);
-        else e = launch_gemm(B, tb, D, true, dA, prm->alpha, acc(0), s);
+        if (!ta) e = launch_gemm(D, false, B, !tb, dA, prm->alpha, acc(0), ws, ws_bytes, s);
+        else e = launch_gemm(B, tb, D, true, dA, prm->alpha, acc(0), ws, ws_bytes, s);
         XT_TRY(hip_status(e, "matmul dA"));
       }
       if (wanted(din, n_din, 1)) {
@@ -343,8 +369,8 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
         for (int i = 0; i < 2; ++i) if (dB.nb[i] != D.nb[i]) return fail(XT_ERR_SHAPE, "dB batch extents must match the output's");
         hipError_t e;
         // stored dB: !tb -> op(A)^T d ; tb -> d^T op(A)
-        if (!tb) e = launch_gemm(A, !ta, D, false, dB, prm->alpha, acc(1), s);
-        else e = launch_gemm(D, true, A, ta, dB, prm->alpha, acc(1), s);
+        if (!tb) e = launch_gemm(A, !ta, D, false, dB, prm->alpha, acc(1), ws, ws_bytes, s);
+        else e = launch_gemm(D, true, A, ta, dB, prm->alpha, acc(1), ws, ws_bytes, s);
         XT_TRY(hip_status(e, "matmul dB"));
       }
       return XT_OK;

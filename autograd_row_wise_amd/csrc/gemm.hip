@@ -17,6 +17,7 @@
 // Accumulation is f32; the epilogue scales by alpha, optionally adds the
 // existing C, and rounds once to C's dtype.
 #include <algorithm>
+#include <cstdint>
 
 #include "common.h"
 #include "internal.h"
@@ -136,15 +137,19 @@ __global__ __launch_bounds__(NT) void gemm_k(
     const TA* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
     const TA* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
     TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
-    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c) {
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
+    int64_t kchunk, int64_t nbatch, int64_t scs) {
   constexpr int BK = gcfg<TA>::BK, LDK = BK + gcfg<TA>::PAD;
   __shared__ __align__(16) TA As[2][BM * LDK];
   __shared__ __align__(16) TA Bs[2][BN * LDK];
 
-  const int64_t z = blockIdx.z, b0 = z / nb1, b1 = z % nb1;
-  A += b0 * sa0 + b1 * sa1;
-  B += b0 * sb0 + b1 * sb1;
-  C += b0 * sc0 + b1 * sc1;
+  // gridDim.z = splits x batches; split s sums k in [s*kchunk, (s+1)*kchunk)
+  const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
+  const int64_t kb = split * kchunk;
+  A += b0 * sa0 + b1 * sa1 + (TRANS_A ? kb * lda : kb);
+  B += b0 * sb0 + b1 * sb1 + (TRANS_B ? kb : kb * ldb);
+  C += b0 * sc0 + b1 * sc1 + split * scs;
+  K = K - kb < kchunk ? K - kb : kchunk;
   const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int w = threadIdx.x / WAVE;
   const int wm = (w / 2) * 64, wn = (w % 2) * 64;
@@ -314,15 +319,19 @@ __global__ __launch_bounds__(NT) void gemm_big_k(
     const TA* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
     const TA* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
     TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
-    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c) {
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
+    int64_t kchunk, int64_t nbatch, int64_t scs) {
   constexpr int BM_ = big<TA>::BM, BN_ = big<TA>::BN, BK_ = big<TA>::BK, TM = big<TA>::TM, TN = big<TA>::TN;
   __shared__ __align__(16) TA As[BM_ * BK_];
   __shared__ __align__(16) TA Bs[BN_ * BK_];
 
-  const int64_t z = blockIdx.z, b0 = z / nb1, b1 = z % nb1;
-  A += b0 * sa0 + b1 * sa1;
-  B += b0 * sb0 + b1 * sb1;
-  C += b0 * sc0 + b1 * sc1;
+  // gridDim.z = splits x batches; split s sums k in [s*kchunk, (s+1)*kchunk)
+  const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
+  const int64_t kb = split * kchunk;
+  A += b0 * sa0 + b1 * sa1 + (TRANS_A ? kb * lda : kb);
+  B += b0 * sb0 + b1 * sb1 + (TRANS_B ? kb : kb * ldb);
+  C += b0 * sc0 + b1 * sc1 + split * scs;
+  K = K - kb < kchunk ? K - kb : kchunk;
   // XCD-aware tile order: block g runs on XCD g % 8; give each XCD a
   // contiguous run of tiles (whole tile rows when they divide evenly)
   const int tiles_n = (int)(N / BN_);
@@ -428,10 +437,6 @@ __global__ __launch_bounds__(NT) void gemm_big_k(
       }
 }
 
-template <typename TA, typename TC>
-hipError_t gemm_small(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
-                      float alpha, bool acc, hipStream_t s);
-
 template <typename TA>
 bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C) {
   const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
@@ -442,63 +447,180 @@ bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_t
   return M % big<TA>::BM == 0 && N % big<TA>::BN == 0 && K % big<TA>::BK == 0 && K > 0 && al(A) && al(B);
 }
 
+// ---------------------------------------------------------------- split-K
+// A product with few output tiles and a long K leaves most CUs idle (weight
+// gradients: a small [K_in, N_out] output summed over thousands of rows).
+// Then K is cut into S slices of whole K tiles; every (tile, slice) pair is
+// one block writing an f32 partial product into the workspace
+// [S][batch][M][N], and a second kernel sums the S partials in slice order
+// (fixed order: bitwise reproducible), scales by alpha, optionally adds C,
+// and rounds once into C.  S is chosen so that tiles x S is about what the
+// chip holds at once, with at least 4 K tiles per slice and at most 16
+// slices, and never more slices than the workspace can hold.
+struct SplitPlan { int64_t S, kchunk; };
+
+// Blocks resident on the 256 CUs at once (a SIMD holds 512 registers per
+// lane; each block puts one wave on each SIMD): the f32 large-tile kernel
+// uses 152 (3 per CU), the bf16 one 512 (1 per CU), the 128 x 128 kernel
+// 172 (2 per CU).
+SplitPlan split_plan(bool bf16, bool bigk, int64_t M, int64_t N, int64_t K, int64_t nbatch, size_t ws_bytes) {
+  const int64_t bm = bigk ? (bf16 ? 256 : 128) : BM, bn = bigk ? (bf16 ? 256 : 128) : BN;
+  const int64_t bk = bigk ? (bf16 ? big<bf16_t>::BK : big<float>::BK) : (bf16 ? gcfg<bf16_t>::BK : gcfg<float>::BK);
+  const int64_t resident = bigk ? (bf16 ? 256 : 768) : 512;
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * nbatch;
+  const int64_t nk = (K + bk - 1) / bk;
+  const int64_t per = nbatch * M * N * (int64_t)sizeof(float);
+  if (tiles <= 0 || nk <= 0 || per <= 0) return {1, K};
+  int64_t S = resident / tiles;
+  S = std::min<int64_t>(S, nk / 4);
+  S = std::min<int64_t>(S, 16);
+  S = std::min<int64_t>(S, (int64_t)(ws_bytes / (size_t)per));
+  if (S < 2) return {1, K};
+  const int64_t kchunk = (nk + S - 1) / S * bk;
+  S = (K + kchunk - 1) / kchunk;
+  if (S < 2) return {1, K};
+  return {S, kchunk};
+}
+
+template <typename TC, int VW>
+__global__ __launch_bounds__(256) void splitk_sum_k(const float* __restrict__ P, int S, int64_t scs,
+                                                   TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
+                                                   int64_t M, int64_t N, int64_t nb1, int64_t items,
+                                                   float alpha, int acc_c) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= items) return;
+  const int64_t e = i * VW;                      // flat index in [batch][M][N]
+  const int64_t n = e % N, mb = e / N, m = mb % M, bz = mb / M;
+  float v[VW];
+  if constexpr (VW == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(P + e);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    for (int k = 1; k < S; ++k) {
+      const float4 r = *reinterpret_cast<const float4*>(P + k * scs + e);
+      v[0] += r.x; v[1] += r.y; v[2] += r.z; v[3] += r.w;
+    }
+  } else {
+    v[0] = P[e];
+    for (int k = 1; k < S; ++k) v[0] += P[k * scs + e];
+  }
+  TC* c = C + (bz / nb1) * sc0 + (bz % nb1) * sc1 + m * ldc + n;
+#pragma unroll
+  for (int j = 0; j < VW; ++j) {
+    float o = alpha * v[j];
+    if (acc_c) o = acc_add(io<TC>::ld(c + j), o);
+    io<TC>::st(c + j, o);
+  }
+}
+
+template <typename TC>
+hipError_t splitk_sum(const float* P, int64_t S, int64_t scs, const xt_tensor& C, int64_t nbatch,
+                      float alpha, bool acc, hipStream_t s) {
+  const int64_t M = C.rows, N = C.cols, total = nbatch * M * N;
+  TC* c = (TC*)C.data;
+  if (N % 4 == 0) {
+    const int64_t items = total / 4;
+    splitk_sum_k<TC, 4><<<(unsigned)((items + 255) / 256), 256, 0, s>>>(
+        P, (int)S, scs, c, C.ld, C.sb[0], C.sb[1], M, N, C.nb[1], items, alpha, acc ? 1 : 0);
+  } else {
+    splitk_sum_k<TC, 1><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+        P, (int)S, scs, c, C.ld, C.sb[0], C.sb[1], M, N, C.nb[1], total, alpha, acc ? 1 : 0);
+  }
+  return hipGetLastError();
+}
+
+// One launch of either kernel family: C (+)= alpha op(A) op(B) over k slices
+// of kchunk (kchunk = K: no split), writing through C's own strides, or
+// (split) into partial slices `scs` elements apart.
 template <typename TA, typename TC>
-hipError_t gemm_go(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
-                   float alpha, bool acc, hipStream_t s) {
-  if (C.rows > 0 && C.cols > 0 && C.nb[0] * C.nb[1] > 0 && big_ok<TA>(A, ta, B, tb, C)) {
-    const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
-    const int64_t nb1 = C.nb[1];
-    dim3 grid((unsigned)((M / big<TA>::BM) * (N / big<TA>::BN)), 1, (unsigned)(C.nb[0] * nb1));
-    const TA* a = (const TA*)A.data;
-    const TA* b = (const TA*)B.data;
-    TC* c = (TC*)C.data;
+hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
+                    TC* c, int64_t ldc, int64_t sc0, int64_t sc1, int64_t M, int64_t N, int64_t K,
+                    int64_t nb0, int64_t nb1, float alpha, bool acc, int64_t S, int64_t kchunk, int64_t scs,
+                    hipStream_t s) {
+  const TA* a = (const TA*)A.data;
+  const TA* b = (const TA*)B.data;
+  const int64_t nbatch = nb0 * nb1;
+  if (bigk) {
+    dim3 grid((unsigned)((M / big<TA>::BM) * (N / big<TA>::BN)), 1, (unsigned)(S * nbatch));
 #define XT_BIG(TA_, TB_)                                                                           \
     gemm_big_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
-                                                     B.sb[1], c, C.ld, C.sb[0], C.sb[1], M, N, K, \
-                                                     nb1, alpha, acc ? 1 : 0)
+                                                     B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1,     \
+                                                     alpha, acc ? 1 : 0, kchunk, nbatch, scs)
     if (!ta && !tb) XT_BIG(false, false);
     else if (!ta && tb) XT_BIG(false, true);
     else if (ta && !tb) XT_BIG(true, false);
     else XT_BIG(true, true);
 #undef XT_BIG
-    return hipGetLastError();
+  } else {
+    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)(S * nbatch));
+#define XT_GEMM_LAUNCH(TA_, TB_)                                                              \
+    gemm_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
+                                                 B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1,     \
+                                                 alpha, acc ? 1 : 0, kchunk, nbatch, scs)
+    if (!ta && !tb) XT_GEMM_LAUNCH(false, false);
+    else if (!ta && tb) XT_GEMM_LAUNCH(false, true);
+    else if (ta && !tb) XT_GEMM_LAUNCH(true, false);
+    else XT_GEMM_LAUNCH(true, true);
+#undef XT_GEMM_LAUNCH
   }
-  return gemm_small<TA, TC>(A, ta, B, tb, C, alpha, acc, s);
+  return hipGetLastError();
 }
 
 template <typename TA, typename TC>
-hipError_t gemm_small(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
-                      float alpha, bool acc, hipStream_t s) {
-  const int64_t M = C.rows, N = C.cols;
-  const int64_t K = ta ? A.rows : A.cols;
-  const int64_t nb0 = C.nb[0], nb1 = C.nb[1];
-  if (M == 0 || N == 0 || nb0 * nb1 == 0) return hipSuccess;
-  dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)(nb0 * nb1));
-  const TA* a = (const TA*)A.data;
-  const TA* b = (const TA*)B.data;
-  TC* c = (TC*)C.data;
-#define XT_GEMM_LAUNCH(TA_, TB_)                                                              \
-  gemm_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
-                                               B.sb[1], c, C.ld, C.sb[0], C.sb[1], M, N, K,  \
-                                               nb1, alpha, acc ? 1 : 0)
-  if (!ta && !tb) XT_GEMM_LAUNCH(false, false);
-  else if (!ta && tb) XT_GEMM_LAUNCH(false, true);
-  else if (ta && !tb) XT_GEMM_LAUNCH(true, false);
-  else XT_GEMM_LAUNCH(true, true);
-#undef XT_GEMM_LAUNCH
-  return hipGetLastError();
+hipError_t gemm_go(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
+                   float alpha, bool acc, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
+  const int64_t nb0 = C.nb[0], nb1 = C.nb[1], nbatch = nb0 * nb1;
+  if (M == 0 || N == 0 || nbatch == 0) return hipSuccess;
+  const bool bigk = big_ok<TA>(A, ta, B, tb, C);
+  const SplitPlan sp = split_plan(sizeof(TA) == 2, bigk, M, N, K, nbatch, ws ? ws_bytes : 0);
+  if (sp.S == 1)
+    return gemm_run<TA, TC>(bigk, A, ta, B, tb, (TC*)C.data, C.ld, C.sb[0], C.sb[1], M, N, K, nb0, nb1,
+                            alpha, acc, 1, K, 0, s);
+  float* P = (float*)ws;
+  const int64_t scs = nbatch * M * N;
+  hipError_t e = gemm_run<TA, float>(bigk, A, ta, B, tb, P, N, nb1 * M * N, M * N, M, N, K, nb0, nb1,
+                                     1.f, false, sp.S, sp.kchunk, scs, s);
+  if (e != hipSuccess) return e;
+  return splitk_sum<TC>(P, sp.S, scs, C, nbatch, alpha, acc, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
-                       const xt_tensor& C, float alpha, bool acc, hipStream_t s) {
+hipError_t launch_gemm(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
+                       float alpha, bool acc, void* ws, size_t ws_bytes, hipStream_t s) {
   if (A.dtype == XT_BF16) {
-    return C.dtype == XT_BF16 ? gemm_go<bf16_t, bf16_t>(A, ta, B, tb, C, alpha, acc, s)
-                              : gemm_go<bf16_t, float>(A, ta, B, tb, C, alpha, acc, s);
+    return C.dtype == XT_BF16 ? gemm_go<bf16_t, bf16_t>(A, ta, B, tb, C, alpha, acc, ws, ws_bytes, s)
+                              : gemm_go<bf16_t, float>(A, ta, B, tb, C, alpha, acc, ws, ws_bytes, s);
   }
-  return C.dtype == XT_BF16 ? gemm_go<float, bf16_t>(A, ta, B, tb, C, alpha, acc, s)
-                            : gemm_go<float, float>(A, ta, B, tb, C, alpha, acc, s);
+  return C.dtype == XT_BF16 ? gemm_go<float, bf16_t>(A, ta, B, tb, C, alpha, acc, ws, ws_bytes, s)
+                            : gemm_go<float, float>(A, ta, B, tb, C, alpha, acc, ws, ws_bytes, s);
+}
+
+size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, int64_t M, int64_t N,
+                      int64_t nbatch) {
+  const int64_t K = ta ? A.rows : A.cols;
+  if (M <= 0 || N <= 0 || K <= 0 || nbatch <= 0) return 0;
+  xt_tensor C{};
+  C.rows = M;
+  C.cols = N;
+  const bool bf = A.dtype == XT_BF16;
+  // Which kernel runs depends on the operands' alignment; when the views
+  // carry no pointers yet, size for the larger of the two plans.
+  bool cand[2] = {false, false};
+  if (A.data && B.data) cand[bf ? big_ok<bf16_t>(A, ta, B, tb, C) : big_ok<float>(A, ta, B, tb, C)] = true;
+  else {
+    cand[0] = true;
+    xt_tensor a = A, b = B;
+    a.data = b.data = nullptr;
+    cand[1] = bf ? big_ok<bf16_t>(a, ta, b, tb, C) : big_ok<float>(a, ta, b, tb, C);
+  }
+  size_t best = 0;
+  for (int k = 0; k < 2; ++k) {
+    if (!cand[k]) continue;
+    const SplitPlan sp = split_plan(bf, k == 1, M, N, K, nbatch, SIZE_MAX);
+    if (sp.S > 1) best = std::max(best, (size_t)sp.S * (size_t)(nbatch * M * N) * sizeof(float));
+  }
+  return best;
 }
 
 }  // namespace xt

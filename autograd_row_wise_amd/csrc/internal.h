@@ -92,9 +92,14 @@ hipError_t launch_rope(const xt_tensor& x, const xt_tensor& y, bool acc, int hea
                        float base, int seq_len, bool inverse, hipStream_t s);
 
 // --- matmul (gemm.hip) ----------------------------------------------------
-// C (+)= alpha * op(A) op(B), batched over nb[0] x nb[1].
-hipError_t launch_gemm(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
-                       const xt_tensor& C, float alpha, bool acc, hipStream_t s);
+// C (+)= alpha * op(A) op(B), batched over nb[0] x nb[1].  With workspace,
+// products with few output tiles and a long K are split along K (f32
+// partials + a fixed-order sum); with less workspace they split less.
+hipError_t launch_gemm(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C,
+                       float alpha, bool acc, void* ws, size_t ws_bytes, hipStream_t s);
+// Workspace that launch_gemm would use for C = op(A) op(B) of M x N, nbatch batches.
+size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, int64_t M, int64_t N,
+                      int64_t nbatch);
 
 // --- misc -------------------------------------------------------------------
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);

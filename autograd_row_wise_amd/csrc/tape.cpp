@@ -81,7 +81,22 @@ struct xt_tape {
   std::vector<void*> owned;      // every slab the tape allocated
   char* cur = nullptr;           // bump region of the newest slab
   size_t left = 0;
+  void* ws = nullptr;            // op workspace, reused by every call (stream order)
+  size_t ws_cap = 0;
   std::string err;
+
+  // Workspace of one op call.  Calls run in stream order on the tape's
+  // stream, so one buffer serves them all; it only grows.
+  void* scratch(size_t bytes) {
+    if (bytes <= ws_cap) return ws;
+    bytes = (bytes + ALIGN - 1) / ALIGN * ALIGN;
+    void* p = alloc(ctx, bytes, (void*)stream);
+    if (!p) return nullptr;
+    owned.push_back(p);
+    ws = p;
+    ws_cap = bytes;
+    return ws;
+  }
 
   void* get(size_t bytes) {
     bytes = (bytes + ALIGN - 1) / ALIGN * ALIGN;
@@ -212,7 +227,10 @@ xt_var apply_impl(xt_tape* t, xt_op op, const xt_params* prm, const xt_var* pare
     o.data = t->get((size_t)span * elem_size(o.dtype));
     if (!o.data) return bad(XT_ERR_ALLOC);
   }
-  s = xt_op_fwd(op, prm, in_vals.data(), n, outs.data(), (int)outs.size(), nullptr, 0, (void*)t->stream);
+  const size_t wsb = xt_workspace_bytes(op, 0, prm, in_vals.data(), n);
+  void* ws = nullptr;
+  if (wsb && !(ws = t->scratch(wsb))) return bad(XT_ERR_ALLOC);
+  s = xt_op_fwd(op, prm, in_vals.data(), n, outs.data(), (int)outs.size(), ws, wsb, (void*)t->stream);
   if (s != XT_OK) return bad(s);
   Node nd;
   nd.op = op;
@@ -362,7 +380,7 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
     const size_t wsb = xt_workspace_bytes(n.op, 1, &n.prm, in_vals.data(), np);
     void* ws = nullptr;
     if (wsb) {
-      ws = t->get(wsb);
+      ws = t->scratch(wsb);
       if (!ws) return XT_ERR_ALLOC;
     }
     // Backward calls: each call serves a set of parent positions whose nodes

@@ -96,8 +96,8 @@ def build_entries(only):
         return torch.empty(shape, dtype={"f32": torch.float32, "bf16": torch.bfloat16, "u8": torch.uint8}[dt],
                            device="cuda")
 
-    def ws(op, prm, ins):
-        n = xt.xt_workspace_bytes(op, 1, prm, ins)
+    def ws(op, prm, ins, is_bwd=1):
+        n = xt.xt_workspace_bytes(op, is_bwd, prm, ins)
         if not n:
             return None, 0
         buf = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -155,14 +155,18 @@ def build_entries(only):
                     keep += [w1, w2, dw1, dw2, o1, o2, dxa, dh]
                     f1 = 2 * R3 * D3 * H3
                     b1 = 4 * (R3 * D3 + D3 * H3 + R3 * H3)
+                    m1f = ws(xt.OP.MATMUL, P(), [V(x), V(w1)], 0)
+                    m1b = ws(xt.OP.MATMUL, P(), [V(x), V(w1)], 1)
+                    m2f = ws(xt.OP.MATMUL, P(), [V(hy), V(w2)], 0)
+                    m2b = ws(xt.OP.MATMUL, P(), [V(hy), V(w2)], 1)
                     E.append(Entry("c3.mlp1.fwd", W3, "f32", "mfma", lambda: xt.xt_op_fwd(
-                        xt.OP.MATMUL, P(), [V(x), V(w1)], [V(o1)]), b1, f1, R3))
+                        xt.OP.MATMUL, P(), [V(x), V(w1)], [V(o1)], *m1f), b1, f1, R3))
                     E.append(Entry("c3.mlp1.bwd", W3, "f32", "mfma", lambda: xt.xt_op_bwd(
-                        xt.OP.MATMUL, P(), V(hd), [V(x), V(w1)], [], [V(dxa), V(dw1)]), 2 * b1, 2 * f1, R3))
+                        xt.OP.MATMUL, P(), V(hd), [V(x), V(w1)], [], [V(dxa), V(dw1)], 0, *m1b), 2 * b1, 2 * f1, R3))
                     E.append(Entry("c3.mlp2.fwd", W3, "f32", "mfma", lambda: xt.xt_op_fwd(
-                        xt.OP.MATMUL, P(), [V(hy), V(w2)], [V(o2)]), b1, f1, R3))
+                        xt.OP.MATMUL, P(), [V(hy), V(w2)], [V(o2)], *m2f), b1, f1, R3))
                     E.append(Entry("c3.mlp2.bwd", W3, "f32", "mfma", lambda: xt.xt_op_bwd(
-                        xt.OP.MATMUL, P(), V(d), [V(hy), V(w2)], [], [V(dh), V(dw2)]), 2 * b1, 2 * f1, R3))
+                        xt.OP.MATMUL, P(), V(d), [V(hy), V(w2)], [], [V(dh), V(dw2)], 0, *m2b), 2 * b1, 2 * f1, R3))
             if want("c3.ce"):
                 lg = device_normal((R3, V3), 3, "logits", 0.0, 2.0)
                 tg = device_uniform_int((R3, 1), 0, V3, 3, "targets")
@@ -278,10 +282,12 @@ def build_entries(only):
             dA, dB = empty((M, K), "bf16"), empty((K, N), "f32")
             keep += [A, B, Dg, dA, dB]
             fl = 2 * M * N * K
+            gw = ws(xt.OP.MATMUL, P(), [V(A), V(B)], 1)
             E.append(Entry("c5.gemm.bwd_dA", W5, "bf16", "mfma", lambda: xt.xt_op_bwd(
-                xt.OP.MATMUL, P(), V(Dg), [V(A), V(B)], [], [V(dA), nullslot(B)]), 2 * (M * N + N * K + M * K), fl, M))
+                xt.OP.MATMUL, P(), V(Dg), [V(A), V(B)], [], [V(dA), nullslot(B)], 0, *gw),
+                2 * (M * N + N * K + M * K), fl, M))
             E.append(Entry("c5.gemm.bwd_dB", W5, "bf16", "mfma", lambda: xt.xt_op_bwd(
-                xt.OP.MATMUL, P(), V(Dg), [V(A), V(B)], [], [nullslot(A), V(dB)]),
+                xt.OP.MATMUL, P(), V(Dg), [V(A), V(B)], [], [nullslot(A), V(dB)], 0, *gw),
                 2 * (M * K + M * N) + 4 * K * N, fl, M))
 
     def c2():

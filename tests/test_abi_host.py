@@ -113,3 +113,25 @@ def test_workspace_query_is_host_only():
         assert w > 0 and w % row == 0 and w // row <= min(R, 512), (op, R, C, w)
     w = xt.xt_workspace_bytes(xt.OP.ADD_BIAS, 1, xt.params(), [shape(65536, 4096, xt.DT.BF16)])
     assert w > 0 and w % (4096 * 4) == 0
+
+
+@needs_lib
+def test_matmul_split_workspace_query():
+    """Weight-gradient shapes (few output tiles, long K) ask for split-K
+    workspace: whole f32 slices of the output, between 2 and 16 of them;
+    shapes with many tiles ask for none."""
+    import autograd_row_wise_amd as xt
+    def shape(rows, cols, dtype=xt.DT.F32):
+        v = xt.Tensor()
+        v.dtype, v.rows, v.cols, v.ld = dtype, rows, cols, cols
+        v.nb[0] = v.nb[1] = 1
+        return v
+    prm = xt.params()
+    # x[8192, 768] @ W[768, 3072]: dW = x^T d is 768 x 3072 summed over 8192 rows
+    w = xt.xt_workspace_bytes(xt.OP.MATMUL, 1, prm, [shape(8192, 768), shape(768, 3072)])
+    slice_ = 768 * 3072 * 4
+    assert w % slice_ == 0 or w % (8192 * 768 * 4) == 0
+    assert 2 * min(slice_, 8192 * 768 * 4) <= w <= 16 * 8192 * 768 * 4
+    # 8192 x 4096 x 4096 bf16 has 256 or more 256 x 256 tiles everywhere: no split
+    assert xt.xt_workspace_bytes(xt.OP.MATMUL, 1, prm, [shape(8192, 4096, xt.DT.BF16), shape(4096, 4096, xt.DT.BF16)]) == 0
+    assert xt.xt_workspace_bytes(xt.OP.MATMUL, 0, prm, [shape(8192, 4096, xt.DT.BF16), shape(4096, 4096, xt.DT.BF16)]) == 0

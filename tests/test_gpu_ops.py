@@ -375,3 +375,69 @@ def test_matmul(dtype, M, N, K, ta, tb, batch):
     sA, sB = ops.matmul_bwd(np.abs(Dv), absA, absB, alpha, bool(ta), bool(tb))
     close_f32(host(dA).reshape(dA_ref.shape), dA_ref, sum_scale(sA, N), what="dA")
     close_f32(host(dB).reshape(dB_ref.shape), dB_ref, sum_scale(sB, M), what="dB")
+
+
+# Few output tiles and a long K: the product is split along K into f32
+# partials summed in a fixed order (needs the workspace xt_workspace_bytes
+# reports; with less it splits less, with none it does not split).
+SPLIT_CASES = [  # (M, N, K, ta, tb, batch)
+    (128, 128, 2048, 1, 0, (1, 1)),     # one large f32 tile, 16 slices
+    (256, 256, 1024, 1, 0, (1, 1)),     # one large bf16 tile
+    (200, 130, 1000, 1, 0, (1, 1)),     # ragged: 128 x 128 kernel, ragged last slice
+    (256, 128, 640, 0, 1, (2, 2)),      # batched
+    (96, 64, 1537, 0, 0, (1, 1)),       # K not a multiple of any tile
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N,K,ta,tb,batch", SPLIT_CASES)
+@pytest.mark.parametrize("ws_frac", [1.0, 0.5])
+def test_matmul_split_k(dtype, M, N, K, ta, tb, batch, ws_frac):
+    nb = batch[0] * batch[1]
+    ash = (K, M) if ta else (M, K)
+    bsh = (N, K) if tb else (K, N)
+    A3 = normal((nb,) + ash, 17, "a")
+    B3 = normal((nb,) + bsh, 17, "b", std=0.5)
+    D3 = normal((nb, M, N), 17, "dout")
+    def stack(a3):
+        return a3.reshape(nb * a3.shape[1], a3.shape[2])
+    A, Av = put(stack(A3), dtype)
+    B, Bv = put(stack(B3), dtype)
+    D, Dv = put(stack(D3), dtype)
+    Av, Bv, Dv = (v.reshape((nb,) + s) for v, s in ((Av, ash), (Bv, bsh), (Dv, (M, N))))
+    alpha = 0.5
+    def bview(t, r, c):
+        return xt.view(t, rows=r, cols=c, ld=c, nb=batch, sb=(batch[1] * r * c, r * c))
+    prm = xt.params(alpha=alpha, trans_a=ta, trans_b=tb)
+    ins = [bview(A, *ash), bview(B, *bsh)]
+    wf = xt.xt_workspace_bytes(xt.OP.MATMUL, 0, prm, ins)
+    wb = xt.xt_workspace_bytes(xt.OP.MATMUL, 1, prm, ins)
+    assert wf > 0 or wb > 0, "this shape is meant to split"
+    wsf = torch.empty(max(int(wf * ws_frac), 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(int(wb * ws_frac), 1), dtype=torch.uint8, device="cuda")
+    Cout = empty((nb * M, N), dtype)
+    xt.xt_op_fwd(xt.OP.MATMUL, prm, ins, [bview(Cout, M, N)], wsf.data_ptr(), int(wf * ws_frac))
+    torch.cuda.synchronize()
+    ref = ops.matmul(Av, Bv, alpha, bool(ta), bool(tb))
+    absA = np.abs(Av); absB = np.abs(Bv)
+    A_abs = alpha * ops.matmul(absA, absB, 1.0, bool(ta), bool(tb))
+    got = host(Cout).reshape(nb, M, N)
+    if dtype == "f32":
+        close_f32(got, ref, sum_scale(A_abs, K), what="C")
+    else:
+        close(got, ref, "bf16", what="C")
+    dA, dB = empty((nb * ash[0], ash[1]), dtype), empty((nb * bsh[0], bsh[1]), "f32")
+    dA_ref, dB_ref = ops.matmul_bwd(Dv, Av, Bv, alpha, bool(ta), bool(tb))
+    sA, sB = ops.matmul_bwd(np.abs(Dv), absA, absB, alpha, bool(ta), bool(tb))
+    # second call accumulates onto the first: the result is the sum of two
+    # equal products (one f32 rounding of the add in dB; dA in its dtype)
+    for acc in (0, 3):
+        xt.xt_op_bwd(xt.OP.MATMUL, prm, bview(D, M, N), ins, [], [bview(dA, *ash), bview(dB, *bsh)], acc,
+                     wsb.data_ptr(), int(wb * ws_frac))
+        torch.cuda.synchronize()
+    k = 2.0
+    if dtype == "f32":
+        close_f32(host(dA).reshape(dA_ref.shape), k * dA_ref, k * sum_scale(sA, N), what="dA")
+    else:
+        close(host(dA).reshape(dA_ref.shape), k * dA_ref, "bf16", what="dA")
+    close_f32(host(dB).reshape(dB_ref.shape), k * dB_ref, k * sum_scale(sB, M), what="dB")
