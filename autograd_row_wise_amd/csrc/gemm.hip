@@ -274,9 +274,10 @@ struct BigLoader {
         r[i] = ld_nt_ro(g + (row0 + row) * ld + k0 + c * V);
       }
     } else {
-      // one V x V block: k rows kb*V.., rows mb*V..  (PER_T == V)
-      constexpr int MB = ROWS / V;
-      const int kb = threadIdx.x / MB, mb = threadIdx.x % MB;
+      // one V x V block: k rows kb*V.., rows mb*V..  (PER_T == V); kb
+      // varies fastest so that LDS store phases hit distinct chunk columns
+      constexpr int KB = BK / V;
+      const int kb = threadIdx.x % KB, mb = threadIdx.x / KB;
 #pragma unroll
       for (int i = 0; i < V; ++i) r[i] = ld_nt_ro(g + (k0 + kb * V + i) * ld + row0 + mb * V);
     }
@@ -291,8 +292,8 @@ struct BigLoader {
         L[swz(row, c)] = r[i];
       }
     } else {
-      constexpr int MB = ROWS / V;
-      const int kb = threadIdx.x / MB, mb = threadIdx.x % MB;
+      constexpr int KB = BK / V;
+      const int kb = threadIdx.x % KB, mb = threadIdx.x / KB;
       uint4 t[V];
       if constexpr (V == 8) {
         transpose8x8_bf16(reinterpret_cast<const uint4(&)[8]>(r), reinterpret_cast<uint4(&)[8]>(t));
@@ -437,6 +438,179 @@ __global__ __launch_bounds__(NT) void gemm_big_k(
       }
 }
 
+// ==========================================================================
+// bf16 large-tile kernel with eight waves.  A 512-thread block computes a
+// 256 x 256 tile of C with BK = 64.  The waves form 2 (m) x 4 (n), each
+// owning 128 x 64 of C = 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16
+// (128 AGPRs), so two waves share each SIMD and one wave's LDS reads and
+// waits overlap the other's MFMAs.  LDS holds two K tiles (2 x 64 KB): the
+// next tile is written while the current one is multiplied, with one
+// barrier per K tile.  Waves 0-3 fetch the A tile and waves 4-7 the B tile,
+// eight 16-byte chunks per thread, issued two K tiles ahead of their use
+// (two register sets).  LDS layout and swizzle as in the kernel above.
+// ==========================================================================
+namespace b8 {
+constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+constexpr int TILE = BM * BK;                   // elements of one operand tile
+}  // namespace b8
+
+// 8 x 8 bf16 transpose on native vectors: in[k] holds m = 0..7 of row k;
+// out[m] holds k = 0..7.
+__device__ __forceinline__ void transpose8x8_v(const u32x4_t (&in)[8], u32x4_t (&out)[8]) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(in[2 * j + 1][m >> 1], in[2 * j][m >> 1], sel);
+    out[m] = o;
+  }
+}
+
+template <bool KCONTIG>
+__device__ __forceinline__ void b8_load(u32x4_t (&r)[8], const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
+                                        int t) {
+  if constexpr (KCONTIG) {
+    // rows t/8 + 32 i, k chunk t % 8: eight lanes cover one 128-byte row run
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = t / 8 + i * 32, c = t % 8;
+      r[i] = *reinterpret_cast<const u32x4_t*>(g + (row0 + row) * ld + k0 + c * 8);
+    }
+  } else {
+    // one 8 (k) x 8 (rows) block per thread: k rows 8 kb.., rows 8 mb..;
+    // kb = t % 8 so that the eight lanes of an LDS store phase write eight
+    // different swizzled chunk columns (no bank conflicts); each load still
+    // reads 128 contiguous bytes per group of eight lanes
+    const int kb = t % 8, mb = t / 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(g + (k0 + kb * 8 + i) * ld + row0 + mb * 8);
+  }
+}
+
+template <bool KCONTIG>
+__device__ __forceinline__ void b8_store(const u32x4_t (&r)[8], u32x4_t* L, int t) {
+  if constexpr (KCONTIG) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) L[swz(t / 8 + i * 32, t % 8)] = r[i];
+  } else {
+    const int kb = t % 8, mb = t / 8;
+    u32x4_t o[8];
+    transpose8x8_v(r, o);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) L[swz(mb * 8 + j, kb)] = o[j];
+  }
+}
+
+template <bool TRANS_A, bool TRANS_B>
+__device__ __forceinline__ void b8_fetch(u32x4_t (&r)[8], bool fetchA, const bf16_t* A, int64_t lda, int64_t m0,
+                                         const bf16_t* B, int64_t ldb, int64_t n0, int64_t k0, int t) {
+  if constexpr (!TRANS_A == TRANS_B) {            // both tiles in one layout: one code path
+    b8_load<TRANS_B>(r, fetchA ? A : B, fetchA ? lda : ldb, fetchA ? m0 : n0, k0, t);
+  } else {
+    if (fetchA) b8_load<!TRANS_A>(r, A, lda, m0, k0, t);
+    else b8_load<TRANS_B>(r, B, ldb, n0, k0, t);
+  }
+}
+
+template <bool TRANS_A, bool TRANS_B>
+__device__ __forceinline__ void b8_put(const u32x4_t (&r)[8], bool fetchA, u32x4_t* L, int t) {
+  if constexpr (!TRANS_A == TRANS_B) {
+    b8_store<TRANS_B>(r, fetchA ? L : L + b8::TILE / 8, t);
+  } else {
+    if (fetchA) b8_store<!TRANS_A>(r, L, t);
+    else b8_store<TRANS_B>(r, L + b8::TILE / 8, t);
+  }
+}
+
+// One K tile of a wave's 128 x 64 block: four k steps of 16, each 4 A and
+// 2 B fragments (one 16-byte LDS read per lane each) and 8 MFMAs.
+__device__ __forceinline__ void b8_mma(const u32x4_t* LA, f32x16_t (&acc)[4][2], int wm, int wn, int lr, int lh) {
+  const u32x4_t* LB = LA + b8::TILE / 8;
+#pragma unroll
+  for (int s = 0; s < b8::BK / 16; ++s) {
+    bf16x8_t a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8_t, LA[swz(wm + i * 32 + lr, 2 * s + lh)]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(bf16x8_t, LB[swz(wn + j * 32 + lr, 2 * s + lh)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <typename TC, bool TRANS_A, bool TRANS_B>
+__global__ __launch_bounds__(b8::NT) void gemm_b8_k(
+    const bf16_t* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
+    const bf16_t* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
+    TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
+    int64_t kchunk, int64_t nbatch, int64_t scs) {
+  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = b8::BK, TILE = b8::TILE;
+  __shared__ __align__(16) bf16_t lds[2][2 * TILE];      // [stage][A tile, B tile]
+
+  const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
+  const int64_t kb0 = split * kchunk;
+  A += b0 * sa0 + b1 * sa1 + (TRANS_A ? kb0 * lda : kb0);
+  B += b0 * sb0 + b1 * sb1 + (TRANS_B ? kb0 : kb0 * ldb);
+  C += b0 * sc0 + b1 * sc1 + split * scs;
+  K = K - kb0 < kchunk ? K - kb0 : kchunk;
+
+  const int tiles_n = (int)(N / BN8);
+  const int tiles = (int)(M / BM8) * tiles_n;
+  const int g = blockIdx.x;
+  const int tt = (tiles % 8 == 0) ? (g % 8) * (tiles / 8) + g / 8 : g;
+  const int64_t m0 = (int64_t)(tt / tiles_n) * BM8, n0 = (int64_t)(tt % tiles_n) * BN8;
+
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const bool fetchA = w < 4;                     // wave-uniform role
+  const int t = threadIdx.x % 256;
+  const int wm = (w / 4) * 128, wn = (w % 4) * 64;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int nk = (int)(K / BK);
+  const int lr = l % 32, lh = l / 32;
+  u32x4_t r0[8];
+  b8_fetch<TRANS_A, TRANS_B>(r0, fetchA, A, lda, m0, B, ldb, n0, 0, t);
+  b8_put<TRANS_A, TRANS_B>(r0, fetchA, reinterpret_cast<u32x4_t*>(lds[0]), t);
+  if (nk > 1) b8_fetch<TRANS_A, TRANS_B>(r0, fetchA, A, lda, m0, B, ldb, n0, BK, t);
+  __syncthreads();
+  // K tile kt: multiply stage kt&1 while tile kt+1 is in flight; then write
+  // it into the other stage and fetch tile kt+2.
+  for (int kt = 0; kt < nk; ++kt) {
+    b8_mma(reinterpret_cast<const u32x4_t*>(lds[kt & 1]), acc, wm, wn, lr, lh);
+    if (kt + 1 < nk) {
+      b8_put<TRANS_A, TRANS_B>(r0, fetchA, reinterpret_cast<u32x4_t*>(lds[(kt + 1) & 1]), t);
+      if (kt + 2 < nk) b8_fetch<TRANS_A, TRANS_B>(r0, fetchA, A, lda, m0, B, ldb, n0, (int64_t)(kt + 2) * BK, t);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm + i * 32 + 8 * (q / 4) + 4 * (l / 32) + (q % 4);
+        const int64_t col = n0 + wn + j * 32 + (l % 32);
+        TC* p = C + row * ldc + col;
+        float v = alpha * acc[i][j][q];
+        if (acc_c) v = acc_add(io<TC>::ld(p), v);
+        io<TC>::st(p, v);
+      }
+}
+
 template <typename TA>
 bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C) {
   const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
@@ -539,7 +713,20 @@ hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, 
   const TA* a = (const TA*)A.data;
   const TA* b = (const TA*)B.data;
   const int64_t nbatch = nb0 * nb1;
-  if (bigk) {
+  if constexpr (sizeof(TA) == 2) {
+   if (bigk) {
+    dim3 grid((unsigned)((M / b8::BM) * (N / b8::BN)), 1, (unsigned)(S * nbatch));
+    const bf16_t* a8 = (const bf16_t*)A.data;
+    const bf16_t* b8p = (const bf16_t*)B.data;
+#define XT_B8(TA_, TB_)                                                                                   gemm_b8_k<TC, TA_, TB_><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0],                                                      B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1, alpha,                                                      acc ? 1 : 0, kchunk, nbatch, scs)
+    if (!ta && !tb) XT_B8(false, false);
+    else if (!ta && tb) XT_B8(false, true);
+    else if (ta && !tb) XT_B8(true, false);
+    else XT_B8(true, true);
+#undef XT_B8
+    return hipGetLastError();
+   }
+  } else if (bigk) {
     dim3 grid((unsigned)((M / big<TA>::BM) * (N / big<TA>::BN)), 1, (unsigned)(S * nbatch));
 #define XT_BIG(TA_, TB_)                                                                           \
     gemm_big_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
@@ -550,7 +737,9 @@ hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, 
     else if (ta && !tb) XT_BIG(true, false);
     else XT_BIG(true, true);
 #undef XT_BIG
-  } else {
+    return hipGetLastError();
+  }
+  {
     dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)(S * nbatch));
 #define XT_GEMM_LAUNCH(TA_, TB_)                                                              \
     gemm_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
