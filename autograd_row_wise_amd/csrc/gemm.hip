@@ -226,9 +226,9 @@ __global__ __launch_bounds__(NT) void gemm_k(
 //         accumulators of v_mfma_f32_32x32x2_f32.
 //
 // Both operands sit in LDS as [row][k] (k contiguous) rows of 128 bytes =
-// eight 16-byte chunks; chunk c of row r is stored at chunk c ^ (r & 7) so
-// the lanes of an MFMA fragment read (32 consecutive rows, one chunk)
-// spread over all banks without padding.  Operands stored transposed in
+// eight 16-byte chunks, XOR-swizzled (swz below) so that the lanes of an
+// MFMA fragment read (32 consecutive rows, one chunk) spread over all banks
+// without padding.  Operands stored transposed in
 // HBM ([K][rows]) are read as 8 x 8 (bf16) or 4 x 4 (f32) blocks with
 // 16-byte loads and transposed in registers (v_perm_b32 for bf16) before
 // the 16-byte LDS stores.  The next K tile is fetched into registers while
@@ -240,7 +240,13 @@ template <typename TA> struct big;
 template <> struct big<bf16_t> { static constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4; };
 template <> struct big<float> { static constexpr int BM = 128, BN = 128, BK = 32, TM = 2, TN = 2; };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// 16-byte chunk c of LDS row r (rows of 128 bytes) is stored at chunk
+// c ^ ((r >> 1) & 7): gfx950's LDS serves a 128-bit access sixteen lanes
+// (256 bytes, all 64 banks) at a time, and the sixteen rows an MFMA
+// fragment read touches at once then land in sixteen different 16-byte bank
+// groups (two rows share a 256-byte bank row; the XOR term differs between
+// rows of equal parity).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 // 8 x 8 bf16 transpose: in[k] holds m = 0..7 of row k; out[m] holds k = 0..7.
 __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&out)[8]) {
@@ -454,19 +460,6 @@ constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
 constexpr int TILE = BM * BK;                   // elements of one operand tile
 }  // namespace b8
 
-// 8 x 8 bf16 transpose on native vectors: in[k] holds m = 0..7 of row k;
-// out[m] holds k = 0..7.
-__device__ __forceinline__ void transpose8x8_v(const u32x4_t (&in)[8], u32x4_t (&out)[8]) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-    u32x4_t o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(in[2 * j + 1][m >> 1], in[2 * j][m >> 1], sel);
-    out[m] = o;
-  }
-}
-
 template <bool KCONTIG>
 __device__ __forceinline__ void b8_load(u32x4_t (&r)[8], const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
                                         int t) {
@@ -494,11 +487,23 @@ __device__ __forceinline__ void b8_store(const u32x4_t (&r)[8], u32x4_t* L, int 
 #pragma unroll
     for (int i = 0; i < 8; ++i) L[swz(t / 8 + i * 32, t % 8)] = r[i];
   } else {
-    const int kb = t % 8, mb = t / 8;
-    u32x4_t o[8];
-    transpose8x8_v(r, o);
+    // Transposed in registers: row m of the block is, per pair of k rows,
+    // the m-th bf16 of each (v_perm_b32 picks the low or high halves).
+    // Lanes with odd mb emit their rows in the order j ^ 1 (only the perm
+    // selector changes), so the two groups of eight lanes in a sixteen-lane
+    // LDS phase write rows of opposite parity: opposite halves of the
+    // 256-byte bank row, no conflicts.
+    const int kb = t % 8, mb = t / 8, flip = mb & 1;
+    const uint32_t lo = 0x05040100u, hi = 0x07060302u;
+    const uint32_t sel_even = flip ? hi : lo, sel_odd = flip ? lo : hi;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) L[swz(mb * 8 + j, kb)] = o[j];
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t sel = (j & 1) ? sel_odd : sel_even;
+      u32x4_t o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(r[2 * w + 1][j >> 1], r[2 * w][j >> 1], sel);
+      L[swz(mb * 8 + (j ^ flip), kb)] = o;
+    }
   }
 }
 
