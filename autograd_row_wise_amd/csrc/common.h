@@ -129,13 +129,27 @@ __device__ __forceinline__ uint4 load_raw(const T* row, I c0, I n) {
 // A row slice held as raw packs: pack j of group lane gl covers columns
 // [(j*G + gl)*VEC, +VEC).
 template <typename T, int NV, int G>
+struct RowPacks;
+
+// Column of element 0 of pack j held by lane gl of a G-lane row group.  The
+// group's waves split the row into contiguous runs (wave w owns packs
+// [w*NV*64, (w+1)*NV*64)), and within a wave pack j of lane l is pack
+// j*64 + l of the run: one load instruction covers 64 consecutive packs
+// (1 KB) and a lane's NV packs lie at compile-time offsets (1 KB apart)
+// from one base address.
+template <int NV, int VEC>
+__device__ __forceinline__ int pack_col(int j, int gl) {
+  return (((gl / WAVE) * NV + j) * WAVE + (gl % WAVE)) * VEC;
+}
+
+template <typename T, int NV, int G>
 struct RowPacks {
   uint4 q[NV];
   // Whole packs only: the row width is a multiple of VEC on this path.
   __device__ __forceinline__ void load(const T* row, int gl, int C, bool active) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int c0 = (j * G + gl) * io<T>::VEC;
+      const int c0 = pack_col<NV, io<T>::VEC>(j, gl);
       q[j] = (active && c0 < C) ? ld_nt(row + c0) : make_uint4(0, 0, 0, 0);
     }
   }

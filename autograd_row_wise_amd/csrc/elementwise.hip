@@ -334,6 +334,59 @@ __global__ __launch_bounds__(EW_BLOCK) void dropout_k(
   }
 }
 
+// Dense fast path: x, y and the mask are contiguous, 16-byte aligned and
+// the element count is a whole number of packs.  One pack per thread over a
+// full grid (no loop, no partial packs), 32-bit lane arithmetic for the
+// hash: per element two 64-bit products by constants, the second reduced to
+// the high word it needs.  The counter of element i is i itself.
+template <typename T, int MODE, bool ACC>
+__global__ __launch_bounds__(EW_BLOCK) void dropout_flat_k(
+    const void* __restrict__ x, void* __restrict__ y, uint8_t* __restrict__ mask, int64_t npacks,
+    uint32_t thr, float scale, uint64_t seed) {
+  constexpr int V = io<T>::VEC;
+  constexpr uint32_t M1L = 0x1CE4E5B9u, M1H = 0xBF58476Du, M2L = 0x133111EBu, M2H = 0x94D049BBu;
+  const int64_t p = (int64_t)blockIdx.x * EW_BLOCK + threadIdx.x;
+  if (p >= npacks) return;
+  const int64_t i0 = p * V;
+  uint4 xq{}, oq{};
+  uint8_t m[V];
+  if (MODE != 1) xq = ld_nt(reinterpret_cast<const T*>(x) + i0);
+  if (MODE == 2) {
+    unpack_mask(mask + i0, 0, V, V, true, m);
+    if constexpr (ACC) oq = ld_nt(reinterpret_cast<const T*>(y) + i0);
+  } else {
+    uint64_t kg = (uint64_t)i0 * GOLDEN;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      uint64_t z = (seed ^ kg) + GOLDEN;
+      z ^= z >> 30;
+      const uint32_t zl = (uint32_t)z, zh = (uint32_t)(z >> 32);
+      const uint64_t pl = (uint64_t)zl * M1L;
+      const uint32_t h1 = (uint32_t)(pl >> 32) + zl * M1H + zh * M1L;
+      uint64_t z1 = ((uint64_t)h1 << 32) | (uint32_t)pl;
+      z1 ^= z1 >> 27;
+      const uint32_t al = (uint32_t)z1, ah = (uint32_t)(z1 >> 32);
+      const uint32_t top = __umulhi(al, M2L) + al * M2H + ah * M2L;   // bits 32..63 of z1 * M2
+      m[k] = (top >> 8) >= thr ? 1 : 0;
+      kg += GOLDEN;
+    }
+    if (mask) store_mask(mask + i0, 0, V, V, true, m);
+  }
+  if (MODE != 1) {
+    float v[V];
+    io<T>::unpack(xq, v);
+#pragma unroll
+    for (int k = 0; k < V; ++k) v[k] = m[k] ? v[k] * scale : 0.f;
+    if constexpr (ACC) {
+      float o[V];
+      io<T>::unpack(oq, o);
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = acc_add(o[k], v[k]);
+    }
+    st_nt(reinterpret_cast<T*>(y) + i0, io<T>::pack(v));
+  }
+}
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int es(int dt) { return dt == XT_F32 ? 4 : (dt == XT_BF16 ? 2 : (dt == XT_I32 ? 4 : 1)); }
@@ -440,6 +493,13 @@ static hipError_t dropout_go(const xt_tensor* x, const xt_tensor* y, const xt_te
   const void* xp = x ? x->data : nullptr;
   void* yp = y ? y->data : nullptr;
   uint8_t* mp = mask ? (uint8_t*)mask->data : nullptr;
+  if (vec && Rw == 1 && Cw % V == 0) {
+    const int64_t np = Cw / V;
+    const unsigned g = (unsigned)cdiv(np, EW_BLOCK);
+    if (acc) dropout_flat_k<T, MODE, true><<<g, EW_BLOCK, 0, s>>>(xp, yp, mp, np, thr, scale, seed);
+    else dropout_flat_k<T, MODE, false><<<g, EW_BLOCK, 0, s>>>(xp, yp, mp, np, thr, scale, seed);
+    return hipGetLastError();
+  }
 #define XT_DROP(VEC_, ACC_) \
   dropout_k<T, MODE, VEC_, ACC_><<<grid, EW_BLOCK, 0, s>>>(xp, ldx, yp, ldy, mp, ldm, Rw, Cw, Clw, 0, thr, scale, seed)
   if (vec) { if (acc) XT_DROP(true, true); else XT_DROP(true, false); }

@@ -94,6 +94,100 @@ __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t
   }
 }
 
+// Pipelined form for 16-byte packs and rows of at most 2 * RB pack pairs.
+// The block works on tiles of `rpi` rows (several short rows per tile, so
+// every thread has work); thread slot s = tid + j*RB, j < 2, owns pack pair
+// s % items of tile row s / items.  The frequencies base^(-2i/D) are
+// computed once per block (f64, LDS); per tile, the angles pos * freq are
+// formed in f64 and their cos/sin rounded to f32 into one of two LDS
+// buffers, while the next tile's packs are already being fetched: one
+// barrier per tile, loads of tile t+1 in flight during tile t.
+template <typename T>
+__global__ __launch_bounds__(RB) void rope_pipe_k(const void* __restrict__ x, int64_t ldx,
+                                                  void* __restrict__ y, int64_t ldy, int acc,
+                                                  int64_t R, int head_dim, double base, int seq_len,
+                                                  float sign, int items, int rpi) {
+  constexpr int V = io<T>::VEC, NIT = 2;
+  extern __shared__ double rsh[];                 // freq[half] (f64), then cs[2][rpi][2*half] (f32)
+  const int half = head_dim / 2, per_head = half / V;
+  double* freq = rsh;
+  float* cs = reinterpret_cast<float*>(rsh + half);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < half; i += RB) freq[i] = pow(base, -2.0 * (double)i / (double)head_dim);
+
+  int srow[NIT], scol[NIT], sv[NIT];
+  bool sok[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    const int sl = tid + j * RB;
+    sok[j] = sl < rpi * items;
+    const int it = sok[j] ? sl % items : 0;
+    srow[j] = sok[j] ? sl / items : 0;
+    sv[j] = it % per_head;
+    scol[j] = (it / per_head) * head_dim + sv[j] * V;
+  }
+  const int64_t tiles = (R + rpi - 1) / rpi;
+  const T* X = reinterpret_cast<const T*>(x);
+  T* Y = reinterpret_cast<T*>(y);
+  uint4 ca[NIT], cb[NIT], na[NIT], nb[NIT];
+  auto fetch = [&](int64_t tile, uint4 (&pa)[NIT], uint4 (&pb)[NIT]) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int64_t r = tile * rpi + srow[j];
+      if (sok[j] && r < R) {
+        const T* xr = X + r * ldx + scol[j];
+        pa[j] = ld_nt(xr);
+        pb[j] = ld_nt(xr + half);
+      }
+    }
+  };
+  int64_t t = blockIdx.x;
+  if (t < tiles) fetch(t, ca, cb);
+  __syncthreads();                                // freq ready
+  for (int k = 0; t < tiles; t += gridDim.x, ++k) {
+    float* cb_ = cs + (k & 1) * (rpi * 2 * half);
+    for (int idx = tid; idx < rpi * half; idx += RB) {
+      const int rr = idx / half, i = idx % half;
+      const int64_t r = t * rpi + rr;
+      const double th = (double)(r % seq_len) * freq[i];
+      double sn, cn;
+      sincos(th, &sn, &cn);
+      cb_[rr * 2 * half + i] = (float)cn;
+      cb_[rr * 2 * half + half + i] = sign * (float)sn;
+    }
+    const int64_t tn = t + gridDim.x;
+    if (tn < tiles) fetch(tn, na, nb);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int64_t r = t * rpi + srow[j];
+      if (!sok[j] || r >= R) continue;
+      float a[V], b[V], ya[V], yb[V];
+      io<T>::unpack(ca[j], a);
+      io<T>::unpack(cb[j], b);
+      const float* crow = cb_ + srow[j] * 2 * half + sv[j] * V;
+      T* yr = Y + r * ldy + scol[j];
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        const float c = crow[q], sn = crow[half + q];
+        ya[q] = a[q] * c - b[q] * sn;
+        yb[q] = a[q] * sn + b[q] * c;
+      }
+      if (acc) {
+        float oa[V], ob[V];
+        io<T>::unpack(ld_nt(yr), oa);
+        io<T>::unpack(ld_nt(yr + half), ob);
+#pragma unroll
+        for (int q = 0; q < V; ++q) { ya[q] = acc_add(oa[q], ya[q]); yb[q] = acc_add(ob[q], yb[q]); }
+      }
+      st_nt(yr, io<T>::pack(ya));
+      st_nt(yr + half, io<T>::pack(yb));
+    }
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) { ca[j] = na[j]; cb[j] = nb[j]; }
+  }
+}
+
 int es_(int dt) { return dt == XT_F32 ? 4 : 2; }
 
 }  // namespace
@@ -106,9 +200,25 @@ hipError_t launch_rope(const xt_tensor& x, const xt_tensor& y, bool acc, int hea
   const int V = x.dtype == XT_F32 ? 4 : 8;
   const bool vec = (half % V) == 0 && (((uintptr_t)x.data) & 15) == 0 && (((uintptr_t)y.data) & 15) == 0 &&
                    ((x.ld * es_(x.dtype)) & 15) == 0 && ((y.ld * es_(y.dtype)) & 15) == 0;
+  const float sign = inverse ? -1.f : 1.f;
+  const int64_t items = (C / head_dim) * (half / V);
+  if (vec && items <= 2 * RB) {
+    // rows per tile: enough pack pairs for every thread, angle buffers <= 32 KB
+    const int64_t rpi_lds = (32768 - 8 * (int64_t)half) / (16 * (int64_t)half);
+    const int rpi = (int)std::max<int64_t>(1, std::min<int64_t>((2 * RB) / items, rpi_lds));
+    const int64_t tiles = (R + rpi - 1) / rpi;
+    const unsigned g = (unsigned)std::min<int64_t>(tiles, 2048);
+    const size_t sh = (size_t)half * sizeof(double) + (size_t)2 * rpi * 2 * half * sizeof(float);
+    if (x.dtype == XT_F32)
+      rope_pipe_k<float><<<g, RB, sh, s>>>(x.data, x.ld, y.data, y.ld, acc, R, head_dim, base, seq_len, sign,
+                                           (int)items, rpi);
+    else
+      rope_pipe_k<bf16_t><<<g, RB, sh, s>>>(x.data, x.ld, y.data, y.ld, acc, R, head_dim, base, seq_len, sign,
+                                            (int)items, rpi);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)std::min<int64_t>(R, 8192);
   const size_t shm = (size_t)2 * half * sizeof(float);
-  const float sign = inverse ? -1.f : 1.f;
   if (x.dtype == XT_F32) {
     if (vec) rope_k<float, true><<<grid, RB, shm, s>>>(x.data, x.ld, y.data, y.ld, acc, R, C, head_dim, base, seq_len, sign);
     else rope_k<float, false><<<grid, RB, shm, s>>>(x.data, x.ld, y.data, y.ld, acc, R, C, head_dim, base, seq_len, sign);

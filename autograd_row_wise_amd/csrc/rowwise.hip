@@ -18,6 +18,9 @@
 // Generic path (rows that do not fit in registers or are not 16-byte
 // aligned): one 256-thread block per row, several passes over global memory.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "common.h"
 #include "internal.h"
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
   const int64_t stride = (int64_t)gridDim.x * NG;
   float gam[NV][V];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
+  for (int j = 0; j < NV; ++j) load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
   RowPacks<T, NV, G> cur, nxt;
   int64_t base = (int64_t)blockIdx.x * NG;
   cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
       T* yr = row_ptr_w<T>(y, r, ldy);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int c0 = (j * G + gl) * V;
+        const int c0 = pack_col<NV, V>(j, gl);
         if (c0 < Ci) {
           float o[V];
 #pragma unroll
@@ -123,7 +126,7 @@ __device__ __forceinline__ void fold_partials(float (&pp)[NP][NV][V], float* red
         for (int j = 0; j < NV; ++j)
 #pragma unroll
           for (int k = 0; k < V; ++k) {
-            const int c = (j * G + gl) * V + k;
+            const int c = pack_col<NV, V>(j, gl) + k;
             if (c < C) red[q * C + c] = (gi == 0) ? pp[q][j][k] : red[q * C + c] + pp[q][j][k];
           }
     }
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
   float gam[NV][V], pp[1][NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
+    load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
 #pragma unroll
     for (int k = 0; k < V; ++k) pp[0][j][k] = 0.f;
   }
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
       T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int c0 = (j * G + gl) * V;
+        const int c0 = pack_col<NV, V>(j, gl);
         if (c0 < Ci) {
           float o[V];
 #pragma unroll
@@ -214,8 +217,8 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
   float gam[NV][V], bet[NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
-    load_f32s<V, int>(beta, (j * G + gl) * V, Ci, bet[j]);
+    load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
+    load_f32s<V, int>(beta, pack_col<NV, V>(j, gl), Ci, bet[j]);
   }
   RowPacks<T, NV, G> cur, nxt;
   int64_t base = (int64_t)blockIdx.x * NG;
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         const float t = v[j][k] - mu;
-        if ((j * G + gl) * V + k < Ci) q += t * t;
+        if (pack_col<NV, V>(j, gl) + k < Ci) q += t * t;
       }
     const float var = group_sum<RW>(q, lds) * invC;
     const float rs = rsqrtf(var + eps);
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
       T* yr = row_ptr_w<T>(y, r, ldy);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int c0 = (j * G + gl) * V;
+        const int c0 = pack_col<NV, V>(j, gl);
         if (c0 < Ci) {
           float o[V];
 #pragma unroll
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
   float gam[NV][V], pp[2][NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V, int>(gamma, (j * G + gl) * V, Ci, gam[j]);
+    load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
 #pragma unroll
     for (int k = 0; k < V; ++k) { pp[0][j][k] = 0.f; pp[1][j][k] = 0.f; }
   }
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int c0 = (j * G + gl) * V;
+      const int c0 = pack_col<NV, V>(j, gl);
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         const bool ok = c0 + k < Ci;
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
       T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int c0 = (j * G + gl) * V;
+        const int c0 = pack_col<NV, V>(j, gl);
         if (c0 < Ci) {
           float o[V];
 #pragma unroll
@@ -337,43 +340,51 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
 }
 
 // ================================================================== softmax
-template <typename T, int RW, int NV, int BLOCK>
+// The causal limit is applied per pack (one subtraction per pack, the
+// element offsets are immediates), so no per-element column indices stay
+// live.
+template <typename T, int RW, int NV, int BLOCK, bool CAUSAL>
 __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
     const void* __restrict__ x, int64_t ldx, void* __restrict__ y, int64_t ldy,
-    int64_t R, int64_t C, float alpha, int causal, int seq_len) {
+    int64_t R, int64_t C, float alpha, int seq_len) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
   __shared__ float lds[BLOCK / WAVE];
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
   const float NEG_INF = -__builtin_inff();
   const int64_t stride = (int64_t)gridDim.x * NG;
-  RowPacks<T, NV, G> cur, nxt;
+  // Two register sets of raw packs in a ring: the packs of row r+2 strides
+  // are fetched into the set of row r as soon as row r is unpacked (after
+  // the max barrier), so each row has about one and a half row times of
+  // lead; the current row is held once, in f32.
+  RowPacks<T, NV, G> b0, b1;
   int64_t base = (int64_t)blockIdx.x * NG;
-  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
-  for (; base < R; base += stride) {
-    const int64_t r = base + g, rn = base + stride + g;
+  b0.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
+  if (base + stride < R) b1.load(row_ptr<T>(x, base + stride + g < R ? base + stride + g : 0, ldx), gl, Ci, base + stride + g < R);
+  auto step = [&](RowPacks<T, NV, G>& cur, int64_t bs) {
+    const int64_t r = bs + g, rn = bs + 2 * stride + g;
     const bool active = r < R;
-    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
-    const int lim = causal ? (int)min(C, (int64_t)(r % seq_len) + 1) : Ci;   // valid columns
+    const int lim = !active ? 0 : (CAUSAL ? (int)min(C, (int64_t)(r % seq_len) + 1) : Ci);
     float v[NV][V];
     cur.unpack(v);
     float m = NEG_INF;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int c0 = (j * G + gl) * V;
+      const int left = lim - pack_col<NV, V>(j, gl);
 #pragma unroll
       for (int k = 0; k < V; ++k) {
-        v[j][k] = (active && c0 + k < lim) ? alpha * v[j][k] : NEG_INF;
+        v[j][k] = k < left ? alpha * v[j][k] : NEG_INF;
         m = fmaxf(m, v[j][k]);
       }
     }
     m = group_max<RW>(m, lds);
+    if (bs + 2 * stride < R) cur.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) {
-        v[j][k] = fast_exp(v[j][k] - m);        // masked: exp(-inf) = 0
+        v[j][k] = fast_exp(v[j][k] - m);
         s += v[j][k];
       }
     s = group_sum<RW>(s, lds);
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
       T* yr = row_ptr_w<T>(y, r, ldy);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int c0 = (j * G + gl) * V;
+        const int c0 = pack_col<NV, V>(j, gl);
         if (c0 < Ci) {
           float o[V];
 #pragma unroll
@@ -391,7 +402,10 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
         }
       }
     }
-    cur = nxt;
+  };
+  for (; base < R; base += 2 * stride) {
+    step(b0, base);
+    if (base + stride < R) step(b1, base + stride);
   }
 }
 
@@ -431,7 +445,7 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
       T* dxr = row_ptr_w<T>(dx, r, lddx);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int c0 = (j * G + gl) * V;
+        const int c0 = pack_col<NV, V>(j, gl);
         if (c0 < Ci) {
           float o[V];
 #pragma unroll
@@ -735,6 +749,33 @@ size_t row_bwd_workspace(RowKind kind, int dtype, int64_t R, int64_t C, bool ali
   return (size_t)p.grid * np * C * sizeof(float);
 }
 
+// Blocks of kernel f (block threads, shm bytes of dynamic LDS) that the
+// current device holds at once: occupancy per CU times the CU count, cached
+// per (device, kernel, shape).  Row kernels loop over rows, so a grid of
+// this size keeps every block resident (no second round of blocks) and
+// lets each block run its prefetch pipeline over many rows.
+static int resident_blocks(const void* f, int block, size_t shm) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1 << 30;
+  const auto key = std::make_tuple(dev, f, block, shm);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, block, shm) != hipSuccess || cus <= 0 || per_cu <= 0) {
+    (void)hipGetLastError();
+    return 1 << 30;                               // unknown: keep the planned grid
+  }
+  return cache[key] = per_cu * cus;
+}
+
+static int fit_grid(const void* f, int block, size_t shm, int want) {
+  return std::max(1, std::min(want, resident_blocks(f, block, shm)));
+}
+
 // Dispatch over the (RW, NV, BLOCK) shapes plan_rows can return.
 #define XT_ROW_CASE(RW_, NV_, B_, ...) \
   else if (p.rw == RW_ && p.nv == NV_ && p.block == B_) { constexpr int RW = RW_, NV = NV_, BLOCK = B_; (void)BLOCK; __VA_ARGS__; }
@@ -771,7 +812,8 @@ static hipError_t rms_fwd_t(const xt_tensor& x, const float* gamma, const xt_ten
   const RowPlan p = plan_rows(RK_RMS_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
   if (p.fast) {
     XT_ROW_SWITCH_FWD(
-        rms_fwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC));
+        auto kf = rms_fwd_fast<T, RW, NV, BLOCK>;
+        kf<<<fit_grid((const void*)kf, BLOCK, 0, p.grid), BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC));
   } else {
     rms_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
   }
@@ -800,16 +842,18 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
   const int64_t R = d.rows, C = d.cols;
   const float invC = 1.0f / (float)C;
   const bool al = aligned16(d) && aligned16(x) && (!dx || aligned16(*dx));
-  const RowPlan p = clamp_to_workspace(plan_rows(RK_RMS_BWD, d.dtype, R, C, al), 1, C, ws_bytes, dgamma != nullptr);
+  RowPlan p = clamp_to_workspace(plan_rows(RK_RMS_BWD, d.dtype, R, C, al), 1, C, ws_bytes, dgamma != nullptr);
   if (p.grid < 1) return hipErrorInvalidValue;
   float* part = dgamma ? (float*)ws : nullptr;
-  const int64_t rpb = cdiv(R, p.grid);
   if (p.fast) {
     const size_t shm = dgamma ? (size_t)C * sizeof(float) : 0;
     XT_ROW_SWITCH_BWD(
-      rms_bwd_fast<T, RW, NV><<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
-                                                             dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC, rpb));
+      auto kf = rms_bwd_fast<T, RW, NV>;
+      p.grid = fit_grid((const void*)kf, BWD_BLOCK, shm, p.grid);
+      kf<<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
+                                        dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC, cdiv(R, p.grid)));
   } else {
+    const int64_t rpb = cdiv(R, p.grid);
     if (dx)
       rms_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld, dx->data, dx->ld, acc_dx, R, C, invC);
     if (dgamma)
@@ -836,7 +880,8 @@ static hipError_t ln_fwd_t(const xt_tensor& x, const float* gamma, const float* 
   const RowPlan p = plan_rows(RK_LN_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
   if (p.fast) {
     XT_ROW_SWITCH_FWD(
-        ln_fwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC));
+        auto kf = ln_fwd_fast<T, RW, NV, BLOCK>;
+        kf<<<fit_grid((const void*)kf, BLOCK, 0, p.grid), BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC));
   } else {
     ln_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
   }
@@ -860,17 +905,19 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
   const float invC = 1.0f / (float)C;
   const bool al = aligned16(d) && aligned16(x) && (!dx || aligned16(*dx));
   const bool want_p = dgamma || dbeta;
-  const RowPlan p = clamp_to_workspace(plan_rows(RK_LN_BWD, d.dtype, R, C, al), 2, C, ws_bytes, want_p);
+  RowPlan p = clamp_to_workspace(plan_rows(RK_LN_BWD, d.dtype, R, C, al), 2, C, ws_bytes, want_p);
   if (p.grid < 1) return hipErrorInvalidValue;
   float* part = want_p ? (float*)ws : nullptr;
-  const int64_t rpb = cdiv(R, p.grid);
   if (p.fast) {
     const size_t shm = want_p ? (size_t)2 * C * sizeof(float) : 0;
     XT_ROW_SWITCH_BWD(
-      ln_bwd_fast<T, RW, NV><<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
-                                                            (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr, dx ? dx->ld : 0,
-                                                            acc_dx, part, R, C, invC, rpb));
+      auto kf = ln_bwd_fast<T, RW, NV>;
+      p.grid = fit_grid((const void*)kf, BWD_BLOCK, shm, p.grid);
+      kf<<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
+                                        (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr, dx ? dx->ld : 0,
+                                        acc_dx, part, R, C, invC, cdiv(R, p.grid)));
   } else {
+    const int64_t rpb = cdiv(R, p.grid);
     if (dx)
       ln_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
                                                  (const float*)rstd.data, rstd.ld, dx->data, dx->ld, acc_dx, R, C, invC);
@@ -900,7 +947,10 @@ static hipError_t sm_fwd_t(const xt_tensor& x, const xt_tensor& y, float alpha, 
   const RowPlan p = plan_rows(RK_SM_FWD, x.dtype, R, C, aligned16(x) && aligned16(y));
   if (p.fast) {
     XT_ROW_SWITCH_FWD(
-        sm_fwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len));
+        // softmax keeps the planned (larger) grid: measured faster for long
+        // rows than one resident block per CU
+        auto kf = causal ? sm_fwd_fast<T, RW, NV, BLOCK, true> : sm_fwd_fast<T, RW, NV, BLOCK, false>;
+        kf<<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, seq_len));
   } else {
     sm_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
   }

@@ -90,7 +90,9 @@ def build_entries(only):
 
     V, P = xt.view, xt.params
     E = []
-    want = (lambda n: True) if not only else (lambda n: any(n.startswith(o) for o in only))
+    # a name is wanted when it and a requested prefix agree as far as both go
+    # ("c4" selects every bf16 16384 x 4096 op; "c4.rope" only rope)
+    want = (lambda n: True) if not only else (lambda n: any(n.startswith(o) or o.startswith(n) for o in only))
 
     def empty(shape, dt):
         return torch.empty(shape, dtype={"f32": torch.float32, "bf16": torch.bfloat16, "u8": torch.uint8}[dt],

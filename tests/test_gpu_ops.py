@@ -213,7 +213,9 @@ def test_swiglu(dtype, R, C, ld):
 
 # --------------------------------------------------------------------- rope
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("R,H,Dh,S", [(8, 4, 16, 8), (300, 4, 64, 256), (33, 2, 128, 4096), (10, 3, 6, 5)])
+@pytest.mark.parametrize("R,H,Dh,S", [(8, 4, 16, 8), (300, 4, 64, 256), (33, 2, 128, 4096), (10, 3, 6, 5),
+                                     (5, 80, 128, 16),        # rows longer than one pipelined tile
+                                     (20000, 8, 64, 1000)])   # more tiles than blocks: pipelined loop
 def test_rope(dtype, R, H, Dh, S):
     C = H * Dh
     x, xv = put(normal((R, C), 7, "x"), dtype)
@@ -227,6 +229,10 @@ def test_rope(dtype, R, H, Dh, S):
     if dtype == "f32":   # position 0 rows are the identity, bit for bit
         for r in range(0, R, S):
             assert np.array_equal(host(y)[r], xv[r])
+    # accumulate: dx += rope_bwd(d) onto the previous dx
+    prev = host(dx)
+    bwd(xt.OP.ROPE, prm, d, [x], [], [dx], acc=1)
+    close(host(dx), prev + ops.rope_bwd(dv, Dh, 10000.0, S), dtype, what="dx+=")
 
 
 # ----------------------------------------------------------------- add_bias
