@@ -77,15 +77,16 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
   float gam[NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
-  RowPacks<T, NV, G> cur, nxt;
+  RowPacks<T, NV, G> b0, b1;
   int64_t base = (int64_t)blockIdx.x * NG;
-  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
-  for (; base < R; base += stride) {
-    const int64_t r = base + g, rn = base + stride + g;
+  b0.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
+  if (base + stride < R) b1.load(row_ptr<T>(x, base + stride + g < R ? base + stride + g : 0, ldx), gl, Ci, base + stride + g < R);
+  auto step = [&](RowPacks<T, NV, G>& cur, int64_t bs) {
+    const int64_t r = bs + g, rn = bs + 2 * stride + g;
     const bool active = r < R;
-    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float v[NV][V];
     cur.unpack(v);
+    if (bs + 2 * stride < R) cur.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -107,7 +108,10 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
       }
       if (gl == 0) ir[r * ldir] = irv;
     }
-    cur = nxt;
+  };
+  for (; base < R; base += 2 * stride) {
+    step(b0, base);
+    if (base + stride < R) step(b1, base + stride);
   }
 }
 
@@ -156,22 +160,28 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
   }
   const int64_t start = (int64_t)blockIdx.x * rpb;
   const int64_t end = min(R, start + rpb);
-  RowPacks<T, NV, G> cd, cx, nd, nx;
+  // two register sets in a ring: rows base+2*NG are fetched into the set of
+  // row base as soon as it is unpacked
+  RowPacks<T, NV, G> d0, x0, d1, x1;
   {
-    const int64_t r = start + g;
-    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
-    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
-  }
-  for (int64_t base = start; base < end; base += NG) {
-    const int64_t r = base + g, rn = base + NG + g;
-    const bool active = r < end;
-    if (base + NG < end) {
-      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
-      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
+    const int64_t r = start + g, r1 = start + NG + g;
+    d0.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
+    x0.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
+    if (start + NG < end) {
+      d1.load(row_ptr<T>(d, r1 < end ? r1 : 0, ldd), gl, Ci, r1 < end);
+      x1.load(row_ptr<T>(x, r1 < end ? r1 : 0, ldx), gl, Ci, r1 < end);
     }
+  }
+  auto step = [&](RowPacks<T, NV, G>& cd, RowPacks<T, NV, G>& cx, int64_t base) {
+    const int64_t r = base + g, rn = base + 2 * NG + g;
+    const bool active = r < end;
     float dv[NV][V], xv[NV][V];
     cd.unpack(dv);
     cx.unpack(xv);
+    if (base + 2 * NG < end) {
+      cd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
+      cx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
+    }
     float dot = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -196,8 +206,10 @@ __global__ __launch_bounds__(BWD_BLOCK) void rms_bwd_fast(
         }
       }
     }
-    cd = nd;
-    cx = nx;
+  };
+  for (int64_t base = start; base < end; base += 2 * NG) {
+    step(d0, x0, base);
+    if (base + NG < end) step(d1, x1, base + NG);
   }
   if (part) fold_partials<NV, V, G, NG, 1, BWD_BLOCK>(pp, red, part, C);
 }
@@ -220,15 +232,16 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
     load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
     load_f32s<V, int>(beta, pack_col<NV, V>(j, gl), Ci, bet[j]);
   }
-  RowPacks<T, NV, G> cur, nxt;
+  RowPacks<T, NV, G> b0, b1;
   int64_t base = (int64_t)blockIdx.x * NG;
-  cur.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
-  for (; base < R; base += stride) {
-    const int64_t r = base + g, rn = base + stride + g;
+  b0.load(row_ptr<T>(x, base + g < R ? base + g : 0, ldx), gl, Ci, base + g < R);
+  if (base + stride < R) b1.load(row_ptr<T>(x, base + stride + g < R ? base + stride + g : 0, ldx), gl, Ci, base + stride + g < R);
+  auto step = [&](RowPacks<T, NV, G>& cur, int64_t bs) {
+    const int64_t r = bs + g, rn = bs + 2 * stride + g;
     const bool active = r < R;
-    if (base + stride < R) nxt.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float v[NV][V];
     cur.unpack(v);
+    if (bs + 2 * stride < R) cur.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -259,7 +272,10 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
       }
       if (gl == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
     }
-    cur = nxt;
+  };
+  for (; base < R; base += 2 * stride) {
+    step(b0, base);
+    if (base + stride < R) step(b1, base + stride);
   }
 }
 
@@ -283,24 +299,28 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
   }
   const int64_t start = (int64_t)blockIdx.x * rpb;
   const int64_t end = min(R, start + rpb);
-  RowPacks<T, NV, G> cd, cx, nd, nx;
+  RowPacks<T, NV, G> d0, x0, d1, x1;
   {
-    const int64_t r = start + g;
-    cd.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
-    cx.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
-  }
-  for (int64_t base = start; base < end; base += NG) {
-    const int64_t r = base + g, rn = base + NG + g;
-    const bool active = r < end;
-    if (base + NG < end) {
-      nd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
-      nx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
+    const int64_t r = start + g, r1 = start + NG + g;
+    d0.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
+    x0.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
+    if (start + NG < end) {
+      d1.load(row_ptr<T>(d, r1 < end ? r1 : 0, ldd), gl, Ci, r1 < end);
+      x1.load(row_ptr<T>(x, r1 < end ? r1 : 0, ldx), gl, Ci, r1 < end);
     }
+  }
+  auto step = [&](RowPacks<T, NV, G>& cd, RowPacks<T, NV, G>& cx, int64_t base) {
+    const int64_t r = base + g, rn = base + 2 * NG + g;
+    const bool active = r < end;
     const float mu = active ? mean[r * ldm] : 0.f;
     const float rs = active ? rstd[r * ldr] : 0.f;
     float dv[NV][V], xh[NV][V];
     cd.unpack(dv);
     cx.unpack(xh);
+    if (base + 2 * NG < end) {
+      cd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
+      cx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
+    }
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -333,8 +353,10 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
         }
       }
     }
-    cd = nd;
-    cx = nx;
+  };
+  for (int64_t base = start; base < end; base += 2 * NG) {
+    step(d0, x0, base);
+    if (base + NG < end) step(d1, x1, base + NG);
   }
   if (part) fold_partials<NV, V, G, NG, 2, BWD_BLOCK>(pp, red, part, C);
 }
