@@ -70,6 +70,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None, help="run only ops whose name starts with one of these")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the rows/s sweep over d = 768..4096")
     ap.add_argument("--ops-json", default=None, help="also write the per-op table to this file")
     return ap.parse_args()
 
@@ -327,10 +328,97 @@ def build_entries(only):
 
 
 # --------------------------------------------------------------------------
-def cpu_baseline(frac_rows=1 / 32):
+SWEEP_DIMS = (768, 1024, 2048, 3072, 4096)
+
+
+def sweep(steps, warmup):
+    """rows/s against the row width d for the row-wise ops: every op fwd and
+    bwd at d in SWEEP_DIMS with R = 2^30 / (s*d) rows (1 GiB per activation
+    tensor), f32 and bf16; timed with HIP events on the launch stream."""
+    import torch
+    import autograd_row_wise_amd as xt
+    from synth import device_normal
+
+    V, P = xt.view, xt.params
+    big = 1 << 30
+    res = []
+    for dt, s_ in (("f32", 4), ("bf16", 2)):
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        nel = big // s_
+        X = device_normal((nel // 4096, 4096), 7, "x", dtype=dt)
+        D = device_normal((nel // 4096, 4096), 7, "dout", dtype=dt)
+        Y = torch.empty_like(X)
+        DX = torch.empty_like(X)
+        st1 = torch.empty(big // (s_ * 768), dtype=torch.float32, device="cuda")
+        st2 = torch.empty_like(st1)
+        gam = torch.ones(4096, dtype=torch.float32, device="cuda")
+        bet = torch.zeros(4096, dtype=torch.float32, device="cuda")
+        dg = torch.empty(4096, dtype=torch.float32, device="cuda")
+        db = torch.empty(4096, dtype=torch.float32, device="cuda")
+        for d in SWEEP_DIMS:
+            R = big // (s_ * d)
+            N = R * d
+            x, dd, y, dx = (t.view(-1)[:N].view(R, d) for t in (X, D, Y, DX))
+            a, b = st1[:R].view(R, 1), st2[:R].view(R, 1)
+            g, bt, gg, gb = gam[:d].view(1, d), bet[:d].view(1, d), dg[:d].view(1, d), db[:d].view(1, d)
+            def wsp(op, prm, ins):
+                n = xt.xt_workspace_bytes(op, 1, prm, ins)
+                w = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+                return w, (w.data_ptr() if n else None), n
+            pe = P(eps=1e-5)
+            w_rms = wsp(xt.OP.RMS_NORM, pe, [V(x), V(g)])
+            w_ln = wsp(xt.OP.LAYER_NORM, pe, [V(x), V(g), V(bt)])
+            pr = P(head_dim=128, seq_len=4096, rope_base=10000.0)
+            ops = {
+                "rms_norm": (lambda: xt.xt_op_fwd(xt.OP.RMS_NORM, pe, [V(x), V(g)], [V(y), V(a)]),
+                             lambda: xt.xt_op_bwd(xt.OP.RMS_NORM, pe, V(dd), [V(x), V(g)], [V(a)], [V(dx), V(gg)], 0,
+                                                  w_rms[1], w_rms[2]),
+                             2 * s_ * N + 4 * R, 3 * s_ * N + 4 * R),
+                "layer_norm": (lambda: xt.xt_op_fwd(xt.OP.LAYER_NORM, pe, [V(x), V(g), V(bt)], [V(y), V(a), V(b)]),
+                               lambda: xt.xt_op_bwd(xt.OP.LAYER_NORM, pe, V(dd), [V(x), V(g), V(bt)], [V(a), V(b)],
+                                                    [V(dx), V(gg), V(gb)], 0, w_ln[1], w_ln[2]),
+                               2 * s_ * N + 8 * R, 3 * s_ * N + 8 * R),
+                "softmax": (lambda: xt.xt_op_fwd(xt.OP.SOFTMAX, P(), [V(x)], [V(y)]),
+                            lambda: xt.xt_op_bwd(xt.OP.SOFTMAX, P(), V(dd), [V(x)], [V(y)], [V(dx)]),
+                            2 * s_ * N, 3 * s_ * N),
+                "rope": (lambda: xt.xt_op_fwd(xt.OP.ROPE, pr, [V(x)], [V(y)]),
+                         lambda: xt.xt_op_bwd(xt.OP.ROPE, pr, V(dd), [V(x)], [], [V(dx)]),
+                         2 * s_ * N, 2 * s_ * N),
+                "silu": (lambda: xt.xt_op_fwd(xt.OP.SILU, P(), [V(x)], [V(y)]),
+                         lambda: xt.xt_op_bwd(xt.OP.SILU, P(), V(dd), [V(x)], [], [V(dx)]),
+                         2 * s_ * N, 3 * s_ * N),
+            }
+            stream = torch.cuda.current_stream()
+            for name, (f, bwd, bf, bb) in ops.items():
+                ms = []
+                for fn in (f, bwd):
+                    for _ in range(warmup):
+                        fn()
+                    ev = []
+                    for _ in range(steps):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        fn()
+                        e1.record(stream)
+                        ev.append((e0, e1))
+                    torch.cuda.synchronize()
+                    ms.append(sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps)
+                gbps = (bf + bb) / ((ms[0] + ms[1]) * 1e-3) / 1e9
+                res.append({"op": name, "dtype": dt, "d": d, "rows": R, "fwd_ms": round(ms[0], 4),
+                            "bwd_ms": round(ms[1], 4), "fwd_rows_per_s": round(R / (ms[0] * 1e-3)),
+                            "bwd_rows_per_s": round(R / (ms[1] * 1e-3)), "fwdbwd_GBps": round(gbps, 1),
+                            "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        del X, D, Y, DX
+        torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------
+def cpu_baseline(frac_rows=1 / 32, min_seconds=10.0, max_passes=12):
     """The oracle (numpy f64, single thread) on the first `frac_rows` of the
-    rows of every memory-bound op of the step; returns GB/s over the sample's
-    algorithmic bytes."""
+    rows of every memory-bound op of the step, repeated until at least
+    `min_seconds` of oracle time (at most `max_passes` passes); returns GB/s
+    over the sample's algorithmic bytes."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -369,17 +457,19 @@ def cpu_baseline(frac_rows=1 / 32):
     lg5 = synth.host_normal((R5, 128256), 5, "logits", 0.0, 3.0).astype(np.float64)
     t5 = synth.host_uniform_int((R5,), 0, 128256, 5, "targets")
     jobs.append(("ce5", 3 * 2 * R5 * 128256, lambda: ops.cross_entropy_bwd(1.0, lg5, t5, ops.cross_entropy(lg5, t5)[1])))
-    total_b, total_t = 0, 0.0
+    total_b, total_t, passes = 0, 0.0, 0
     with threadpool_limits(limits=1):
-        for name, nb, fn in jobs:
-            t0 = time.perf_counter()
-            fn()
-            total_t += time.perf_counter() - t0
-            total_b += nb
+        while passes < max_passes and (passes == 0 or total_t < min_seconds):
+            for name, nb, fn in jobs:
+                t0 = time.perf_counter()
+                fn()
+                total_t += time.perf_counter() - t0
+                total_b += nb
+            passes += 1
     return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"numpy f64 oracle, fwd+bwd of layer_norm, gelu, cross_entropy (both vocabularies), rms_norm, "
-                      f"rope, dropout, swiglu, softmax on the first 1/{int(round(1 / frac_rows))} of each op's rows; "
-                      f"{total_b / 1e9:.2f} GB algorithmic in {total_t:.1f} s"}
+                      f"rope, dropout, swiglu, softmax on the first 1/{int(round(1 / frac_rows))} of each op's rows, "
+                      f"{passes} pass(es); {total_b / 1e9:.2f} GB algorithmic in {total_t:.1f} s"}
 
 
 # --------------------------------------------------------------------------
@@ -476,6 +566,9 @@ def main():
     if args.ops_json:
         with open(args.ops_json, "w") as f:
             json.dump(ops_out, f, indent=1)
+    if not args.no_sweep and not args.only:
+        out["sweep"] = {"what": "fwd and bwd of each row-wise op at 1 GiB per activation tensor, R = 2^30/(s*d)",
+                        "entries": sweep(args.steps, args.warmup)}
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline()
