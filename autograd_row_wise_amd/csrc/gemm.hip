@@ -616,6 +616,144 @@ __global__ __launch_bounds__(b8::NT) void gemm_b8_k(
       }
 }
 
+// --------------------------------------------------------------------------
+// bf16 NT products (both operands stored k-contiguous: dA = d B^T, and every
+// product whose second operand is read transposed) skip the register
+// staging: each lane issues global_load_lds_dwordx4, which writes its 16
+// bytes straight into LDS at the wave's destination + 16 * lane.  K tiles
+// are 32 deep (LDS rows of 64 bytes, four 16-byte chunks, chunk c of row r
+// at c ^ ((r >> 2) & 3): sixteen consecutive rows read at one chunk hit
+// sixteen distinct 16-byte bank groups), held in a ring of four LDS stages
+// (4 x 32 KB): tile kt+3 is requested while tile kt is multiplied, and each
+// wave waits only until its transfers of tile kt+1 have landed (the two
+// newer tiles stay in flight) before the barrier that publishes them.
+// --------------------------------------------------------------------------
+namespace b8d {
+constexpr int BK = 32, STAGES = 4;
+constexpr int TILE = 256 * BK;                       // elements of one operand tile
+}  // namespace b8d
+
+__device__ __forceinline__ int swz4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+
+// Four DMA instructions per wave per tile: operand rows row0.., k0.., both
+// 256 x 32; instruction j of wave w fills slots 64 blk .. 64 blk + 63.
+__device__ __forceinline__ void b8d_dma_tile(const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
+                                             bf16_t* __restrict__ lds_tile, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int blk = w * 2 + j;                       // 64 slots = rows 16 blk .. 16 blk + 15
+    const int row = blk * 16 + l / 4;
+    const int c = (l % 4) ^ ((row >> 2) & 3);
+    __builtin_amdgcn_global_load_lds(g + (row0 + row) * ld + k0 + c * 8, lds_tile + blk * 64 * 8, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void b8d_mma(const u32x4_t* LA, f32x16_t (&acc)[4][2], int wm, int wn, int lr, int lh) {
+  const u32x4_t* LB = LA + b8d::TILE / 8;
+#pragma unroll
+  for (int s = 0; s < b8d::BK / 16; ++s) {
+    bf16x8_t a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8_t, LA[swz4(wm + i * 32 + lr, 2 * s + lh)]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(bf16x8_t, LB[swz4(wn + j * 32 + lr, 2 * s + lh)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One K tile: request tile kt+3 into `nxt`, multiply out of `cur`; restrict
+// pointers let the compiler see that the reads of `cur` do not depend on the
+// transfers into `nxt`.
+__device__ __forceinline__ void b8d_step(const bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt, bool more,
+                                         const bf16_t* A, int64_t lda, int64_t m0, const bf16_t* B, int64_t ldb,
+                                         int64_t n0, int64_t k0, f32x16_t (&acc)[4][2], int w, int l, int wm,
+                                         int wn, int lr, int lh) {
+  if (more) {
+    b8d_dma_tile(A, lda, m0, k0, nxt, w, l);
+    b8d_dma_tile(B, ldb, n0, k0, nxt + b8d::TILE, w, l);
+  }
+  b8d_mma(reinterpret_cast<const u32x4_t*>(cur), acc, wm, wn, lr, lh);
+}
+
+template <typename TC>
+__global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
+    const bf16_t* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
+    const bf16_t* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
+    TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
+    int64_t kchunk, int64_t nbatch, int64_t scs) {
+  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = b8d::BK, TILE = b8d::TILE, NS = b8d::STAGES;
+  __shared__ __align__(16) bf16_t lds[NS][2 * TILE];       // [stage][A tile, B tile]
+
+  const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
+  const int64_t kb0 = split * kchunk;
+  A += b0 * sa0 + b1 * sa1 + kb0;                            // A [M][K], B [N][K]
+  B += b0 * sb0 + b1 * sb1 + kb0;
+  C += b0 * sc0 + b1 * sc1 + split * scs;
+  K = K - kb0 < kchunk ? K - kb0 : kchunk;
+
+  const int tiles_n = (int)(N / BN8);
+  const int tiles = (int)(M / BM8) * tiles_n;
+  const int g = blockIdx.x;
+  const int tt = (tiles % 8 == 0) ? (g % 8) * (tiles / 8) + g / 8 : g;
+  const int64_t m0 = (int64_t)(tt / tiles_n) * BM8, n0 = (int64_t)(tt % tiles_n) * BN8;
+
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const int wm = (w / 4) * 128, wn = (w % 4) * 64;
+  const int lr = l % 32, lh = l / 32;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int nk = (int)(K / BK);
+  // prologue: tiles 0, 1, 2 requested; tile 0 landed and published
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) {
+      b8d_dma_tile(A, lda, m0, (int64_t)p * BK, lds[p], w, l);
+      b8d_dma_tile(B, ldb, n0, (int64_t)p * BK, lds[p] + TILE, w, l);
+    }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    b8d_step(lds[kt % NS], lds[(kt + NS - 1) % NS], kt + NS - 1 < nk, A, lda, m0, B, ldb, n0,
+             (int64_t)(kt + NS - 1) * BK, acc, w, l, wm, wn, lr, lh);
+    // Tile kt+1 must have landed: its 4 transfers are older than the (up
+    // to) 8 of tiles kt+2 and kt+3, so vmcnt <= 8 suffices; lgkmcnt 0 makes
+    // this wave's reads of stage kt complete before anyone may overwrite it
+    // (the next step requests tile kt+4 into that stage).  Then a bare
+    // s_barrier publishes tile kt+1: a full __syncthreads() fence would
+    // wait for every transfer in flight.  The empty asm statements keep the
+    // compiler from moving LDS accesses across the barrier.
+    __builtin_amdgcn_s_waitcnt(0x078);              // vmcnt(8) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm + i * 32 + 8 * (q / 4) + 4 * (l / 32) + (q % 4);
+        const int64_t col = n0 + wn + j * 32 + (l % 32);
+        TC* p = C + row * ldc + col;
+        float v = alpha * acc[i][j][q];
+        if (acc_c) v = acc_add(io<TC>::ld(p), v);
+        io<TC>::st(p, v);
+      }
+}
+
 template <typename TA>
 bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C) {
   const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
@@ -723,6 +861,11 @@ hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, 
     dim3 grid((unsigned)((M / b8::BM) * (N / b8::BN)), 1, (unsigned)(S * nbatch));
     const bf16_t* a8 = (const bf16_t*)A.data;
     const bf16_t* b8p = (const bf16_t*)B.data;
+    if (!ta && tb) {
+      gemm_b8dma_k<TC><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0], B.sb[1], c, ldc, sc0,
+                                               sc1, M, N, K, nb1, alpha, acc ? 1 : 0, kchunk, nbatch, scs);
+      return hipGetLastError();
+    }
 #define XT_B8(TA_, TB_)                                                                                   gemm_b8_k<TC, TA_, TB_><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0],                                                      B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1, alpha,                                                      acc ? 1 : 0, kchunk, nbatch, scs)
     if (!ta && !tb) XT_B8(false, false);
     else if (!ta && tb) XT_B8(false, true);
