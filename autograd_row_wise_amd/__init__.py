@@ -47,7 +47,7 @@ class Tensor(C.Structure):
 class Params(C.Structure):
     _fields_ = [("eps", C.c_float), ("alpha", C.c_float), ("causal", C.c_int32),
                 ("seq_len", C.c_int32), ("head_dim", C.c_int32), ("rope_base", C.c_float),
-                ("p", C.c_float), ("reserved0", C.c_int32), ("seed", C.c_uint64),
+                ("p", C.c_float), ("gelu_tanh", C.c_int32), ("seed", C.c_uint64),
                 ("trans_a", C.c_int32), ("trans_b", C.c_int32)]
 
 
@@ -168,8 +168,8 @@ def empty_view(t) -> Tensor:
 
 
 def params(eps=1e-5, alpha=1.0, causal=0, seq_len=0, head_dim=0, rope_base=10000.0, p=0.0,
-           seed=0, trans_a=0, trans_b=0) -> Params:
-    return Params(eps, alpha, int(causal), int(seq_len), int(head_dim), rope_base, p, 0,
+           seed=0, trans_a=0, trans_b=0, gelu_tanh=0) -> Params:
+    return Params(eps, alpha, int(causal), int(seq_len), int(head_dim), rope_base, p, int(gelu_tanh),
                   int(seed) & 0xFFFFFFFFFFFFFFFF, int(trans_a), int(trans_b))
 
 

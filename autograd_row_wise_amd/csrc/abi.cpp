@@ -243,8 +243,11 @@ xt_status xt_op_fwd(xt_op op, const xt_params* prm, const xt_tensor* in, int n_i
       XT_TRY(need(1, 1));
       XT_TRY(check_act(&in[0], "x"));
       XT_TRY(check_like(&out[0], in[0], "y"));
+      if (op == XT_OP_GELU && prm->gelu_tanh != 0 && prm->gelu_tanh != 1)
+        return fail(XT_ERR_INVALID_ARG, "gelu_tanh must be 0 (erf form) or 1 (tanh form)");
       EwArgs e{{&in[0], nullptr, nullptr}, {&out[0], nullptr}, 0u, 1.f, nullptr};
-      return hip_status(launch_ew(op == XT_OP_SILU ? EW_SILU : EW_GELU, e, s), "silu/gelu");
+      const EwOp k = op == XT_OP_SILU ? EW_SILU : (prm->gelu_tanh ? EW_GELU_TANH : EW_GELU);
+      return hip_status(launch_ew(k, e, s), "silu/gelu");
     }
     case XT_OP_SWIGLU: {
       XT_TRY(need(2, 1));
@@ -425,8 +428,11 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
       XT_TRY(check_like(&in[0], *dout, "x"));
       if (!wanted(din, n_din, 0)) return XT_OK;
       XT_TRY(check_like(&din[0], *dout, "dx"));
+      if (op == XT_OP_GELU && prm->gelu_tanh != 0 && prm->gelu_tanh != 1)
+        return fail(XT_ERR_INVALID_ARG, "gelu_tanh must be 0 (erf form) or 1 (tanh form)");
       EwArgs e{{dout, &in[0], nullptr}, {&din[0], nullptr}, acc(0) ? 1u : 0u, 1.f, nullptr};
-      return hip_status(launch_ew(op == XT_OP_SILU ? EW_SILU_BWD : EW_GELU_BWD, e, s), "silu/gelu backward");
+      const EwOp k = op == XT_OP_SILU ? EW_SILU_BWD : (prm->gelu_tanh ? EW_GELU_TANH_BWD : EW_GELU_BWD);
+      return hip_status(launch_ew(k, e, s), "silu/gelu backward");
     }
     case XT_OP_SWIGLU: {
       XT_TRY(need(2, 0, 2));

@@ -79,6 +79,34 @@ __device__ __forceinline__ float dgelu_(float x) {
   return cdf + x * pdf;
 }
 
+// tanh form of GELU (Hendrycks & Gimpel, "Gaussian Error Linear Units"):
+// g(x) = x (1 + tanh u) / 2, u = sqrt(2/pi) (x + 0.044715 x^3);
+// g'(x) = (1 + tanh u) / 2 + x (1 - tanh^2 u) u'(x) / 2.
+// With a = e^{-2|u|} in (0, 1] and s = 1 / (1 + a): 1 + tanh u = 2s for
+// u >= 0 and 2as for u < 0, and 1 - tanh^2 u = 4as^2. Neither form
+// subtracts nearly equal numbers or overflows, so both keep full relative
+// precision far into the tails.
+__device__ __forceinline__ void tanh_parts_(float x, float& onep, float& sech2, float& du) {
+  const float k = 0.79788456080286536f;  // sqrt(2/pi)
+  const float x2 = x * x;
+  const float u = k * x * (1.0f + 0.044715f * x2);
+  const float a = __expf(-2.0f * fabsf(u));
+  const float s = 1.0f / (1.0f + a);
+  onep = 2.0f * s * (u < 0.0f ? a : 1.0f);
+  sech2 = 4.0f * a * s * s;
+  du = k * (1.0f + 3.0f * 0.044715f * x2);
+}
+__device__ __forceinline__ float gelu_tanh_(float x) {
+  float onep, sech2, du;
+  tanh_parts_(x, onep, sech2, du);
+  return 0.5f * x * onep;
+}
+__device__ __forceinline__ float dgelu_tanh_(float x) {
+  float onep, sech2, du;
+  tanh_parts_(x, onep, sech2, du);
+  return 0.5f * onep + 0.5f * x * sech2 * du;
+}
+
 // One element: reads up to 3 inputs, produces up to 2 outputs.
 template <int OP>
 __device__ __forceinline__ void ew_apply(const float* in, float* out, float alpha, float colv) {
@@ -92,6 +120,8 @@ __device__ __forceinline__ void ew_apply(const float* in, float* out, float alph
   else if constexpr (OP == EW_MUL_BWD) { out[0] = in[0] * in[2]; out[1] = in[0] * in[1]; }
   else if constexpr (OP == EW_SILU_BWD) out[0] = in[0] * dsilu_(in[1]);
   else if constexpr (OP == EW_GELU_BWD) out[0] = in[0] * dgelu_(in[1]);
+  else if constexpr (OP == EW_GELU_TANH) out[0] = gelu_tanh_(in[0]);
+  else if constexpr (OP == EW_GELU_TANH_BWD) out[0] = in[0] * dgelu_tanh_(in[1]);
   else if constexpr (OP == EW_SWIGLU_BWD) {
     const float g = in[1], u = in[2], d = in[0];
     out[0] = (d * u) * dsilu_(g);
@@ -101,7 +131,8 @@ __device__ __forceinline__ void ew_apply(const float* in, float* out, float alph
 
 template <int OP> constexpr int n_in() {
   return (OP == EW_MUL_BWD || OP == EW_SWIGLU_BWD) ? 3
-         : (OP == EW_ADD || OP == EW_MUL || OP == EW_SWIGLU || OP == EW_SILU_BWD || OP == EW_GELU_BWD) ? 2 : 1;
+         : (OP == EW_ADD || OP == EW_MUL || OP == EW_SWIGLU || OP == EW_SILU_BWD || OP == EW_GELU_BWD ||
+            OP == EW_GELU_TANH_BWD) ? 2 : 1;
 }
 template <int OP> constexpr int n_out() {
   return (OP == EW_MUL_BWD || OP == EW_SWIGLU_BWD || OP == EW_SCALE) ? 2 : 1;
@@ -490,6 +521,8 @@ hipError_t launch_ew(EwOp op, const EwArgs& e, hipStream_t s) {
     case EW_MUL_BWD: return ew_dt<EW_MUL_BWD>(e, s);
     case EW_SILU_BWD: return ew_dt<EW_SILU_BWD>(e, s);
     case EW_GELU_BWD: return ew_dt<EW_GELU_BWD>(e, s);
+    case EW_GELU_TANH: return ew_dt<EW_GELU_TANH>(e, s);
+    case EW_GELU_TANH_BWD: return ew_dt<EW_GELU_TANH_BWD>(e, s);
     case EW_SWIGLU_BWD: return ew_dt<EW_SWIGLU_BWD>(e, s);
     case EW_ACCUMULATE: {
       const int dd = e.out[0]->dtype, sd = e.in[0]->dtype;

@@ -67,6 +67,7 @@ enum EwOp {
   EW_COPY_SCALED,              // out0 (+)= alpha * in0
   EW_MUL_BWD,                  // out0 (+)= d*b, out1 (+)= d*a
   EW_SILU_BWD, EW_GELU_BWD, EW_SWIGLU_BWD,
+  EW_GELU_TANH, EW_GELU_TANH_BWD,
   EW_ACCUMULATE                // out0 += in0 (dtypes may differ)
 };
 struct EwArgs {

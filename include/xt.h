@@ -86,7 +86,7 @@ typedef enum {
   XT_OP_CROSS_ENTROPY = 8, /* L = mean_r(lse_r - x[r, t_r])                */
   XT_OP_SILU = 9,          /* y = x * sigmoid(x)                           */
   XT_OP_SWIGLU = 10,       /* y = silu(g) * u                              */
-  XT_OP_GELU = 11,         /* y = x * Phi(x) (exact, erf form)             */
+  XT_OP_GELU = 11,         /* y = x * Phi(x) (erf form; tanh form if set)  */
   XT_OP_ROPE = 12,         /* rotate-half rotary embedding                 */
   XT_OP_DROPOUT = 13,      /* counter-based inverted dropout               */
   XT_OP_COUNT = 14
@@ -101,7 +101,8 @@ typedef struct {
   int32_t  head_dim;   /* ROPE: even head width; cols must be a multiple     */
   float    rope_base;  /* ROPE: theta(pos, i) = pos * base^(-2i/head_dim)    */
   float    p;          /* DROPOUT: drop probability, 0 <= p < 1              */
-  int32_t  reserved0;  /* must be 0 */
+  int32_t  gelu_tanh;  /* GELU: 0 = exact x*Phi(x); 1 = tanh form
+                          0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))     */
   uint64_t seed;       /* DROPOUT: 64-bit counter-RNG seed                   */
   int32_t  trans_a;    /* MATMUL: read A transposed                          */
   int32_t  trans_b;    /* MATMUL: read B transposed                          */

@@ -254,6 +254,24 @@ def gelu_bwd(d, x):
     return _f(d) * (normal_cdf(X) + X * normal_pdf(X))
 
 
+# Reading: the op's optional tanh form (Hendrycks & Gimpel's approximation
+# of x*Phi(x)), g(x) = x (1 + tanh u)/2 with u = sqrt(2/pi) (x + 0.044715 x^3),
+# and its derivative by the product and chain rules.
+_GELU_K = math.sqrt(2.0 / math.pi)
+
+
+def gelu_tanh(x):
+    X = _f(x)
+    return 0.5 * X * (1.0 + np.tanh(_GELU_K * (X + 0.044715 * X ** 3)))
+
+
+def gelu_tanh_bwd(d, x):
+    X = _f(x)
+    t = np.tanh(_GELU_K * (X + 0.044715 * X ** 3))
+    du = _GELU_K * (1.0 + 3.0 * 0.044715 * X * X)
+    return _f(d) * (0.5 * (1.0 + t) + 0.5 * X * (1.0 - t * t) * du)
+
+
 # --------------------------------------------------------------------------
 # rope -- [AE] op-backward table row "rope" and "RoPE 反向推导": each pair is
 # rotated by the 2x2 rotation R(theta); R is orthogonal, so the backward

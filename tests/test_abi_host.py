@@ -75,6 +75,10 @@ def test_validation_rejects_without_launch():
     with pytest.raises(xt.XtError) as e:
         xt.xt_op_fwd(xt.OP.SILU, xt.params(), [host_view(2, 4, xt.DT.I32)], [host_view(2, 4)], stream=C.c_void_p(0))
     assert e.value.status == 3
+    # GELU form flag outside {0, 1}
+    with pytest.raises(xt.XtError) as e:
+        xt.xt_op_fwd(xt.OP.GELU, xt.params(gelu_tanh=2), [x], [host_view(2, 4)], stream=C.c_void_p(0))
+    assert e.value.status == 1 and "gelu_tanh" in str(e.value)
     # wrong tensor counts
     with pytest.raises(xt.XtError) as e:
         xt.xt_op_fwd(xt.OP.RMS_NORM, xt.params(), [x], [host_view(2, 4)], stream=C.c_void_p(0))

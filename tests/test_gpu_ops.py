@@ -182,16 +182,18 @@ def test_cross_entropy_bad_targets_give_nan_rows():
 # ------------------------------------------------------ silu / gelu / swiglu
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("R,C,ld", [(8, 64, None), (37, 1001, None), (37, 1001, 1008), (64, 688, None)])
-@pytest.mark.parametrize("name", ["silu", "gelu"])
+@pytest.mark.parametrize("name", ["silu", "gelu", "gelu_tanh"])
 def test_silu_gelu(dtype, R, C, ld, name):
     op = xt.OP.SILU if name == "silu" else xt.OP.GELU
-    f, fb = (ops.silu, ops.silu_bwd) if name == "silu" else (ops.gelu, ops.gelu_bwd)
+    f, fb = {"silu": (ops.silu, ops.silu_bwd), "gelu": (ops.gelu, ops.gelu_bwd),
+             "gelu_tanh": (ops.gelu_tanh, ops.gelu_tanh_bwd)}[name]
+    prm = xt.params(gelu_tanh=int(name == "gelu_tanh"))
     x, xv = put(normal((R, C), 5, "x", std=3.0), dtype, ld)
     d, dv = put(normal((R, C), 5, "dout"), dtype, ld)
     y, dx = out_like(R, C, dtype, ld), out_like(R, C, dtype, ld)
-    fwd(op, xt.params(), [x], [y])
+    fwd(op, prm, [x], [y])
     close(host(y), f(xv), dtype, what="y")
-    bwd(op, xt.params(), d, [x], [], [dx])
+    bwd(op, prm, d, [x], [], [dx])
     close(host(dx), fb(dv, xv), dtype, what="dx")
 
 

@@ -213,6 +213,27 @@ def test_silu_gelu_values():
     np.testing.assert_allclose(ops.normal_pdf(xs), norm.pdf(xs), rtol=1e-13)
 
 
+def test_gelu_tanh_form():
+    """The tanh form is an approximation of x*Phi(x): it must stay within
+    5e-4 of the exact GELU everywhere (its largest gap, near |x| = 2.7, is
+    4.7e-4; a dropped cubic term gives 3.4e-2, a cubic coefficient off by
+    ten percent about 3e-3), match its slope and curvature at 0 (which
+    fixes the sqrt(2/pi) factor), and g(x) - g(-x) = x holds exactly for
+    any odd inner function."""
+    xs = np.linspace(-12.0, 12.0, 240001)
+    assert np.max(np.abs(ops.gelu_tanh(xs) - ops.gelu(xs))) < 5e-4
+    np.testing.assert_allclose(ops.gelu_tanh(xs) - ops.gelu_tanh(-xs), xs, rtol=0, atol=1e-14)
+    assert ops.gelu_tanh([0.0])[0] == 0.0 and ops.gelu_tanh_bwd([1.0], [0.0])[0] == 0.5
+    # second derivative at 0 equals the exact GELU's, 2 phi(0) = sqrt(2/pi)
+    h = 1e-4
+    curv = (ops.gelu_tanh_bwd([1.0], [h])[0] - ops.gelu_tanh_bwd([1.0], [-h])[0]) / (2 * h)
+    assert abs(curv - math.sqrt(2.0 / math.pi)) < 1e-7
+    # tails: x for large positive x, 0 for large negative x
+    assert ops.gelu_tanh([30.0])[0] == 30.0 and abs(ops.gelu_tanh([-30.0])[0]) < 1e-300
+    x, W = rnd(4, 7, scale=2.5), rnd(4, 7)
+    check_fd(ops.gelu_tanh, [ops.gelu_tanh_bwd(W, x)], [x], W)
+
+
 def test_silu_swiglu_gelu_fd():
     x, g, u, W = rnd(3, 5, scale=2.0), rnd(3, 5, scale=2.0), rnd(3, 5), rnd(3, 5)
     check_fd(ops.silu, [ops.silu_bwd(W, x)], [x], W)
