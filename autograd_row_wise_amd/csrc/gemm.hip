@@ -217,24 +217,22 @@ __global__ __launch_bounds__(NT) void gemm_k(
 }
 
 // ==========================================================================
-// Large-tile kernel for aligned problems (every tile full, K a multiple of
-// BK, 16-byte aligned operands).
-//
-//   bf16: 256 x 256 block tile, BK = 64, 4 waves (2 x 2) of 128 x 128, each
-//         wave 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16.
-//   f32 : 128 x 128 block tile, BK = 32, 4 waves of 64 x 64, 2 x 2
-//         accumulators of v_mfma_f32_32x32x2_f32.
+// Large-tile kernel for aligned f32 problems (every tile full, K a multiple
+// of BK, 16-byte aligned operands): 128 x 128 block tile, BK = 32, 4 waves
+// of 64 x 64, 2 x 2 accumulators of v_mfma_f32_32x32x2_f32.
 //
 // Both operands sit in LDS as [row][k] (k contiguous) rows of 128 bytes =
 // eight 16-byte chunks, XOR-swizzled (swz below) so that the lanes of an
 // MFMA fragment read (32 consecutive rows, one chunk) spread over all banks
-// without padding.  Operands stored transposed in
-// HBM ([K][rows]) are read as 8 x 8 (bf16) or 4 x 4 (f32) blocks with
-// 16-byte loads and transposed in registers (v_perm_b32 for bf16) before
-// the 16-byte LDS stores.  The next K tile is fetched into registers while
-// the current one is multiplied.  Tiles are ordered so that each of the 8
-// XCDs (blocks are dealt to XCDs round-robin) owns whole rows of tiles and
-// reuses their A panels in its own L2.
+// without padding.  Operands stored transposed in HBM ([K][rows]) are read
+// as 4 x 4 blocks with 16-byte loads and transposed in registers before the
+// 16-byte LDS stores.  The next K tile is fetched into registers while the
+// current one is multiplied.  Tiles are ordered so that each of the 8 XCDs
+// (blocks are dealt to XCDs round-robin) owns whole rows of tiles and reuses
+// their A panels in its own L2.
+//
+// big<bf16_t> holds the alignment rule of the bf16 large-tile kernel further
+// below (256 x 256 tiles; K, and every split-K slice, a multiple of 64).
 // ==========================================================================
 template <typename TA> struct big;
 template <> struct big<bf16_t> { static constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4; };
@@ -247,21 +245,6 @@ template <> struct big<float> { static constexpr int BM = 128, BN = 128, BK = 32
 // groups (two rows share a 256-byte bank row; the XOR term differs between
 // rows of equal parity).
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
-
-// 8 x 8 bf16 transpose: in[k] holds m = 0..7 of row k; out[m] holds k = 0..7.
-__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&out)[8]) {
-  const uint32_t* w[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) w[k] = reinterpret_cast<const uint32_t*>(&in[k]);
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(w[2 * j + 1][m >> 1], w[2 * j][m >> 1], sel);
-    out[m] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
 
 // One thread's share of a BM x BK operand tile, staged in registers.
 template <typename TA, int ROWS, bool KCONTIG>
@@ -300,18 +283,15 @@ struct BigLoader {
     } else {
       constexpr int KB = BK / V;
       const int kb = threadIdx.x % KB, mb = threadIdx.x / KB;
+      static_assert(V == 4, "register transpose is written for 4 x 4 f32 blocks");
       uint4 t[V];
-      if constexpr (V == 8) {
-        transpose8x8_bf16(reinterpret_cast<const uint4(&)[8]>(r), reinterpret_cast<uint4(&)[8]>(t));
-      } else {
-        // 4 x 4 f32: r[k] = (m0..m3) of k row; t[m] = (k0..k3)
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
+      // 4 x 4 f32: r[k] = (m0..m3) of k row; t[m] = (k0..k3)
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) t[m] = make_uint4(w0[m], w1[m], w2[m], w3[m]);
-      }
+      for (int m = 0; m < 4; ++m) t[m] = make_uint4(w0[m], w1[m], w2[m], w3[m]);
 #pragma unroll
       for (int j = 0; j < V; ++j) L[swz(mb * V + j, kb)] = t[j];
     }
@@ -445,254 +425,196 @@ __global__ __launch_bounds__(NT) void gemm_big_k(
 }
 
 // ==========================================================================
-// bf16 large-tile kernel with eight waves.  A 512-thread block computes a
-// 256 x 256 tile of C with BK = 64.  The waves form 2 (m) x 4 (n), each
-// owning 128 x 64 of C = 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16
-// (128 AGPRs), so two waves share each SIMD and one wave's LDS reads and
-// waits overlap the other's MFMAs.  LDS holds two K tiles (2 x 64 KB): the
-// next tile is written while the current one is multiplied, with one
-// barrier per K tile.  Waves 0-3 fetch the A tile and waves 4-7 the B tile,
-// eight 16-byte chunks per thread, issued two K tiles ahead of their use
-// (two register sets).  LDS layout and swizzle as in the kernel above.
+// bf16 large-tile kernel.  A 512-thread block (8 waves, 2 per SIMD) computes
+// a 256 x 256 tile of C; the waves form 2 (m) x 4 (n), each owning 128 x 64
+// of C = 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16, so one wave's LDS
+// reads and waits overlap the other's MFMAs on the same SIMD.
+//
+// Operands reach LDS without staging registers: each lane issues
+// global_load_lds_dwordx4, which writes its 16 bytes straight into LDS at
+// the wave's destination + 16 * lane.  An operand stored k-contiguous lands
+// as [row][k]; one stored transposed lands as [k][row] and is turned into
+// MFMA fragments by the transposing LDS read (ds_read_b64_tr_b16), so all
+// four layouts (d B^T, A^T d, ...) share the kernel and no transpose copy
+// exists.  K tiles are 32 deep in a ring of four 32 KB stages.  Step kt
+// multiplies tile kt while tile kt+3 is requested, and reads the first
+// fragments of tile kt+1 before its closing barrier, so MFMAs restart right
+// after it; tile kt+2 must have landed by then.
+//
+// Tile order: blocks are dealt to the 8 XCDs round-robin; XCD x takes the
+// contiguous tile range x * tiles / 8 .., walked in groups of four tile rows
+// (tile_of), so the 32 tiles an XCD runs at once form a 4 x 8 patch whose A
+// and B panels its L2 shares.
 // ==========================================================================
 namespace b8 {
-constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
-constexpr int TILE = BM * BK;                   // elements of one operand tile
+constexpr int BM = 256, BN = 256, NT = 512;
 }  // namespace b8
 
-template <bool KCONTIG>
-__device__ __forceinline__ void b8_load(u32x4_t (&r)[8], const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
-                                        int t) {
-  if constexpr (KCONTIG) {
-    // rows t/8 + 32 i, k chunk t % 8: eight lanes cover one 128-byte row run
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = t / 8 + i * 32, c = t % 8;
-      r[i] = *reinterpret_cast<const u32x4_t*>(g + (row0 + row) * ld + k0 + c * 8);
-    }
-  } else {
-    // one 8 (k) x 8 (rows) block per thread: k rows 8 kb.., rows 8 mb..;
-    // kb = t % 8 so that the eight lanes of an LDS store phase write eight
-    // different swizzled chunk columns (no bank conflicts); each load still
-    // reads 128 contiguous bytes per group of eight lanes
-    const int kb = t % 8, mb = t / 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(g + (k0 + kb * 8 + i) * ld + row0 + mb * 8);
-  }
+// Tile tt (in an XCD's range) -> (m0, n0): groups of GM tile rows, column by
+// column within a group.
+__device__ __forceinline__ void tile_of(int tt, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0, int bm, int bn) {
+  const int GM = 4, span = GM * tiles_n, first = (tt / span) * GM;
+  const int gm = tiles_m - first < GM ? tiles_m - first : GM, r = tt % span;
+  m0 = (int64_t)(first + r % gm) * bm; n0 = (int64_t)(r / gm) * bn;
 }
 
-template <bool KCONTIG>
-__device__ __forceinline__ void b8_store(const u32x4_t (&r)[8], u32x4_t* L, int t) {
-  if constexpr (KCONTIG) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) L[swz(t / 8 + i * 32, t % 8)] = r[i];
-  } else {
-    // Transposed in registers: row m of the block is, per pair of k rows,
-    // the m-th bf16 of each (v_perm_b32 picks the low or high halves).
-    // Lanes with odd mb emit their rows in the order j ^ 1 (only the perm
-    // selector changes), so the two groups of eight lanes in a sixteen-lane
-    // LDS phase write rows of opposite parity: opposite halves of the
-    // 256-byte bank row, no conflicts.
-    const int kb = t % 8, mb = t / 8, flip = mb & 1;
-    const uint32_t lo = 0x05040100u, hi = 0x07060302u;
-    const uint32_t sel_even = flip ? hi : lo, sel_odd = flip ? lo : hi;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? sel_odd : sel_even;
-      u32x4_t o;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(r[2 * w + 1][j >> 1], r[2 * w][j >> 1], sel);
-      L[swz(mb * 8 + (j ^ flip), kb)] = o;
-    }
-  }
-}
-
-template <bool TRANS_A, bool TRANS_B>
-__device__ __forceinline__ void b8_fetch(u32x4_t (&r)[8], bool fetchA, const bf16_t* A, int64_t lda, int64_t m0,
-                                         const bf16_t* B, int64_t ldb, int64_t n0, int64_t k0, int t) {
-  if constexpr (!TRANS_A == TRANS_B) {            // both tiles in one layout: one code path
-    b8_load<TRANS_B>(r, fetchA ? A : B, fetchA ? lda : ldb, fetchA ? m0 : n0, k0, t);
-  } else {
-    if (fetchA) b8_load<!TRANS_A>(r, A, lda, m0, k0, t);
-    else b8_load<TRANS_B>(r, B, ldb, n0, k0, t);
-  }
-}
-
-template <bool TRANS_A, bool TRANS_B>
-__device__ __forceinline__ void b8_put(const u32x4_t (&r)[8], bool fetchA, u32x4_t* L, int t) {
-  if constexpr (!TRANS_A == TRANS_B) {
-    b8_store<TRANS_B>(r, fetchA ? L : L + b8::TILE / 8, t);
-  } else {
-    if (fetchA) b8_store<!TRANS_A>(r, L, t);
-    else b8_store<TRANS_B>(r, L + b8::TILE / 8, t);
-  }
-}
-
-// One K tile of a wave's 128 x 64 block: four k steps of 16, each 4 A and
-// 2 B fragments (one 16-byte LDS read per lane each) and 8 MFMAs.
-__device__ __forceinline__ void b8_mma(const u32x4_t* LA, f32x16_t (&acc)[4][2], int wm, int wn, int lr, int lh) {
-  const u32x4_t* LB = LA + b8::TILE / 8;
-#pragma unroll
-  for (int s = 0; s < b8::BK / 16; ++s) {
-    bf16x8_t a[4], b[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8_t, LA[swz(wm + i * 32 + lr, 2 * s + lh)]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(bf16x8_t, LB[swz(wn + j * 32 + lr, 2 * s + lh)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-template <typename TC, bool TRANS_A, bool TRANS_B>
-__global__ __launch_bounds__(b8::NT) void gemm_b8_k(
-    const bf16_t* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
-    const bf16_t* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
-    TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
-    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
-    int64_t kchunk, int64_t nbatch, int64_t scs) {
-  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = b8::BK, TILE = b8::TILE;
-  __shared__ __align__(16) bf16_t lds[2][2 * TILE];      // [stage][A tile, B tile]
-
-  const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
-  const int64_t kb0 = split * kchunk;
-  A += b0 * sa0 + b1 * sa1 + (TRANS_A ? kb0 * lda : kb0);
-  B += b0 * sb0 + b1 * sb1 + (TRANS_B ? kb0 : kb0 * ldb);
-  C += b0 * sc0 + b1 * sc1 + split * scs;
-  K = K - kb0 < kchunk ? K - kb0 : kchunk;
-
-  const int tiles_n = (int)(N / BN8);
-  const int tiles = (int)(M / BM8) * tiles_n;
-  const int g = blockIdx.x;
-  const int tt = (tiles % 8 == 0) ? (g % 8) * (tiles / 8) + g / 8 : g;
-  const int64_t m0 = (int64_t)(tt / tiles_n) * BM8, n0 = (int64_t)(tt % tiles_n) * BN8;
-
-  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
-  const bool fetchA = w < 4;                     // wave-uniform role
-  const int t = threadIdx.x % 256;
-  const int wm = (w / 4) * 128, wn = (w % 4) * 64;
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  const int nk = (int)(K / BK);
-  const int lr = l % 32, lh = l / 32;
-  u32x4_t r0[8];
-  b8_fetch<TRANS_A, TRANS_B>(r0, fetchA, A, lda, m0, B, ldb, n0, 0, t);
-  b8_put<TRANS_A, TRANS_B>(r0, fetchA, reinterpret_cast<u32x4_t*>(lds[0]), t);
-  if (nk > 1) b8_fetch<TRANS_A, TRANS_B>(r0, fetchA, A, lda, m0, B, ldb, n0, BK, t);
-  __syncthreads();
-  // K tile kt: multiply stage kt&1 while tile kt+1 is in flight; then write
-  // it into the other stage and fetch tile kt+2.
-  for (int kt = 0; kt < nk; ++kt) {
-    b8_mma(reinterpret_cast<const u32x4_t*>(lds[kt & 1]), acc, wm, wn, lr, lh);
-    if (kt + 1 < nk) {
-      b8_put<TRANS_A, TRANS_B>(r0, fetchA, reinterpret_cast<u32x4_t*>(lds[(kt + 1) & 1]), t);
-      if (kt + 2 < nk) b8_fetch<TRANS_A, TRANS_B>(r0, fetchA, A, lda, m0, B, ldb, n0, (int64_t)(kt + 2) * BK, t);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm + i * 32 + 8 * (q / 4) + 4 * (l / 32) + (q % 4);
-        const int64_t col = n0 + wn + j * 32 + (l % 32);
-        TC* p = C + row * ldc + col;
-        float v = alpha * acc[i][j][q];
-        if (acc_c) v = acc_add(io<TC>::ld(p), v);
-        io<TC>::st(p, v);
-      }
-}
-
-// --------------------------------------------------------------------------
-// bf16 NT products (both operands stored k-contiguous: dA = d B^T, and every
-// product whose second operand is read transposed) skip the register
-// staging: each lane issues global_load_lds_dwordx4, which writes its 16
-// bytes straight into LDS at the wave's destination + 16 * lane.  K tiles
-// are 32 deep (LDS rows of 64 bytes, four 16-byte chunks, chunk c of row r
-// at c ^ ((r >> 2) & 3): sixteen consecutive rows read at one chunk hit
-// sixteen distinct 16-byte bank groups), held in a ring of four LDS stages
-// (4 x 32 KB): tile kt+3 is requested while tile kt is multiplied, and each
-// wave waits only until its transfers of tile kt+1 have landed (the two
-// newer tiles stay in flight) before the barrier that publishes them.
-// --------------------------------------------------------------------------
 namespace b8d {
-constexpr int BK = 32, STAGES = 4;
+constexpr int BK = 32, NS = 4;
 constexpr int TILE = 256 * BK;                       // elements of one operand tile
 }  // namespace b8d
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
 __device__ __forceinline__ int swz4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
 
-// Four DMA instructions per wave per tile: operand rows row0.., k0.., both
-// 256 x 32; instruction j of wave w fills slots 64 blk .. 64 blk + 63.
+// One operand tile (256 rows x 32 k) into LDS: two 1 KB transfers per wave.
+// k-contiguous operands land as [row][k] (64-byte rows, chunk c of row r at
+// c ^ ((r >> 2) & 3)); the others as [k][row] (512-byte k-rows, chunk c of
+// k-row kr at c ^ 4 (kr & 3)).
+template <bool KCONTIG>
 __device__ __forceinline__ void b8d_dma_tile(const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
                                              bf16_t* __restrict__ lds_tile, int w, int l) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int blk = w * 2 + j;                       // 64 slots = rows 16 blk .. 16 blk + 15
-    const int row = blk * 16 + l / 4;
-    const int c = (l % 4) ^ ((row >> 2) & 3);
-    __builtin_amdgcn_global_load_lds(g + (row0 + row) * ld + k0 + c * 8, lds_tile + blk * 64 * 8, 16, 0, 0);
+    const int blk = w * 2 + j;                       // LDS slots 64 blk .. 64 blk + 63
+    const bf16_t* src;
+    if constexpr (KCONTIG) {                         // rows 16 blk .. +15, 4 chunks each
+      const int row = blk * 16 + l / 4;
+      const int c = (l % 4) ^ ((row >> 2) & 3);
+      src = g + (row0 + row) * ld + k0 + c * 8;
+    } else {                                         // k-rows 2 blk, 2 blk + 1, 32 chunks each
+      const int kr = blk * 2 + l / 32;
+      const int c = (l % 32) ^ (4 * (kr & 3));
+      src = g + (k0 + kr) * ld + row0 + c * 8;
+    }
+    __builtin_amdgcn_global_load_lds(src, lds_tile + blk * 64 * 8, 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void b8d_mma(const u32x4_t* LA, f32x16_t (&acc)[4][2], int wm, int wn, int lr, int lh) {
-  const u32x4_t* LB = LA + b8d::TILE / 8;
+// MFMA operand of fragment rows f0 .. f0+31, k 16 s .. 16 s + 15 (lane l:
+// row f0 + l % 32, k 16 s + 8 (l / 32) .. +7).  From a [k][row] tile it takes
+// two transposing reads (ds_read_b64_tr_b16: within each group of 16 lanes,
+// lane j receives element j % 4 of the 8-byte rows that lanes 4 v + j / 4
+// address, v = 0..3).
+template <bool KCONTIG>
+__device__ __forceinline__ bf16x8_t b8d_frag(const bf16_t* __restrict__ tile, int f0, int s, int l) {
+  if constexpr (KCONTIG) {
+    const u32x4_t* L = reinterpret_cast<const u32x4_t*>(tile);
+    return __builtin_bit_cast(bf16x8_t, L[swz4(f0 + l % 32, 2 * s + l / 32)]);
+  } else {
+    const int g = l / 16, q = l % 16;                // source role of this lane within its group
+    const int row = f0 + 16 * (g & 1) + 4 * (q & 3); // 4 consecutive rows from here
+    const int c = row / 8, half = (row / 4) & 1;
+    s16x4_t v[2];
 #pragma unroll
-  for (int s = 0; s < b8d::BK / 16; ++s) {
-    bf16x8_t a[4], b[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8_t, LA[swz4(wm + i * 32 + lr, 2 * s + lh)]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(bf16x8_t, LB[swz4(wn + j * 32 + lr, 2 * s + lh)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      const int kr = 16 * s + 8 * (g >> 1) + 4 * h + q / 4;
+      const bf16_t* p = tile + kr * 256 + ((c ^ (4 * (kr & 3))) * 8) + half * 4;
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+    }
+    const short __attribute__((ext_vector_type(8))) w8 = {v[0][0], v[0][1], v[0][2], v[0][3],
+                                                          v[1][0], v[1][1], v[1][2], v[1][3]};
+    return __builtin_bit_cast(bf16x8_t, w8);
   }
 }
 
-// One K tile: request tile kt+3 into `nxt`, multiply out of `cur`; restrict
-// pointers let the compiler see that the reads of `cur` do not depend on the
-// transfers into `nxt`.
-__device__ __forceinline__ void b8d_step(const bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt, bool more,
-                                         const bf16_t* A, int64_t lda, int64_t m0, const bf16_t* B, int64_t ldb,
-                                         int64_t n0, int64_t k0, f32x16_t (&acc)[4][2], int w, int l, int wm,
-                                         int wn, int lr, int lh) {
-  if (more) {
-    b8d_dma_tile(A, lda, m0, k0, nxt, w, l);
-    b8d_dma_tile(B, ldb, n0, k0, nxt + b8d::TILE, w, l);
-  }
-  b8d_mma(reinterpret_cast<const u32x4_t*>(cur), acc, wm, wn, lr, lh);
+struct b8d_frags { bf16x8_t a[4], b[2]; };
+
+// Fragments of k substep s of the stage at `st` ([A tile, B tile]).
+template <bool KA, bool KB>
+__device__ __forceinline__ void b8d_read(const bf16_t* __restrict__ st, int s, b8d_frags& f, int wm, int wn, int l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = b8d_frag<KA>(st, wm + i * 32, s, l);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f.b[j] = b8d_frag<KB>(st + b8d::TILE, wn + j * 32, s, l);
 }
 
-template <typename TC>
+__device__ __forceinline__ void b8d_mfma(const b8d_frags& f, f32x16_t (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Issue order for one substep: its 8 MFMAs with the NR LDS reads of the
+// next substep's fragments spread between them.
+template <int NR>
+__device__ __forceinline__ void b8d_sched_half() {
+  if constexpr (NR == 6) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  } else if constexpr (NR == 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  } else if constexpr (NR == 10) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
+// One K tile kt: multiply substep 0 (fragments already in f0) while substep
+// 1 of tile kt is read from `cur`; request tile kt+NS-1 into `dst`; multiply
+// substep 1 while substep 0 of tile kt+1 is read from `ahead`.  Three
+// restrict pointers: the compiler sees that neither read depends on the
+// transfer, and inserts no wait for it.
+template <bool KA, bool KB>
+__device__ __forceinline__ void b8d_step(const bf16_t* __restrict__ cur, const bf16_t* __restrict__ ahead,
+                                         bf16_t* __restrict__ dst, const bf16_t* A, int64_t lda, int64_t m0,
+                                         const bf16_t* B, int64_t ldb, int64_t n0, int64_t k0, b8d_frags& f0,
+                                         b8d_frags& f1, f32x16_t (&acc)[4][2], int w, int l, int wm, int wn) {
+  b8d_frags f2;
+  b8d_read<KA, KB>(cur, 1, f1, wm, wn, l);
+  b8d_mfma(f0, acc);
+  b8d_dma_tile<KA>(A, lda, m0, k0, dst, w, l);
+  b8d_dma_tile<KB>(B, ldb, n0, k0, dst + b8d::TILE, w, l);
+  b8d_read<KA, KB>(ahead, 0, f2, wm, wn, l);
+  b8d_mfma(f1, acc);
+  f0 = f2;
+  constexpr int NR = (KA ? 4 : 8) + (KB ? 2 : 4);
+  b8d_sched_half<NR>();
+  __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+  b8d_sched_half<NR>();
+}
+
+// bf16 products of 256 x 256 tiles, 8 waves (2 per SIMD, 2 (m) x 4 (n), 128 x
+// 64 each as 4 x 2 MFMA 32x32x16 accumulators).  Operands reach LDS through
+// global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
+// destination + 16 lane, with no staging registers and no ds_write.  K tiles
+// are 32 deep in a ring of NS = 4 stages of 32 KB; tile kt+3 is requested in
+// the middle of step kt and must have landed by the end of step kt+1.
+template <typename TC, bool KA, bool KB>
 __global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
     const bf16_t* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
     const bf16_t* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
     TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
     int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
     int64_t kchunk, int64_t nbatch, int64_t scs) {
-  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = b8d::BK, TILE = b8d::TILE, NS = b8d::STAGES;
+  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = b8d::BK, TILE = b8d::TILE, NS = b8d::NS;
   __shared__ __align__(16) bf16_t lds[NS][2 * TILE];       // [stage][A tile, B tile]
 
   const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
   const int64_t kb0 = split * kchunk;
-  A += b0 * sa0 + b1 * sa1 + kb0;                            // A [M][K], B [N][K]
-  B += b0 * sb0 + b1 * sb1 + kb0;
+  A += b0 * sa0 + b1 * sa1 + (KA ? kb0 : kb0 * lda);
+  B += b0 * sb0 + b1 * sb1 + (KB ? kb0 : kb0 * ldb);
   C += b0 * sc0 + b1 * sc1 + split * scs;
   K = K - kb0 < kchunk ? K - kb0 : kchunk;
 
@@ -700,11 +622,11 @@ __global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
   const int tiles = (int)(M / BM8) * tiles_n;
   const int g = blockIdx.x;
   const int tt = (tiles % 8 == 0) ? (g % 8) * (tiles / 8) + g / 8 : g;
-  const int64_t m0 = (int64_t)(tt / tiles_n) * BM8, n0 = (int64_t)(tt % tiles_n) * BN8;
+  int64_t m0, n0;
+  tile_of(tt, (int)(M / BM8), tiles_n, m0, n0, BM8, BN8);
 
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   const int wm = (w / 4) * 128, wn = (w % 4) * 64;
-  const int lr = l % 32, lh = l / 32;
   f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -714,30 +636,36 @@ __global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   const int nk = (int)(K / BK);
-  // prologue: tiles 0, 1, 2 requested; tile 0 landed and published
+  // prologue: tiles 0 .. NS-2 requested and landed, substep 0 of tile 0 read
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < nk) {
-      b8d_dma_tile(A, lda, m0, (int64_t)p * BK, lds[p], w, l);
-      b8d_dma_tile(B, ldb, n0, (int64_t)p * BK, lds[p] + TILE, w, l);
+      b8d_dma_tile<KA>(A, lda, m0, (int64_t)p * BK, lds[p], w, l);
+      b8d_dma_tile<KB>(B, ldb, n0, (int64_t)p * BK, lds[p] + TILE, w, l);
     }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  b8d_frags f0, f1;
+  b8d_read<KA, KB>(lds[0], 0, f0, wm, wn, l);
   for (int kt = 0; kt < nk; ++kt) {
-    b8d_step(lds[kt % NS], lds[(kt + NS - 1) % NS], kt + NS - 1 < nk, A, lda, m0, B, ldb, n0,
-             (int64_t)(kt + NS - 1) * BK, acc, w, l, wm, wn, lr, lh);
-    // Tile kt+1 must have landed: its 4 transfers are older than the (up
-    // to) 8 of tiles kt+2 and kt+3, so vmcnt <= 8 suffices; lgkmcnt 0 makes
-    // this wave's reads of stage kt complete before anyone may overwrite it
-    // (the next step requests tile kt+4 into that stage).  Then a bare
-    // s_barrier publishes tile kt+1: a full __syncthreads() fence would
-    // wait for every transfer in flight.  The empty asm statements keep the
-    // compiler from moving LDS accesses across the barrier.
-    __builtin_amdgcn_s_waitcnt(0x078);              // vmcnt(8) expcnt(7) lgkmcnt(0)
+    // past the last tile the transfers re-read the last tile into a stage
+    // that is never read again, so every step issues the same four
+    const int kn = kt + NS - 1 < nk ? kt + NS - 1 : nk - 1;
+    b8d_step<KA, KB>(lds[kt % NS], lds[(kt + 1) % NS], lds[(kt + NS - 1) % NS], A, lda, m0, B, ldb, n0,
+                     (int64_t)kn * BK, f0, f1, acc, w, l, wm, wn);
+    // Tile kt+2 must have landed before the barrier publishes it (the next
+    // step reads its substep 0 ahead); only the four transfers of the one
+    // newer tile (kt+3) may stay in flight: vmcnt(4).  lgkmcnt(0): this
+    // wave's reads of stage kt are complete before anyone refills it.  A
+    // bare s_barrier: a __syncthreads() fence would wait for every transfer
+    // in flight.  The empty asm statements keep the compiler from moving
+    // LDS accesses across it.
+    __builtin_amdgcn_s_waitcnt(0x074);                       // vmcnt(4) expcnt(7) lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+  __builtin_amdgcn_s_waitcnt(0);                             // the re-read transfers have landed
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -861,17 +789,15 @@ hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, 
     dim3 grid((unsigned)((M / b8::BM) * (N / b8::BN)), 1, (unsigned)(S * nbatch));
     const bf16_t* a8 = (const bf16_t*)A.data;
     const bf16_t* b8p = (const bf16_t*)B.data;
-    if (!ta && tb) {
-      gemm_b8dma_k<TC><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0], B.sb[1], c, ldc, sc0,
-                                               sc1, M, N, K, nb1, alpha, acc ? 1 : 0, kchunk, nbatch, scs);
-      return hipGetLastError();
-    }
-#define XT_B8(TA_, TB_)                                                                                   gemm_b8_k<TC, TA_, TB_><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0],                                                      B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1, alpha,                                                      acc ? 1 : 0, kchunk, nbatch, scs)
-    if (!ta && !tb) XT_B8(false, false);
-    else if (!ta && tb) XT_B8(false, true);
-    else if (ta && !tb) XT_B8(true, false);
-    else XT_B8(true, true);
-#undef XT_B8
+#define XT_B8D(KA_, KB_)                                                                                   \
+    gemm_b8dma_k<TC, KA_, KB_><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0], B.sb[1], c, \
+                                                       ldc, sc0, sc1, M, N, K, nb1, alpha, acc ? 1 : 0, kchunk,  \
+                                                       nbatch, scs)
+    if (!ta && tb) XT_B8D(true, true);
+    else if (ta && !tb) XT_B8D(false, false);
+    else if (!ta && !tb) XT_B8D(true, false);
+    else XT_B8D(false, true);
+#undef XT_B8D
     return hipGetLastError();
    }
   } else if (bigk) {
