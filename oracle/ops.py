@@ -317,3 +317,42 @@ def rope_bwd(d, head_dim: int, base: float, seq_len: int, positions=None):
 # --------------------------------------------------------------------------
 def grad_accumulate(dst, src):
     return _f(dst) + _f(src)
+
+
+# --------------------------------------------------------------------------
+# Gradient buffers after the backward -- [BP] kernel-pair table (the helper
+# kernels k_grad_norm_partial, k_grad_norm_final and k_grad_scale, named for
+# gradient clipping) and "Ackumulation över mikrobatcher" (scale_grads(1/n)
+# averages the microbatch sum, zero_grads() clears the buffers).
+# Readings (the pages name the kernels only):
+#   * the norm is the global L2 norm over every element of every gradient
+#     tensor, sqrt(sum g^2);
+#   * clipping follows Pascanu, Mikolov & Bengio, "On the difficulty of
+#     training recurrent neural networks" (2013), section 3.2: when the norm
+#     exceeds the threshold, every gradient is multiplied by threshold/norm;
+#     otherwise (or with no threshold, max_norm <= 0) the factor is 1;
+#   * a scaled element is the f32 product of the stored value and the f32
+#     factor, rounded once into the storage type (for bf16: the f32 product
+#     rounded to bf16).
+# --------------------------------------------------------------------------
+def grad_norm(grads):
+    """sqrt of the sum of squares of every element of every tensor in the
+    list (an empty list has norm 0)."""
+    total = 0.0
+    for g in grads:
+        G = _f(g)
+        total += float(np.sum(G * G))
+    return math.sqrt(total)
+
+
+def clip_coefficient(norm: float, max_norm: float) -> float:
+    if max_norm > 0 and norm > max_norm:
+        return max_norm / norm
+    return 1.0
+
+
+def scale_grad(g, factor: float, dtype: str = "f32"):
+    """One gradient tensor times ``factor`` (an f32 value), as stored."""
+    from .numerics import round_bf16, round_f32
+    prod = _f(g) * float(np.float32(factor))
+    return round_bf16(prod) if dtype == "bf16" else round_f32(prod)

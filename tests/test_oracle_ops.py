@@ -295,3 +295,48 @@ def test_grad_accumulate_and_bf16_rounding():
     np.testing.assert_array_equal(round_bf16([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9]),
                                   [1.0, 1.0 + 2 ** -6, 1.0])
     np.testing.assert_array_equal(bf16_to_f64(np.array([0x3F80, 0xC000], dtype=np.uint16)), [1.0, -2.0])
+
+
+# ------------------------------------------------------- gradient buffers
+def test_grad_norm_closed_forms():
+    # 3-4-5 across two tensors; 100 ones in four tensors -> 10
+    assert ops.grad_norm([np.array([[3.0]]), np.array([[4.0]])]) == 5.0
+    assert ops.grad_norm([np.ones((5, 5)) for _ in range(4)]) == 10.0
+    assert ops.grad_norm([]) == 0.0
+    assert ops.grad_norm([np.zeros((0, 7)), np.array([[0.0, -2.0]])]) == 2.0
+
+
+def test_grad_norm_against_library_norm_and_scaling():
+    gs = [rnd(3, 5), rnd(1, 17, scale=3.0), rnd(40, 2)]
+    flat = np.concatenate([g.ravel() for g in gs])
+    n = ops.grad_norm(gs)
+    assert abs(n - np.linalg.norm(flat)) <= 1e-13 * n
+    # power-of-two scaling is exact
+    assert ops.grad_norm([2.0 * g for g in gs]) == 2.0 * n
+
+
+def test_clip_coefficient_rule():
+    assert ops.clip_coefficient(5.0, 1.0) == 0.2
+    assert ops.clip_coefficient(0.5, 1.0) == 1.0
+    assert ops.clip_coefficient(1.0, 1.0) == 1.0      # not above the threshold
+    assert ops.clip_coefficient(5.0, 0.0) == 1.0      # no threshold
+    # after clipping, the global norm is the threshold
+    gs = [rnd(4, 6, scale=5.0), rnd(2, 3, scale=5.0)]
+    c = ops.clip_coefficient(ops.grad_norm(gs), 1.5)
+    assert c < 1.0 and abs(ops.grad_norm([c * g for g in gs]) - 1.5) < 1e-12
+
+
+def test_scale_grad_rounding():
+    x = rnd(6, 9, scale=4.0).astype(np.float32).astype(np.float64)
+    assert np.array_equal(ops.scale_grad(x, 1.0), x)
+    assert np.array_equal(ops.scale_grad(x, 2.0), 2.0 * x)
+    assert np.array_equal(ops.scale_grad(x, 0.0), 0.0 * x)
+    # f32: the correctly rounded f32 product
+    f = np.float32(0.1)
+    assert np.array_equal(ops.scale_grad(x, f), (x.astype(np.float32) * f).astype(np.float64))
+    # bf16 storage: values stay on the bf16 grid; a power of two keeps them exact
+    from oracle.numerics import round_bf16
+    xb = round_bf16(x)
+    yb = ops.scale_grad(xb, 0.3, "bf16")
+    assert np.array_equal(round_bf16(yb), yb)
+    assert np.array_equal(ops.scale_grad(xb, 0.25, "bf16"), 0.25 * xb)
