@@ -77,6 +77,14 @@ lib.xt_grad_accumulate.restype = C.c_int
 lib.xt_grad_accumulate.argtypes = [_TP, _TP, C.c_void_p]
 lib.xt_dropout_mask.restype = C.c_int
 lib.xt_dropout_mask.argtypes = [_TP, C.c_float, C.c_uint64, C.c_void_p]
+lib.xt_grad_norm_workspace.restype = C.c_size_t
+lib.xt_grad_norm_workspace.argtypes = [_TP, C.c_int32]
+lib.xt_grad_norm.restype = C.c_int
+lib.xt_grad_norm.argtypes = [_TP, C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+lib.xt_grads_scale.restype = C.c_int
+lib.xt_grads_scale.argtypes = [_TP, C.c_int32, C.c_float, C.c_void_p, C.c_void_p]
+lib.xt_grads_zero.restype = C.c_int
+lib.xt_grads_zero.argtypes = [_TP, C.c_int32, C.c_void_p]
 lib.xt_tape_create.restype = C.c_void_p
 lib.xt_tape_create.argtypes = [_ALLOC, _FREE, C.c_void_p, C.c_void_p]
 lib.xt_tape_destroy.argtypes = [C.c_void_p]
@@ -143,9 +151,12 @@ def view(t, rows=None, cols=None, ld=None, nb=(1, 1), sb=(0, 0), offset=0) -> Te
     if rows is None:
         if t.dim() == 2:
             rows, cols = t.shape
-            ld = t.stride(0) if ld is None else ld
-            if t.stride(1) != 1:
-                raise ValueError("columns must be contiguous")
+            if t.numel() == 0:          # an empty tensor's strides carry no layout
+                ld = cols if ld is None else ld
+            else:
+                ld = t.stride(0) if ld is None else ld
+                if t.stride(1) != 1:
+                    raise ValueError("columns must be contiguous")
         elif t.dim() == 1:
             rows, cols = 1, t.shape[0]
             ld = cols if ld is None else ld
@@ -215,6 +226,27 @@ def xt_grad_accumulate(dst: Tensor, src: Tensor, stream=None) -> None:
 def xt_dropout_mask(mask: Tensor, p: float, seed: int, stream=None) -> None:
     _check(lib.xt_dropout_mask(C.byref(mask), p, int(seed) & 0xFFFFFFFFFFFFFFFF, _stream(stream)),
            "xt_dropout_mask")
+
+
+def xt_grad_norm_workspace(grads) -> int:
+    a, n = _arr(grads)
+    return lib.xt_grad_norm_workspace(a, n)
+
+
+def xt_grad_norm(grads, max_norm: float, out, ws=None, ws_bytes=0, stream=None) -> None:
+    """out: device pointer (int or c_void_p) of two f32: the norm and the clipping coefficient."""
+    a, n = _arr(grads)
+    _check(lib.xt_grad_norm(a, n, max_norm, out, ws, ws_bytes, _stream(stream)), "xt_grad_norm")
+
+
+def xt_grads_scale(grads, alpha: float = 1.0, scale=None, stream=None) -> None:
+    a, n = _arr(grads)
+    _check(lib.xt_grads_scale(a, n, alpha, scale, _stream(stream)), "xt_grads_scale")
+
+
+def xt_grads_zero(grads, stream=None) -> None:
+    a, n = _arr(grads)
+    _check(lib.xt_grads_zero(a, n, _stream(stream)), "xt_grads_zero")
 
 
 def workspace(op: int, is_bwd: int, prm: Params, ins):

@@ -549,4 +549,45 @@ xt_status xt_dropout_mask(const xt_tensor* mask, float p, uint64_t seed, void* s
   return hip_status(launch_dropout_mask_only(*mask, dropout_thr(p), seed, (hipStream_t)stream), "dropout_mask");
 }
 
+// ---- gradient buffers after the backward ----
+static xt_status check_grad_list(const xt_tensor* g, int32_t n) {
+  if (n < 0) return fail(XT_ERR_INVALID_ARG, "negative tensor count");
+  if (n > 0 && !g) return fail(XT_ERR_INVALID_ARG, "null tensor list");
+  for (int32_t i = 0; i < n; ++i) {
+    char name[32];
+    snprintf(name, sizeof name, "grads[%d]", (int)i);
+    XT_TRY(check_act(&g[i], name));
+  }
+  return XT_OK;
+}
+
+size_t xt_grad_norm_workspace(const xt_tensor* grads, int32_t n) {
+  if (check_grad_list(grads, n) != XT_OK) return 0;
+  return (size_t)grad_norm_units(grads, n) * sizeof(double);
+}
+
+xt_status xt_grad_norm(const xt_tensor* grads, int32_t n, float max_norm, float* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  XT_TRY(check_grad_list(grads, n));
+  if (!out) return fail(XT_ERR_INVALID_ARG, "grad_norm: null output");
+  if (!(max_norm >= 0.f)) return fail(XT_ERR_INVALID_ARG, "grad_norm: max_norm must be >= 0 (0 = no clipping)");
+  const int64_t units = grad_norm_units(grads, n);
+  if (units > 0x7fffffff) return fail(XT_ERR_UNSUPPORTED, "grad_norm: too many work units");
+  const size_t need = (size_t)units * sizeof(double);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(XT_ERR_WORKSPACE, "grad_norm needs %zu bytes of workspace", need);
+  if (((uintptr_t)ws) % 8 != 0) return fail(XT_ERR_INVALID_ARG, "grad_norm: workspace must be 8-byte aligned");
+  return hip_status(launch_grad_norm(grads, n, max_norm, out, (double*)ws, (hipStream_t)stream), "grad_norm");
+}
+
+xt_status xt_grads_scale(const xt_tensor* grads, int32_t n, float alpha, const float* scale, void* stream) {
+  XT_TRY(check_grad_list(grads, n));
+  return hip_status(launch_grads_scale(grads, n, false, alpha, scale, (hipStream_t)stream), "grads_scale");
+}
+
+xt_status xt_grads_zero(const xt_tensor* grads, int32_t n, void* stream) {
+  XT_TRY(check_grad_list(grads, n));
+  return hip_status(launch_grads_scale(grads, n, true, 0.f, nullptr, (hipStream_t)stream), "grads_zero");
+}
+
 }  // extern "C"

@@ -105,4 +105,11 @@ size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, 
 // --- misc -------------------------------------------------------------------
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
+// gradbuf.hip: global gradient norm (two passes through `part`, f64 per
+// work unit) and in-place scaling / zeroing of a list of gradient tensors.
+int64_t grad_norm_units(const xt_tensor* g, int n);
+hipError_t launch_grad_norm(const xt_tensor* g, int n, float max_norm, float* out, double* part, hipStream_t s);
+hipError_t launch_grads_scale(const xt_tensor* g, int n, bool zero, float alpha, const float* scale,
+                              hipStream_t s);
+
 }  // namespace xt

@@ -13,7 +13,10 @@ batch of synthetic input, each at the shape its workload names:
     32768 x 32768, dbias column sum over 65536 x 4096, matmul backward of
     8192 x 4096 x 4096;
   * the tiny transformer block (batch 4, seq 256, d 256, 4 x 64 heads,
-    SwiGLU 688, vocab 4096, f32) recorded on the tape, fwd+bwd.
+    SwiGLU 688, vocab 4096, f32) recorded on the tape, fwd+bwd;
+  * after the backward: the global gradient norm and the clip scaling over
+    every gradient buffer of a 12-layer model of GPT-2-small width (about
+    124M f32 in 124 tensors).
 Inputs are drawn on the GPU before timing (torch's seeded generator).
 
 `value` is the step's algorithmic HBM bytes / step time (GB/s): what the
@@ -320,10 +323,38 @@ def build_entries(only):
                 + 2 * 2 * shp.B * shp.H * shp.S * shp.S * shp.Dh
             E.append(Entry("c2.block.fwdbwd", "tiny block 4x256x256 f32", "f32", "block", run_block, 0, 3 * fl,
                            shp.B * shp.S))
+    def f3():
+        nonlocal keep
+        if not want("f3"):
+            return
+        # every gradient buffer of a 12-layer model of GPT-2-small width
+        # (d 768, MLP 3072, vocabulary 50257, 1024 positions), f32
+        shapes = []
+        for _ in range(12):
+            shapes += [(768, 768)] * 4 + [(768, 3072), (3072, 768)] + [(1, 768)] * 4
+        shapes += [(50257, 768), (1024, 768), (1, 768), (1, 768)]
+        gr = [device_normal(sh, 8, 200 + k, 0.0, 1e-3) for k, sh in enumerate(shapes)]
+        keep += gr
+        gv = [V(t) for t in gr]
+        n = sum(t.numel() for t in gr)
+        nb = xt.xt_grad_norm_workspace(gv)
+        wsb = torch.empty(max(nb, 8), dtype=torch.uint8, device="cuda")
+        out = torch.empty(2, dtype=torch.float32, device="cuda")
+        one = torch.ones(1, dtype=torch.float32, device="cuda")
+        keep += [wsb, out, one]
+        W = "gpt2s-f32 12-layer gradient set"
+        E.append(Entry("f3.grad_norm", W, "f32", "hbm",
+                       lambda: xt.xt_grad_norm(gv, 1.0, out.data_ptr(), wsb.data_ptr(), nb), 4 * n, rows=len(gr)))
+        # the clip step multiplies by a device-side coefficient (here 1.0, so
+        # the buffers keep their values from step to step)
+        E.append(Entry("f3.grads_scale", W, "f32", "hbm",
+                       lambda: xt.xt_grads_scale(gv, 1.0, one.data_ptr()), 8 * n, rows=len(gr)))
+
     c3()
     c4()
     c5()
     c2()
+    f3()
     return E, keep
 
 
@@ -555,7 +586,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32+bf16", "data": "synthetic",
         "config": {"workload": "hot-path suite: every op fwd+bwd at the gpt2s-f32 8x1024x768, bf16 16384x4096 and "
-                               "bf16-stress shapes, plus the tiny transformer block on the tape",
+                               "bf16-stress shapes, the tiny transformer block on the tape, and the global "
+                               "gradient norm and clip scaling over a 12-layer gpt2s-width gradient set",
                    "parallelism": "none (1 GPU)"},
         "memory_bound_GBps": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1) if hbm_ms else None,
         "memory_bound_frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if hbm_ms else None,

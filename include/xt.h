@@ -185,6 +185,40 @@ xt_status xt_grad_accumulate(const xt_tensor* dst, const xt_tensor* src, void* s
  * [DO] "RNG：counter-based".  0 <= p < 1, mask dtype XT_U8. */
 xt_status xt_dropout_mask(const xt_tensor* mask, float p, uint64_t seed, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Gradient buffers after the backward.  [BP] kernel-pair table: the helper
+ * kernels k_grad_norm_partial, k_grad_norm_final and k_grad_scale for
+ * gradient clipping; [BP] "Ackumulation över mikrobatcher": scale_grads(1/n)
+ * averages the summed microbatch gradients, zero_grads() clears them.
+ * `grads` is a host array of n caller views (f32 or bf16, unbatched, any
+ * ld >= cols; empty tensors are skipped); the data are device memory.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace xt_grad_norm needs for this list: 8 per work
+ * unit of 8192 elements of a row (a contiguous tensor is one row).  0 for
+ * an invalid list. */
+size_t xt_grad_norm_workspace(const xt_tensor* grads, int32_t n);
+
+/* Global L2 norm over every element of every tensor, and the clipping
+ * coefficient of Pascanu, Mikolov & Bengio (2013, section 3.2):
+ *   out[0] = sqrt(sum g^2)  (squares exact in f64, summed in f64 in a fixed
+ *            order by a partial pass and a final pass, rounded once to f32);
+ *   out[1] = max_norm / norm if max_norm > 0 and norm > max_norm, else 1.
+ * out: device, two f32.  max_norm >= 0 (0 = no clipping).  ws: device,
+ * 8-byte aligned, xt_grad_norm_workspace bytes.  Bitwise reproducible for a
+ * given list.  An empty list gives norm 0. */
+xt_status xt_grad_norm(const xt_tensor* grads, int32_t n, float max_norm, float* out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* In place: g = g * f with f = alpha, or f = alpha * scale[0] (f32) when
+ * `scale` (a device f32, e.g. out + 1 of xt_grad_norm) is not NULL; each
+ * element is the f32 product rounded once into g's dtype.  Reading the
+ * factor on the device keeps clipping free of host synchronisation. */
+xt_status xt_grads_scale(const xt_tensor* grads, int32_t n, float alpha, const float* scale, void* stream);
+
+/* In place: g = 0 (a fill kernel, so it may be captured in a HIP graph). */
+xt_status xt_grads_zero(const xt_tensor* grads, int32_t n, void* stream);
+
 const char* xt_status_str(xt_status s);
 const char* xt_last_error(void);    /* thread-local detail of the last failure */
 int         xt_abi_version(void);   /* 1 */

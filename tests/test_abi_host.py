@@ -98,6 +98,41 @@ def test_validation_rejects_without_launch():
 
 
 @needs_lib
+def test_grad_buffer_validation_without_launch():
+    import autograd_row_wise_amd as xt
+    import numpy as np
+
+    buf = np.zeros(64, dtype=np.float32)
+    def host_view(rows, cols, dtype=xt.DT.F32, nb=1):
+        v = xt.Tensor()
+        v.data = C.c_void_p(buf.ctypes.data)
+        v.dtype = dtype
+        v.rows, v.cols, v.ld = rows, cols, cols
+        v.nb[0], v.nb[1] = nb, 1
+        return v
+    g = [host_view(2, 4), host_view(1, 3, xt.DT.BF16)]
+    # two units of 8192 elements at most -> 8 bytes each
+    assert xt.xt_grad_norm_workspace(g) == 2 * 8
+    assert xt.xt_grad_norm_workspace([host_view(3, 8192 * 2 + 1)]) == 7 * 8   # contiguous: one row of 49155
+    with pytest.raises(xt.XtError) as e:            # no workspace
+        xt.xt_grad_norm(g, 1.0, buf.ctypes.data, None, 0, stream=C.c_void_p(0))
+    assert e.value.status == 5
+    with pytest.raises(xt.XtError) as e:            # negative threshold
+        xt.xt_grad_norm(g, -1.0, buf.ctypes.data, buf.ctypes.data, 256, stream=C.c_void_p(0))
+    assert e.value.status == 1
+    with pytest.raises(xt.XtError) as e:            # null output
+        xt.xt_grad_norm(g, 1.0, None, buf.ctypes.data, 256, stream=C.c_void_p(0))
+    assert e.value.status == 1
+    with pytest.raises(xt.XtError) as e:            # u8 is not a gradient dtype
+        xt.xt_grads_scale([host_view(2, 4, xt.DT.U8)], 0.5, stream=C.c_void_p(0))
+    assert e.value.status == 3
+    with pytest.raises(xt.XtError) as e:            # batched views are rejected
+        xt.xt_grads_zero([host_view(2, 4, nb=2)], stream=C.c_void_p(0))
+    assert e.value.status == 2
+    assert xt.xt_grad_norm_workspace([host_view(2, 4, xt.DT.U8)]) == 0
+
+
+@needs_lib
 def test_workspace_query_is_host_only():
     import autograd_row_wise_amd as xt
     def shape(rows, cols, dtype=xt.DT.F32):
