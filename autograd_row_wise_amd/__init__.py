@@ -108,6 +108,10 @@ lib.xt_tape_backward_seeded.restype = C.c_int
 lib.xt_tape_backward_seeded.argtypes = [C.c_void_p, C.c_int64, _TP]
 lib.xt_tape_zero_grad.restype = C.c_int
 lib.xt_tape_zero_grad.argtypes = [C.c_void_p]
+lib.xt_tape_checkpoint_begin.restype = C.c_int
+lib.xt_tape_checkpoint_begin.argtypes = [C.c_void_p]
+lib.xt_tape_checkpoint_end.restype = C.c_int
+lib.xt_tape_checkpoint_end.argtypes = [C.c_void_p, C.c_int64]
 lib.xt_tape_num_nodes.restype = C.c_int64
 lib.xt_tape_num_nodes.argtypes = [C.c_void_p]
 
@@ -311,6 +315,13 @@ class Tape:
         else:
             r = lib.xt_tape_apply_layout(self.h, op, C.byref(prm), arr, len(parents), C.byref(layout))
         return self._var(r, "xt_tape_apply")
+
+    def checkpoint_begin(self) -> None:
+        _check(lib.xt_tape_checkpoint_begin(self.h), "xt_tape_checkpoint_begin")
+
+    def checkpoint_end(self, out: int) -> int:
+        _check(lib.xt_tape_checkpoint_end(self.h, out), "xt_tape_checkpoint_end")
+        return out
 
     def view(self, parent: int, layout: Tensor) -> int:
         return self._var(lib.xt_tape_view(self.h, parent, C.byref(layout)), "xt_tape_view")

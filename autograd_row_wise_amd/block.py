@@ -65,10 +65,14 @@ def attention(tape: Tape, q: int, k: int, v: int, B: int, S: int, H: int, Dh: in
     return tape.view(out, layout(B * S, D, D, dtype))
 
 
-def block(tape: Tape, w: dict, x: int, targets: int, shp: BlockShape, dtype: int,
-          p_drop: float = 0.0, base_seed: int = 0, layer: int = 0, eps: float = 1e-5) -> int:
-    """Records the block; `w` maps g1 g2 g3 wq wk wv wo wg wu wd wout to leaf vars.
-    Returns the loss var."""
+def block_layer(tape: Tape, w: dict, x: int, shp: BlockShape, dtype: int, p_drop: float = 0.0,
+                base_seed: int = 0, layer_index: int = 0, eps: float = 1e-5, checkpoint: bool = False,
+                taps: dict | None = None) -> int:
+    """Records the two residual halves of one layer; returns h2.  With
+    `checkpoint`, the layer is one recompute segment whose output is h2.
+    `taps` (optional) receives the vars of n1 and of the two dropout nodes."""
+    if checkpoint:
+        tape.checkpoint_begin()
     mm = params()
     n1 = tape.apply(OP.RMS_NORM, params(eps=eps), x, w["g1"])
     rope = params(head_dim=shp.Dh, seq_len=shp.S, rope_base=10000.0)
@@ -76,15 +80,28 @@ def block(tape: Tape, w: dict, x: int, targets: int, shp: BlockShape, dtype: int
     k = tape.apply(OP.ROPE, rope, tape.apply(OP.MATMUL, mm, n1, w["wk"]))
     v = tape.apply(OP.MATMUL, mm, n1, w["wv"])
     a = tape.apply(OP.MATMUL, mm, attention(tape, q, k, v, shp.B, shp.S, shp.H, shp.Dh, dtype), w["wo"])
-    a = tape.apply(OP.DROPOUT, params(p=p_drop, seed=base_seed ^ layer ^ SITE_ATTN), a)
+    a = tape.apply(OP.DROPOUT, params(p=p_drop, seed=base_seed ^ layer_index ^ SITE_ATTN), a)
     h = tape.apply(OP.ADD, params(), x, a)
     n2 = tape.apply(OP.RMS_NORM, params(eps=eps), h, w["g2"])
     m = tape.apply(OP.SWIGLU, params(), tape.apply(OP.MATMUL, mm, n2, w["wg"]),
                    tape.apply(OP.MATMUL, mm, n2, w["wu"]))
     m = tape.apply(OP.MATMUL, mm, m, w["wd"])
-    m = tape.apply(OP.DROPOUT, params(p=p_drop, seed=base_seed ^ layer ^ SITE_FFN), m)
+    m = tape.apply(OP.DROPOUT, params(p=p_drop, seed=base_seed ^ layer_index ^ SITE_FFN), m)
     h2 = tape.apply(OP.ADD, params(), h, m)
-    logits = tape.apply(OP.MATMUL, mm, tape.apply(OP.RMS_NORM, params(eps=eps), h2, w["g3"]), w["wout"])
+    if taps is not None:
+        taps.update(n1=n1, drop_attn=a, drop_ffn=m)
+    if checkpoint:
+        tape.checkpoint_end(h2)
+    return h2
+
+
+def block(tape: Tape, w: dict, x: int, targets: int, shp: BlockShape, dtype: int,
+          p_drop: float = 0.0, base_seed: int = 0, layer: int = 0, eps: float = 1e-5,
+          checkpoint: bool = False) -> int:
+    """Records the block; `w` maps g1 g2 g3 wq wk wv wo wg wu wd wout to leaf vars.
+    Returns the loss var."""
+    h2 = block_layer(tape, w, x, shp, dtype, p_drop, base_seed, layer, eps, checkpoint)
+    logits = tape.apply(OP.MATMUL, params(), tape.apply(OP.RMS_NORM, params(eps=eps), h2, w["g3"]), w["wout"])
     return tape.apply(OP.CROSS_ENTROPY, params(), logits, targets)
 
 

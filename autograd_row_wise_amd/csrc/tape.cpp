@@ -15,6 +15,16 @@
 // All device memory (values, saved tensors, gradients, workspace) comes from
 // the caller's allocator callbacks; all work is enqueued on one stream and
 // nothing here synchronises.
+//
+// Activation recompute ([DO] "RNG：counter-based": a checkpoint segment
+// re-runs its forward during backward, which is why the dropout mask is a
+// pure function of (seed, element index)): the ops recorded between
+// xt_tape_checkpoint_begin and xt_tape_checkpoint_end form a segment whose
+// values and saved tensors live in a recompute arena that the next segment
+// reuses; only the segment's output is copied out and stays readable.  The
+// reverse walk reaches a segment through its output (no other node of a
+// segment may be used outside it), re-runs the segment's ops into the arena
+// and then runs their backward calls, newest first.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -61,6 +71,13 @@ struct Node {
   bool grad_live = false;        // a gradient has been written (this pass / since zero_grad)
   int64_t root = -1;             // views: the node owning the buffers
   int64_t offset = 0;            // views: element offset from the parent's value
+  int seg = -1;                  // checkpoint segment whose arena holds the buffers
+  bool seg_out = false;          // the segment's output (value copied out of the arena)
+  uint64_t epoch = 0;            // arena epoch the buffers were written in
+};
+
+struct Segment {
+  xt_var first = 0, last = -1, out = -1;
 };
 
 }  // namespace
@@ -84,6 +101,39 @@ struct xt_tape {
   void* ws = nullptr;            // op workspace, reused by every call (stream order)
   size_t ws_cap = 0;
   std::string err;
+  // recompute arena: chunks reused from the start by every segment (forward
+  // or recompute); `epoch` counts the rewinds
+  std::vector<std::pair<char*, size_t>> arena;
+  size_t a_chunk = 0, a_off = 0;
+  uint64_t epoch = 1;
+  int open_seg = -1;
+  std::vector<Segment> segs;
+
+  void rewind() {
+    a_chunk = 0;
+    a_off = 0;
+    ++epoch;
+  }
+
+  void* aget(size_t bytes) {
+    bytes = (bytes + ALIGN - 1) / ALIGN * ALIGN;
+    if (bytes == 0) bytes = ALIGN;
+    while (a_chunk < arena.size() && arena[a_chunk].second - a_off < bytes) {
+      ++a_chunk;
+      a_off = 0;
+    }
+    if (a_chunk == arena.size()) {
+      const size_t n = bytes > SLAB ? bytes : SLAB;
+      void* p = alloc(ctx, n, (void*)stream);
+      if (!p) return nullptr;
+      owned.push_back(p);
+      arena.push_back({static_cast<char*>(p), n});
+      a_off = 0;
+    }
+    char* p = arena[a_chunk].first + a_off;
+    a_off += bytes;
+    return p;
+  }
 
   // Workspace of one op call.  Calls run in stream order on the tape's
   // stream, so one buffer serves them all; it only grows.
@@ -121,6 +171,20 @@ namespace {
 xt_var bad(xt_status s) { return -(xt_var)s; }
 
 bool valid_var(const xt_tape* t, xt_var v) { return t && v >= 0 && v < (xt_var)t->nodes.size(); }
+
+// A node later ops may read: outside every segment, a segment's output, or
+// a node of the segment being recorded.
+bool usable(const xt_tape* t, xt_var v) {
+  const Node& n = t->nodes[v];
+  return n.seg < 0 || n.seg_out || n.seg == t->open_seg;
+}
+
+// Whether v's buffers hold its current values (a closed segment's arena
+// buffers are only valid between its recompute and the next rewind).
+bool current(const xt_tape* t, xt_var v) {
+  const Node& n = t->nodes[v];
+  return n.seg < 0 || n.epoch == t->epoch;
+}
 
 // Owner of the gradient storage of node v (itself unless it is a view).
 int64_t grad_owner(const xt_tape* t, xt_var v) {
@@ -204,7 +268,7 @@ xt_var apply_impl(xt_tape* t, xt_op op, const xt_params* prm, const xt_var* pare
   if (!t || !prm || (n > 0 && !parents)) return bad(XT_ERR_INVALID_ARG);
   if (op < 0 || op >= XT_OP_COUNT || n < 1 || n > 3) return bad(XT_ERR_INVALID_ARG);
   for (int i = 0; i < n; ++i)
-    if (!valid_var(t, parents[i])) return bad(XT_ERR_INVALID_ARG);
+    if (!valid_var(t, parents[i]) || !usable(t, parents[i])) return bad(XT_ERR_INVALID_ARG);
   // [DO] "dropout 节点": p == 0 is the identity and records no node
   if (op == XT_OP_DROPOUT && prm->p == 0.f) return parents[0];
 
@@ -222,9 +286,10 @@ xt_var apply_impl(xt_tape* t, xt_op op, const xt_params* prm, const xt_var* pare
     l.data = nullptr;
     outs[0] = l;
   }
+  const bool in_seg = t->open_seg >= 0;
   for (auto& o : outs) {
-    const int64_t span = span_elems(o);
-    o.data = t->get((size_t)span * elem_size(o.dtype));
+    const size_t bytes = (size_t)span_elems(o) * elem_size(o.dtype);
+    o.data = in_seg ? t->aget(bytes) : t->get(bytes);
     if (!o.data) return bad(XT_ERR_ALLOC);
   }
   const size_t wsb = xt_workspace_bytes(op, 0, prm, in_vals.data(), n);
@@ -239,8 +304,49 @@ xt_var apply_impl(xt_tape* t, xt_op op, const xt_params* prm, const xt_var* pare
   nd.value = outs[0];
   nd.extra.assign(outs.begin() + 1, outs.end());
   for (int i = 0; i < n; ++i) nd.needs_grad = nd.needs_grad || t->nodes[parents[i]].needs_grad;
+  nd.seg = t->open_seg;
+  nd.epoch = t->epoch;
   t->nodes.push_back(nd);
   return (xt_var)t->nodes.size() - 1;
+}
+
+// Re-runs segment `sg`'s ops into the (rewound) arena, in recording order:
+// the same ops on the same inputs, so the values, saved tensors and dropout
+// masks are the ones the first forward computed.  The output's value stays
+// in its copy outside the arena; its saved tensors are rewritten.
+xt_status recompute(xt_tape* t, int sg) {
+  const Segment& S = t->segs[sg];
+  t->rewind();
+  for (xt_var u = S.first; u <= S.last; ++u) {
+    Node& n = t->nodes[u];
+    if (n.seg != sg) continue;
+    if (n.view) {
+      const Node& r = t->nodes[n.root];
+      n.value.data = (char*)r.value.data + n.offset * elem_size(n.value.dtype);
+      n.epoch = t->epoch;
+      continue;
+    }
+    const int np = (int)n.parents.size();
+    std::vector<xt_tensor> in_vals(np);
+    for (int i = 0; i < np; ++i) in_vals[i] = t->nodes[n.parents[i]].value;
+    std::vector<xt_tensor> outs;
+    outs.push_back(n.value);
+    for (const auto& e : n.extra) outs.push_back(e);
+    for (auto& o : outs) {
+      o.data = t->aget((size_t)span_elems(o) * elem_size(o.dtype));
+      if (!o.data) return XT_ERR_ALLOC;
+    }
+    const size_t wsb = xt_workspace_bytes(n.op, 0, &n.prm, in_vals.data(), np);
+    void* ws = nullptr;
+    if (wsb && !(ws = t->scratch(wsb))) return XT_ERR_ALLOC;
+    const xt_status s = xt_op_fwd(n.op, &n.prm, in_vals.data(), np, outs.data(), (int)outs.size(), ws, wsb,
+                                  (void*)t->stream);
+    if (s != XT_OK) return s;
+    if (!n.seg_out) n.value = outs[0];
+    for (size_t i = 0; i < n.extra.size(); ++i) n.extra[i] = outs[i + 1];
+    n.epoch = t->epoch;
+  }
+  return XT_OK;
 }
 
 }  // namespace
@@ -289,7 +395,7 @@ xt_var xt_tape_apply_layout(xt_tape* t, xt_op op, const xt_params* prm, const xt
 }
 
 xt_var xt_tape_view(xt_tape* t, xt_var parent, const xt_tensor* layout) {
-  if (!valid_var(t, parent) || !layout) return bad(XT_ERR_INVALID_ARG);
+  if (!valid_var(t, parent) || !layout || !usable(t, parent)) return bad(XT_ERR_INVALID_ARG);
   const Node& p = t->nodes[parent];
   const int64_t off = (int64_t)(intptr_t)layout->data;
   xt_tensor v = *layout;
@@ -305,12 +411,15 @@ xt_var xt_tape_view(xt_tape* t, xt_var parent, const xt_tensor* layout) {
   nd.root = p.view ? p.root : parent;
   nd.offset = off;
   nd.needs_grad = p.needs_grad;
+  nd.seg = (p.seg >= 0 && !p.seg_out) ? p.seg : -1;   // shares its root's buffer
+  nd.epoch = t->epoch;
   t->nodes.push_back(nd);
   return (xt_var)t->nodes.size() - 1;
 }
 
 xt_status xt_tape_value(xt_tape* t, xt_var v, xt_tensor* out) {
   if (!valid_var(t, v) || !out) return XT_ERR_INVALID_ARG;
+  if (!t->nodes[v].seg_out && !current(t, v)) return XT_ERR_INVALID_ARG;   // in a rewound arena
   *out = t->nodes[v].value;
   return XT_OK;
 }
@@ -318,7 +427,7 @@ xt_status xt_tape_value(xt_tape* t, xt_var v, xt_tensor* out) {
 xt_status xt_tape_saved(xt_tape* t, xt_var v, int k, xt_tensor* out) {
   if (!valid_var(t, v) || !out || k < 1) return XT_ERR_INVALID_ARG;
   const Node& n = t->nodes[v];
-  if (k - 1 >= (int)n.extra.size()) return XT_ERR_INVALID_ARG;
+  if (k - 1 >= (int)n.extra.size() || !current(t, v)) return XT_ERR_INVALID_ARG;
   *out = n.extra[k - 1];
   return XT_OK;
 }
@@ -333,6 +442,43 @@ xt_status xt_tape_grad(xt_tape* t, xt_var v, xt_tensor* out) {
 xt_status xt_tape_zero_grad(xt_tape* t) {
   if (!t) return XT_ERR_INVALID_ARG;
   for (auto& n : t->nodes) n.grad_live = false;
+  return XT_OK;
+}
+
+xt_status xt_tape_checkpoint_begin(xt_tape* t) {
+  if (!t || t->open_seg >= 0) return XT_ERR_INVALID_ARG;
+  Segment sg;
+  sg.first = (xt_var)t->nodes.size();
+  t->segs.push_back(sg);
+  t->open_seg = (int)t->segs.size() - 1;
+  t->rewind();
+  return XT_OK;
+}
+
+xt_status xt_tape_checkpoint_end(xt_tape* t, xt_var out) {
+  if (!t || t->open_seg < 0 || !valid_var(t, out)) return XT_ERR_INVALID_ARG;
+  Node& o = t->nodes[out];
+  if (o.seg != t->open_seg || o.view || o.leaf) return XT_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)span_elems(o.value) * elem_size(o.value.dtype);
+  void* dst = t->get(bytes);
+  if (!dst) return XT_ERR_ALLOC;
+  if (bytes && hipMemcpyAsync(dst, o.value.data, bytes, hipMemcpyDeviceToDevice, t->stream) != hipSuccess)
+    return XT_ERR_HIP;
+  o.value.data = dst;
+  o.seg_out = true;
+  Segment& sg = t->segs[t->open_seg];
+  sg.last = (xt_var)t->nodes.size() - 1;
+  sg.out = out;
+  // views of the output recorded inside the segment now read the copy
+  for (xt_var u = sg.first; u <= sg.last; ++u) {
+    Node& n = t->nodes[u];
+    if (n.view && n.root == out) {
+      n.value.data = (char*)dst + n.offset * elem_size(n.value.dtype);
+      n.seg = -1;
+    }
+  }
+  t->open_seg = -1;
+  t->rewind();
   return XT_OK;
 }
 
@@ -368,10 +514,9 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
   s = seed(t->nodes[out].grad, grad_live(t, out));
   if (s != XT_OK) return s;
   set_grad_live(t, out);
-  for (auto it = order.rbegin(); it != order.rend(); ++it) {
-    const xt_var v = *it;
+  auto visit = [&](xt_var v) -> xt_status {
     Node& n = t->nodes[v];
-    if (n.leaf || n.view || !n.needs_grad || !grad_live(t, v)) continue;
+    if (n.leaf || n.view || !n.needs_grad || !grad_live(t, v)) return XT_OK;
     const int np = (int)n.parents.size();
     std::vector<xt_tensor> in_vals(np);
     for (int i = 0; i < np; ++i) in_vals[i] = t->nodes[n.parents[i]].value;
@@ -413,7 +558,35 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
       if (s != XT_OK) break;
       for (xt_var q : used) set_grad_live(t, q);
     }
+    return s;
+  };
+  // A segment is reached through its output, after every consumer of the
+  // output; its other nodes feed only each other and the output, so the
+  // whole segment is recomputed and its backward calls run right there,
+  // newest node first (recording order is a topological order).
+  std::vector<char> seg_done(t->segs.size(), 0);
+  for (auto it = order.rbegin(); it != order.rend(); ++it) {
+    const xt_var v = *it;
+    const int sg = t->nodes[v].seg;
+    if (sg < 0) {
+      s = visit(v);
+      if (s != XT_OK) return s;
+      continue;
+    }
+    if (seg_done[sg]) continue;
+    if (v != t->segs[sg].out) return XT_ERR_INVALID_ARG;
+    seg_done[sg] = 1;
+    bool need = false;
+    for (xt_var u = t->segs[sg].first; u <= t->segs[sg].last; ++u)
+      need = need || (state[u] == 2 && t->nodes[u].seg == sg && grad_live(t, u) && t->nodes[u].needs_grad);
+    if (!need) continue;
+    s = recompute(t, sg);
     if (s != XT_OK) return s;
+    for (xt_var u = t->segs[sg].last; u >= t->segs[sg].first; --u) {
+      if (state[u] != 2 || t->nodes[u].seg != sg) continue;
+      s = visit(u);
+      if (s != XT_OK) return s;
+    }
   }
   return XT_OK;
 }
@@ -422,7 +595,7 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
 extern "C" {
 
 xt_status xt_tape_backward(xt_tape* t, xt_var loss) {
-  if (!valid_var(t, loss)) return XT_ERR_INVALID_ARG;
+  if (!valid_var(t, loss) || t->open_seg >= 0) return XT_ERR_INVALID_ARG;
   const Node& L = t->nodes[loss];
   if (L.value.rows * L.value.cols * L.value.nb[0] * L.value.nb[1] != 1 || L.value.dtype != XT_F32)
     return XT_ERR_SHAPE;
@@ -433,7 +606,7 @@ xt_status xt_tape_backward(xt_tape* t, xt_var loss) {
 }
 
 xt_status xt_tape_backward_seeded(xt_tape* t, xt_var out, const xt_tensor* dout) {
-  if (!valid_var(t, out) || !dout) return XT_ERR_INVALID_ARG;
+  if (!valid_var(t, out) || !dout || t->open_seg >= 0) return XT_ERR_INVALID_ARG;
   const Node& n = t->nodes[out];
   if (dout->rows != n.value.rows || dout->cols != n.value.cols || dout->nb[0] != 1 ||
       dout->nb[1] != 1 || n.value.nb[0] != 1 || n.value.nb[1] != 1)

@@ -309,20 +309,25 @@ def build_entries(only):
             keep += list(Wt.values()) + [bx2, bt2]
             holder = {}
 
-            def run_block():
-                if "tape" in holder:
-                    holder["tape"].close()
+            def run_block(ckpt=False, key="tape"):
+                if key in holder:
+                    holder[key].close()
                 t = xt.Tape()
                 w = xb.leaves(t, Wt)
-                loss = xb.block(t, w, t.leaf(V(bx2)), t.leaf(V(bt2), requires_grad=False), shp, xt.DT.F32)
+                loss = xb.block(t, w, t.leaf(V(bx2)), t.leaf(V(bt2), requires_grad=False), shp, xt.DT.F32,
+                                checkpoint=ckpt)
                 t.backward(loss)
-                holder["tape"] = t
+                holder[key] = t
             # GEMM flops of one fwd+bwd (for the record; the block is launch/cache bound)
             T, D = shp.B * shp.S, shp.D
             fl = 2 * T * D * D * 4 + 2 * T * D * shp.hidden * 3 + 2 * T * D * shp.vocab \
                 + 2 * 2 * shp.B * shp.H * shp.S * shp.S * shp.Dh
             E.append(Entry("c2.block.fwdbwd", "tiny block 4x256x256 f32", "f32", "block", run_block, 0, 3 * fl,
                            shp.B * shp.S))
+            # the same block as one recompute segment: the layer's forward runs
+            # twice (the GEMM flops of the record count it once)
+            E.append(Entry("c2.block.fwdbwd_recompute", "tiny block 4x256x256 f32", "f32", "block",
+                           lambda: run_block(True, "tape_ckpt"), 0, 3 * fl, shp.B * shp.S))
     def f3():
         nonlocal keep
         if not want("f3"):

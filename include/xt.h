@@ -283,6 +283,24 @@ xt_status xt_tape_backward_seeded(xt_tape* t, xt_var out, const xt_tensor* dout)
 /* View of v's gradient; data == NULL if no gradient reached v. */
 xt_status xt_tape_grad(xt_tape* t, xt_var v, xt_tensor* out_view);
 xt_status xt_tape_zero_grad(xt_tape* t);
+/* Activation recompute.  [DO] "RNG：counter-based": activation recompute is
+ * why the dropout mask is a pure function of (seed, element index) -- a
+ * checkpoint segment re-runs its forward during backward and must draw the
+ * same masks.  Ops recorded between _begin and _end form a segment: their
+ * values and saved tensors live in a recompute arena that the next segment
+ * (or recompute) reuses, so the tape holds one segment's activations at a
+ * time.  _end(out) copies the segment's output `out` (an op node recorded
+ * inside it, not a view) out of the arena; later ops may use `out` (and
+ * nodes from before the segment) but no other node of the segment
+ * (XT_ERR_INVALID_ARG).  xt_tape_value / xt_tape_saved of a segment's other
+ * nodes fail once its arena has been reused; after a backward they read the
+ * recomputed values until the next segment or recompute.  The reverse walk
+ * re-runs a segment's ops when it reaches `out`, then runs their backward
+ * calls: the gradients are bitwise those of the same graph recorded without
+ * segments.  Segments do not nest; backward with a segment open is
+ * XT_ERR_INVALID_ARG. */
+xt_status xt_tape_checkpoint_begin(xt_tape* t);
+xt_status xt_tape_checkpoint_end(xt_tape* t, xt_var out);
 int64_t   xt_tape_num_nodes(const xt_tape* t);
 
 #ifdef __cplusplus
