@@ -356,3 +356,33 @@ def scale_grad(g, factor: float, dtype: str = "f32"):
     from .numerics import round_bf16, round_f32
     prod = _f(g) * float(np.float32(factor))
     return round_bf16(prod) if dtype == "bf16" else round_f32(prod)
+
+
+# --------------------------------------------------------------------------
+# Token embedding -- [BP] kernel-pair table (k_embed_fwd / k_embed_bwd,
+# "token-inbäddningsuppslag") and the forward of "Framåtgåendet"
+# (x = embed(token_ids), and the tied output projection LN(x) @ embed^T,
+# whose gradient reaches the same table as a second contribution).
+#   y[r, :] = E[ids[r], :];   dE[v, :] = sum over r with ids[r] = v of d[r, :]
+# Readings: ids are int32; an id outside [0, V) gives a NaN output row and
+# contributes nothing to dE; the sum runs over r in increasing order.
+# --------------------------------------------------------------------------
+def embed(table, ids):
+    E = _f(table)
+    ids = np.asarray(ids).reshape(-1)
+    V, D = E.shape
+    y = np.full((ids.size, D), np.nan)
+    for r, v in enumerate(ids):
+        if 0 <= v < V:
+            y[r] = E[v]
+    return y
+
+
+def embed_bwd(d, ids, vocab: int):
+    D_ = _f(d)
+    ids = np.asarray(ids).reshape(-1)
+    dE = np.zeros((vocab, D_.shape[1]))
+    for r, v in enumerate(ids):
+        if 0 <= v < vocab:
+            dE[v] += D_[r]
+    return dE

@@ -340,3 +340,28 @@ def test_scale_grad_rounding():
     yb = ops.scale_grad(xb, 0.3, "bf16")
     assert np.array_equal(round_bf16(yb), yb)
     assert np.array_equal(ops.scale_grad(xb, 0.25, "bf16"), 0.25 * xb)
+
+
+# ------------------------------------------------------------ embedding
+def test_embed_is_a_one_hot_product():
+    V, D, R = 7, 5, 23
+    E = rnd(V, D)
+    ids = RNG.integers(0, V, size=R)
+    onehot = np.zeros((R, V))
+    onehot[np.arange(R), ids] = 1.0
+    np.testing.assert_array_equal(ops.embed(E, ids), onehot @ E)           # exact: one nonzero per row
+    d = rnd(R, D)
+    np.testing.assert_allclose(ops.embed_bwd(d, ids, V), onehot.T @ d, rtol=1e-14, atol=1e-14)
+    # counts: with d = 1 every dE row holds the number of uses of its id
+    cnt = ops.embed_bwd(np.ones((R, 1)), ids, V)[:, 0]
+    np.testing.assert_array_equal(cnt, np.bincount(ids, minlength=V))
+    check_fd(lambda e: ops.embed(e, ids), [ops.embed_bwd(d, ids, V)], [E], d)
+
+
+def test_embed_out_of_range_ids():
+    E = rnd(4, 3)
+    y = ops.embed(E, [0, 4, -1, 3])
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
+    np.testing.assert_array_equal(y[[0, 3]], E[[0, 3]])
+    dE = ops.embed_bwd(np.ones((4, 3)), [0, 4, -1, 0], 4)
+    np.testing.assert_array_equal(dE, [[2, 2, 2], [0, 0, 0], [0, 0, 0], [0, 0, 0]])
