@@ -192,6 +192,7 @@ size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm, const xt_t
     case XT_OP_RMS_NORM: return row_ws_bound(RK_RMS_BWD, in[0].dtype, R, C);
     case XT_OP_LAYER_NORM: return row_ws_bound(RK_LN_BWD, in[0].dtype, R, C);
     case XT_OP_ADD_BIAS: return colsum_workspace(in[0].dtype, R, C);
+    case XT_OP_EMBED: return n_in >= 2 ? embed_bwd_workspace(in[1].rows, in[0].cols) : 0;
     default: return 0;
   }
 }
@@ -326,6 +327,17 @@ xt_status xt_op_fwd(xt_op op, const xt_params* prm, const xt_tensor* in, int n_i
         mask = &out[1];
       }
       return hip_status(launch_dropout_fwd(in[0], out[0], mask, dropout_thr(prm->p), dropout_scale(prm->p), prm->seed, s), "dropout");
+    }
+    case XT_OP_EMBED: {
+      XT_TRY(need(2, 1));
+      XT_TRY(check_act(&in[0], "E"));
+      XT_TRY(check_view(&in[1], "ids"));
+      if (in[1].dtype != XT_I32 || in[1].cols != 1) return fail(XT_ERR_SHAPE, "ids must be [R, 1] int32");
+      if (in[1].rows > 0x7fffffff) return fail(XT_ERR_UNSUPPORTED, "embed: at most 2^31-1 rows");
+      XT_TRY(check_act(&out[0], "y"));
+      if (out[0].dtype != in[0].dtype || out[0].rows != in[1].rows || out[0].cols != in[0].cols)
+        return fail(XT_ERR_SHAPE, "embed output must be [R, D] in E's dtype");
+      return hip_status(launch_embed_fwd(in[0], (const int32_t*)in[1].data, in[1].ld, out[0], s), "embed");
     }
     default:
       return fail(XT_ERR_INVALID_ARG, "unknown op %d", (int)op);
@@ -527,6 +539,23 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
       if (!wanted(din, n_din, 0)) return XT_OK;
       XT_TRY(check_like(&din[0], *dout, "dx"));
       return hip_status(launch_dropout_bwd(*dout, saved[0], din[0], acc(0), dropout_scale(prm->p), s), "dropout backward");
+    }
+    case XT_OP_EMBED: {
+      if (n_in != 2 || n_saved != 0 || n_din < 1 || n_din > 2)
+        return fail(XT_ERR_INVALID_ARG, "embed backward takes E, ids, no saved tensors and 1 or 2 gradient slots");
+      if (n_din == 2 && din[1].data) return fail(XT_ERR_INVALID_ARG, "ids have no gradient");
+      XT_TRY(check_act(&in[0], "E"));
+      XT_TRY(check_view(&in[1], "ids"));
+      if (in[1].dtype != XT_I32 || in[1].cols != 1) return fail(XT_ERR_SHAPE, "ids must be [R, 1] int32");
+      if (in[1].rows > 0x7fffffff) return fail(XT_ERR_UNSUPPORTED, "embed: at most 2^31-1 rows");
+      XT_TRY(check_act(dout, "dout"));
+      if (dout->rows != in[1].rows || dout->cols != in[0].cols || dout->dtype != in[0].dtype)
+        return fail(XT_ERR_SHAPE, "embed dout must be [R, D] in E's dtype");
+      if (!wanted(din, n_din, 0)) return XT_OK;
+      XT_TRY(check_like(&din[0], in[0], "dE"));
+      if (ws_need && (!ws || ws_bytes < ws_need)) return fail(XT_ERR_WORKSPACE, "embed backward needs %zu bytes of workspace", ws_need);
+      return hip_status(launch_embed_bwd(*dout, (const int32_t*)in[1].data, in[1].ld, din[0], acc(0), ws, s),
+                        "embed backward");
     }
     default:
       return fail(XT_ERR_INVALID_ARG, "unknown op %d", (int)op);

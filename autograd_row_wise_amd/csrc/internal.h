@@ -105,6 +105,13 @@ size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, 
 // --- misc -------------------------------------------------------------------
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
+// embed.hip: token-embedding gather and its deterministic scatter-add
+// backward (per-chunk LDS sort of (id, row) keys into `ws`, then per-run sums).
+size_t embed_bwd_workspace(int64_t R, int64_t D);
+hipError_t launch_embed_fwd(const xt_tensor& E, const int32_t* ids, int64_t ldi, const xt_tensor& y, hipStream_t s);
+hipError_t launch_embed_bwd(const xt_tensor& d, const int32_t* ids, int64_t ldi, const xt_tensor& dE, bool acc,
+                            void* ws, hipStream_t s);
+
 // gradbuf.hip: global gradient norm (two passes through `part`, f64 per
 // work unit) and in-place scaling / zeroing of a list of gradient tensors.
 int64_t grad_norm_units(const xt_tensor* g, int n);

@@ -233,6 +233,9 @@ xt_status out_shapes(xt_op op, const xt_params& prm, const std::vector<const xt_
       outs.push_back(c);
       return XT_OK;
     }
+    case XT_OP_EMBED:
+      outs.push_back(dense(nullptr, x.dtype, in[1]->rows, x.cols));
+      return XT_OK;
     case XT_OP_CROSS_ENTROPY:
       outs.push_back(dense(nullptr, XT_F32, 1, 1));
       outs.push_back(dense(nullptr, XT_F32, x.rows, 1));
@@ -533,7 +536,7 @@ xt_status reverse_pass(xt_tape* t, xt_var out, Seed seed) {
     // taken in ascending order, so repeated uses of one node push in order.
     std::vector<char> served(np, 0);
     auto wants = [&](int j) {
-      return t->nodes[n.parents[j]].needs_grad && !(n.op == XT_OP_CROSS_ENTROPY && j == 1);
+      return t->nodes[n.parents[j]].needs_grad && !((n.op == XT_OP_CROSS_ENTROPY || n.op == XT_OP_EMBED) && j == 1);
     };
     for (int k = 0; k < np && s == XT_OK; ++k) {
       if (served[k] || !wants(k)) continue;

@@ -16,7 +16,9 @@ batch of synthetic input, each at the shape its workload names:
     SwiGLU 688, vocab 4096, f32) recorded on the tape, fwd+bwd;
   * after the backward: the global gradient norm and the clip scaling over
     every gradient buffer of a 12-layer model of GPT-2-small width (about
-    124M f32 in 124 tensors).
+    124M f32 in 124 tensors);
+  * the token embedding of the same model: 8 x 1024 Zipf(1.1)-distributed
+    tokens into a 50257 x 768 f32 table, gather and scatter-add backward.
 Inputs are drawn on the GPU before timing (torch's seeded generator).
 
 `value` is the step's algorithmic HBM bytes / step time (GB/s): what the
@@ -355,11 +357,33 @@ def build_entries(only):
         E.append(Entry("f3.grads_scale", W, "f32", "hbm",
                        lambda: xt.xt_grads_scale(gv, 1.0, one.data_ptr()), 8 * n, rows=len(gr)))
 
+    def f2():
+        nonlocal keep
+        if not want("f2"):
+            return
+        # token embedding at the GPT-2-small shape: 8 x 1024 Zipf(1.1) tokens
+        # into a 50257 x 768 f32 table
+        import synth
+        Vv, Dd, Rr = 50257, 768, 8192
+        tab = device_normal((Vv, Dd), 10, "emb", 0.0, 0.02)
+        ids = torch.from_numpy(synth.host_zipf_int((Rr, 1), Vv, 1.1, 10, "ids")).cuda()
+        y, d, dE = empty((Rr, Dd), "f32"), device_normal((Rr, Dd), 10, "dout"), empty((Vv, Dd), "f32")
+        keep += [tab, ids, y, d, dE]
+        ins = [V(tab), V(ids)]
+        wsp, wsn = ws(xt.OP.EMBED, P(), ins)
+        W = "gpt2s-f32 embedding 8192 tokens x 50257 x 768"
+        E.append(Entry("f2.embed.fwd", W, "f32", "hbm", lambda: xt.xt_op_fwd(xt.OP.EMBED, P(), ins, [V(y)]),
+                       2 * 4 * Rr * Dd + 4 * Rr, rows=Rr))
+        E.append(Entry("f2.embed.bwd", W, "f32", "hbm", lambda: xt.xt_op_bwd(
+            xt.OP.EMBED, P(), V(d), ins, [], [V(dE), nullslot(ids)], 0, wsp, wsn),
+            4 * Rr * Dd + 4 * Vv * Dd + 4 * Rr, rows=Rr))
+
     c3()
     c4()
     c5()
     c2()
     f3()
+    f2()
     return E, keep
 
 
@@ -592,7 +616,8 @@ def main():
         "dtype": "f32+bf16", "data": "synthetic",
         "config": {"workload": "hot-path suite: every op fwd+bwd at the gpt2s-f32 8x1024x768, bf16 16384x4096 and "
                                "bf16-stress shapes, the tiny transformer block on the tape, and the global "
-                               "gradient norm and clip scaling over a 12-layer gpt2s-width gradient set",
+                               "gradient norm and clip scaling over a 12-layer gpt2s-width gradient set, and the gpt2s token "
+                               "embedding fwd+bwd",
                    "parallelism": "none (1 GPU)"},
         "memory_bound_GBps": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1) if hbm_ms else None,
         "memory_bound_frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if hbm_ms else None,

@@ -89,7 +89,8 @@ typedef enum {
   XT_OP_GELU = 11,         /* y = x * Phi(x) (erf form; tanh form if set)  */
   XT_OP_ROPE = 12,         /* rotate-half rotary embedding                 */
   XT_OP_DROPOUT = 13,      /* counter-based inverted dropout               */
-  XT_OP_COUNT = 14
+  XT_OP_EMBED = 14,        /* y[r,:] = E[ids[r],:] (token embedding)       */
+  XT_OP_COUNT = 15
 } xt_op;
 
 typedef struct {
@@ -128,6 +129,17 @@ typedef struct {
  *  SWIGLU        g, u               y                            dg, du
  *  ROPE          x                  y                            dx
  *  DROPOUT       x                  y, mask[R,C] u8 (1 = keep)   dx
+ *  EMBED         E[V,D], ids[R,1]   y[R,D] (E's dtype)           dE (+ a NULL
+ *                i32                                             slot for ids)
+ *
+ * EMBED: [BP] kernel pairs (k_embed_fwd / k_embed_bwd) and the forward of
+ * "Framåtgåendet" (x = embed(token_ids)); the tied output projection
+ * LN(x) @ E^T is a MATMUL with trans_b on the same table.  An id outside
+ * [0, V) gives a NaN output row and contributes nothing to dE.  dE[v] is
+ * the sum of d over the rows with id v (f32: sums of 32 consecutive rows
+ * of the id, in row order, added in order; one rounding into dE); it needs
+ * workspace (24 bytes per row and 8 D bytes per 32 rows) and is bitwise
+ * reproducible.
  *
  * Backward "saved" lists: MATMUL none (reads in); RMS_NORM {inv_rms};
  * LAYER_NORM {mean, rstd}; SOFTMAX {y}; CROSS_ENTROPY {lse}; DROPOUT {mask};
@@ -143,7 +155,8 @@ typedef struct {
 /* Bytes of workspace xt_op_fwd (is_bwd = 0) or xt_op_bwd (is_bwd = 1) needs
  * for these inputs; 0 if none.  Ops that need workspace: the backward of
  * RMS_NORM, LAYER_NORM and ADD_BIAS (per-block partial parameter
- * gradients, summed by a fixed-order second pass). */
+ * gradients, summed by a fixed-order second pass) and of EMBED (sorted
+ * (id, row) keys); the MATMUL forward and backward when split-K pays. */
 size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm,
                           const xt_tensor* in, int n_in);
 

@@ -110,6 +110,13 @@ class Tape:
         return self._push(ops.rope(self._v(x), head_dim, base, seq_len), [x],
                           lambda d: [ops.rope_bwd(d, head_dim, base, seq_len)])
 
+    def embed(self, table, ids):
+        """Token embedding ([BP] k_embed_fwd / k_embed_bwd); ids are data,
+        not a node."""
+        E = self._v(table)
+        t = np.asarray(ids).reshape(-1)
+        return self._push(ops.embed(E, t), [table], lambda d: [ops.embed_bwd(d, t, E.shape[0])])
+
     def dropout(self, x, p, seed):
         if p == 0.0:                     # [DO]: p == 0 records nothing
             return x

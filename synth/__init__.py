@@ -22,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "host_normal", "host_uniform_int", "host_bf16_bits", "bf16_bits_to_f32",
+    "host_normal", "host_uniform_int", "host_zipf_int", "host_bf16_bits", "bf16_bits_to_f32",
     "device_normal", "device_uniform_int", "STREAMS",
 ]
 
@@ -32,7 +32,7 @@ STREAMS = {
     "x": 1, "gamma": 2, "beta": 3, "bias": 4, "targets": 5, "dout": 6,
     "g": 7, "u": 8, "a": 9, "b": 10, "w": 11, "logits": 12, "q": 13, "k": 14,
     "v": 15, "resid": 16, "d2": 17, "d3": 18, "wq": 20, "wk": 21, "wv": 22,
-    "wo": 23, "wg": 24, "wu": 25, "wd": 26, "wout": 27, "w1": 28, "w2": 29,
+    "wo": 23, "wg": 24, "wu": 25, "wd": 26, "wout": 27, "w1": 28, "w2": 29, "ids": 30, "emb": 31,
 }
 
 
@@ -80,6 +80,14 @@ def host_uniform_int(shape, low: int, high: int, seed: int, stream) -> np.ndarra
     """Uniform int32 in [low, high) from stream ``(seed, stream)``."""
     g = np.random.default_rng([int(seed), _stream(stream)])
     return g.integers(low, high, size=shape, dtype=np.int64).astype(np.int32)
+
+
+def host_zipf_int(shape, vocab: int, a: float, seed: int, stream) -> np.ndarray:
+    """Token ids with a Zipf(a) rank distribution folded into [0, vocab)
+    (rank k -> id (k - 1) mod vocab), int32, from stream ``(seed, stream)``:
+    a few ids repeat very often, most rarely, as in text."""
+    g = np.random.default_rng([int(seed), _stream(stream)])
+    return ((g.zipf(a, size=shape) - 1) % vocab).astype(np.int32)
 
 
 def _torch_gen(seed: int, stream, device):
