@@ -386,3 +386,63 @@ def embed_bwd(d, ids, vocab: int):
         if 0 <= v < vocab:
             dE[v] += D_[r]
     return dE
+
+
+# --------------------------------------------------------------------------
+# Fused attention -- [AE] "Attention 用组合": attention is
+# softmax(scale(Q K^T, alpha) [+ causal]) V, whose backward the tape derives
+# from the matmul and softmax rows of the op-backward table.  The fused form
+# computes the same thing per (sequence, head) without materialising the
+# probabilities; its saved row statistic is the log-sum-exp of the scaled,
+# masked scores (the softmax normaliser), from which the backward rebuilds
+# the probabilities.
+# Layout (a reading): q, k, v and the output are [B*S, H*Dh] matrices, row
+# b*S + s holding token s of sequence b, columns h*Dh .. h*Dh+Dh-1 head h;
+# the log-sum-exp is [B*S, H].  Causal: key t is visible to query s iff
+# t <= s.
+# --------------------------------------------------------------------------
+def _heads(x, S, H, Dh):
+    X = _f(x)
+    B = X.shape[0] // S
+    return X.reshape(B, S, H, Dh).transpose(0, 2, 1, 3)          # [B, H, S, Dh]
+
+
+def _unheads(x):
+    B, H, S, Dh = x.shape
+    return x.transpose(0, 2, 1, 3).reshape(B * S, H * Dh)
+
+
+def attention(q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float, causal: bool = True):
+    """Returns (out [B*S, H*Dh], lse [B*S, H])."""
+    Q, K, Vv = (_heads(t, seq_len, heads, head_dim) for t in (q, k, v))
+    Z = alpha * np.matmul(Q, np.swapaxes(K, -1, -2))               # [B, H, S, S]
+    if causal:
+        keep = np.arange(seq_len)[None, :] <= np.arange(seq_len)[:, None]
+        Z = np.where(keep, Z, -np.inf)
+    m = np.max(Z, axis=-1, keepdims=True)
+    e = np.exp(Z - m)
+    s = np.sum(e, axis=-1, keepdims=True)
+    P = e / s
+    lse = (m + np.log(s))[..., 0]                                  # [B, H, S]
+    out = _unheads(np.matmul(P, Vv))
+    return out, lse.transpose(0, 2, 1).reshape(-1, heads)
+
+
+def attention_bwd(d, q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float, causal: bool = True):
+    """(dq, dk, dv) by the composition's chain rule: P = softmax(alpha Q K^T),
+    dV = P^T dO, dP = dO V^T, dZ = P (dP - rowsum(dP P)), dQ = alpha dZ K,
+    dK = alpha dZ^T Q."""
+    Q, K, Vv = (_heads(t, seq_len, heads, head_dim) for t in (q, k, v))
+    dO = _heads(d, seq_len, heads, head_dim)
+    Z = alpha * np.matmul(Q, np.swapaxes(K, -1, -2))
+    if causal:
+        keep = np.arange(seq_len)[None, :] <= np.arange(seq_len)[:, None]
+        Z = np.where(keep, Z, -np.inf)
+    e = np.exp(Z - np.max(Z, axis=-1, keepdims=True))
+    P = e / np.sum(e, axis=-1, keepdims=True)
+    dV = np.matmul(np.swapaxes(P, -1, -2), dO)
+    dP = np.matmul(dO, np.swapaxes(Vv, -1, -2))
+    dZ = P * (dP - np.sum(dP * P, axis=-1, keepdims=True))
+    dQ = alpha * np.matmul(dZ, K)
+    dK = alpha * np.matmul(np.swapaxes(dZ, -1, -2), Q)
+    return _unheads(dQ), _unheads(dK), _unheads(dV)

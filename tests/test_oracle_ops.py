@@ -365,3 +365,44 @@ def test_embed_out_of_range_ids():
     np.testing.assert_array_equal(y[[0, 3]], E[[0, 3]])
     dE = ops.embed_bwd(np.ones((4, 3)), [0, 4, -1, 0], 4)
     np.testing.assert_array_equal(dE, [[2, 2, 2], [0, 0, 0], [0, 0, 0], [0, 0, 0]])
+
+
+# --------------------------------------------------------- fused attention
+def _compose_attention(q, k, v, S, H, Dh, alpha):
+    """The [AE] composition with the separately pinned ops, per (b, h)."""
+    B = q.shape[0] // S
+    out = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            rs, cs = slice(b * S, (b + 1) * S), slice(h * Dh, (h + 1) * Dh)
+            P = ops.softmax(ops.matmul(q[rs, cs], k[rs, cs], trans_b=True), alpha, True, S)
+            out[rs, cs] = ops.matmul(P, v[rs, cs])
+    return out
+
+
+def test_attention_equals_the_composition_and_closed_forms():
+    S, H, Dh, B = 7, 2, 4, 3
+    q, k, v = rnd(B * S, H * Dh), rnd(B * S, H * Dh), rnd(B * S, H * Dh)
+    o, lse = ops.attention(q, k, v, S, H, Dh, 0.5)
+    np.testing.assert_allclose(o, _compose_attention(q, k, v, S, H, Dh, 0.5), rtol=1e-13, atol=1e-13)
+    # the first token attends to itself only: out = v there
+    for b in range(B):
+        np.testing.assert_allclose(o[b * S], v[b * S], rtol=1e-14)
+    # q = 0: uniform over the causal prefix, lse = log(s + 1)
+    o0, l0 = ops.attention(np.zeros_like(q), k, v, S, H, Dh, 0.5)
+    for b in range(B):
+        for s in range(S):
+            np.testing.assert_allclose(o0[b * S + s], v[b * S: b * S + s + 1].mean(axis=0), rtol=1e-13, atol=1e-14)
+            np.testing.assert_allclose(l0[b * S + s], math.log(s + 1), rtol=1e-14)
+    # lse by its definition on one (b, h, s)
+    b, h, s = 1, 1, 5
+    z = 0.5 * k[b * S: b * S + s + 1, h * Dh:(h + 1) * Dh] @ q[b * S + s, h * Dh:(h + 1) * Dh]
+    assert abs(lse[b * S + s, h] - math.log(np.sum(np.exp(z)))) < 1e-13
+
+
+def test_attention_bwd_fd():
+    S, H, Dh, B = 5, 2, 3, 2
+    q, k, v = rnd(B * S, H * Dh), rnd(B * S, H * Dh), rnd(B * S, H * Dh)
+    W = rnd(B * S, H * Dh)
+    f = lambda q_, k_, v_: ops.attention(q_, k_, v_, S, H, Dh, 0.7)[0]  # noqa: E731
+    check_fd(f, list(ops.attention_bwd(W, q, k, v, S, H, Dh, 0.7)), [q, k, v], W)
