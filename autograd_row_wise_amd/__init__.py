@@ -35,7 +35,7 @@ class DT:
 
 class OP:
     MATMUL, ADD, MUL, SCALE, ADD_BIAS, RMS_NORM, LAYER_NORM, SOFTMAX, CROSS_ENTROPY, \
-        SILU, SWIGLU, GELU, ROPE, DROPOUT, EMBED = range(15)
+        SILU, SWIGLU, GELU, ROPE, DROPOUT, EMBED, ATTENTION = range(16)
 
 
 class Tensor(C.Structure):

@@ -65,9 +65,15 @@ def attention(tape: Tape, q: int, k: int, v: int, B: int, S: int, H: int, Dh: in
     return tape.view(out, layout(B * S, D, D, dtype))
 
 
+def fused_attention(tape: Tape, q: int, k: int, v: int, S: int, Dh: int, causal: bool = True) -> int:
+    """The same attention as one fused op (no [S, S] probabilities stored)."""
+    return tape.apply(OP.ATTENTION, params(alpha=1.0 / math.sqrt(Dh), causal=int(causal), seq_len=S, head_dim=Dh),
+                      q, k, v)
+
+
 def block_layer(tape: Tape, w: dict, x: int, shp: BlockShape, dtype: int, p_drop: float = 0.0,
                 base_seed: int = 0, layer_index: int = 0, eps: float = 1e-5, checkpoint: bool = False,
-                taps: dict | None = None) -> int:
+                taps: dict | None = None, fused_attention_op: bool = False) -> int:
     """Records the two residual halves of one layer; returns h2.  With
     `checkpoint`, the layer is one recompute segment whose output is h2.
     `taps` (optional) receives the vars of n1 and of the two dropout nodes."""
@@ -79,7 +85,9 @@ def block_layer(tape: Tape, w: dict, x: int, shp: BlockShape, dtype: int, p_drop
     q = tape.apply(OP.ROPE, rope, tape.apply(OP.MATMUL, mm, n1, w["wq"]))
     k = tape.apply(OP.ROPE, rope, tape.apply(OP.MATMUL, mm, n1, w["wk"]))
     v = tape.apply(OP.MATMUL, mm, n1, w["wv"])
-    a = tape.apply(OP.MATMUL, mm, attention(tape, q, k, v, shp.B, shp.S, shp.H, shp.Dh, dtype), w["wo"])
+    att = (fused_attention(tape, q, k, v, shp.S, shp.Dh) if fused_attention_op
+           else attention(tape, q, k, v, shp.B, shp.S, shp.H, shp.Dh, dtype))
+    a = tape.apply(OP.MATMUL, mm, att, w["wo"])
     a = tape.apply(OP.DROPOUT, params(p=p_drop, seed=base_seed ^ layer_index ^ SITE_ATTN), a)
     h = tape.apply(OP.ADD, params(), x, a)
     n2 = tape.apply(OP.RMS_NORM, params(eps=eps), h, w["g2"])
@@ -97,10 +105,11 @@ def block_layer(tape: Tape, w: dict, x: int, shp: BlockShape, dtype: int, p_drop
 
 def block(tape: Tape, w: dict, x: int, targets: int, shp: BlockShape, dtype: int,
           p_drop: float = 0.0, base_seed: int = 0, layer: int = 0, eps: float = 1e-5,
-          checkpoint: bool = False) -> int:
+          checkpoint: bool = False, fused_attention: bool = False) -> int:
     """Records the block; `w` maps g1 g2 g3 wq wk wv wo wg wu wd wout to leaf vars.
     Returns the loss var."""
-    h2 = block_layer(tape, w, x, shp, dtype, p_drop, base_seed, layer, eps, checkpoint)
+    h2 = block_layer(tape, w, x, shp, dtype, p_drop, base_seed, layer, eps, checkpoint,
+                     fused_attention_op=fused_attention)
     logits = tape.apply(OP.MATMUL, params(), tape.apply(OP.RMS_NORM, params(eps=eps), h2, w["g3"]), w["wout"])
     return tape.apply(OP.CROSS_ENTROPY, params(), logits, targets)
 

@@ -183,6 +183,35 @@ const char* xt_last_error(void) { return g_err.c_str(); }
 
 int xt_abi_version(void) { return 1; }
 
+// Fused attention: q, k, v (and every [R, H*Dh] tensor passed with them)
+// share shape, dtype and row stride; fills the geometry of `a`.
+xt_status check_attention(const xt_params* prm, const xt_tensor* in, AttnArgs& a) {
+  XT_TRY(check_act(&in[0], "q"));
+  XT_TRY(check_like(&in[1], in[0], "k"));
+  XT_TRY(check_like(&in[2], in[0], "v"));
+  if (in[1].ld != in[0].ld || in[2].ld != in[0].ld) return fail(XT_ERR_SHAPE, "attention: q, k, v must share a row stride");
+  const int Dh = prm->head_dim;
+  if (Dh != 32 && Dh != 64 && Dh != 128) return fail(XT_ERR_UNSUPPORTED, "attention head_dim must be 32, 64 or 128");
+  if (in[0].cols % Dh) return fail(XT_ERR_SHAPE, "attention: cols must be a multiple of head_dim");
+  if (prm->seq_len <= 0) return fail(XT_ERR_INVALID_ARG, "attention needs seq_len > 0");
+  if (in[0].rows % prm->seq_len) return fail(XT_ERR_SHAPE, "attention: rows must be a multiple of seq_len");
+  if (prm->causal != 0 && prm->causal != 1) return fail(XT_ERR_INVALID_ARG, "attention causal must be 0 or 1");
+  a = AttnArgs{};
+  a.q = in[0].data; a.k = in[1].data; a.v = in[2].data;
+  a.S = prm->seq_len; a.B = in[0].rows / prm->seq_len; a.H = in[0].cols / Dh; a.Dh = Dh; a.ld = in[0].ld;
+  if (a.B > 65535 || a.H > 65535) return fail(XT_ERR_UNSUPPORTED, "attention: at most 65535 sequences and heads");
+  a.alpha = prm->alpha;
+  a.causal = prm->causal;
+  a.bf16 = in[0].dtype == XT_BF16;
+  return XT_OK;
+}
+
+xt_status check_lse(const xt_tensor* t, const AttnArgs& a) {
+  XT_TRY(check_view(t, "lse"));
+  if (t->dtype != XT_F32 || t->rows != a.B * a.S || t->cols != a.H) return fail(XT_ERR_SHAPE, "lse must be [R, H] f32");
+  return XT_OK;
+}
+
 size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm, const xt_tensor* in, int n_in) {
   if (!in || n_in < 1) return 0;
   if (op == XT_OP_MATMUL) return matmul_ws(prm, in, n_in, is_bwd);
@@ -193,6 +222,8 @@ size_t xt_workspace_bytes(xt_op op, int is_bwd, const xt_params* prm, const xt_t
     case XT_OP_LAYER_NORM: return row_ws_bound(RK_LN_BWD, in[0].dtype, R, C);
     case XT_OP_ADD_BIAS: return colsum_workspace(in[0].dtype, R, C);
     case XT_OP_EMBED: return n_in >= 2 ? embed_bwd_workspace(in[1].rows, in[0].cols) : 0;
+    case XT_OP_ATTENTION:
+      return prm && prm->head_dim > 0 && R > 0 ? (size_t)R * (size_t)(C / prm->head_dim) * sizeof(float) : 0;
     default: return 0;
   }
 }
@@ -327,6 +358,18 @@ xt_status xt_op_fwd(xt_op op, const xt_params* prm, const xt_tensor* in, int n_i
         mask = &out[1];
       }
       return hip_status(launch_dropout_fwd(in[0], out[0], mask, dropout_thr(prm->p), dropout_scale(prm->p), prm->seed, s), "dropout");
+    }
+    case XT_OP_ATTENTION: {
+      XT_TRY(need(3, 2));
+      AttnArgs a;
+      XT_TRY(check_attention(prm, in, a));
+      XT_TRY(check_like(&out[0], in[0], "out"));
+      if (out[0].ld != in[0].ld) return fail(XT_ERR_SHAPE, "attention: out must share q's row stride");
+      XT_TRY(check_lse(&out[1], a));
+      a.out = out[0].data;
+      a.lse = (float*)out[1].data;
+      a.ldl = out[1].ld;
+      return hip_status(launch_attention_fwd(a, s), "attention");
     }
     case XT_OP_EMBED: {
       XT_TRY(need(2, 1));
@@ -539,6 +582,32 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
       if (!wanted(din, n_din, 0)) return XT_OK;
       XT_TRY(check_like(&din[0], *dout, "dx"));
       return hip_status(launch_dropout_bwd(*dout, saved[0], din[0], acc(0), dropout_scale(prm->p), s), "dropout backward");
+    }
+    case XT_OP_ATTENTION: {
+      XT_TRY(need(3, 2, 3));
+      AttnArgs a;
+      XT_TRY(check_attention(prm, in, a));
+      XT_TRY(check_like(dout, in[0], "dout"));
+      XT_TRY(check_like(&saved[0], in[0], "out"));
+      if (dout->ld != in[0].ld || saved[0].ld != in[0].ld) return fail(XT_ERR_SHAPE, "attention: dout and out must share q's row stride");
+      XT_TRY(check_lse(&saved[1], a));
+      for (int i = 0; i < 3; ++i) {
+        if (!wanted(din, n_din, i)) continue;
+        XT_TRY(check_like(&din[i], in[0], i == 0 ? "dq" : i == 1 ? "dk" : "dv"));
+        if (din[i].ld != in[0].ld) return fail(XT_ERR_SHAPE, "attention: gradients must share q's row stride");
+      }
+      if (!wanted(din, n_din, 0) && !wanted(din, n_din, 1) && !wanted(din, n_din, 2)) return XT_OK;
+      if (ws_need && (!ws || ws_bytes < ws_need)) return fail(XT_ERR_WORKSPACE, "attention backward needs %zu bytes of workspace", ws_need);
+      a.out = saved[0].data;
+      a.lse = (float*)saved[1].data;
+      a.ldl = saved[1].ld;
+      a.dout = dout->data;
+      a.dd = (float*)ws;
+      a.dq = wanted(din, n_din, 0) ? din[0].data : nullptr;
+      a.dk = wanted(din, n_din, 1) ? din[1].data : nullptr;
+      a.dv = wanted(din, n_din, 2) ? din[2].data : nullptr;
+      a.acc_dq = acc(0); a.acc_dk = acc(1); a.acc_dv = acc(2);
+      return hip_status(launch_attention_bwd(a, s), "attention backward");
     }
     case XT_OP_EMBED: {
       if (n_in != 2 || n_saved != 0 || n_din < 1 || n_din > 2)

@@ -112,6 +112,27 @@ hipError_t launch_embed_fwd(const xt_tensor& E, const int32_t* ids, int64_t ldi,
 hipError_t launch_embed_bwd(const xt_tensor& d, const int32_t* ids, int64_t ldi, const xt_tensor& dE, bool acc,
                             void* ws, hipStream_t s);
 
+// attention.hip: fused (flash-style) attention over [B*S, H*Dh] q, k, v.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;          // forward output; read by the backward (D = rowsum(dO * O))
+  float* lse;         // [B*S, H] log-sum-exp, row stride ldl
+  const void* dout;   // backward
+  float* dd;          // backward workspace: [B*S, H] f32
+  void* dq;
+  void* dk;
+  void* dv;
+  int acc_dq, acc_dk, acc_dv;
+  int64_t B, S, H, Dh, ld, ldl;
+  float alpha;
+  int causal;
+  bool bf16;
+};
+hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_bwd(const AttnArgs& a, hipStream_t s);
+
 // gradbuf.hip: global gradient norm (two passes through `part`, f64 per
 // work unit) and in-place scaling / zeroing of a list of gradient tensors.
 int64_t grad_norm_units(const xt_tensor* g, int n);

@@ -236,6 +236,11 @@ xt_status out_shapes(xt_op op, const xt_params& prm, const std::vector<const xt_
     case XT_OP_EMBED:
       outs.push_back(dense(nullptr, x.dtype, in[1]->rows, x.cols));
       return XT_OK;
+    case XT_OP_ATTENTION:
+      if (prm.head_dim <= 0) return XT_ERR_INVALID_ARG;
+      outs.push_back(dense(nullptr, x.dtype, x.rows, x.cols));
+      outs.push_back(dense(nullptr, XT_F32, x.rows, x.cols / prm.head_dim));
+      return XT_OK;
     case XT_OP_CROSS_ENTROPY:
       outs.push_back(dense(nullptr, XT_F32, 1, 1));
       outs.push_back(dense(nullptr, XT_F32, x.rows, 1));
@@ -262,6 +267,7 @@ std::vector<xt_tensor> saved_of(const Node& n) {
     case XT_OP_SOFTMAX: return {n.value};
     case XT_OP_CROSS_ENTROPY: return {n.extra[0]};
     case XT_OP_DROPOUT: return {n.extra[0]};
+    case XT_OP_ATTENTION: return {n.value, n.extra[0]};
     default: return {};
   }
 }

@@ -18,7 +18,9 @@ batch of synthetic input, each at the shape its workload names:
     every gradient buffer of a 12-layer model of GPT-2-small width (about
     124M f32 in 124 tensors);
   * the token embedding of the same model: 8 x 1024 Zipf(1.1)-distributed
-    tokens into a 50257 x 768 f32 table, gather and scatter-add backward.
+    tokens into a 50257 x 768 f32 table, gather and scatter-add backward;
+  * fused causal attention fwd+bwd: 2 x 2048 tokens, 16 heads x 128, bf16
+    storage (f32 arithmetic on the matrix cores).
 Inputs are drawn on the GPU before timing (torch's seeded generator).
 
 `value` is the step's algorithmic HBM bytes / step time (GB/s): what the
@@ -311,13 +313,13 @@ def build_entries(only):
             keep += list(Wt.values()) + [bx2, bt2]
             holder = {}
 
-            def run_block(ckpt=False, key="tape"):
+            def run_block(ckpt=False, key="tape", fused=False):
                 if key in holder:
                     holder[key].close()
                 t = xt.Tape()
                 w = xb.leaves(t, Wt)
                 loss = xb.block(t, w, t.leaf(V(bx2)), t.leaf(V(bt2), requires_grad=False), shp, xt.DT.F32,
-                                checkpoint=ckpt)
+                                checkpoint=ckpt, fused_attention=fused)
                 t.backward(loss)
                 holder[key] = t
             # GEMM flops of one fwd+bwd (for the record; the block is launch/cache bound)
@@ -330,6 +332,9 @@ def build_entries(only):
             # twice (the GEMM flops of the record count it once)
             E.append(Entry("c2.block.fwdbwd_recompute", "tiny block 4x256x256 f32", "f32", "block",
                            lambda: run_block(True, "tape_ckpt"), 0, 3 * fl, shp.B * shp.S))
+            # the same block with the fused attention op
+            E.append(Entry("c2.block.fwdbwd_fused_attention", "tiny block 4x256x256 f32", "f32", "block",
+                           lambda: run_block(False, "tape_fused", True), 0, 3 * fl, shp.B * shp.S))
     def f3():
         nonlocal keep
         if not want("f3"):
@@ -378,12 +383,40 @@ def build_entries(only):
             xt.OP.EMBED, P(), V(d), ins, [], [V(dE), nullslot(ids)], 0, wsp, wsn),
             4 * Rr * Dd + 4 * Vv * Dd + 4 * Rr, rows=Rr))
 
+    def f1():
+        nonlocal keep
+        if not want("f1"):
+            return
+        # fused causal attention: 2 sequences x 2048 tokens, 16 heads x 128,
+        # bf16 storage, f32 arithmetic on the matrix cores
+        B1, S1, H1, D1 = 2, 2048, 16, 128
+        R1, C1 = B1 * S1, H1 * D1
+        q = device_normal((R1, C1), 12, "q", dtype="bf16")
+        k = device_normal((R1, C1), 12, "k", dtype="bf16")
+        v = device_normal((R1, C1), 12, "v", dtype="bf16")
+        d = device_normal((R1, C1), 12, "dout", dtype="bf16")
+        out, lse = empty((R1, C1), "bf16"), empty((R1, H1), "f32")
+        dq, dk, dv = empty((R1, C1), "bf16"), empty((R1, C1), "bf16"), empty((R1, C1), "bf16")
+        keep += [q, k, v, d, out, lse, dq, dk, dv]
+        prm = P(alpha=1.0 / math.sqrt(D1), causal=1, seq_len=S1, head_dim=D1)
+        ins = [V(q), V(k), V(v)]
+        wsp, wsn = ws(xt.OP.ATTENTION, prm, ins)
+        # causal: half of the S x S scores; two products forward, five backward
+        prod = 2.0 * S1 * S1 * D1 * B1 * H1 / 2
+        W = "attention 2x2048 tokens, 16 heads x 128, causal, bf16 storage"
+        E.append(Entry("f1.attn.fwd", W, "f32", "mfma", lambda: xt.xt_op_fwd(
+            xt.OP.ATTENTION, prm, ins, [V(out), V(lse)]), 4 * 2 * R1 * C1, 2 * prod, R1))
+        E.append(Entry("f1.attn.bwd", W, "f32", "mfma", lambda: xt.xt_op_bwd(
+            xt.OP.ATTENTION, prm, V(d), ins, [V(out), V(lse)], [V(dq), V(dk), V(dv)], 0, wsp, wsn),
+            2 * 8 * R1 * C1, 5 * prod, R1))
+
     c3()
     c4()
     c5()
     c2()
     f3()
     f2()
+    f1()
     return E, keep
 
 
@@ -616,8 +649,8 @@ def main():
         "dtype": "f32+bf16", "data": "synthetic",
         "config": {"workload": "hot-path suite: every op fwd+bwd at the gpt2s-f32 8x1024x768, bf16 16384x4096 and "
                                "bf16-stress shapes, the tiny transformer block on the tape, and the global "
-                               "gradient norm and clip scaling over a 12-layer gpt2s-width gradient set, and the gpt2s token "
-                               "embedding fwd+bwd",
+                               "gradient norm and clip scaling over a 12-layer gpt2s-width gradient set, the gpt2s token "
+                               "embedding fwd+bwd and fused causal attention 2x2048x16x128",
                    "parallelism": "none (1 GPU)"},
         "memory_bound_GBps": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1) if hbm_ms else None,
         "memory_bound_frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if hbm_ms else None,

@@ -90,7 +90,8 @@ typedef enum {
   XT_OP_ROPE = 12,         /* rotate-half rotary embedding                 */
   XT_OP_DROPOUT = 13,      /* counter-based inverted dropout               */
   XT_OP_EMBED = 14,        /* y[r,:] = E[ids[r],:] (token embedding)       */
-  XT_OP_COUNT = 15
+  XT_OP_ATTENTION = 15,    /* softmax(alpha Q K^T [+ causal]) V, fused     */
+  XT_OP_COUNT = 16
 } xt_op;
 
 typedef struct {
@@ -131,6 +132,7 @@ typedef struct {
  *  DROPOUT       x                  y, mask[R,C] u8 (1 = keep)   dx
  *  EMBED         E[V,D], ids[R,1]   y[R,D] (E's dtype)           dE (+ a NULL
  *                i32                                             slot for ids)
+ *  ATTENTION     q, k, v [R, H*Dh]  out [R, H*Dh], lse [R, H] f32  dq, dk, dv
  *
  * EMBED: [BP] kernel pairs (k_embed_fwd / k_embed_bwd) and the forward of
  * "Framåtgåendet" (x = embed(token_ids)); the tied output projection
@@ -141,8 +143,19 @@ typedef struct {
  * workspace (24 bytes per row and 8 D bytes per 32 rows) and is bitwise
  * reproducible.
  *
+ * ATTENTION: [AE] "Attention 用组合" computed without materialising the
+ * probabilities.  R = B*S rows (row b*S + s = token s of sequence b), head h
+ * in columns h*Dh ..; head_dim = Dh in {32, 64, 128}, seq_len = S (R a
+ * multiple of S), alpha = the score scale (1/sqrt(Dh) usually), causal =
+ * key t visible to query s iff t <= s.  q, k, v, out, dout and the
+ * gradients share one row stride.  lse[r, h] is the log-sum-exp of the
+ * scaled, masked scores of that query; the backward rebuilds the
+ * probabilities from it and needs R*H*4 bytes of workspace.  Arithmetic is
+ * f32 (MFMA 32x32x2 f32) for f32 and bf16 storage.  Bitwise reproducible.
+ *
  * Backward "saved" lists: MATMUL none (reads in); RMS_NORM {inv_rms};
  * LAYER_NORM {mean, rstd}; SOFTMAX {y}; CROSS_ENTROPY {lse}; DROPOUT {mask};
+ * ATTENTION {out, lse};
  * every other op none.  `dout` is the gradient of out[0] (for
  * CROSS_ENTROPY: a device f32[1,1] holding dL).
  *

@@ -1,0 +1,139 @@
+"""GPU parity of the fused attention (XT_OP_ATTENTION) through the C ABI
+against the oracle: output, log-sum-exp and the three gradients, causal and
+not, Dh 32 / 64 / 128, sequence lengths that leave ragged 32-row tiles, f32
+and bf16 storage, accumulate mode, bitwise reproducibility; and the fused op
+on the tape inside the tiny block against the composed attention."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import ops
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if True:  # GPU-only imports are deferred so CPU collection never loads libxt
+    try:
+        import torch
+        import autograd_row_wise_amd as xt
+        from xt_testutil import close, dev, host
+    except Exception:  # pragma: no cover - CPU host without the library
+        pass
+
+
+def put(a, dtype):
+    bits = synth.host_bf16_bits(a) if dtype == "bf16" else a.astype(np.float32)
+    vals = synth.bf16_bits_to_f32(bits).astype(np.float64) if dtype == "bf16" else bits.astype(np.float64)
+    return dev(bits, dtype), vals
+
+
+def norm_close(got, ref, tol, what):
+    """Element-wise at `tol` of the tensor's largest magnitude: every entry is
+    a sum over up to S keys and Dh features."""
+    err = np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30)
+    assert err <= tol, (what, err)
+
+
+CASES = [  # B, S, H, Dh, causal, dtype
+    (2, 40, 2, 32, 1, "f32"),
+    (1, 256, 4, 64, 1, "f32"),
+    (3, 77, 1, 64, 0, "f32"),
+    (1, 100, 2, 128, 1, "f32"),
+    (2, 130, 2, 64, 1, "bf16"),
+    (1, 64, 3, 128, 0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,S,H,Dh,causal,dtype", CASES)
+def test_attention_fwd_bwd(B, S, H, Dh, causal, dtype):
+    R, C = B * S, H * Dh
+    alpha = 1.0 / math.sqrt(Dh)
+    q, qv = put(synth.host_normal((R, C), 11, "q"), dtype)
+    k, kv = put(synth.host_normal((R, C), 11, "k"), dtype)
+    v, vv = put(synth.host_normal((R, C), 11, "v"), dtype)
+    d, dv = put(synth.host_normal((R, C), 11, "dout"), dtype)
+    prm = xt.params(alpha=alpha, causal=causal, seq_len=S, head_dim=Dh)
+    out = torch.empty((R, C), dtype=q.dtype, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    ins = [xt.view(q), xt.view(k), xt.view(v)]
+    xt.xt_op_fwd(xt.OP.ATTENTION, prm, ins, [xt.view(out), xt.view(lse)])
+    torch.cuda.synchronize()
+    o_ref, l_ref = ops.attention(qv, kv, vv, S, H, Dh, alpha, bool(causal))
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    norm_close(host(out), o_ref, tol, "out")
+    np.testing.assert_allclose(host(lse), l_ref, rtol=1e-5, atol=1e-5)
+    grads = [torch.empty((R, C), dtype=q.dtype, device="cuda") for _ in range(3)]
+    w, wp, wb = xt.workspace(xt.OP.ATTENTION, 1, prm, ins)
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(d), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in grads], 0, wp, wb)
+    torch.cuda.synchronize()
+    # the oracle's backward reads the stored output the kernel read
+    refs = ops.attention_bwd(dv, qv, kv, vv, S, H, Dh, alpha, bool(causal))
+    got = [host(g) for g in grads]
+    for name, g, r in zip(("dq", "dk", "dv"), got, refs):
+        norm_close(g, r, 1e-5 if dtype == "f32" else 3e-2, name)
+    # bitwise reproducible; accumulate adds onto what is there
+    again = [torch.zeros_like(g) for g in grads]
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(d), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in again], 0, wp, wb)
+    torch.cuda.synchronize()
+    for a, b in zip(again, got):
+        assert np.array_equal(host(a), b)
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(d), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in again], 0b111, wp, wb)
+    torch.cuda.synchronize()
+    for a, r in zip(again, refs):
+        norm_close(host(a), 2 * r, 1e-5 if dtype == "f32" else 3e-2, "accumulated")
+    del w
+
+
+def test_attention_validation():
+    R, S, Dh = 64, 32, 48
+    t = torch.zeros((R, 2 * Dh), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((R, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(xt.XtError) as e:
+        xt.xt_op_fwd(xt.OP.ATTENTION, xt.params(seq_len=S, head_dim=Dh), [xt.view(t)] * 3,
+                     [xt.view(t), xt.view(lse)])
+    assert e.value.status == 4                          # head_dim 48 not built
+    with pytest.raises(xt.XtError) as e:
+        xt.xt_op_fwd(xt.OP.ATTENTION, xt.params(seq_len=30, head_dim=32), [xt.view(t)] * 3,
+                     [xt.view(t), xt.view(lse)])
+    assert e.value.status == 2                          # rows not a multiple of seq_len
+
+
+def test_fused_attention_in_the_block_equals_the_composed_one():
+    """The tiny block (batch 4, seq 256, d 256, 4 x 64 heads, f32) with the
+    fused op instead of the matmul / softmax composition."""
+    from autograd_row_wise_amd import block as xb
+    from oracle_block import block_loss
+    shp = xb.BlockShape(B=4, S=256, H=4, Dh=64, hidden=688, vocab=4096)
+    g = {}
+    for kname, s in xb.WEIGHT_SHAPES(shp).items():
+        g[kname] = np.ones(s, np.float32) if kname.startswith("g") else synth.host_normal(s, 0, kname, 0.0, 0.02)
+    x0 = synth.host_normal((shp.B * shp.S, shp.D), 0, "x")
+    t0 = synth.host_uniform_int((shp.B * shp.S,), 0, shp.vocab, 0, "targets")
+    res = {}
+    for fused in (False, True):
+        W = {kname: dev(val) for kname, val in g.items()}
+        x, tt = dev(x0), dev(t0.reshape(-1, 1), "i32")
+        tp = xt.Tape()
+        w = xb.leaves(tp, W)
+        vx = tp.leaf(xt.view(x))
+        loss = xb.block(tp, w, vx, tp.leaf(xt.view(tt), requires_grad=False), shp, xt.DT.F32,
+                        fused_attention=fused)
+        tp.backward(loss)
+        torch.cuda.synchronize()
+        res[fused] = (host(xt.to_torch(tp.value(loss)))[0, 0],
+                      {kname: host(xt.to_torch(tp.grad(vv))) for kname, vv in w.items()})
+        tp.close()
+    o, P, ox, ol = block_loss({kname: val.astype(np.float64) for kname, val in g.items()}, x0.astype(np.float64),
+                              t0, shp.B, shp.S, shp.H, shp.Dh, 0.0, 0)
+    o.backward(ol)
+    L = float(o.value(ol)[0])
+    for fused in (False, True):
+        Lg, grads = res[fused]
+        assert abs(Lg - L) <= 1e-6 + 1e-5 * abs(L)
+        for kname in P:
+            r = o.grad(P[kname]).reshape(grads[kname].shape)
+            norm_close(grads[kname], r, 1e-5, (fused, kname))
