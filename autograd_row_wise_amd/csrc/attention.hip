@@ -334,6 +334,502 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dkv_k(const T* __restrict__ q, 
   }
 }
 
+// ===========================================================================
+// bf16 storage: bf16 MFMAs (v_mfma_f32_32x32x16_bf16, f32 accumulation).
+//
+// Blocks of 4 waves share K / V (or Q / dO) tiles that are staged through a
+// double-buffered LDS ring: each thread loads its 16-byte chunks of tile j+1
+// into registers while tile j is multiplied, and writes them to the other
+// buffer before the block's one barrier per tile.  Each wave owns 32 rows.
+//
+// Score tiles are computed transposed where the softmax runs over the
+// accumulator rows: S^T = K Q^T puts one query per lane (column), its keys
+// in the lane's 16 registers and the other lane half, so a row maximum is 15
+// in-lane max plus one exchange with lane l ^ 32.  An accumulator tile
+// converted to bf16 is directly the B (or A) operand of the next product when
+// its contraction index is taken in the accumulator's own row order
+// (8 (e / 4) + 4 (l / 32) + e % 4 for element e of lane l); the other operand
+// is read in that order by the transposing LDS read ds_read_b64_tr_b16.
+//
+// Rounding: S and dP are exact products of the stored bf16 operands with f32
+// sums; the probabilities P and dS = P (dP - D) are rounded to bf16 to enter
+// the second products (the composed path stores both as bf16 tensors too);
+// maxima, exponentials, row sums and all accumulation are f32.
+// ===========================================================================
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+namespace fa {
+constexpr int NT = 256;            // 4 waves
+// Row strides (elements) of LDS tiles.  RS: tiles read along rows with
+// 16-byte reads (an odd multiple of 16 bytes: 16 consecutive rows hit 16
+// distinct bank groups).  TS: tiles only read transposed (rows v = 0..3 of
+// a read land on distinct 64-byte bank windows).
+template <int DH> constexpr int RS = DH + 8;
+template <int DH> constexpr int TS = DH == 32 ? 32 : DH == 64 ? 96 : 160;
+}  // namespace fa
+
+__device__ __forceinline__ bf16x8_t lds8(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+// Operand from a row-major LDS tile whose rows run along the contraction:
+// lane l gets tile[r0 + 8 (e / 4) + 4 (l / 32) + e % 4][col0 + l % 32] as
+// element e.  ds_read_b64_tr_b16: within each group of 16 lanes, lane j
+// receives element j % 4 of the 8-byte pieces that lanes 4 v + j / 4
+// address, v = 0..3.
+template <int STRIDE>
+__device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* tile, int r0, int col0, int l) {
+  const int g = l / 16, j = l % 16;
+  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+  s16x4_t v[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = r0 + 8 * r + 4 * (g >> 1) + j / 4;
+    v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + row * STRIDE + col));
+  }
+  const short __attribute__((ext_vector_type(8))) w8 = {v[0][0], v[0][1], v[0][2], v[0][3],
+                                                        v[1][0], v[1][1], v[1][2], v[1][3]};
+  return __builtin_bit_cast(bf16x8_t, w8);
+}
+
+// Registers 8 m .. 8 m + 7 of an accumulator as a bf16 operand.
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& c, int m) {
+  const u32x4_t u = {f2bf2(c[8 * m + 0], c[8 * m + 1]), f2bf2(c[8 * m + 2], c[8 * m + 3]),
+                     f2bf2(c[8 * m + 4], c[8 * m + 5]), f2bf2(c[8 * m + 6], c[8 * m + 7])};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ f32x16_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero(f32x16_t& c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = 0.f;
+}
+
+// Row within an accumulator tile of register i of lane half h.
+__device__ __forceinline__ int arow(int i, int h) { return 8 * (i / 4) + 4 * h + (i % 4); }
+
+// This lane's 16-byte pieces of row `row` (clamped into the sequence) of a
+// [B*S, H*Dh] tensor as the fragments of a contraction over the head
+// dimension: piece kk holds columns 16 kk + 8 h .. +7.
+template <int DH>
+__device__ __forceinline__ void row_frags(const bf16_t* x, const Geo& g, int64_t b, int64_t hd, int64_t row, int h,
+                                          bool valid, bf16x8_t (&f)[DH / 16]) {
+  const bf16_t* p = x + (b * g.S + row) * g.ld + hd * DH + 8 * h;
+#pragma unroll
+  for (int kk = 0; kk < DH / 16; ++kk) {
+    if (valid) {
+      f[kk] = *reinterpret_cast<const bf16x8_t*>(p + 16 * kk);
+    } else {
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      f[kk] = __builtin_bit_cast(bf16x8_t, z);
+    }
+  }
+}
+
+// Staging of an R-row tile of two tensors (rows clamped to the sequence):
+// thread t moves 16-byte chunks t, t + 256, ...
+template <int DH, int R>
+struct Stage2 {
+  static constexpr int CPR = DH / 8, NC = R * CPR, N = (NC + fa::NT - 1) / fa::NT;   // chunks per row, tile, thread
+  u32x4_t a[N], b[N];
+  __device__ __forceinline__ void load(const bf16_t* xa, const bf16_t* xb, const Geo& g, int64_t base, int64_t r0,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + fa::NT * i, row = c / CPR, col = c % CPR;
+      if (NC % fa::NT == 0 || c < NC) {
+        const int64_t r = r0 + row < g.S ? r0 + row : g.S - 1;
+        a[i] = *reinterpret_cast<const u32x4_t*>(xa + base + r * g.ld + col * 8);
+        b[i] = *reinterpret_cast<const u32x4_t*>(xb + base + r * g.ld + col * 8);
+      }
+    }
+  }
+  template <int SA, int SB>
+  __device__ __forceinline__ void store(bf16_t* ta, bf16_t* tb, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + fa::NT * i, row = c / CPR, col = c % CPR;
+      if (NC % fa::NT == 0 || c < NC) {
+        *reinterpret_cast<u32x4_t*>(ta + row * SA + col * 8) = a[i];
+        *reinterpret_cast<u32x4_t*>(tb + row * SB + col * 8) = b[i];
+      }
+    }
+  }
+};
+
+// Block -> (row block, sequence * heads + head).  Under a causal mask the
+// heaviest row blocks are dealt first (query blocks from the end of the
+// sequence, key blocks from its start); consecutive blocks take different
+// heads, so a head keeps to one XCD when the head count is a multiple of 8.
+__device__ __forceinline__ void fa_block(int nrb, bool heavy_last, int& rb, int64_t& hb) {
+  const int HB = gridDim.x / nrb, r = blockIdx.x / HB;
+  hb = blockIdx.x % HB;
+  rb = heavy_last ? nrb - 1 - r : r;
+}
+
+// Forward: 128 queries per block (32 per wave), K / V tiles of 64 keys.
+template <int DH>
+__global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v, bf16_t* __restrict__ out,
+                                                      float* __restrict__ lse, Geo g, float alpha, int causal,
+                                                      int nqb) {
+  constexpr int BK = 64, KS = fa::RS<DH>, VS = fa::TS<DH>, KT = BK * KS, ST = KT + BK * VS;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
+  int qb;
+  int64_t hb;
+  fa_block(nqb, causal != 0, qb, hb);
+  const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
+  const int64_t q0 = (int64_t)qb * 128, qw = q0 + 32 * w, qme = qw + c;
+  bf16x8_t qf[DH / 16];
+  row_frags<DH>(q, g, b, hd, qme, h, qme < g.S, qf);
+  const int64_t kend = causal ? (q0 + 128 < g.S ? q0 + 128 : g.S) : g.S;
+  const int nt = (int)((kend + BK - 1) / BK);
+  Stage2<DH, BK> st;
+  st.load(k, v, g, base, 0, tid);
+  st.template store<KS, VS>(lds, lds + KT, tid);
+  __syncthreads();
+  const float sl = alpha * LOG2E;
+  const int klim = causal && qme < g.S ? (int)qme : (int)g.S - 1;   // last key this lane's query sees
+  float m = -INFINITY, ls = 0.f;        // running maximum (log2 units), this lane half's sum
+  f32x16_t o[DH / 32];                  // O^T: rows = head dimension, column = this lane's query
+#pragma unroll
+  for (int bb = 0; bb < DH / 32; ++bb) zero(o[bb]);
+  for (int j = 0; j < nt; ++j) {
+    const int64_t k0 = (int64_t)j * BK;
+    if (j + 1 < nt) st.load(k, v, g, base, k0 + BK, tid);
+    const bf16_t* Kt = lds + (j & 1) * ST;
+    const bf16_t* Vt = Kt + KT;
+    if (!causal || k0 <= qw + 31) {
+      f32x16_t s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        zero(s[t]);
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) s[t] = mfma16(lds8(Kt + (32 * t + c) * KS + 16 * kk + 8 * h), qf[kk], s[t]);
+      }
+      const bool edge = k0 + BK > g.S || (causal && k0 + BK - 1 > qw);
+      float mx = -INFINITY;
+      if (edge) {                       // keys past klim are masked
+        const int kl = klim - (int)k0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = s[t][i] * sl;
+            s[t][i] = 32 * t + arow(i, h) <= kl ? x : -INFINITY;
+            mx = fmaxf(mx, s[t][i]);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            s[t][i] *= sl;
+            mx = fmaxf(mx, s[t][i]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      if (__any(mn > m)) {              // rescale only when some running maximum grew
+        const float sc = __builtin_amdgcn_exp2f(m - mn);
+        ls *= sc;
+#pragma unroll
+        for (int bb = 0; bb < DH / 32; ++bb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[bb][i] *= sc;
+        m = mn;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s[t][i] - m);
+          s[t][i] = p;
+          ls += p;
+        }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const bf16x8_t pf = pack8(s[t], mm);
+#pragma unroll
+          for (int bb = 0; bb < DH / 32; ++bb) o[bb] = mfma16(tr_frag<VS>(Vt, 32 * t + 16 * mm, 32 * bb, l), pf, o[bb]);
+        }
+    }
+    if (j + 1 < nt) st.template store<KS, VS>(lds + ((j + 1) & 1) * ST, lds + ((j + 1) & 1) * ST + KT, tid);
+    __syncthreads();
+  }
+  const float tot = ls + __shfl_xor(ls, 32);
+  if (qme < g.S) {
+    const float inv = 1.f / tot;
+    bf16_t* orow = out + (b * g.S + qme) * g.ld + hd * DH;
+#pragma unroll
+    for (int bb = 0; bb < DH / 32; ++bb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * bb + 8 * i4 + 4 * h;
+        const uint2 u = make_uint2(f2bf2(o[bb][4 * i4] * inv, o[bb][4 * i4 + 1] * inv),
+                                   f2bf2(o[bb][4 * i4 + 2] * inv, o[bb][4 * i4 + 3] * inv));
+        *reinterpret_cast<uint2*>(orow + d) = u;
+      }
+    if (h == 0) lse[(b * g.S + qme) * g.ldl + hd] = (m + __log2f(tot)) * 0.6931471805599453f;
+  }
+}
+
+// Backward, dQ and D: 128 queries per block (32 per wave), K / V tiles of 32
+// keys.  D = rowsum(dO * O) is formed here for the wave's queries and stored
+// for the dK / dV kernel.  With dq == nullptr only D is produced.
+template <int DH>
+__global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                     const bf16_t* __restrict__ out, const float* __restrict__ lse,
+                                                     float* __restrict__ dd, bf16_t* __restrict__ dq, int acc_dq,
+                                                     Geo g, float alpha, int causal, int nqb) {
+  constexpr int BK = 32, KS = fa::RS<DH>, KT = BK * KS, ST = 2 * KT;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
+  int qb;
+  int64_t hb;
+  fa_block(nqb, causal != 0, qb, hb);
+  const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
+  const int64_t q0 = (int64_t)qb * 128, qw = q0 + 32 * w, qme = qw + c;
+  const bool qok = qme < g.S;
+  bf16x8_t qf[DH / 16], df[DH / 16];
+  row_frags<DH>(dout, g, b, hd, qme, h, qok, df);
+  float Dq;
+  {
+    bf16x8_t of[DH / 16];
+    row_frags<DH>(out, g, b, hd, qme, h, qok, of);
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)df[kk][e] * (float)of[kk][e];
+    Dq = acc + __shfl_xor(acc, 32);
+    if (qok && h == 0) dd[(b * g.S + qme) * g.H + hd] = Dq;
+  }
+  if (!dq) return;
+  row_frags<DH>(q, g, b, hd, qme, h, qok, qf);
+  const float sl = alpha * LOG2E;
+  const float L2 = qok ? lse[(b * g.S + qme) * g.ldl + hd] * LOG2E : 0.f;
+  // last key this lane's query sees (-1: a row past the sequence sees none)
+  const int klim = !qok ? -1 : causal ? (int)qme : (int)g.S - 1;
+  const int64_t kend = causal ? (q0 + 128 < g.S ? q0 + 128 : g.S) : g.S;
+  const int nt = (int)((kend + BK - 1) / BK);
+  Stage2<DH, BK> st;
+  st.load(k, v, g, base, 0, tid);
+  st.template store<KS, KS>(lds, lds + KT, tid);
+  __syncthreads();
+  f32x16_t acc[DH / 32];                // dQ^T: rows = head dimension, column = this lane's query
+#pragma unroll
+  for (int bb = 0; bb < DH / 32; ++bb) zero(acc[bb]);
+  for (int j = 0; j < nt; ++j) {
+    const int64_t k0 = (int64_t)j * BK;
+    if (j + 1 < nt) st.load(k, v, g, base, k0 + BK, tid);
+    const bf16_t* Kt = lds + (j & 1) * ST;
+    const bf16_t* Vt = Kt + KT;
+    if (!causal || k0 <= qw + 31) {
+      f32x16_t s, dp;
+      zero(s);
+      zero(dp);
+#pragma unroll
+      for (int kk = 0; kk < DH / 16; ++kk) {
+        s = mfma16(lds8(Kt + c * KS + 16 * kk + 8 * h), qf[kk], s);
+        dp = mfma16(lds8(Vt + c * KS + 16 * kk + 8 * h), df[kk], dp);
+      }
+      const bool edge = k0 + BK > g.S || (causal && k0 + BK - 1 > qw);
+      const int kl = edge ? klim - (int)k0 : BK;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = arow(i, h) <= kl ? __builtin_amdgcn_exp2f(s[i] * sl - L2) : 0.f;
+        s[i] = p * (dp[i] - Dq);
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const bf16x8_t sf = pack8(s, mm);
+#pragma unroll
+        for (int bb = 0; bb < DH / 32; ++bb) acc[bb] = mfma16(tr_frag<KS>(Kt, 16 * mm, 32 * bb, l), sf, acc[bb]);
+      }
+    }
+    if (j + 1 < nt) st.template store<KS, KS>(lds + ((j + 1) & 1) * ST, lds + ((j + 1) & 1) * ST + KT, tid);
+    __syncthreads();
+  }
+  if (qok) {
+    bf16_t* row = dq + (b * g.S + qme) * g.ld + hd * DH;
+#pragma unroll
+    for (int bb = 0; bb < DH / 32; ++bb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * bb + 8 * i4 + 4 * h;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = alpha * acc[bb][4 * i4 + e];
+        if (acc_dq) {
+          const uint2 old = *reinterpret_cast<const uint2*>(row + d);
+          r[0] = acc_add(bf2f(old.x & 0xffffu), r[0]);
+          r[1] = acc_add(bf2f(old.x >> 16), r[1]);
+          r[2] = acc_add(bf2f(old.y & 0xffffu), r[2]);
+          r[3] = acc_add(bf2f(old.y >> 16), r[3]);
+        }
+        *reinterpret_cast<uint2*>(row + d) = make_uint2(f2bf2(r[0], r[1]), f2bf2(r[2], r[3]));
+      }
+  }
+}
+
+// Backward, dK and dV: 128 keys per block (32 per wave), Q / dO tiles of 32
+// queries, with their L and D.  Scores are not transposed here: S = Q K^T
+// has the wave's key per lane (column) and the queries in registers, which
+// is the A-operand order of P^T and dS^T for dV += P^T dO, dK += dS^T Q.
+template <int DH>
+__global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                      const float* __restrict__ lse, const float* __restrict__ dd,
+                                                      bf16_t* __restrict__ dk, int acc_dk, bf16_t* __restrict__ dv,
+                                                      int acc_dv, Geo g, float alpha, int causal, int nkb) {
+  constexpr int BQ = 32, QS = fa::RS<DH>, QT = BQ * QS, ST = 2 * QT + 4 * BQ;   // + L2 and D: 2 BQ f32
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
+  int kb;
+  int64_t hb;
+  fa_block(nkb, false, kb, hb);
+  const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
+  const int64_t k0 = (int64_t)kb * 128, kw = k0 + 32 * w, kme = kw + c;
+  const bool kok = kme < g.S;
+  bf16x8_t kf[DH / 16], vf[DH / 16];
+  row_frags<DH>(k, g, b, hd, kme, h, kok, kf);
+  row_frags<DH>(v, g, b, hd, kme, h, kok, vf);
+  const float sl = alpha * LOG2E;
+  const int64_t qbeg = causal ? k0 / BQ : 0;          // first query tile
+  const int nt = (int)((g.S + BQ - 1) / BQ - qbeg);
+  Stage2<DH, BQ> st;
+  float lq = 0.f;                                     // this thread's L2 or D entry of the staged tile
+  auto load_ld = [&](int64_t r0) {
+    if (tid < 2 * BQ) {
+      const int64_t r = r0 + tid % BQ < g.S ? r0 + tid % BQ : g.S - 1;
+      lq = tid < BQ ? lse[(b * g.S + r) * g.ldl + hd] * LOG2E : dd[(b * g.S + r) * g.H + hd];
+    }
+  };
+  auto store_ld = [&](bf16_t* t) {
+    if (tid < 2 * BQ) reinterpret_cast<float*>(t + 2 * QT)[tid] = lq;
+  };
+  st.load(q, dout, g, base, qbeg * BQ, tid);
+  load_ld(qbeg * BQ);
+  st.template store<QS, QS>(lds, lds + QT, tid);
+  store_ld(lds);
+  __syncthreads();
+  f32x16_t ak[DH / 32], av[DH / 32];   // rows = the wave's keys, column = head dimension
+#pragma unroll
+  for (int bb = 0; bb < DH / 32; ++bb) { zero(ak[bb]); zero(av[bb]); }
+  for (int j = 0; j < nt; ++j) {
+    const int64_t q0 = (qbeg + j) * BQ;
+    if (j + 1 < nt) { st.load(q, dout, g, base, q0 + BQ, tid); load_ld(q0 + BQ); }
+    const bf16_t* Qt = lds + (j & 1) * ST;
+    const bf16_t* Dt = Qt + QT;
+    const float* LD = reinterpret_cast<const float*>(Qt + 2 * QT);   // [0, BQ): L2, [BQ, 2 BQ): D
+    if (!causal || q0 + BQ - 1 >= kw) {
+      f32x16_t s, dp;
+      zero(s);
+      zero(dp);
+#pragma unroll
+      for (int kk = 0; kk < DH / 16; ++kk) {
+        s = mfma16(lds8(Qt + c * QS + 16 * kk + 8 * h), kf[kk], s);
+        dp = mfma16(lds8(Dt + c * QS + 16 * kk + 8 * h), vf[kk], dp);
+      }
+      const bool edge = q0 + BQ > g.S || (causal && q0 < kw + 31) || kw + 31 >= g.S;
+      // visible rows of the tile: qlo .. qhi (empty for a key past the sequence)
+      const int qlo = edge ? (causal ? (int)(kme - q0) : 0) : 0;
+      const int qhi = edge ? (kok ? (int)(g.S - 1 - q0) : -1) : BQ;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 L4 = *reinterpret_cast<const float4*>(LD + 8 * i4 + 4 * h);
+        const float4 D4 = *reinterpret_cast<const float4*>(LD + BQ + 8 * i4 + 4 * h);
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e, r = arow(i, h);
+          const float p = r >= qlo && r <= qhi ? __builtin_amdgcn_exp2f(s[i] * sl - Lv[e]) : 0.f;
+          s[i] = p;
+          dp[i] = p * (dp[i] - Dv[e]);
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const bf16x8_t pf = pack8(s, mm), sf = pack8(dp, mm);
+#pragma unroll
+        for (int bb = 0; bb < DH / 32; ++bb) {
+          av[bb] = mfma16(pf, tr_frag<QS>(Dt, 16 * mm, 32 * bb, l), av[bb]);
+          ak[bb] = mfma16(sf, tr_frag<QS>(Qt, 16 * mm, 32 * bb, l), ak[bb]);
+        }
+      }
+    }
+    if (j + 1 < nt) {
+      bf16_t* nx = lds + ((j + 1) & 1) * ST;
+      st.template store<QS, QS>(nx, nx + QT, tid);
+      store_ld(nx);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t key = kw + arow(i, h);
+    if (key >= g.S) continue;
+    const int64_t off = (b * g.S + key) * g.ld + hd * DH + c;
+#pragma unroll
+    for (int bb = 0; bb < DH / 32; ++bb) {
+      if (dk) {
+        float val = alpha * ak[bb][i];
+        if (acc_dk) val = acc_add(bf2f(dk[off + 32 * bb]), val);
+        dk[off + 32 * bb] = (bf16_t)f2bf(val);
+      }
+      if (dv) {
+        float val = av[bb][i];
+        if (acc_dv) val = acc_add(bf2f(dv[off + 32 * bb]), val);
+        dv[off + 32 * bb] = (bf16_t)f2bf(val);
+      }
+    }
+  }
+}
+
+template <int DH>
+hipError_t fa_fwd(const AttnArgs& a, hipStream_t s) {
+  const Geo g{a.S, a.H, a.ld, a.ldl};
+  const int nqb = (int)((a.S + 127) / 128);
+  fa_fwd_k<DH><<<(unsigned)(nqb * a.H * a.B), fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+                                                               (const bf16_t*)a.v, (bf16_t*)a.out, a.lse, g, a.alpha,
+                                                               a.causal, nqb);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t fa_bwd(const AttnArgs& a, hipStream_t s) {
+  const Geo g{a.S, a.H, a.ld, a.ldl};
+  const int nb = (int)((a.S + 127) / 128);
+  const unsigned grid = (unsigned)(nb * a.H * a.B);
+  fa_dq_k<DH><<<grid, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+                                      (const bf16_t*)a.dout, (const bf16_t*)a.out, a.lse, a.dd, (bf16_t*)a.dq,
+                                      a.acc_dq, g, a.alpha, a.causal, nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || (!a.dk && !a.dv)) return e;
+  fa_dkv_k<DH><<<grid, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+                                       (const bf16_t*)a.dout, a.lse, a.dd, (bf16_t*)a.dk, a.acc_dk, (bf16_t*)a.dv,
+                                       a.acc_dv, g, a.alpha, a.causal, nb);
+  return hipGetLastError();
+}
+
+// The bf16 kernels move 16-byte pieces: every tensor 16-byte aligned with a
+// row stride that keeps rows aligned.
+bool fa_aligned(const AttnArgs& a) {
+  if (a.ld % 8) return false;
+  const void* p[] = {a.q, a.k, a.v, a.out, a.dout, a.dq, a.dk, a.dv};
+  for (const void* x : p)
+    if (x && ((uintptr_t)x & 15u)) return false;
+  return true;
+}
+
 template <typename T, int DH>
 hipError_t fwd_dh(const AttnArgs& a, hipStream_t s) {
   const Geo g{a.S, a.H, a.ld, a.ldl};
@@ -389,11 +885,25 @@ hipError_t bwd_t(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.S == 0 || a.H == 0) return hipSuccess;
+  if (a.bf16 && fa_aligned(a)) {
+    switch (a.Dh) {
+      case 32: return fa_fwd<32>(a, s);
+      case 64: return fa_fwd<64>(a, s);
+      default: return fa_fwd<128>(a, s);
+    }
+  }
   return a.bf16 ? fwd_t<bf16_t>(a, s) : fwd_t<float>(a, s);
 }
 
 hipError_t launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.S == 0 || a.H == 0) return hipSuccess;
+  if (a.bf16 && fa_aligned(a)) {
+    switch (a.Dh) {
+      case 32: return fa_bwd<32>(a, s);
+      case 64: return fa_bwd<64>(a, s);
+      default: return fa_bwd<128>(a, s);
+    }
+  }
   return a.bf16 ? bwd_t<bf16_t>(a, s) : bwd_t<float>(a, s);
 }
 

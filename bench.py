@@ -13,14 +13,17 @@ batch of synthetic input, each at the shape its workload names:
     32768 x 32768, dbias column sum over 65536 x 4096, matmul backward of
     8192 x 4096 x 4096;
   * the tiny transformer block (batch 4, seq 256, d 256, 4 x 64 heads,
-    SwiGLU 688, vocab 4096, f32) recorded on the tape, fwd+bwd;
-  * after the backward: the global gradient norm and the clip scaling over
-    every gradient buffer of a 12-layer model of GPT-2-small width (about
-    124M f32 in 124 tensors);
+    SwiGLU 688, vocab 4096, f32) recorded on the tape, fwd+bwd.
+The ops that widen the path are timed after the step, in a loop of their
+own, and reported under `next_rows` (not in `value`):
+  * the global gradient norm and the clip scaling over every gradient
+    buffer of a 12-layer model of GPT-2-small width (about 124M f32 in 124
+    tensors);
   * the token embedding of the same model: 8 x 1024 Zipf(1.1)-distributed
     tokens into a 50257 x 768 f32 table, gather and scatter-add backward;
   * fused causal attention fwd+bwd: 2 x 2048 tokens, 16 heads x 128, bf16
-    storage (f32 arithmetic on the matrix cores).
+    storage; and the tiny block with it in place of the composed attention;
+  * the tiny block with its layer as one activation-recompute segment.
 Inputs are drawn on the GPU before timing (torch's seeded generator).
 
 `value` is the step's algorithmic HBM bytes / step time (GB/s): what the
@@ -302,7 +305,7 @@ def build_entries(only):
 
     def c2():
         nonlocal keep
-        if want("c2.block"):
+        if any(want(n) for n in ("c2.block", "f4.block", "f1.block")):
             shp = xb.BlockShape(B=4, S=256, H=4, Dh=64, hidden=688, vocab=4096)
             Wt = {}
             for k, s in xb.WEIGHT_SHAPES(shp).items():
@@ -330,10 +333,10 @@ def build_entries(only):
                            shp.B * shp.S))
             # the same block as one recompute segment: the layer's forward runs
             # twice (the GEMM flops of the record count it once)
-            E.append(Entry("c2.block.fwdbwd_recompute", "tiny block 4x256x256 f32", "f32", "block",
+            E.append(Entry("f4.block.fwdbwd_recompute", "tiny block 4x256x256 f32", "f32", "block",
                            lambda: run_block(True, "tape_ckpt"), 0, 3 * fl, shp.B * shp.S))
             # the same block with the fused attention op
-            E.append(Entry("c2.block.fwdbwd_fused_attention", "tiny block 4x256x256 f32", "f32", "block",
+            E.append(Entry("f1.block.fwdbwd_fused_attention", "tiny block 4x256x256 f32", "f32", "block",
                            lambda: run_block(False, "tape_fused", True), 0, 3 * fl, shp.B * shp.S))
     def f3():
         nonlocal keep
@@ -388,7 +391,7 @@ def build_entries(only):
         if not want("f1"):
             return
         # fused causal attention: 2 sequences x 2048 tokens, 16 heads x 128,
-        # bf16 storage, f32 arithmetic on the matrix cores
+        # bf16 storage: bf16 matrix-core products with f32 accumulation
         B1, S1, H1, D1 = 2, 2048, 16, 128
         R1, C1 = B1 * S1, H1 * D1
         q = device_normal((R1, C1), 12, "q", dtype="bf16")
@@ -404,9 +407,9 @@ def build_entries(only):
         # causal: half of the S x S scores; two products forward, five backward
         prod = 2.0 * S1 * S1 * D1 * B1 * H1 / 2
         W = "attention 2x2048 tokens, 16 heads x 128, causal, bf16 storage"
-        E.append(Entry("f1.attn.fwd", W, "f32", "mfma", lambda: xt.xt_op_fwd(
+        E.append(Entry("f1.attn.fwd", W, "bf16", "mfma", lambda: xt.xt_op_fwd(
             xt.OP.ATTENTION, prm, ins, [V(out), V(lse)]), 4 * 2 * R1 * C1, 2 * prod, R1))
-        E.append(Entry("f1.attn.bwd", W, "f32", "mfma", lambda: xt.xt_op_bwd(
+        E.append(Entry("f1.attn.bwd", W, "bf16", "mfma", lambda: xt.xt_op_bwd(
             xt.OP.ATTENTION, prm, V(d), ins, [V(out), V(lse)], [V(dq), V(dk), V(dv)], 0, wsp, wsn),
             2 * 8 * R1 * C1, 5 * prod, R1))
 
@@ -417,7 +420,7 @@ def build_entries(only):
     f3()
     f2()
     f1()
-    return E, keep
+    return [e for e in E if want(e.name)], keep
 
 
 # --------------------------------------------------------------------------
@@ -566,6 +569,54 @@ def cpu_baseline(frac_rows=1 / 32, min_seconds=10.0, max_passes=12):
 
 
 # --------------------------------------------------------------------------
+def time_steps(entries, stream, steps, warmup):
+    """W untimed passes, then K timed passes over `entries`, each op
+    bracketed by HIP events on the launch stream; returns the wall-clock ms
+    per pass (synchronised on both sides)."""
+    import torch
+
+    def one(record):
+        for e in entries:
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                e.fn()
+                b.record(stream)
+                e._ev.append((a, b))
+            else:
+                e.fn()
+
+    for e in entries:
+        e._ev = []
+    for _ in range(warmup):
+        one(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for e in entries:
+        e.times_ms = [a.elapsed_time(b) for a, b in e._ev]
+    return (t1 - t0) * 1e3 / max(steps, 1)
+
+
+def op_record(e):
+    ms = sum(e.times_ms) / len(e.times_ms)
+    rec = {"op": e.name, "workload": e.workload, "dtype": e.dtype, "ms": round(ms, 5)}
+    if e.kind == "hbm":
+        gbps = e.bytes / (ms * 1e-3) / 1e9
+        rec.update(bytes=e.bytes, GBps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
+                   rows_per_s=round(e.rows / (ms * 1e-3), 1))
+    elif e.kind == "mfma":
+        tf = e.flops / (ms * 1e-3) / 1e12
+        rec.update(flops=e.flops, TFLOPs=round(tf, 2), frac=round(tf / MFMA_PEAK_TFLOPS[e.dtype], 4),
+                   bytes=e.bytes)
+    else:
+        rec.update(flops=e.flops, TFLOPs=round(e.flops / (ms * 1e-3) / 1e12, 3), note="tape-driven, cache-resident")
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -578,51 +629,18 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(record):
-        for e in entries:
-            if record:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                e.fn()
-                b.record(stream)
-                e._ev = (a, b)
-            else:
-                e.fn()
-        if record:
-            return [(e, e._ev) for e in entries]
-        return None
+    # The step is every op of the hot path (names c2..c5); the ops that
+    # widen it (names f1..f4) are timed after it, in a loop of their own.
+    main = [e for e in entries if not e.name.startswith("f")]
+    extra = [e for e in entries if e.name.startswith("f")]
+    wall_ms = time_steps(main, stream, args.steps, args.warmup)
+    if extra:
+        time_steps(extra, stream, args.steps, args.warmup)
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    evs = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        evs.append(step(True))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for rec in evs:
-        for e, (a, b) in rec:
-            e.times_ms.append(a.elapsed_time(b))
-    wall_ms = (t1 - t0) * 1e3 / max(args.steps, 1)
-
-    total_bytes = sum(e.bytes for e in entries)
-    ops_out = []
-    for e in entries:
-        ms = sum(e.times_ms) / len(e.times_ms)
-        rec = {"op": e.name, "workload": e.workload, "dtype": e.dtype, "ms": round(ms, 5)}
-        if e.kind == "hbm":
-            gbps = e.bytes / (ms * 1e-3) / 1e9
-            rec.update(bytes=e.bytes, GBps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
-                       rows_per_s=round(e.rows / (ms * 1e-3), 1))
-        elif e.kind == "mfma":
-            tf = e.flops / (ms * 1e-3) / 1e12
-            rec.update(flops=e.flops, TFLOPs=round(tf, 2), frac=round(tf / MFMA_PEAK_TFLOPS[e.dtype], 4),
-                       bytes=e.bytes)
-        else:
-            rec.update(flops=e.flops, TFLOPs=round(e.flops / (ms * 1e-3) / 1e12, 3), note="tape-driven, cache-resident")
-        ops_out.append(rec)
-    dom = max(entries, key=lambda e: sum(e.times_ms)) if entries else None
+    ops_out = [op_record(e) for e in main]
+    extra_out = [op_record(e) for e in extra]
+    total_bytes = sum(e.bytes for e in main)
+    dom = max(main, key=lambda e: sum(e.times_ms)) if main else None
     roof = None
     if dom is not None:
         ms = sum(dom.times_ms) / len(dom.times_ms)
@@ -636,6 +654,7 @@ def main():
             roof = {"bound": "hbm", "kernel": dom.name, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(dom.name),
                     "algorithmic_bytes": dom.bytes}
+    entries = main
     hbm_entries = [e for e in entries if e.kind == "hbm"]
     hbm_ms = sum(sum(e.times_ms) / len(e.times_ms) for e in hbm_entries)
     hbm_bytes = sum(e.bytes for e in hbm_entries)
@@ -648,19 +667,18 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32+bf16", "data": "synthetic",
         "config": {"workload": "hot-path suite: every op fwd+bwd at the gpt2s-f32 8x1024x768, bf16 16384x4096 and "
-                               "bf16-stress shapes, the tiny transformer block on the tape, and the global "
-                               "gradient norm and clip scaling over a 12-layer gpt2s-width gradient set, the gpt2s token "
-                               "embedding fwd+bwd and fused causal attention 2x2048x16x128",
+                               "bf16-stress shapes, and the tiny transformer block on the tape",
                    "parallelism": "none (1 GPU)"},
         "memory_bound_GBps": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9, 1) if hbm_ms else None,
         "memory_bound_frac": round(hbm_bytes / (hbm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if hbm_ms else None,
         "roofline": roof,
         "cpu_baseline": None,
         "ops": ops_out,
+        "next_rows": extra_out,
     }
     if args.ops_json:
         with open(args.ops_json, "w") as f:
-            json.dump(ops_out, f, indent=1)
+            json.dump(ops_out + extra_out, f, indent=1)
     if not args.no_sweep and not args.only:
         out["sweep"] = {"what": "fwd and bwd of each row-wise op at 1 GiB per activation tensor, R = 2^30/(s*d)",
                         "entries": sweep(args.steps, args.warmup)}

@@ -1,8 +1,11 @@
 """GPU parity of the fused attention (XT_OP_ATTENTION) through the C ABI
 against the oracle: output, log-sum-exp and the three gradients, causal and
-not, Dh 32 / 64 / 128, sequence lengths that leave ragged 32-row tiles, f32
-and bf16 storage, accumulate mode, bitwise reproducibility; and the fused op
-on the tape inside the tiny block against the composed attention."""
+not, Dh 32 / 64 / 128, sequence lengths that leave ragged tiles (32-row f32
+tiles; 128-row blocks and 32 / 64-row tiles of the bf16 kernels), f32 and
+bf16 storage, accumulate mode, bitwise reproducibility; the bf16 path on
+unaligned rows (the generic kernels); two heads of the 2 x 2048 x 16 x 128
+bf16 workload against the oracle; and the fused op on the tape inside the
+tiny block against the composed attention."""
 import math
 
 import numpy as np
@@ -42,6 +45,10 @@ CASES = [  # B, S, H, Dh, causal, dtype
     (1, 100, 2, 128, 1, "f32"),
     (2, 130, 2, 64, 1, "bf16"),
     (1, 64, 3, 128, 0, "bf16"),
+    (1, 300, 2, 32, 1, "bf16"),
+    (3, 200, 8, 64, 0, "bf16"),
+    (2, 512, 4, 128, 1, "bf16"),
+    (1, 1, 1, 64, 1, "bf16"),
 ]
 
 
@@ -137,3 +144,65 @@ def test_fused_attention_in_the_block_equals_the_composed_one():
         for kname in P:
             r = o.grad(P[kname]).reshape(grads[kname].shape)
             norm_close(grads[kname], r, 1e-5, (fused, kname))
+
+
+def test_attention_bf16_unaligned_rows():
+    """Row stride C + 4 (not a multiple of 8 elements): the bf16 op takes the
+    generic kernels; same bar as the aligned cases."""
+    B, S, H, Dh = 1, 70, 2, 32
+    R, C, ld = B * S, H * Dh, H * Dh + 4
+    alpha = 1.0 / math.sqrt(Dh)
+
+    def padded(a):
+        bits = synth.host_bf16_bits(a)
+        full = np.zeros((R, ld), np.uint16)
+        full[:, :C] = bits
+        return dev(full, "bf16")[:, :C], synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+    (q, qv), (k, kv), (v, vv), (d, dv) = (padded(synth.host_normal((R, C), 13, n)) for n in ("q", "k", "v", "dout"))
+    prm = xt.params(alpha=alpha, causal=1, seq_len=S, head_dim=Dh)
+    out = torch.empty((R, ld), dtype=torch.bfloat16, device="cuda")[:, :C]
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    ins = [xt.view(q), xt.view(k), xt.view(v)]
+    xt.xt_op_fwd(xt.OP.ATTENTION, prm, ins, [xt.view(out), xt.view(lse)])
+    grads = [torch.empty((R, ld), dtype=torch.bfloat16, device="cuda")[:, :C] for _ in range(3)]
+    w, wp, wb = xt.workspace(xt.OP.ATTENTION, 1, prm, ins)
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(d), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in grads], 0, wp, wb)
+    torch.cuda.synchronize()
+    o_ref, l_ref = ops.attention(qv, kv, vv, S, H, Dh, alpha, True)
+    norm_close(host(out), o_ref, 2e-2, "out")
+    np.testing.assert_allclose(host(lse), l_ref, rtol=1e-5, atol=1e-5)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, ops.attention_bwd(dv, qv, kv, vv, S, H, Dh, alpha, True)):
+        norm_close(host(g), r, 3e-2, name)
+    del w
+
+
+def test_attention_bench_shape_two_heads():
+    """The 2 x 2048 tokens, 16 heads x 128, causal, bf16 workload run whole;
+    heads (sequence 0, head 3) and (sequence 1, head 12) checked in full
+    against the oracle on those heads alone."""
+    B, S, H, Dh = 2, 2048, 16, 128
+    R, C = B * S, H * Dh
+    alpha = 1.0 / math.sqrt(Dh)
+    x = {n: synth.device_normal((R, C), 14, n, dtype="bf16") for n in ("q", "k", "v", "dout")}
+    prm = xt.params(alpha=alpha, causal=1, seq_len=S, head_dim=Dh)
+    out = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    ins = [xt.view(x["q"]), xt.view(x["k"]), xt.view(x["v"])]
+    xt.xt_op_fwd(xt.OP.ATTENTION, prm, ins, [xt.view(out), xt.view(lse)])
+    grads = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    w, wp, wb = xt.workspace(xt.OP.ATTENTION, 1, prm, ins)
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(x["dout"]), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in grads], 0, wp, wb)
+    torch.cuda.synchronize()
+    for b, hd in ((0, 3), (1, 12)):
+        rows, cols = slice(b * S, (b + 1) * S), slice(hd * Dh, (hd + 1) * Dh)
+        sl = {n: host(t[rows, cols]) for n, t in x.items()}
+        o_ref, l_ref = ops.attention(sl["q"], sl["k"], sl["v"], S, 1, Dh, alpha, True)
+        norm_close(host(out[rows, cols]), o_ref, 2e-2, ("out", b, hd))
+        np.testing.assert_allclose(host(lse[rows, hd:hd + 1]), l_ref, rtol=1e-5, atol=1e-5)
+        refs = ops.attention_bwd(sl["dout"], sl["q"], sl["k"], sl["v"], S, 1, Dh, alpha, True)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+            norm_close(host(g[rows, cols]), r, 3e-2, (name, b, hd))
+    del w
