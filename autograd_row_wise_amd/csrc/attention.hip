@@ -460,14 +460,18 @@ struct Stage2 {
   }
 };
 
-// Block -> (row block, sequence * heads + head).  Under a causal mask the
-// heaviest row blocks are dealt first (query blocks from the end of the
-// sequence, key blocks from its start); consecutive blocks take different
-// heads, so a head keeps to one XCD when the head count is a multiple of 8.
-__device__ __forceinline__ void fa_block(int nrb, bool heavy_last, int& rb, int64_t& hb) {
-  const int HB = gridDim.x / nrb, r = blockIdx.x / HB;
+// Block -> (row block, sequence * heads + head).  Consecutive blocks take
+// different heads, so a head keeps to one XCD when the head count is a
+// multiple of 8.  Under a causal mask the work of a row block grows (query
+// blocks) or shrinks (key blocks) along the sequence; blocks are dealt
+// zig-zag: the heavier half first, heaviest first, then the lighter half,
+// lightest first, so a compute unit that takes block i and later block
+// i + half the grid gets about the same total work as any other.
+__device__ __forceinline__ void fa_block(int nrb, int heavy_end, int& rb, int64_t& hb) {
+  const int HB = gridDim.x / nrb, r = blockIdx.x / HB, half = (nrb + 1) / 2;
   hb = blockIdx.x % HB;
-  rb = heavy_last ? nrb - 1 - r : r;
+  const int heavy = r < half ? r : nrb - 1 - (r - half);   // rank from the heaviest
+  rb = heavy_end > 0 ? nrb - 1 - heavy : heavy_end < 0 ? heavy : r;
 }
 
 // Forward: 128 queries per block (32 per wave), K / V tiles of 64 keys.
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
   int qb;
   int64_t hb;
-  fa_block(nqb, causal != 0, qb, hb);
+  fa_block(nqb, causal ? 1 : 0, qb, hb);
   const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
   const int64_t q0 = (int64_t)qb * 128, qw = q0 + 32 * w, qme = qw + c;
   bf16x8_t qf[DH / 16];
@@ -498,12 +502,21 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
   f32x16_t o[DH / 32];                  // O^T: rows = head dimension, column = this lane's query
 #pragma unroll
   for (int bb = 0; bb < DH / 32; ++bb) zero(o[bb]);
-  for (int j = 0; j < nt; ++j) {
+  // Tiles 0 .. nact-1 hold keys this wave's queries see; the rest (causal)
+  // only pass through the staging ring.  Two loops, so the accumulators
+  // never merge with a skipped tile.
+  const int nact = causal ? (int)((qw + 31) / BK + 1 < nt ? (qw + 31) / BK + 1 : nt) : nt;
+  auto stage_next = [&](int j) {
+    if (j + 1 < nt) st.template store<KS, VS>(lds + ((j + 1) & 1) * ST, lds + ((j + 1) & 1) * ST + KT, tid);
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j < nact; ++j) {
     const int64_t k0 = (int64_t)j * BK;
     if (j + 1 < nt) st.load(k, v, g, base, k0 + BK, tid);
     const bf16_t* Kt = lds + (j & 1) * ST;
     const bf16_t* Vt = Kt + KT;
-    if (!causal || k0 <= qw + 31) {
+    {
       f32x16_t s[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -511,6 +524,8 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
 #pragma unroll
         for (int kk = 0; kk < DH / 16; ++kk) s[t] = mfma16(lds8(Kt + (32 * t + c) * KS + 16 * kk + 8 * h), qf[kk], s[t]);
       }
+      // Row maximum of the raw scores (alpha > 0, so the order is that of
+      // alpha S); masked keys become -inf.
       const bool edge = k0 + BK > g.S || (causal && k0 + BK - 1 > qw);
       float mx = -INFINITY;
       if (edge) {                       // keys past klim are masked
@@ -519,23 +534,22 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float x = s[t][i] * sl;
-            s[t][i] = 32 * t + arow(i, h) <= kl ? x : -INFINITY;
+            s[t][i] = 32 * t + arow(i, h) <= kl ? s[t][i] : -INFINITY;
             mx = fmaxf(mx, s[t][i]);
           }
       } else {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[t][i] *= sl;
-            mx = fmaxf(mx, s[t][i]);
-          }
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m, mx);
-      if (__any(mn > m)) {              // rescale only when some running maximum grew
-        const float sc = __builtin_amdgcn_exp2f(m - mn);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+      // The reference point m only moves when some row's maximum exceeds it
+      // by more than 8 (log2 units): exponentials stay below 2^8, and the
+      // final division by the row sum cancels the choice of m exactly.
+      if (__any(mx > m + 8.f)) {
+        const float mn = fmaxf(m, mx);
+        const float sc = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first tile (m = -inf)
         ls *= sc;
 #pragma unroll
         for (int bb = 0; bb < DH / 32; ++bb)
@@ -547,7 +561,7 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[t][i] - m);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], sl, -m));
           s[t][i] = p;
           ls += p;
         }
@@ -560,8 +574,11 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
           for (int bb = 0; bb < DH / 32; ++bb) o[bb] = mfma16(tr_frag<VS>(Vt, 32 * t + 16 * mm, 32 * bb, l), pf, o[bb]);
         }
     }
-    if (j + 1 < nt) st.template store<KS, VS>(lds + ((j + 1) & 1) * ST, lds + ((j + 1) & 1) * ST + KT, tid);
-    __syncthreads();
+    stage_next(j);
+  }
+  for (; j < nt; ++j) {
+    if (j + 1 < nt) st.load(k, v, g, base, (int64_t)(j + 1) * BK, tid);
+    stage_next(j);
   }
   const float tot = ls + __shfl_xor(ls, 32);
   if (qme < g.S) {
@@ -594,7 +611,7 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
   int qb;
   int64_t hb;
-  fa_block(nqb, causal != 0, qb, hb);
+  fa_block(nqb, causal ? 1 : 0, qb, hb);
   const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
   const int64_t q0 = (int64_t)qb * 128, qw = q0 + 32 * w, qme = qw + c;
   const bool qok = qme < g.S;
@@ -627,12 +644,18 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
   f32x16_t acc[DH / 32];                // dQ^T: rows = head dimension, column = this lane's query
 #pragma unroll
   for (int bb = 0; bb < DH / 32; ++bb) zero(acc[bb]);
-  for (int j = 0; j < nt; ++j) {
+  const int nact = causal ? (int)((qw + 31) / BK + 1 < nt ? (qw + 31) / BK + 1 : nt) : nt;
+  auto stage_next = [&](int j) {
+    if (j + 1 < nt) st.template store<KS, KS>(lds + ((j + 1) & 1) * ST, lds + ((j + 1) & 1) * ST + KT, tid);
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j < nact; ++j) {
     const int64_t k0 = (int64_t)j * BK;
     if (j + 1 < nt) st.load(k, v, g, base, k0 + BK, tid);
     const bf16_t* Kt = lds + (j & 1) * ST;
     const bf16_t* Vt = Kt + KT;
-    if (!causal || k0 <= qw + 31) {
+    {
       f32x16_t s, dp;
       zero(s);
       zero(dp);
@@ -642,11 +665,16 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
         dp = mfma16(lds8(Vt + c * KS + 16 * kk + 8 * h), df[kk], dp);
       }
       const bool edge = k0 + BK > g.S || (causal && k0 + BK - 1 > qw);
-      const int kl = edge ? klim - (int)k0 : BK;
+      if (edge) {
+        const int kl = klim - (int)k0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = arow(i, h) <= kl ? __builtin_amdgcn_exp2f(s[i] * sl - L2) : 0.f;
-        s[i] = p * (dp[i] - Dq);
+        for (int i = 0; i < 16; ++i) {
+          const float p = arow(i, h) <= kl ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -L2)) : 0.f;
+          s[i] = p * (dp[i] - Dq);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -L2)) * (dp[i] - Dq);
       }
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
@@ -655,8 +683,11 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
         for (int bb = 0; bb < DH / 32; ++bb) acc[bb] = mfma16(tr_frag<KS>(Kt, 16 * mm, 32 * bb, l), sf, acc[bb]);
       }
     }
-    if (j + 1 < nt) st.template store<KS, KS>(lds + ((j + 1) & 1) * ST, lds + ((j + 1) & 1) * ST + KT, tid);
-    __syncthreads();
+    stage_next(j);
+  }
+  for (; j < nt; ++j) {
+    if (j + 1 < nt) st.load(k, v, g, base, (int64_t)(j + 1) * BK, tid);
+    stage_next(j);
   }
   if (qok) {
     bf16_t* row = dq + (b * g.S + qme) * g.ld + hd * DH;
@@ -684,6 +715,8 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
 // queries, with their L and D.  Scores are not transposed here: S = Q K^T
 // has the wave's key per lane (column) and the queries in registers, which
 // is the A-operand order of P^T and dS^T for dV += P^T dO, dK += dS^T Q.
+// The block's K and V rows stay in LDS for the whole kernel (registers go to
+// the two 32 x Dh accumulators).
 template <int DH>
 __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
@@ -691,17 +724,24 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
                                                       bf16_t* __restrict__ dk, int acc_dk, bf16_t* __restrict__ dv,
                                                       int acc_dv, Geo g, float alpha, int causal, int nkb) {
   constexpr int BQ = 32, QS = fa::RS<DH>, QT = BQ * QS, ST = 2 * QT + 4 * BQ;   // + L2 and D: 2 BQ f32
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST];
+  constexpr int KV = 128 * QS;                        // the block's K (then V) rows
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST + 2 * KV];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
   int kb;
   int64_t hb;
-  fa_block(nkb, false, kb, hb);
+  fa_block(nkb, causal ? -1 : 0, kb, hb);
   const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
   const int64_t k0 = (int64_t)kb * 128, kw = k0 + 32 * w, kme = kw + c;
   const bool kok = kme < g.S;
-  bf16x8_t kf[DH / 16], vf[DH / 16];
-  row_frags<DH>(k, g, b, hd, kme, h, kok, kf);
-  row_frags<DH>(v, g, b, hd, kme, h, kok, vf);
+  bf16_t* const Kb = lds + 2 * ST;                    // rows k0 .. k0 + 127 (clamped)
+  bf16_t* const Vb = Kb + KV;
+  {
+    Stage2<DH, 128> kv;
+    kv.load(k, v, g, base, k0, tid);
+    kv.template store<QS, QS>(Kb, Vb, tid);
+  }
+  const bf16_t* const Kw = Kb + 32 * w * QS + c * QS + 8 * h;   // this lane's key row, piece kk at + 16 kk
+  const bf16_t* const Vw = Vb + 32 * w * QS + c * QS + 8 * h;
   const float sl = alpha * LOG2E;
   const int64_t qbeg = causal ? k0 / BQ : 0;          // first query tile
   const int nt = (int)((g.S + BQ - 1) / BQ - qbeg);
@@ -724,36 +764,67 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
   f32x16_t ak[DH / 32], av[DH / 32];   // rows = the wave's keys, column = head dimension
 #pragma unroll
   for (int bb = 0; bb < DH / 32; ++bb) { zero(ak[bb]); zero(av[bb]); }
-  for (int j = 0; j < nt; ++j) {
+  // Query tiles before jfirst lie wholly before this wave's keys (causal):
+  // they only pass through the staging ring.
+  int jfirst = 0;
+  if (causal) {
+    const int64_t f = (kw - BQ + 1 + BQ - 1) / BQ - qbeg;   // first tile with q0 + BQ - 1 >= kw
+    jfirst = f < 0 ? 0 : f > nt ? nt : (int)f;
+  }
+  auto stage_next = [&](int j) {
+    if (j + 1 < nt) {
+      bf16_t* nx = lds + ((j + 1) & 1) * ST;
+      st.template store<QS, QS>(nx, nx + QT, tid);
+      store_ld(nx);
+    }
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j < jfirst; ++j) {
+    if (j + 1 < nt) { st.load(q, dout, g, base, (qbeg + j + 1) * BQ, tid); load_ld((qbeg + j + 1) * BQ); }
+    stage_next(j);
+  }
+  for (; j < nt; ++j) {
     const int64_t q0 = (qbeg + j) * BQ;
     if (j + 1 < nt) { st.load(q, dout, g, base, q0 + BQ, tid); load_ld(q0 + BQ); }
     const bf16_t* Qt = lds + (j & 1) * ST;
     const bf16_t* Dt = Qt + QT;
     const float* LD = reinterpret_cast<const float*>(Qt + 2 * QT);   // [0, BQ): L2, [BQ, 2 BQ): D
-    if (!causal || q0 + BQ - 1 >= kw) {
+    {
       f32x16_t s, dp;
       zero(s);
       zero(dp);
 #pragma unroll
       for (int kk = 0; kk < DH / 16; ++kk) {
-        s = mfma16(lds8(Qt + c * QS + 16 * kk + 8 * h), kf[kk], s);
-        dp = mfma16(lds8(Dt + c * QS + 16 * kk + 8 * h), vf[kk], dp);
+        s = mfma16(lds8(Qt + c * QS + 16 * kk + 8 * h), lds8(Kw + 16 * kk), s);
+        dp = mfma16(lds8(Dt + c * QS + 16 * kk + 8 * h), lds8(Vw + 16 * kk), dp);
       }
       const bool edge = q0 + BQ > g.S || (causal && q0 < kw + 31) || kw + 31 >= g.S;
-      // visible rows of the tile: qlo .. qhi (empty for a key past the sequence)
-      const int qlo = edge ? (causal ? (int)(kme - q0) : 0) : 0;
-      const int qhi = edge ? (kok ? (int)(g.S - 1 - q0) : -1) : BQ;
+      float Lv[16], Dv[16];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const float4 L4 = *reinterpret_cast<const float4*>(LD + 8 * i4 + 4 * h);
         const float4 D4 = *reinterpret_cast<const float4*>(LD + BQ + 8 * i4 + 4 * h);
-        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+        Lv[4 * i4] = L4.x; Lv[4 * i4 + 1] = L4.y; Lv[4 * i4 + 2] = L4.z; Lv[4 * i4 + 3] = L4.w;
+        Dv[4 * i4] = D4.x; Dv[4 * i4 + 1] = D4.y; Dv[4 * i4 + 2] = D4.z; Dv[4 * i4 + 3] = D4.w;
+      }
+      if (edge) {
+        // visible rows of the tile: qlo .. qhi (none for a key past the sequence)
+        const int qlo = causal ? (int)(kme - q0) : 0;
+        const int qhi = kok ? (int)(g.S - 1 - q0) : -1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e, r = arow(i, h);
-          const float p = r >= qlo && r <= qhi ? __builtin_amdgcn_exp2f(s[i] * sl - Lv[e]) : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          const int r = arow(i, h);
+          const float p = r >= qlo && r <= qhi ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -Lv[i])) : 0.f;
           s[i] = p;
-          dp[i] = p * (dp[i] - Dv[e]);
+          dp[i] = p * (dp[i] - Dv[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -Lv[i]));
+          s[i] = p;
+          dp[i] = p * (dp[i] - Dv[i]);
         }
       }
 #pragma unroll
@@ -766,12 +837,7 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
         }
       }
     }
-    if (j + 1 < nt) {
-      bf16_t* nx = lds + ((j + 1) & 1) * ST;
-      st.template store<QS, QS>(nx, nx + QT, tid);
-      store_ld(nx);
-    }
-    __syncthreads();
+    stage_next(j);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -821,9 +887,9 @@ hipError_t fa_bwd(const AttnArgs& a, hipStream_t s) {
 }
 
 // The bf16 kernels move 16-byte pieces: every tensor 16-byte aligned with a
-// row stride that keeps rows aligned.
+// row stride that keeps rows aligned; and they take alpha > 0.
 bool fa_aligned(const AttnArgs& a) {
-  if (a.ld % 8) return false;
+  if (a.ld % 8 || !(a.alpha > 0.f)) return false;   // the forward orders scores by the raw products
   const void* p[] = {a.q, a.k, a.v, a.out, a.dout, a.dq, a.dk, a.dv};
   for (const void* x : p)
     if (x && ((uintptr_t)x & 15u)) return false;
