@@ -27,12 +27,16 @@ own, and reported under `next_rows` (not in `value`):
 Inputs are drawn on the GPU before timing (torch's seeded generator).
 
 `value` is the step's algorithmic HBM bytes / step time (GB/s): what the
-method must read and write, not what the caches move.  Per-op figures
-(bytes, time from HIP events on the launch stream, GB/s or TFLOP/s,
-fraction of peak) are in `ops`; `roofline` is for the op with the largest
-share of step time.  `cpu_baseline` is the CPU oracle on a bounded sample.
+method must read and write, not what the caches move.  The step's launches
+are captured once into a HIP graph and replayed (the tape-driven block runs
+eagerly after it); each op's time comes from a graph of that op launched
+several times in a row, with HIP events around the replay, so the Python
+launch path is not in the per-op figures (--eager times every launch from
+Python instead).  Per-op figures (bytes, time, GB/s or TFLOP/s, fraction of
+peak) are in `ops`; `roofline` is for the op with the largest share of step
+time.  `cpu_baseline` is the CPU oracle on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--eager]
 """
 from __future__ import annotations
 
@@ -80,6 +84,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None, help="run only ops whose name starts with one of these")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every op from Python each step instead of replaying captured HIP graphs")
     ap.add_argument("--no-sweep", action="store_true", help="skip the rows/s sweep over d = 768..4096")
     ap.add_argument("--ops-json", default=None, help="also write the per-op table to this file")
     return ap.parse_args()
@@ -601,9 +607,89 @@ def time_steps(entries, stream, steps, warmup):
     return (t1 - t0) * 1e3 / max(steps, 1)
 
 
+def capture(fns, reps=1):
+    """A HIP graph of `fns` called in order, `reps` times (torch's capture
+    stream is current while they launch, so the library's kernels land in
+    the graph).  One eager call first, as torch asks before a capture."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            for fn in fns:
+                fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(entries, stream, steps, warmup, target_ms=0.3):
+    """Per-op GPU time without the Python launch path: each op captured
+    `reps` times in a row into one graph (enough launches to fill about
+    target_ms), replayed with HIP events around each replay; the op's time is
+    the replay's / reps."""
+    import torch
+    for e in entries:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(3):
+            e.fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        est = a.elapsed_time(b) / 3
+        e.reps = max(1, min(50, math.ceil(target_ms / max(est, 1e-4))))
+        g = capture([e.fn], e.reps)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        e.times_ms = [x.elapsed_time(y) / e.reps for x, y in ev]
+        del g
+
+
+def time_step_graph(entries, stream, steps, warmup):
+    """The step as one HIP graph of every capturable op (the tape-driven
+    block runs eagerly after it): wall-clock ms per step, synchronised on
+    both sides of the K timed steps."""
+    import torch
+    cap = [e for e in entries if e.kind != "block"]
+    eager = [e for e in entries if e.kind == "block"]
+    g = capture([e.fn for e in cap]) if cap else None
+    for _ in range(warmup):
+        if g is not None:
+            g.replay()
+        for e in eager:
+            e.fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if g is not None:
+            g.replay()
+        for e in eager:
+            e.fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del g
+    return (t1 - t0) * 1e3 / max(steps, 1)
+
+
 def op_record(e):
     ms = sum(e.times_ms) / len(e.times_ms)
     rec = {"op": e.name, "workload": e.workload, "dtype": e.dtype, "ms": round(ms, 5)}
+    if getattr(e, "reps", None):
+        rec["launches_per_replay"] = e.reps
     if e.kind == "hbm":
         gbps = e.bytes / (ms * 1e-3) / 1e9
         rec.update(bytes=e.bytes, GBps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4),
@@ -633,9 +719,17 @@ def main():
     # widen it (names f1..f4) are timed after it, in a loop of their own.
     main = [e for e in entries if not e.name.startswith("f")]
     extra = [e for e in entries if e.name.startswith("f")]
-    wall_ms = time_steps(main, stream, args.steps, args.warmup)
-    if extra:
-        time_steps(extra, stream, args.steps, args.warmup)
+    if args.eager:
+        wall_ms = time_steps(main, stream, args.steps, args.warmup)
+        if extra:
+            time_steps(extra, stream, args.steps, args.warmup)
+    else:
+        # the step replays one graph; per-op times come from graphs of each
+        # op alone (the tape-driven block is timed eagerly in both)
+        wall_ms = time_step_graph(main, stream, args.steps, args.warmup)
+        for group in (main, extra):
+            time_graphs([e for e in group if e.kind != "block"], stream, args.steps, args.warmup)
+            time_steps([e for e in group if e.kind == "block"], stream, args.steps, args.warmup)
 
     ops_out = [op_record(e) for e in main]
     extra_out = [op_record(e) for e in extra]
@@ -675,6 +769,9 @@ def main():
         "cpu_baseline": None,
         "ops": ops_out,
         "next_rows": extra_out,
+        "timing": ("eager: every op launched from Python, HIP events around each launch" if args.eager else
+                   "HIP graphs: the step is one graph replay (the tape-driven block eager after it); each op's "
+                   "time is a graph of that op launched reps times in a row, HIP events around the replay / reps"),
     }
     if args.ops_json:
         with open(args.ops_json, "w") as f:
