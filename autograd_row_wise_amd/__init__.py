@@ -26,6 +26,12 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is not built: run `python autograd_row_wise_amd/build.py` "
         "(or __graft_entry__.build()); there is no non-HIP fallback")
 
+# torch loads the HIP runtime its device memory and streams come from; libxt
+# must bind to that same runtime, so torch is loaded first.  (Loaded the other
+# way round, the process holds two HIP runtimes and libxt's launches find no
+# device.)
+import torch  # noqa: E402,F401
+
 lib = C.CDLL(LIB_PATH)
 
 
