@@ -651,12 +651,15 @@ __global__ __launch_bounds__(GEN_BLOCK) void sm_bwd_gen(
 }
 
 // ============================================================ column sums
-// Second pass: out[c] (+)= sum_b part[b*stride + c] over b = 0..P-1 in a
+// Second pass: column c of the partial rows, summed over b = 0..P-1 in a
 // fixed order (wave w takes b = w, w+16, ..., then the 16 wave sums are
-// added in wave order).  64 columns per block.
+// added in wave order), goes to out0[c] for c < n0 and to out1[c - n0]
+// otherwise (the two parameter gradients of layer_norm in one launch), each
+// stored or added (acc0 / acc1).  64 columns per block.
 __global__ __launch_bounds__(1024) void fold_columns(const float* __restrict__ part, int64_t P,
-                                                    int64_t stride, int64_t C,
-                                                    float* __restrict__ out, int acc) {
+                                                    int64_t stride, int64_t C, float* __restrict__ out0,
+                                                    int acc0, int64_t n0, float* __restrict__ out1,
+                                                    int acc1) {
   __shared__ float lds[16][64];
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   const int64_t c = (int64_t)blockIdx.x * 64 + l;
@@ -684,7 +687,8 @@ __global__ __launch_bounds__(1024) void fold_columns(const float* __restrict__ p
     float t = lds[0][l];
 #pragma unroll
     for (int i = 1; i < 16; ++i) t += lds[i][l];
-    out[c] = acc ? acc_add(out[c], t) : t;
+    float* o = c < n0 ? out0 + c : out1 + (c - n0);
+    *o = (c < n0 ? acc0 : acc1) ? acc_add(*o, t) : t;
   }
 }
 
@@ -706,14 +710,19 @@ __global__ __launch_bounds__(1024) void colsum_partials(
   for (int k = 0; k < V; ++k) a[k] = 0.f;
   if (c0 < C) {
     int64_t r = start + ph;
-    for (; r + 3 * nph < end; r += 4 * nph) {
-      float v0[V], v1[V], v2[V], v3[V];
-      load_pack<T>(row_ptr<T>(d, r, ldd), c0, C, v0, 0.f);
-      load_pack<T>(row_ptr<T>(d, r + nph, ldd), c0, C, v1, 0.f);
-      load_pack<T>(row_ptr<T>(d, r + 2 * nph, ldd), c0, C, v2, 0.f);
-      load_pack<T>(row_ptr<T>(d, r + 3 * nph, ldd), c0, C, v3, 0.f);
+    // eight rows' packs in flight per thread, added in row order
+    constexpr int U = 8;
+    for (; r + (U - 1) * nph < end; r += U * nph) {
+      uint4 q[U];
 #pragma unroll
-      for (int k = 0; k < V; ++k) a[k] += v0[k] + v1[k] + v2[k] + v3[k];
+      for (int u = 0; u < U; ++u) q[u] = load_raw<T>(row_ptr<T>(d, r + u * nph, ldd), c0, C);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v[V];
+        io<T>::unpack(q[u], v);
+#pragma unroll
+        for (int k = 0; k < V; ++k) a[k] += v[k];
+      }
     }
     for (; r < end; r += nph) {
       float v0[V];
@@ -929,7 +938,7 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
     if (dgamma)
       norm_partials_gen<T, 0><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)ir.data, ir.ld, nullptr, 0, part, R, C, rpb);
   }
-  if (dgamma) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, C, C, dgamma, acc_dg);
+  if (dgamma) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, C, C, dgamma, acc_dg, C, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -995,8 +1004,12 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
       norm_partials_gen<T, 1><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)mean.data, mean.ld,
                                                            (const float*)rstd.data, rstd.ld, part, R, C, rpb);
   }
-  if (dgamma) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, 2 * C, C, dgamma, acc_dg);
-  if (dbeta) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part + C, p.grid, 2 * C, C, dbeta, acc_db);
+  if (dgamma && dbeta)        // partial rows are [dgamma | dbeta]: one fold over 2C columns
+    fold_columns<<<(unsigned)cdiv(2 * C, 64), 1024, 0, s>>>(part, p.grid, 2 * C, 2 * C, dgamma, acc_dg, C, dbeta, acc_db);
+  else if (dgamma)
+    fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, 2 * C, C, dgamma, acc_dg, C, nullptr, 0);
+  else if (dbeta)
+    fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part + C, p.grid, 2 * C, C, dbeta, acc_db, C, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1102,7 +1115,7 @@ hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, siz
     else
       colsum_partials_gen<bf16_t><<<dim3(1, p.gy), GEN_BLOCK, 0, s>>>(d.data, d.ld, R, C, p.rpb, part);
   }
-  fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.gy, C, C, out, acc);
+  fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.gy, C, C, out, acc, C, nullptr, 0);
   return hipGetLastError();
 }
 
