@@ -9,11 +9,14 @@
 // Fast path: a row is held in registers by a group of RW waves (RW = 1, 4 or
 // 16), each thread keeping NV 16-byte packs, so x (and d) are read from HBM
 // exactly once per op.  Reductions are wave butterflies then a fixed-order
-// LDS combine: results do not depend on scheduling.  Backward kernels run one
-// 1024-thread block per CU; each thread accumulates the parameter-gradient
-// terms of its own columns over the block's rows, the groups of a block are
-// folded in LDS in group order, and one partial row per block goes to the
-// workspace.  A separate pass sums the partial rows in block order.
+// LDS combine: results do not depend on scheduling.  Backward kernels run at
+// most 512 blocks of 512 threads (one or two per CU) whose rows interleave
+// (block b, group g takes rows b NG + g + k gridDim NG: the rows in flight
+// form one contiguous window, measured 5-15% faster than a contiguous run of
+// rows per block); each thread accumulates the parameter-gradient terms of
+// its own columns over the block's rows, the groups of a block are folded in
+// LDS in group order, and one partial row per block goes to the workspace.
+// A separate pass sums the partial rows in block order.
 //
 // Generic path (rows that do not fit in registers or are not 16-byte
 // aligned): one 256-thread block per row, several passes over global memory.
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && NV <= 2 ? 4 : 1) void 
     const void* __restrict__ d, int64_t ldd, const void* __restrict__ x, int64_t ldx,
     const float* __restrict__ gamma, const float* __restrict__ ir, int64_t ldir,
     void* __restrict__ dx, int64_t lddx, int acc_dx, float* __restrict__ part,
-    int64_t R, int64_t C, float invC, int64_t rpb) {
+    int64_t R, int64_t C, float invC) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BWD_BLOCK / G;
   extern __shared__ float red[];               // C floats
   __shared__ float lds[BWD_BLOCK / WAVE];
@@ -179,8 +182,10 @@ __global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && NV <= 2 ? 4 : 1) void 
 #pragma unroll
     for (int k = 0; k < V; ++k) pp[0][j][k] = 0.f;
   }
-  const int64_t start = (int64_t)blockIdx.x * rpb;
-  const int64_t end = min(R, start + rpb);
+  // rows interleaved over the blocks: step k of group g is row
+  // blockIdx.x NG + g + k gridDim.x NG, so the rows in flight across the
+  // chip at any time form one contiguous window of the tensor
+  const int64_t stride = (int64_t)gridDim.x * NG, first = (int64_t)blockIdx.x * NG, end = R;
   // two register sets of raw packs: while row base is reduced and written,
   // row base+NG is in flight; a set is refilled (row base+2NG) once its row
   // is written.  Only raw packs stay live (unpacked pack by pack where
@@ -189,16 +194,16 @@ __global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && NV <= 2 ? 4 : 1) void 
   // tensors than the unpacked ring at two waves per SIMD.
   RowPacks<T, NV, G> d0, x0, d1, x1;
   {
-    const int64_t r = start + g, r1 = start + NG + g;
+    const int64_t r = first + g, r1 = first + stride + g;
     d0.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
     x0.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
-    if (start + NG < end) {
+    if (first + stride < end) {
       d1.load(row_ptr<T>(d, r1 < end ? r1 : 0, ldd), gl, Ci, r1 < end);
       x1.load(row_ptr<T>(x, r1 < end ? r1 : 0, ldx), gl, Ci, r1 < end);
     }
   }
   auto step = [&](RowPacks<T, NV, G>& cd, RowPacks<T, NV, G>& cx, int64_t base) {
-    const int64_t r = base + g, rn = base + 2 * NG + g;
+    const int64_t r = base + g, rn = base + 2 * stride + g;
     const bool active = r < end;
     const float irv = active ? ir[r * ldir] : 0.f;
     float dot = 0.f;
@@ -232,14 +237,14 @@ __global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && NV <= 2 ? 4 : 1) void 
         }
       }
     }
-    if (base + 2 * NG < end) {
+    if (base + 2 * stride < end) {
       cd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
       cx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
     }
   };
-  for (int64_t base = start; base < end; base += 2 * NG) {
+  for (int64_t base = first; base < end; base += 2 * stride) {
     step(d0, x0, base);
-    if (base + NG < end) step(d1, x1, base + NG);
+    if (base + stride < end) step(d1, x1, base + stride);
   }
   if (part) fold_partials<NV, V, G, NG, 1, BWD_BLOCK>(pp, red, part, C);
 }
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
     const void* __restrict__ d, int64_t ldd, const void* __restrict__ x, int64_t ldx,
     const float* __restrict__ gamma, const float* __restrict__ mean, int64_t ldm,
     const float* __restrict__ rstd, int64_t ldr, void* __restrict__ dx, int64_t lddx,
-    int acc_dx, float* __restrict__ part, int64_t R, int64_t C, float invC, int64_t rpb) {
+    int acc_dx, float* __restrict__ part, int64_t R, int64_t C, float invC) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BWD_BLOCK / G;
   extern __shared__ float red[];               // 2C floats
   __shared__ float lds[2 * BWD_BLOCK / WAVE];
@@ -327,27 +332,29 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
 #pragma unroll
     for (int k = 0; k < V; ++k) { pp[0][j][k] = 0.f; pp[1][j][k] = 0.f; }
   }
-  const int64_t start = (int64_t)blockIdx.x * rpb;
-  const int64_t end = min(R, start + rpb);
+  // rows interleaved over the blocks: step k of group g is row
+  // blockIdx.x NG + g + k gridDim.x NG, so the rows in flight across the
+  // chip at any time form one contiguous window of the tensor
+  const int64_t stride = (int64_t)gridDim.x * NG, first = (int64_t)blockIdx.x * NG, end = R;
   RowPacks<T, NV, G> d0, x0, d1, x1;
   {
-    const int64_t r = start + g, r1 = start + NG + g;
+    const int64_t r = first + g, r1 = first + stride + g;
     d0.load(row_ptr<T>(d, r < end ? r : 0, ldd), gl, Ci, r < end);
     x0.load(row_ptr<T>(x, r < end ? r : 0, ldx), gl, Ci, r < end);
-    if (start + NG < end) {
+    if (first + stride < end) {
       d1.load(row_ptr<T>(d, r1 < end ? r1 : 0, ldd), gl, Ci, r1 < end);
       x1.load(row_ptr<T>(x, r1 < end ? r1 : 0, ldx), gl, Ci, r1 < end);
     }
   }
   auto step = [&](RowPacks<T, NV, G>& cd, RowPacks<T, NV, G>& cx, int64_t base) {
-    const int64_t r = base + g, rn = base + 2 * NG + g;
+    const int64_t r = base + g, rn = base + 2 * stride + g;
     const bool active = r < end;
     const float mu = active ? mean[r * ldm] : 0.f;
     const float rs = active ? rstd[r * ldr] : 0.f;
     float dv[NV][V], xh[NV][V];
     cd.unpack(dv);
     cx.unpack(xh);
-    if (base + 2 * NG < end) {
+    if (base + 2 * stride < end) {
       cd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
       cx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
     }
@@ -384,9 +391,9 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
       }
     }
   };
-  for (int64_t base = start; base < end; base += 2 * NG) {
+  for (int64_t base = first; base < end; base += 2 * stride) {
     step(d0, x0, base);
-    if (base + NG < end) step(d1, x1, base + NG);
+    if (base + stride < end) step(d1, x1, base + stride);
   }
   if (part) fold_partials<NV, V, G, NG, 2, BWD_BLOCK>(pp, red, part, C);
 }
@@ -694,28 +701,29 @@ __global__ __launch_bounds__(1024) void fold_columns(const float* __restrict__ p
 
 // First pass of a plain column sum (add_bias backward): a 1024-thread block
 // holds TPC threads per row (one 16-byte pack each) and 1024/TPC row phases;
-// block (bx, by) covers packs [bx*TPC, ...) of rows [by*rpb, ...).  The row
+// block (bx, by) covers packs [bx*TPC, ...) of rows by*nph + phase + k*gy*nph.  The row
 // phases are folded in LDS in phase order; one partial row per block row.
 template <typename T>
 __global__ __launch_bounds__(1024) void colsum_partials(
-    const void* __restrict__ d, int64_t ldd, int64_t R, int64_t C, int tpc, int64_t rpb,
+    const void* __restrict__ d, int64_t ldd, int64_t R, int64_t C, int tpc,
     float* __restrict__ part) {
   constexpr int V = io<T>::VEC;
   extern __shared__ float red[];                 // tpc * V floats
   const int ph = threadIdx.x / tpc, t = threadIdx.x % tpc, nph = 1024 / tpc;
   const int64_t c0 = ((int64_t)blockIdx.x * tpc + t) * V;
-  const int64_t start = (int64_t)blockIdx.y * rpb, end = min(R, start + rpb);
+  // rows interleaved over the block rows (contiguous window in flight)
+  const int64_t end = R, rstep = (int64_t)gridDim.y * nph;
   float a[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) a[k] = 0.f;
   if (c0 < C) {
-    int64_t r = start + ph;
+    int64_t r = (int64_t)blockIdx.y * nph + ph;
     // eight rows' packs in flight per thread, added in row order
     constexpr int U = 8;
-    for (; r + (U - 1) * nph < end; r += U * nph) {
+    for (; r + (U - 1) * rstep < end; r += U * rstep) {
       uint4 q[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) q[u] = load_raw<T>(row_ptr<T>(d, r + u * nph, ldd), c0, C);
+      for (int u = 0; u < U; ++u) q[u] = load_raw<T>(row_ptr<T>(d, r + u * rstep, ldd), c0, C);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float v[V];
@@ -724,7 +732,7 @@ __global__ __launch_bounds__(1024) void colsum_partials(
         for (int k = 0; k < V; ++k) a[k] += v[k];
       }
     }
-    for (; r < end; r += nph) {
+    for (; r < end; r += rstep) {
       float v0[V];
       load_pack<T>(row_ptr<T>(d, r, ldd), c0, C, v0, 0.f);
 #pragma unroll
@@ -930,7 +938,7 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
       auto kf = rms_bwd_fast<T, RW, NV>;
       p.grid = fit_grid((const void*)kf, BWD_BLOCK, shm, p.grid);
       kf<<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
-                                        dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC, cdiv(R, p.grid)));
+                                        dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC));
   } else {
     const int64_t rpb = cdiv(R, p.grid);
     if (dx)
@@ -994,7 +1002,7 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
       p.grid = fit_grid((const void*)kf, BWD_BLOCK, shm, p.grid);
       kf<<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
                                         (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr, dx ? dx->ld : 0,
-                                        acc_dx, part, R, C, invC, cdiv(R, p.grid)));
+                                        acc_dx, part, R, C, invC));
   } else {
     const int64_t rpb = cdiv(R, p.grid);
     if (dx)
@@ -1106,9 +1114,9 @@ hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, siz
   if (al) {
     const size_t shm = (size_t)p.tpc * V * sizeof(float);
     if (d.dtype == XT_F32)
-      colsum_partials<float><<<dim3(p.gx, p.gy), 1024, shm, s>>>(d.data, d.ld, R, C, p.tpc, p.rpb, part);
+      colsum_partials<float><<<dim3(p.gx, p.gy), 1024, shm, s>>>(d.data, d.ld, R, C, p.tpc, part);
     else
-      colsum_partials<bf16_t><<<dim3(p.gx, p.gy), 1024, shm, s>>>(d.data, d.ld, R, C, p.tpc, p.rpb, part);
+      colsum_partials<bf16_t><<<dim3(p.gx, p.gy), 1024, shm, s>>>(d.data, d.ld, R, C, p.tpc, part);
   } else {
     if (d.dtype == XT_F32)
       colsum_partials_gen<float><<<dim3(1, p.gy), GEN_BLOCK, 0, s>>>(d.data, d.ld, R, C, p.rpb, part);
