@@ -343,7 +343,8 @@ xt_status xt_op_fwd(xt_op op, const xt_params* prm, const xt_tensor* in, int n_i
       if (in[0].cols % prm->head_dim) return fail(XT_ERR_SHAPE, "rope: cols must be a multiple of head_dim");
       if (prm->seq_len <= 0) return fail(XT_ERR_INVALID_ARG, "rope needs seq_len > 0");
       if (!(prm->rope_base > 0.f)) return fail(XT_ERR_INVALID_ARG, "rope_base must be > 0");
-      if (in[0].data == out[0].data) return fail(XT_ERR_INVALID_ARG, "rope cannot run in place");
+      if (in[0].rows * in[0].cols > 0 && in[0].data == out[0].data)
+        return fail(XT_ERR_INVALID_ARG, "rope cannot run in place");
       return hip_status(launch_rope(in[0], out[0], false, prm->head_dim, prm->rope_base, prm->seq_len, false, s), "rope");
     }
     case XT_OP_DROPOUT: {

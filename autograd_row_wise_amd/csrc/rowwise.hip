@@ -953,7 +953,10 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
 hipError_t launch_rms_bwd(const xt_tensor& d, const xt_tensor& x, const float* gamma,
                           const xt_tensor& inv_rms, const xt_tensor* dx, bool acc_dx,
                           float* dgamma, bool acc_dgamma, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (d.rows == 0) return hipSuccess;
+  if (d.rows == 0) {                 // dgamma is a sum over no rows: zero
+    if (dgamma && !acc_dgamma) return launch_fill_f32(dgamma, d.cols, 0.f, s);
+    return hipSuccess;
+  }
   return d.dtype == XT_F32 ? rms_bwd_t<float>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, ws_bytes, s)
                            : rms_bwd_t<bf16_t>(d, x, gamma, inv_rms, dx, acc_dx, dgamma, acc_dgamma, ws, ws_bytes, s);
 }
@@ -1025,7 +1028,12 @@ hipError_t launch_ln_bwd(const xt_tensor& d, const xt_tensor& x, const float* ga
                          const xt_tensor& mean, const xt_tensor& rstd,
                          const xt_tensor* dx, bool acc_dx, float* dgamma, bool acc_dgamma,
                          float* dbeta, bool acc_dbeta, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (d.rows == 0) return hipSuccess;
+  if (d.rows == 0) {                 // dgamma, dbeta are sums over no rows: zero
+    hipError_t e = hipSuccess;
+    if (dgamma && !acc_dgamma) e = launch_fill_f32(dgamma, d.cols, 0.f, s);
+    if (e == hipSuccess && dbeta && !acc_dbeta) e = launch_fill_f32(dbeta, d.cols, 0.f, s);
+    return e;
+  }
   return d.dtype == XT_F32
              ? ln_bwd_t<float>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, ws_bytes, s)
              : ln_bwd_t<bf16_t>(d, x, gamma, mean, rstd, dx, acc_dx, dgamma, acc_dgamma, dbeta, acc_dbeta, ws, ws_bytes, s);
