@@ -38,11 +38,11 @@ template <> struct gcfg<float> { static constexpr int BK = 16, PAD = 4; };
 // Non-transposed storage ([rows][K], k contiguous): each thread moves
 // 16-byte chunks along k.  Transposed storage ([K][rows]): chunks along rows,
 // scattered into the [row][k] LDS layout.
-template <typename TA, bool KCONTIG>
+template <typename TA, bool KCONTIG, int ROWS = BM>
 struct TileLoader {
   static constexpr int BK = gcfg<TA>::BK;
   static constexpr int V = 16 / sizeof(TA);                    // elements per chunk
-  static constexpr int CHUNKS = BM * BK / V;                   // chunks per tile
+  static constexpr int CHUNKS = ROWS * BK / V;                 // chunks per tile
   static constexpr int PER_T = CHUNKS / NT;                    // chunks per thread
   uint4 r[PER_T];
 
@@ -54,7 +54,7 @@ struct TileLoader {
       const int c = i * NT + threadIdx.x;
       int row, kk;
       if (KCONTIG) { row = c / (BK / V); kk = (c % (BK / V)) * V; }
-      else { kk = c / (BM / V); row = (c % (BM / V)) * V; }
+      else { kk = c / (ROWS / V); row = (c % (ROWS / V)) * V; }
       const int64_t gr = row0 + row, gk = k0 + kk;
       if (full) {
         const TA* p = KCONTIG ? g + gr * ld + gk : g + gk * ld + gr;
@@ -80,7 +80,7 @@ struct TileLoader {
         const int row = c / (BK / V), kk = (c % (BK / V)) * V;
         *reinterpret_cast<uint4*>(lds + row * LDK + kk) = r[i];
       } else {
-        const int kk = c / (BM / V), row = (c % (BM / V)) * V;
+        const int kk = c / (ROWS / V), row = (c % (ROWS / V)) * V;
         const TA* v = reinterpret_cast<const TA*>(&r[i]);
 #pragma unroll
         for (int j = 0; j < V; ++j) lds[(row + j) * LDK + kk] = v[j];
@@ -89,31 +89,31 @@ struct TileLoader {
   }
 };
 
-template <typename TA>
+template <typename TA, int TT = 2>
 __device__ __forceinline__ void mfma_tile(const TA* As, const TA* Bs, int wm, int wn,
-                                          f32x16_t (&acc)[2][2]) {
+                                          f32x16_t (&acc)[TT][TT]) {
   constexpr int BK = gcfg<TA>::BK, LDK = BK + gcfg<TA>::PAD;
   const int l = threadIdx.x % WAVE;
   const int lr = l % 32, lk = (l / 32) * 8;
   if constexpr (sizeof(TA) == 2) {
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8_t a[2], b[2];
+      bf16x8_t a[TT], b[TT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < TT; ++t) {
         a[t] = *reinterpret_cast<const bf16x8_t*>(As + (wm + t * 32 + lr) * LDK + ks + lk);
         b[t] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn + t * 32 + lr) * LDK + ks + lk);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   } else {
-    float a[2][8], b[2][8];
+    float a[TT][8], b[TT][8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TT; ++t) {
       const float4* pa = reinterpret_cast<const float4*>(As + (wm + t * 32 + lr) * LDK + lk);
       const float4* pb = reinterpret_cast<const float4*>(Bs + (wn + t * 32 + lr) * LDK + lk);
       const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
@@ -125,23 +125,25 @@ __device__ __forceinline__ void mfma_tile(const TA* As, const TA* Bs, int wm, in
 #pragma unroll
     for (int k = 0; k < 8; ++k)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][k], b[j][k], acc[i][j], 0, 0, 0);
   }
 }
 
-template <typename TA, typename TC, bool TRANS_A, bool TRANS_B>
+// TB x TB tiles of C (TB = 128, or 64 for products with few 128-tiles: four
+// times the blocks, each wave one 32 x 32 accumulator).
+template <typename TA, typename TC, bool TRANS_A, bool TRANS_B, int TB = BM>
 __global__ __launch_bounds__(NT) void gemm_k(
     const TA* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
     const TA* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
     TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
     int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
     int64_t kchunk, int64_t nbatch, int64_t scs) {
-  constexpr int BK = gcfg<TA>::BK, LDK = BK + gcfg<TA>::PAD;
-  __shared__ __align__(16) TA As[2][BM * LDK];
-  __shared__ __align__(16) TA Bs[2][BN * LDK];
+  constexpr int BK = gcfg<TA>::BK, LDK = BK + gcfg<TA>::PAD, TT = TB / 64;
+  __shared__ __align__(16) TA As[2][TB * LDK];
+  __shared__ __align__(16) TA Bs[2][TB * LDK];
 
   // gridDim.z = splits x batches; split s sums k in [s*kchunk, (s+1)*kchunk)
   const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
@@ -150,23 +152,23 @@ __global__ __launch_bounds__(NT) void gemm_k(
   B += b0 * sb0 + b1 * sb1 + (TRANS_B ? kb : kb * ldb);
   C += b0 * sc0 + b1 * sc1 + split * scs;
   K = K - kb < kchunk ? K - kb : kchunk;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
   const int w = threadIdx.x / WAVE;
-  const int wm = (w / 2) * 64, wn = (w % 2) * 64;
+  const int wm = (w / 2) * (TB / 2), wn = (w % 2) * (TB / 2);
 
   // A as [M][K] is k-contiguous unless transposed; B as [K][N] is k-contiguous
   // only when transposed ([N][K] storage).
-  TileLoader<TA, !TRANS_A> la;
-  TileLoader<TA, TRANS_B> lb;
-  const bool fullMN = (m0 + BM <= M) && (n0 + BN <= N);
+  TileLoader<TA, !TRANS_A, TB> la;
+  TileLoader<TA, TRANS_B, TB> lb;
+  const bool fullMN = (m0 + TB <= M) && (n0 + TB <= N);
   const bool alA = (((uintptr_t)A) & 15) == 0 && ((lda * (int64_t)sizeof(TA)) & 15) == 0;
   const bool alB = (((uintptr_t)B) & 15) == 0 && ((ldb * (int64_t)sizeof(TA)) & 15) == 0;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[TT][TT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TT; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(NT) void gemm_k(
         la.load(A, lda, m0, M, k0, K, full);
         lb.load(B, ldb, n0, N, k0, K, full);
       }
-      mfma_tile<TA>(As[cur], Bs[cur], wm, wn, acc);
+      mfma_tile<TA, TT>(As[cur], Bs[cur], wm, wn, acc);
       if (more) {
         la.store(As[cur ^ 1]);
         lb.store(Bs[cur ^ 1]);
@@ -200,9 +202,9 @@ __global__ __launch_bounds__(NT) void gemm_k(
   // row 8*(q/4) + 4*(l/32) + q%4, column l%32 of the tile
   const int l = threadIdx.x % WAVE;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TT; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm + i * 32 + 8 * (q / 4) + 4 * (l / 32) + (q % 4);
@@ -682,6 +684,19 @@ __global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
       }
 }
 
+// f32 products with at most 256 tiles of 64 x 64 (one per CU) run those
+// tiles: a product of a few hundred rows (the tiny block's projections and
+// attention scores) then spreads over four times the CUs of its 128 x 128
+// tiles instead of being split along K and summed in a second pass.  Larger
+// outputs keep the 128 x 128 kernels (with split-K for long K).
+template <typename TA>
+bool small_tiles(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C) {
+  (void)A; (void)ta; (void)B; (void)tb;
+  if constexpr (sizeof(TA) == 2) return false;
+  const int64_t t64 = ((C.rows + 63) / 64) * ((C.cols + 63) / 64) * C.nb[0] * C.nb[1];
+  return t64 > 0 && t64 <= 256;
+}
+
 template <typename TA>
 bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C) {
   const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
@@ -708,16 +723,20 @@ struct SplitPlan { int64_t S, kchunk; };
 // lane; each block puts one wave on each SIMD): the f32 large-tile kernel
 // uses 152 (3 per CU), the bf16 one 512 (1 per CU), the 128 x 128 kernel
 // 172 (2 per CU).
-SplitPlan split_plan(bool bf16, bool bigk, int64_t M, int64_t N, int64_t K, int64_t nbatch, size_t ws_bytes) {
-  const int64_t bm = bigk ? (bf16 ? 256 : 128) : BM, bn = bigk ? (bf16 ? 256 : 128) : BN;
+SplitPlan split_plan(bool bf16, bool bigk, bool small, int64_t M, int64_t N, int64_t K, int64_t nbatch,
+                     size_t ws_bytes) {
+  const int64_t tb = small ? 64 : BM;
+  const int64_t bm = bigk ? (bf16 ? 256 : 128) : tb, bn = bigk ? (bf16 ? 256 : 128) : tb;
   const int64_t bk = bigk ? (bf16 ? big<bf16_t>::BK : big<float>::BK) : (bf16 ? gcfg<bf16_t>::BK : gcfg<float>::BK);
-  const int64_t resident = bigk ? (bf16 ? 256 : 768) : 512;
+  const int64_t resident = bigk ? (bf16 ? 256 : 768) : (small ? 256 : 512);
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * nbatch;
   const int64_t nk = (K + bk - 1) / bk;
   const int64_t per = nbatch * M * N * (int64_t)sizeof(float);
   if (tiles <= 0 || nk <= 0 || per <= 0) return {1, K};
   int64_t S = resident / tiles;
-  S = std::min<int64_t>(S, nk / 4);
+  // a slice must be long enough to pay for the summing pass: at least 4 K
+  // tiles, and for the 64-tiles at least 256 of K
+  S = std::min<int64_t>(S, small ? K / 256 : nk / 4);
   S = std::min<int64_t>(S, 16);
   S = std::min<int64_t>(S, (int64_t)(ws_bytes / (size_t)per));
   if (S < 2) return {1, K};
@@ -777,7 +796,7 @@ hipError_t splitk_sum(const float* P, int64_t S, int64_t scs, const xt_tensor& C
 // of kchunk (kchunk = K: no split), writing through C's own strides, or
 // (split) into partial slices `scs` elements apart.
 template <typename TA, typename TC>
-hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
+hipError_t gemm_run(bool bigk, bool small, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
                     TC* c, int64_t ldc, int64_t sc0, int64_t sc1, int64_t M, int64_t N, int64_t K,
                     int64_t nb0, int64_t nb1, float alpha, bool acc, int64_t S, int64_t kchunk, int64_t scs,
                     hipStream_t s) {
@@ -814,11 +833,17 @@ hipError_t gemm_run(bool bigk, const xt_tensor& A, bool ta, const xt_tensor& B, 
     return hipGetLastError();
   }
   {
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)(S * nbatch));
-#define XT_GEMM_LAUNCH(TA_, TB_)                                                              \
-    gemm_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0], \
-                                                 B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1,     \
-                                                 alpha, acc ? 1 : 0, kchunk, nbatch, scs)
+    const int tbs = small ? 64 : BM;
+    dim3 grid((unsigned)((N + tbs - 1) / tbs), (unsigned)((M + tbs - 1) / tbs), (unsigned)(S * nbatch));
+#define XT_GEMM_LAUNCH(TA_, TB_)                                                                        \
+    if (small)                                                                                          \
+      gemm_k<TA, TC, TA_, TB_, 64><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0],    \
+                                                       B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1, alpha, \
+                                                       acc ? 1 : 0, kchunk, nbatch, scs);              \
+    else                                                                                                \
+      gemm_k<TA, TC, TA_, TB_><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0],        \
+                                                   B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1,            \
+                                                   alpha, acc ? 1 : 0, kchunk, nbatch, scs)
     if (!ta && !tb) XT_GEMM_LAUNCH(false, false);
     else if (!ta && tb) XT_GEMM_LAUNCH(false, true);
     else if (ta && !tb) XT_GEMM_LAUNCH(true, false);
@@ -834,14 +859,15 @@ hipError_t gemm_go(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, con
   const int64_t M = C.rows, N = C.cols, K = ta ? A.rows : A.cols;
   const int64_t nb0 = C.nb[0], nb1 = C.nb[1], nbatch = nb0 * nb1;
   if (M == 0 || N == 0 || nbatch == 0) return hipSuccess;
-  const bool bigk = big_ok<TA>(A, ta, B, tb, C);
-  const SplitPlan sp = split_plan(sizeof(TA) == 2, bigk, M, N, K, nbatch, ws ? ws_bytes : 0);
+  const bool small = small_tiles<TA>(A, ta, B, tb, C);
+  const bool bigk = !small && big_ok<TA>(A, ta, B, tb, C);
+  const SplitPlan sp = split_plan(sizeof(TA) == 2, bigk, small, M, N, K, nbatch, ws ? ws_bytes : 0);
   if (sp.S == 1)
-    return gemm_run<TA, TC>(bigk, A, ta, B, tb, (TC*)C.data, C.ld, C.sb[0], C.sb[1], M, N, K, nb0, nb1,
+    return gemm_run<TA, TC>(bigk, small, A, ta, B, tb, (TC*)C.data, C.ld, C.sb[0], C.sb[1], M, N, K, nb0, nb1,
                             alpha, acc, 1, K, 0, s);
   float* P = (float*)ws;
   const int64_t scs = nbatch * M * N;
-  hipError_t e = gemm_run<TA, float>(bigk, A, ta, B, tb, P, N, nb1 * M * N, M * N, M, N, K, nb0, nb1,
+  hipError_t e = gemm_run<TA, float>(bigk, small, A, ta, B, tb, P, N, nb1 * M * N, M * N, M, N, K, nb0, nb1,
                                      1.f, false, sp.S, sp.kchunk, scs, s);
   if (e != hipSuccess) return e;
   return splitk_sum<TC>(P, sp.S, scs, C, nbatch, alpha, acc, s);
@@ -866,6 +892,8 @@ size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, 
   xt_tensor C{};
   C.rows = M;
   C.cols = N;
+  C.nb[0] = nbatch;
+  C.nb[1] = 1;
   const bool bf = A.dtype == XT_BF16;
   // Which kernel runs depends on the operands' alignment; when the views
   // carry no pointers yet, size for the larger of the two plans.
@@ -877,10 +905,12 @@ size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, 
     a.data = b.data = nullptr;
     cand[1] = bf ? big_ok<bf16_t>(a, ta, b, tb, C) : big_ok<float>(a, ta, b, tb, C);
   }
+  const bool small = bf ? small_tiles<bf16_t>(A, ta, B, tb, C) : small_tiles<float>(A, ta, B, tb, C);
+  if (small) cand[0] = cand[1] = false;
   size_t best = 0;
-  for (int k = 0; k < 2; ++k) {
-    if (!cand[k]) continue;
-    const SplitPlan sp = split_plan(bf, k == 1, M, N, K, nbatch, SIZE_MAX);
+  for (int k = 0; k < 3; ++k) {
+    if (k < 2 ? !cand[k] : !small) continue;
+    const SplitPlan sp = split_plan(bf, k == 1, k == 2, M, N, K, nbatch, SIZE_MAX);
     if (sp.S > 1) best = std::max(best, (size_t)sp.S * (size_t)(nbatch * M * N) * sizeof(float));
   }
   return best;
