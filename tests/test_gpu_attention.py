@@ -4,8 +4,9 @@ not, Dh 32 / 64 / 128, sequence lengths that leave ragged tiles (32-row f32
 tiles; 128-row blocks and 32 / 64-row tiles of the bf16 kernels), f32 and
 bf16 storage, accumulate mode, bitwise reproducibility; the bf16 path on
 unaligned rows (the generic kernels); two heads of the 2 x 2048 x 16 x 128
-bf16 workload against the oracle; and the fused op on the tape inside the
-tiny block against the composed attention."""
+bf16 workload against the oracle; two heads of a 2 x 4096-token causal
+product large enough for the paired grid; and the fused op on the tape
+inside the tiny block against the composed attention."""
 import math
 
 import numpy as np
@@ -206,3 +207,26 @@ def test_attention_bench_shape_two_heads():
         for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
             norm_close(host(g[rows, cols]), r, 3e-2, (name, b, hd))
     del w
+
+
+def test_attention_causal_paired_query_blocks():
+    """2 x 4096 tokens, 16 heads x 128, causal, bf16: 512 (heaviest,
+    lightest) pairs of 128-query blocks, two per CU on a 256-CU MI355X, so
+    the forward runs its paired grid.  Heads (sequence 0, head 5) and
+    (sequence 1, head 14) checked in full against the oracle."""
+    B, S, H, Dh = 2, 4096, 16, 128
+    R, C = B * S, H * Dh
+    alpha = 1.0 / math.sqrt(Dh)
+    x = {n: synth.device_normal((R, C), 15, n, dtype="bf16") for n in ("q", "k", "v")}
+    prm = xt.params(alpha=alpha, causal=1, seq_len=S, head_dim=Dh)
+    out = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    xt.xt_op_fwd(xt.OP.ATTENTION, prm, [xt.view(x["q"]), xt.view(x["k"]), xt.view(x["v"])],
+                 [xt.view(out), xt.view(lse)])
+    torch.cuda.synchronize()
+    for b, hd in ((0, 5), (1, 14)):
+        rows, cols = slice(b * S, (b + 1) * S), slice(hd * Dh, (hd + 1) * Dh)
+        sl = {n: host(t[rows, cols]) for n, t in x.items()}
+        o_ref, l_ref = ops.attention(sl["q"], sl["k"], sl["v"], S, 1, Dh, alpha, True)
+        norm_close(host(out[rows, cols]), o_ref, 2e-2, ("out", b, hd))
+        np.testing.assert_allclose(host(lse[rows, hd:hd + 1]), l_ref, rtol=1e-5, atol=1e-5)
