@@ -621,13 +621,13 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                      const bf16_t* __restrict__ out, const float* __restrict__ lse,
                                                      float* __restrict__ dd, bf16_t* __restrict__ dq, int acc_dq,
-                                                     Geo g, float alpha, int causal, int nqb) {
+                                                     Geo g, float alpha, int causal, int nqb, int pair) {
   constexpr int BK = 32, KS = fa::RS<DH>, KT = BK * KS, ST = 2 * KT;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
-  int qb;
   int64_t hb;
-  fa_block(nqb, causal ? 1 : 0, qb, hb);
+  // one query block of (sequence, head) hb
+  auto run = [&](int qb) {
   const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
   const int64_t q0 = (int64_t)qb * 128, qw = q0 + 32 * w, qme = qw + c;
   const bool qok = qme < g.S;
@@ -724,6 +724,20 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
         }
         *reinterpret_cast<uint2*>(row + d) = make_uint2(f2bf2(r[0], r[1]), f2bf2(r[2], r[3]));
       }
+  }
+  };
+  if (pair) {                        // (heaviest, lightest) pairs, as in the forward
+    const int np = (nqb + 1) / 2, HB = gridDim.x / np, r = blockIdx.x / HB;
+    hb = blockIdx.x % HB;
+    run(nqb - 1 - r);
+    if (r != nqb - 1 - r) {
+      __syncthreads();
+      run(r);
+    }
+  } else {
+    int qb;
+    fa_block(nqb, causal ? 1 : 0, qb, hb);
+    run(qb);
   }
 }
 
@@ -886,17 +900,21 @@ int device_cus() {
   return cus;
 }
 
+// Causal query blocks go in (heaviest, lightest) pairs when the paired grid
+// still holds two blocks per CU (measured, forward: 1 x 8192 tokens, 16
+// heads: 359 -> 315 us); with fewer pairs, one block per CU runs slower than
+// the unpaired grid (2 x 2048 tokens: 63 -> 73 us).
+int fa_pair(const AttnArgs& a, int nqb) {
+  const int64_t pairs = (int64_t)((nqb + 1) / 2) * a.H * a.B;
+  const int cus = device_cus();
+  return a.causal && nqb > 1 && cus > 0 && pairs >= 2 * (int64_t)cus ? 1 : 0;
+}
+
 template <int DH>
 hipError_t fa_fwd(const AttnArgs& a, hipStream_t s) {
   const Geo g{a.S, a.H, a.ld, a.ldl};
   const int nqb = (int)((a.S + 127) / 128);
-  // Causal query blocks go in (heaviest, lightest) pairs when the paired
-  // grid still holds two blocks per CU (measured: 1 x 8192 tokens, 16
-  // heads: 348 -> 302 us); with fewer pairs, one block per CU runs slower
-  // than the unpaired grid (2 x 2048 tokens: 63 -> 73 us).
-  const int64_t pairs = (int64_t)((nqb + 1) / 2) * a.H * a.B;
-  const int cus = device_cus();
-  const int pair = a.causal && nqb > 1 && cus > 0 && pairs >= 2 * (int64_t)cus ? 1 : 0;
+  const int pair = fa_pair(a, nqb);
   const int nb = pair ? (nqb + 1) / 2 : nqb;
   fa_fwd_k<DH><<<(unsigned)(nb * a.H * a.B), fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                               (const bf16_t*)a.v, (bf16_t*)a.out, a.lse, g, a.alpha,
@@ -909,9 +927,11 @@ hipError_t fa_bwd(const AttnArgs& a, hipStream_t s) {
   const Geo g{a.S, a.H, a.ld, a.ldl};
   const int nb = (int)((a.S + 127) / 128);
   const unsigned grid = (unsigned)(nb * a.H * a.B);
-  fa_dq_k<DH><<<grid, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
-                                      (const bf16_t*)a.dout, (const bf16_t*)a.out, a.lse, a.dd, (bf16_t*)a.dq,
-                                      a.acc_dq, g, a.alpha, a.causal, nb);
+  const int pair = fa_pair(a, nb);
+  const unsigned gq = pair ? (unsigned)((nb + 1) / 2 * a.H * a.B) : grid;
+  fa_dq_k<DH><<<gq, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+                                    (const bf16_t*)a.dout, (const bf16_t*)a.out, a.lse, a.dd, (bf16_t*)a.dq,
+                                    a.acc_dq, g, a.alpha, a.causal, nb, pair);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (!a.dk && !a.dv)) return e;
   fa_dkv_k<DH><<<grid, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,

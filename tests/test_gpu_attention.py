@@ -212,17 +212,22 @@ def test_attention_bench_shape_two_heads():
 def test_attention_causal_paired_query_blocks():
     """2 x 4096 tokens, 16 heads x 128, causal, bf16: 512 (heaviest,
     lightest) pairs of 128-query blocks, two per CU on a 256-CU MI355X, so
-    the forward runs its paired grid.  Heads (sequence 0, head 5) and
-    (sequence 1, head 14) checked in full against the oracle."""
+    the forward and the dQ pass run their paired grids.  Heads (sequence 0,
+    head 5) and (sequence 1, head 14) checked in full against the oracle:
+    output, log-sum-exp and the three gradients."""
     B, S, H, Dh = 2, 4096, 16, 128
     R, C = B * S, H * Dh
     alpha = 1.0 / math.sqrt(Dh)
-    x = {n: synth.device_normal((R, C), 15, n, dtype="bf16") for n in ("q", "k", "v")}
+    x = {n: synth.device_normal((R, C), 15, n, dtype="bf16") for n in ("q", "k", "v", "dout")}
     prm = xt.params(alpha=alpha, causal=1, seq_len=S, head_dim=Dh)
     out = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
-    xt.xt_op_fwd(xt.OP.ATTENTION, prm, [xt.view(x["q"]), xt.view(x["k"]), xt.view(x["v"])],
-                 [xt.view(out), xt.view(lse)])
+    ins = [xt.view(x["q"]), xt.view(x["k"]), xt.view(x["v"])]
+    xt.xt_op_fwd(xt.OP.ATTENTION, prm, ins, [xt.view(out), xt.view(lse)])
+    grads = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    w, wp, wb = xt.workspace(xt.OP.ATTENTION, 1, prm, ins)
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(x["dout"]), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in grads], 0, wp, wb)
     torch.cuda.synchronize()
     for b, hd in ((0, 5), (1, 14)):
         rows, cols = slice(b * S, (b + 1) * S), slice(hd * Dh, (hd + 1) * Dh)
@@ -230,3 +235,7 @@ def test_attention_causal_paired_query_blocks():
         o_ref, l_ref = ops.attention(sl["q"], sl["k"], sl["v"], S, 1, Dh, alpha, True)
         norm_close(host(out[rows, cols]), o_ref, 2e-2, ("out", b, hd))
         np.testing.assert_allclose(host(lse[rows, hd:hd + 1]), l_ref, rtol=1e-5, atol=1e-5)
+        refs = ops.attention_bwd(sl["dout"], sl["q"], sl["k"], sl["v"], S, 1, Dh, alpha, True)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+            norm_close(host(g[rows, cols]), r, 3e-2, (name, b, hd))
+    del w
