@@ -19,6 +19,7 @@
 // pass) and the total is added to dE[v]: one rounding per dE row.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <utility>
 
@@ -95,9 +96,35 @@ __device__ __forceinline__ uint64_t bitonic_keep(uint64_t mine, uint64_t other, 
   return lo == up ? mn : mx;
 }
 
+// Zero fill of the table gradient by blocks [nsort, gridDim.x) of the sort
+// launch, so the 50257 x 768 f32 fill (154 MB, the largest step of the
+// backward) streams while the few sort blocks run.  z: first byte of dE,
+// nrows rows of rowb bytes, ldz bytes apart.
+__device__ __forceinline__ void zero_rows(char* __restrict__ z, int64_t ldz, int64_t rowb, int64_t nrows, int f,
+                                          int nf) {
+  const int t = threadIdx.x;
+  const bool al = ((uintptr_t)z % 16 == 0) && (ldz % 16 == 0) && (rowb % 16 == 0);
+  if (al && ldz == rowb) {                            // one contiguous range of 16-byte packs
+    const int64_t np = nrows * rowb / 16;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    u32x4_t* P = reinterpret_cast<u32x4_t*>(z);
+    for (int64_t i = (int64_t)f * SORT_T + t; i < np; i += (int64_t)nf * SORT_T) __builtin_nontemporal_store(zero, P + i);
+  } else {                                            // row by row, 2-byte stores (both element types)
+    for (int64_t r = f; r < nrows; r += nf) {
+      uint16_t* row = reinterpret_cast<uint16_t*>(z + r * ldz);
+      for (int64_t c = t; c < rowb / 2; c += SORT_T) row[c] = 0;
+    }
+  }
+}
+
 __global__ __launch_bounds__(SORT_T) void embed_sort_k(const int32_t* __restrict__ ids, int64_t ldi, int64_t R,
-                                                        int64_t V, uint64_t* __restrict__ keys) {
+                                                        int64_t V, uint64_t* __restrict__ keys, char* __restrict__ z,
+                                                        int64_t ldz, int64_t rowb, int nsort) {
   static_assert(L == 2 * SORT_T, "two keys per thread");
+  if ((int)blockIdx.x >= nsort) {
+    zero_rows(z, ldz, rowb, V, (int)blockIdx.x - nsort, (int)gridDim.x - nsort);
+    return;
+  }
   __shared__ uint64_t k[L];
   const int64_t r0 = (int64_t)blockIdx.x * L;
   const int n = (int)(R - r0 < L ? R - r0 : L);
@@ -307,13 +334,17 @@ template <typename T>
 hipError_t bwd_t(const xt_tensor& d, const int32_t* ids, int64_t ldi, const xt_tensor& dE, bool acc, void* ws,
                  hipStream_t s) {
   const int64_t R = d.rows, D = d.cols, V = dE.rows;
-  if (!acc) {
-    const hipError_t e = launch_grads_scale(&dE, 1, true, 0.f, nullptr, s);
-    if (e != hipSuccess) return e;
+  if (R == 0 || D == 0) {               // no rows: dE is zero unless accumulating
+    if (acc || D == 0) return hipSuccess;
+    return launch_grads_scale(&dE, 1, true, 0.f, nullptr, s);
   }
-  if (R == 0 || D == 0) return hipSuccess;
   EmbedWs w = carve(ws, R);
-  embed_sort_k<<<(unsigned)((R + L - 1) / L), SORT_T, 0, s>>>(ids, ldi, R, V, w.k0);
+  const int nsort = (int)((R + L - 1) / L);
+  const int64_t rowb = D * (int64_t)sizeof(T), tb = V * rowb;
+  // fill blocks: about 64 KB of zeros each, at most 2048
+  const int nfill = acc || tb == 0 ? 0 : (int)std::min<int64_t>(2048, std::max<int64_t>(1, tb / 65536));
+  embed_sort_k<<<(unsigned)(nsort + nfill), SORT_T, 0, s>>>(ids, ldi, R, V, w.k0, (char*)dE.data,
+                                                            dE.ld * (int64_t)sizeof(T), rowb, nsort);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint64_t *src = w.k0, *dst = w.k1;
