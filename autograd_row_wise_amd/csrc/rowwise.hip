@@ -39,8 +39,8 @@ constexpr int BWD_GRID_MAX = 512;     // two backward blocks per CU
 // whichever CU is free stream 8-15% faster than resident blocks looping over
 // many rows each (no tail of late blocks).  rms/layer-norm forward blocks
 // still take NORM_FWD_STEPS row steps per group, which amortises the gamma
-// (and beta) loads; softmax rows of 8 waves or more keep a 4096-block grid,
-// measured faster for 32K-wide rows.
+// (and beta) loads; softmax rows of 8 waves or more keep a 4096-block grid
+// (8192 for the backward), measured faster for 32K-wide rows.
 constexpr int NORM_FWD_STEPS = 4;
 constexpr int LONG_ROW_GRID = 4096;
 constexpr int GEN_BLOCK = 256;
@@ -830,7 +830,8 @@ RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
     int64_t g;
     if (is_bwd(kind)) g = std::min<int64_t>(cdiv(R, p.groups), BWD_GRID_MAX);
     else if (kind == RK_RMS_FWD || kind == RK_LN_FWD) g = cdiv(R, (int64_t)p.groups * NORM_FWD_STEPS);
-    else g = p.rw <= 4 ? cdiv(R, p.groups) : std::min<int64_t>(cdiv(R, p.groups), LONG_ROW_GRID);
+    else g = p.rw <= 4 ? cdiv(R, p.groups)
+                       : std::min<int64_t>(cdiv(R, p.groups), kind == RK_SM_BWD ? 2 * LONG_ROW_GRID : LONG_ROW_GRID);
     p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(g, INT32_MAX));
   } else {
     p.rw = 4; p.nv = 0; p.block = GEN_BLOCK; p.groups = 1;
