@@ -43,7 +43,18 @@ xt_status check_view(const xt_tensor* t, const char* name) {
   if (t->rows < 0 || t->cols < 0) return fail(XT_ERR_SHAPE, "%s: negative shape", name);
   if (t->rows > 0 && t->ld < t->cols) return fail(XT_ERR_SHAPE, "%s: ld (%lld) < cols (%lld)", name, (long long)t->ld, (long long)t->cols);
   if (t->nb[0] < 1 || t->nb[1] < 1) return fail(XT_ERR_SHAPE, "%s: batch extents must be >= 1", name);
-  if (t->rows * t->cols > 0 && !t->data) return fail(XT_ERR_INVALID_ARG, "%s: null data", name);
+  if (t->sb[0] < 0 || t->sb[1] < 0) return fail(XT_ERR_SHAPE, "%s: negative batch stride", name);
+  if (t->rows > 0 && t->cols > 0) {
+    // one past the last element, in elements: every index the kernels form
+    // stays below it, so it must not wrap (bound: 2^56 elements)
+    int64_t end = 0, b0 = 0, b1 = 0;
+    if (__builtin_mul_overflow(t->rows - 1, t->ld, &end) || __builtin_add_overflow(end, t->cols, &end) ||
+        __builtin_mul_overflow(t->nb[0] - 1, t->sb[0], &b0) || __builtin_add_overflow(end, b0, &end) ||
+        __builtin_mul_overflow(t->nb[1] - 1, t->sb[1], &b1) || __builtin_add_overflow(end, b1, &end) ||
+        end > (INT64_C(1) << 56))
+      return fail(XT_ERR_SHAPE, "%s: extent of the view overflows", name);
+    if (!t->data) return fail(XT_ERR_INVALID_ARG, "%s: null data", name);
+  }
   return XT_OK;
 }
 

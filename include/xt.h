@@ -62,6 +62,9 @@ typedef enum { XT_F32 = 0, XT_BF16 = 1, XT_I32 = 2, XT_U8 = 3 } xt_dtype;
  * A caller-owned device view, row-major: element (r, c) of batch (i, j)
  * lives at data + i*sb[0] + j*sb[1] + r*ld + c  (all in elements).
  * Unbatched views use nb = {1, 1}, sb = {0, 0}; only MATMUL reads nb/sb.
+ * Batch strides are >= 0 (0 broadcasts); a non-empty view's extent,
+ * (nb[0]-1)*sb[0] + (nb[1]-1)*sb[1] + (rows-1)*ld + cols, must stay within
+ * 2^56 elements, else XT_ERR_SHAPE.
  * bf16 is the upper half of an IEEE binary32 (round-to-nearest-even).
  */
 typedef struct {

@@ -62,6 +62,16 @@ def test_validation_rejects_without_launch():
     with pytest.raises(xt.XtError) as e:
         xt.xt_op_fwd(xt.OP.SILU, xt.params(), [host_view(2, 4, ld=3)], [host_view(2, 4)], stream=C.c_void_p(0))
     assert e.value.status == 2
+    # a view whose extent wraps 64-bit element offsets, and a negative batch stride
+    for big in (host_view(1 << 40, 1 << 40), host_view(2, 4, ld=(1 << 62))):
+        with pytest.raises(xt.XtError) as e:
+            xt.xt_op_fwd(xt.OP.SILU, xt.params(), [big], [host_view(2, 4)], stream=C.c_void_p(0))
+        assert e.value.status == 2 and "extent" in str(e.value)
+    neg = host_view(2, 4)
+    neg.sb[0] = -8
+    with pytest.raises(xt.XtError) as e:
+        xt.xt_op_fwd(xt.OP.SILU, xt.params(), [neg], [host_view(2, 4)], stream=C.c_void_p(0))
+    assert e.value.status == 2 and "negative batch stride" in str(e.value)
     # shape mismatch
     with pytest.raises(xt.XtError) as e:
         xt.xt_op_fwd(xt.OP.ADD, xt.params(), [x, host_view(2, 3)], [host_view(2, 4)], stream=C.c_void_p(0))
