@@ -24,7 +24,9 @@ if True:  # GPU-only imports are deferred so CPU collection never loads libxt
 DTYPES = ["f32", "bf16"]
 # (rows, cols, ld): ld None = contiguous
 LAYOUTS = [(8, 64, None), (37, 1000, None), (37, 1000, 1008), (37, 1001, None), (37, 1001, 1008),
-           (5, 3001, 3008), (3, 20000, None), (130, 256, None), (9, 32768, None)]
+           (5, 3001, 3008), (3, 20000, None), (130, 256, None), (9, 32768, None),
+           # wider than any register-resident row: the general kernels, ragged and strided
+           (3, 40000, None), (2, 65601, 65608)]
 
 
 def put(a_f32: np.ndarray, dtype: str, ld=None):
