@@ -9,14 +9,20 @@
 // probability tile as exp(alpha S - L).
 //
 // Layout: q, k, v and out are [B*S, H*Dh] (row b*S + s, head h in columns
-// h*Dh ..); L is [B*S, H] f32.  One wave per 32 query rows (forward, dQ) or
-// 32 key rows (dK, dV) of one (sequence, head).  Products are
-// v_mfma_f32_32x32x2f32 in f32 (bf16 storage is widened on load): for a
-// contraction of length n, MFMA j takes index h*(n/2) + j from lane half h
-// for both operands (a fixed permutation of the summation order).  A
-// probability tile leaves the MFMA in the accumulator layout (row by
-// register, column by lane); it goes through a per-wave 32 x 33 LDS tile to
-// become the A operand of the next product.
+// h*Dh ..); L is [B*S, H] f32.  Two kernel families:
+//   - f32 storage, and bf16 rows that are not 16-byte aligned: one wave per
+//     32 query rows (forward, dQ) or 32 key rows (dK, dV) of one (sequence,
+//     head); products are v_mfma_f32_32x32x2f32 in f32 (bf16 widened on
+//     load): for a contraction of length n, MFMA j takes index h*(n/2) + j
+//     from lane half h for both operands (a fixed permutation of the
+//     summation order).  A probability tile leaves the MFMA in the
+//     accumulator layout (row by register, column by lane); it goes through
+//     a per-wave 32 x 33 LDS tile to become the A operand of the next
+//     product.
+//   - aligned bf16 storage: blocks of four waves on the bf16 matrix cores
+//     (v_mfma_f32_32x32x16_bf16, f32 accumulation), with the f32
+//     probabilities split into two bf16 parts so every product keeps f32
+//     accuracy (see the section below).
 //
 // The backward is three launches with no atomics: D = rowsum(dO * O) per
 // (row, head); dQ per query tile over its key tiles; dK and dV per key tile
@@ -351,10 +357,13 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dkv_k(const T* __restrict__ q, 
 // (8 (e / 4) + 4 (l / 32) + e % 4 for element e of lane l); the other operand
 // is read in that order by the transposing LDS read ds_read_b64_tr_b16.
 //
-// Rounding: S and dP are exact products of the stored bf16 operands with f32
-// sums; the probabilities P and dS = P (dP - D) are rounded to bf16 to enter
-// the second products (the composed path stores both as bf16 tensors too);
-// maxima, exponentials, row sums and all accumulation are f32.
+// Precision: S and dP are exact products of the stored bf16 operands with
+// f32 sums.  The probabilities P and dS = P (dP - D) are f32 values; they
+// enter the second products (P V, P^T dO, dS K, dS^T Q) as two bf16 parts,
+// hi + lo (split8), two MFMAs per product, so those products are as
+// accurate as f32 arithmetic would make them, not rounded to bf16.  Maxima,
+// exponentials, row sums and all accumulation are f32; only the outputs
+// are rounded, once, to bf16 storage.
 // ===========================================================================
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -392,11 +401,26 @@ __device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* tile, int r0, int col0
   return __builtin_bit_cast(bf16x8_t, w8);
 }
 
-// Registers 8 m .. 8 m + 7 of an accumulator as a bf16 operand.
-__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& c, int m) {
-  const u32x4_t u = {f2bf2(c[8 * m + 0], c[8 * m + 1]), f2bf2(c[8 * m + 2], c[8 * m + 3]),
-                     f2bf2(c[8 * m + 4], c[8 * m + 5]), f2bf2(c[8 * m + 6], c[8 * m + 7])};
-  return __builtin_bit_cast(bf16x8_t, u);
+// Registers 8 m .. 8 m + 7 of an accumulator as a pair of bf16 operands
+// whose sum carries the f32 values to about 2^-17: hi = bf16(x) (nearest),
+// lo = bf16(x - hi).  x - hi is exact in f32 (the rounding error of a
+// nearest rounding to 8 significant bits), so hi + lo differs from x by at
+// most 2^-9 |x - hi| <= 2^-18 |x|; a product taken as A hi + A lo is then
+// f32-accurate, not bf16-accurate, in this operand.
+struct Split8 {
+  bf16x8_t hi, lo;
+};
+__device__ __forceinline__ Split8 split8(const f32x16_t& c, int m) {
+  uint32_t h[4], r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = c[8 * m + 2 * q], b = c[8 * m + 2 * q + 1];
+    const uint32_t u = f2bf2(a, b);
+    h[q] = u;
+    r[q] = f2bf2(a - __uint_as_float(u << 16), b - __uint_as_float(u & 0xffff0000u));
+  }
+  const u32x4_t uh = {h[0], h[1], h[2], h[3]}, ur = {r[0], r[1], r[2], r[3]};
+  return Split8{__builtin_bit_cast(bf16x8_t, uh), __builtin_bit_cast(bf16x8_t, ur)};
 }
 
 __device__ __forceinline__ f32x16_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
@@ -569,9 +593,13 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const bf16x8_t pf = pack8(s[t], mm);
+          const Split8 pf = split8(s[t], mm);
 #pragma unroll
-          for (int bb = 0; bb < DH / 32; ++bb) o[bb] = mfma16(tr_frag<VS>(Vt, 32 * t + 16 * mm, 32 * bb, l), pf, o[bb]);
+          for (int bb = 0; bb < DH / 32; ++bb) {
+            const bf16x8_t vf = tr_frag<VS>(Vt, 32 * t + 16 * mm, 32 * bb, l);
+            o[bb] = mfma16(vf, pf.lo, o[bb]);
+            o[bb] = mfma16(vf, pf.hi, o[bb]);
+          }
         }
     }
     stage_next(j);
@@ -694,9 +722,13 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
       }
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const bf16x8_t sf = pack8(s, mm);
+        const Split8 sf = split8(s, mm);
 #pragma unroll
-        for (int bb = 0; bb < DH / 32; ++bb) acc[bb] = mfma16(tr_frag<KS>(Kt, 16 * mm, 32 * bb, l), sf, acc[bb]);
+        for (int bb = 0; bb < DH / 32; ++bb) {
+          const bf16x8_t kf = tr_frag<KS>(Kt, 16 * mm, 32 * bb, l);
+          acc[bb] = mfma16(kf, sf.lo, acc[bb]);
+          acc[bb] = mfma16(kf, sf.hi, acc[bb]);
+        }
       }
     }
     stage_next(j);
@@ -859,11 +891,14 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
       }
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const bf16x8_t pf = pack8(s, mm), sf = pack8(dp, mm);
+        const Split8 pf = split8(s, mm), sf = split8(dp, mm);
 #pragma unroll
         for (int bb = 0; bb < DH / 32; ++bb) {
-          av[bb] = mfma16(pf, tr_frag<QS>(Dt, 16 * mm, 32 * bb, l), av[bb]);
-          ak[bb] = mfma16(sf, tr_frag<QS>(Qt, 16 * mm, 32 * bb, l), ak[bb]);
+          const bf16x8_t df = tr_frag<QS>(Dt, 16 * mm, 32 * bb, l), qf = tr_frag<QS>(Qt, 16 * mm, 32 * bb, l);
+          av[bb] = mfma16(pf.lo, df, av[bb]);
+          av[bb] = mfma16(pf.hi, df, av[bb]);
+          ak[bb] = mfma16(sf.lo, qf, ak[bb]);
+          ak[bb] = mfma16(sf.hi, qf, ak[bb]);
         }
       }
     }

@@ -154,7 +154,14 @@ typedef struct {
  * gradients share one row stride.  lse[r, h] is the log-sum-exp of the
  * scaled, masked scores of that query; the backward rebuilds the
  * probabilities from it and needs R*H*4 bytes of workspace.  Arithmetic is
- * f32 (MFMA 32x32x2 f32) for f32 and bf16 storage.  Bitwise reproducible.
+ * f32-accurate for both storage types: f32 storage (and bf16 rows not
+ * 16-byte aligned) runs f32 matrix-core products (MFMA 32x32x2 f32); aligned
+ * bf16 storage runs bf16 matrix-core products with f32 accumulation, where
+ * the operands are the stored bf16 values, except the f32 probabilities P
+ * and dS = P (dP - D), which enter as the sum of two bf16 parts (hi = P
+ * rounded, lo = the remainder rounded), so no product sees P or dS rounded
+ * to bf16.  Only the outputs are rounded to the storage type.  Bitwise
+ * reproducible.
  *
  * Backward "saved" lists: MATMUL none (reads in); RMS_NORM {inv_rms};
  * LAYER_NORM {mean, rstd}; SOFTMAX {y}; CROSS_ENTROPY {lse}; DROPOUT {mask};

@@ -412,6 +412,16 @@ def _unheads(x):
     return x.transpose(0, 2, 1, 3).reshape(B * S, H * Dh)
 
 
+def _probs(Q, K, seq_len, alpha, causal):
+    """P = softmax(alpha Q K^T) over keys, masked keys (t > s) at probability 0."""
+    Z = alpha * np.matmul(Q, np.swapaxes(K, -1, -2))
+    if causal:
+        keep = np.arange(seq_len)[None, :] <= np.arange(seq_len)[:, None]
+        Z = np.where(keep, Z, -np.inf)
+    e = np.exp(Z - np.max(Z, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
 def attention(q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float, causal: bool = True):
     """Returns (out [B*S, H*Dh], lse [B*S, H])."""
     Q, K, Vv = (_heads(t, seq_len, heads, head_dim) for t in (q, k, v))
@@ -428,21 +438,46 @@ def attention(q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float, ca
     return out, lse.transpose(0, 2, 1).reshape(-1, heads)
 
 
-def attention_bwd(d, q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float, causal: bool = True):
+def attention_bwd(d, q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float, causal: bool = True,
+                  out=None):
     """(dq, dk, dv) by the composition's chain rule: P = softmax(alpha Q K^T),
     dV = P^T dO, dP = dO V^T, dZ = P (dP - rowsum(dP P)), dQ = alpha dZ K,
-    dK = alpha dZ^T Q."""
+    dK = alpha dZ^T Q.
+
+    rowsum(dP P) = rowsum(dO (P V)) = rowsum(dO O): given ``out`` (the
+    forward output as it was stored, e.g. rounded to bf16), the row term is
+    formed from it, as a backward that reads the saved output does; without
+    it, from the exact P."""
     Q, K, Vv = (_heads(t, seq_len, heads, head_dim) for t in (q, k, v))
     dO = _heads(d, seq_len, heads, head_dim)
-    Z = alpha * np.matmul(Q, np.swapaxes(K, -1, -2))
-    if causal:
-        keep = np.arange(seq_len)[None, :] <= np.arange(seq_len)[:, None]
-        Z = np.where(keep, Z, -np.inf)
-    e = np.exp(Z - np.max(Z, axis=-1, keepdims=True))
-    P = e / np.sum(e, axis=-1, keepdims=True)
+    P = _probs(Q, K, seq_len, alpha, causal)
     dV = np.matmul(np.swapaxes(P, -1, -2), dO)
     dP = np.matmul(dO, np.swapaxes(Vv, -1, -2))
-    dZ = P * (dP - np.sum(dP * P, axis=-1, keepdims=True))
+    if out is None:
+        Drow = np.sum(dP * P, axis=-1, keepdims=True)
+    else:
+        Drow = np.sum(dO * _heads(out, seq_len, heads, head_dim), axis=-1, keepdims=True)
+    dZ = P * (dP - Drow)
     dQ = alpha * np.matmul(dZ, K)
     dK = alpha * np.matmul(np.swapaxes(dZ, -1, -2), Q)
     return _unheads(dQ), _unheads(dK), _unheads(dV)
+
+
+def attention_term_magnitudes(d, q, k, v, seq_len: int, heads: int, head_dim: int, alpha: float,
+                              causal: bool = True):
+    """For each output of the attention forward and backward, the sum of the
+    magnitudes of the terms it adds up: out = sum_t P V_t, dv = sum_s P dO_s,
+    and dq = alpha sum_t dZ K_t, dk = alpha sum_s dZ Q_s with each dZ = P dP -
+    P D itself two terms (D = rowsum(dP P)).  Returns (|P| |V|, alpha |Z'|
+    |K|, alpha |Z'|^T |Q|, |P|^T |dO|) with Z' = P (|dP| + |D|), in the
+    [B*S, H*Dh] layout: the size of a long sum, against which its rounding
+    error is judged (a sum near zero is still judged at the size of its
+    terms)."""
+    Q, K, Vv = (_heads(t, seq_len, heads, head_dim) for t in (q, k, v))
+    dO = _heads(d, seq_len, heads, head_dim)
+    P = _probs(Q, K, seq_len, alpha, causal)
+    dP = np.matmul(dO, np.swapaxes(Vv, -1, -2))
+    dZ = P * (np.abs(dP) + np.abs(np.sum(dP * P, axis=-1, keepdims=True)))
+    return (_unheads(np.matmul(P, np.abs(Vv))), _unheads(alpha * np.matmul(dZ, np.abs(K))),
+            _unheads(alpha * np.matmul(np.swapaxes(dZ, -1, -2), np.abs(Q))),
+            _unheads(np.matmul(np.swapaxes(P, -1, -2), np.abs(dO))))

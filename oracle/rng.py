@@ -2,14 +2,18 @@
 "dropout 节点的 backward", and the fp32 decision rule of
 "与既有特性的组合" (bf16 only loads and stores the activation).
 
-For element index i (the logical row-major index r*cols + c) and a 64-bit
-seed:
-    key  = seed XOR (i * 0x9E3779B97F4A7C15)          (mod 2^64)
-    h    = splitmix64(key)
-    u    = (h >> 40) / 2^24                            (exact in f32)
-    keep = u >= p                                      (p rounded to f32)
-    y    = keep ? x * s : 0,   s = 1/(1-p) in f32
-and the backward applies the same mask: dx = d * mask * s.
+What the page fixes: each element draws its keep/drop decision from a pure
+function of the 64-bit seed and the element's own index (no generator state
+is carried between elements), so the same (seed, index) pair always gives
+the same decision and a re-run reproduces the mask.  Here the index is the
+logical row-major position r*cols + c; it is spread over 64 bits by a
+multiply with the golden-ratio constant and mixed into the seed with an
+exclusive or; the hash of that key supplies 24 uniform bits, read as a
+fraction in [0, 1) exactly representable in f32; an element is kept when
+that fraction is at least p (p rounded to f32), and a kept element is
+scaled by the f32 value of 1/(1-p) (inverted dropout).  The backward uses
+the same mask and scale on the incoming gradient.  ``dropout_mask`` and the
+functions below carry the exact constants and shifts.
 
 Reading for "splitmix64" (the page only says "a few rounds of xorshift and
 multiply"): the output of Steele, Lea and Flood's SplitMix64 generator

@@ -17,7 +17,7 @@ if True:  # GPU-only imports are deferred so CPU collection never loads libxt
     try:
         import torch
         import autograd_row_wise_amd as xt
-        from xt_testutil import close, close_f32, dev, host, sum_scale
+        from xt_testutil import close, close_chain_f32, close_f32, dev, host, sum_scale
     except Exception:  # pragma: no cover - CPU host without the library
         pass
 
@@ -154,8 +154,7 @@ def test_tied_embedding_on_the_tape():
     ol = o.cross_entropy(o.matmul(oh, oE, trans_b=True), tgt)
     o.backward(ol)
     gE = host(xt.to_torch(t.grad(vE)))
-    r = o.grad(oE)
-    assert np.max(np.abs(gE - r)) <= 1e-5 * np.max(np.abs(r))
+    close_chain_f32(gE, o.grad(oE), what="tied embedding dE")
     Lg = host(xt.to_torch(t.value(loss)))[0, 0]
     assert abs(Lg - float(o.value(ol)[0])) <= 1e-5 * abs(Lg)
     t.close()

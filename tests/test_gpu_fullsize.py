@@ -133,16 +133,17 @@ def test_c3_mlp_gemms_sampled(which):
     dA, dB = empty((M, K), "f32"), empty((K, N), "f32")
     bwd(xt.OP.MATMUL, P(), Dg, [A, B], [], [dA, dB])
     g = np.random.default_rng(1)
-    ri, ci = g.integers(0, M, 64), g.integers(0, N, 64)
-    Ar, Bc = host(A[ri]), host(B[:, ci])
-    ref = np.sum(Ar * Bc.T, axis=1)
-    close_f32(host(C)[ri, ci], ref, sum_scale(np.sum(np.abs(Ar * Bc.T), axis=1), K), what="C")
-    # dA[i, k] = sum_n D[i, n] B[k, n];  dB[k, n] = sum_i A[i, k] D[i, n]
-    ki = g.integers(0, K, 64)
-    Dr, Bk = host(Dg[ri]), host(B[ki])
-    close_f32(host(dA)[ri, ki], np.sum(Dr * Bk, axis=1), sum_scale(np.sum(np.abs(Dr * Bk), axis=1), N), what="dA")
-    Acol, Dcol = host(A[:, ki]), host(Dg[:, ci])
-    close_f32(host(dB)[ki, ci], np.sum(Acol * Dcol, axis=0), sum_scale(np.sum(np.abs(Acol * Dcol), axis=0), M), what="dB")
+    ri, ci = np.unique(g.integers(0, M, 64)), np.unique(g.integers(0, N, 64))
+    Ah, Bh = host(A), host(B)
+    Ar, Dr, Dc = Ah[ri], host(Dg[ri]), host(Dg[:, ci])
+    # sampled rows of C = A B and of dA = d B^T, sampled columns of dB = A^T d,
+    # each from the oracle's matmul / matmul_bwd on the sampled slices
+    close_f32(host(C[ri]), ops.matmul(Ar, Bh), sum_scale(ops.matmul(np.abs(Ar), np.abs(Bh)), K), what="C rows")
+    dA_ref = ops.matmul_bwd(Dr, Ar, Bh)[0]
+    close_f32(host(dA[ri]), dA_ref, sum_scale(ops.matmul(np.abs(Dr), np.abs(Bh), trans_b=True), N), what="dA rows")
+    dB_ref = ops.matmul_bwd(Dc, Ah, Bh[:, ci])[1]
+    close_f32(host(dB[:, ci]), dB_ref, sum_scale(ops.matmul(np.abs(Ah), np.abs(Dc), trans_a=True), M),
+              what="dB columns")
 
 
 # ----------------------------------------------------- bf16 16384 x 4096
@@ -279,9 +280,12 @@ def test_c5_gemm_bwd_sampled():
     bwd(xt.OP.MATMUL, P(), Dg, [A, B], [], [dA, None])
     bwd(xt.OP.MATMUL, P(), Dg, [A, B], [], [None, dB])
     g = np.random.default_rng(2)
-    ri, ki, ci = g.integers(0, M, 96), g.integers(0, K, 96), g.integers(0, N, 96)
-    Dr, Bk = host(Dg[ri]), host(B[ki])
-    close_bf16(host(dA)[ri, ki], np.sum(Dr * Bk, axis=1), what="dA")
-    Acol, Dcol = host(A[:, ki]), host(Dg[:, ci])
-    close_f32(host(dB)[ki, ci], np.sum(Acol * Dcol, axis=0), sum_scale(np.sum(np.abs(Acol * Dcol), axis=0), M),
-              what="dB")
+    ri, ci = np.unique(g.integers(0, M, 96)), np.unique(g.integers(0, N, 96))
+    Ah, Bh = host(A), host(B)
+    Dr, Dc = host(Dg[ri]), host(Dg[:, ci])
+    # sampled rows of dA = d B^T and sampled columns of dB = A^T d from the
+    # oracle's matmul_bwd on the sampled slices
+    close_bf16(host(dA[ri]), ops.matmul_bwd(Dr, Ah[ri], Bh)[0], what="dA rows")
+    dB_ref = ops.matmul_bwd(Dc, Ah, Bh[:, ci])[1]
+    close_f32(host(dB[:, ci]), dB_ref, sum_scale(ops.matmul(np.abs(Ah), np.abs(Dc), trans_a=True), M),
+              what="dB columns")

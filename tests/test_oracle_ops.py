@@ -406,3 +406,38 @@ def test_attention_bwd_fd():
     W = rnd(B * S, H * Dh)
     f = lambda q_, k_, v_: ops.attention(q_, k_, v_, S, H, Dh, 0.7)[0]  # noqa: E731
     check_fd(f, list(ops.attention_bwd(W, q, k, v, S, H, Dh, 0.7)), [q, k, v], W)
+
+
+def test_attention_bwd_from_the_stored_output():
+    """rowsum(dP * P) = rowsum(dO * O): fed the exact output, the backward that
+    reads the stored output equals the one that forms the row term from P;
+    the row term does not enter dV."""
+    S, H, Dh, B = 6, 2, 4, 2
+    q, k, v, d = (rnd(B * S, H * Dh) for _ in range(4))
+    for causal in (True, False):
+        o, _ = ops.attention(q, k, v, S, H, Dh, 0.6, causal)
+        ref = ops.attention_bwd(d, q, k, v, S, H, Dh, 0.6, causal)
+        got = ops.attention_bwd(d, q, k, v, S, H, Dh, 0.6, causal, out=o)
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+        moved = ops.attention_bwd(d, q, k, v, S, H, Dh, 0.6, causal, out=o + 0.01)
+        np.testing.assert_array_equal(moved[2], ref[2])
+        assert np.max(np.abs(moved[0] - ref[0])) > 1e-4
+
+
+def test_attention_term_magnitudes():
+    """Each magnitude bounds its sum (triangle inequality) and equals it when
+    every term is nonnegative: v >= 0 for the output, dO >= 0 for dV."""
+    S, H, Dh, B = 7, 2, 4, 2
+    q, k, v, d = (rnd(B * S, H * Dh) for _ in range(4))
+    o, _ = ops.attention(q, k, v, S, H, Dh, 0.5)
+    dq, dk, dv = ops.attention_bwd(d, q, k, v, S, H, Dh, 0.5)
+    A = ops.attention_term_magnitudes(d, q, k, v, S, H, Dh, 0.5)
+    for got, mag in zip((o, dq, dk, dv), A):
+        assert np.all(np.abs(got) <= mag * (1 + 1e-12) + 1e-15)
+    o_pos, _ = ops.attention(q, k, np.abs(v), S, H, Dh, 0.5)
+    np.testing.assert_allclose(ops.attention_term_magnitudes(d, q, k, np.abs(v), S, H, Dh, 0.5)[0], o_pos,
+                               rtol=1e-13)
+    dv_pos = ops.attention_bwd(np.abs(d), q, k, v, S, H, Dh, 0.5)[2]
+    np.testing.assert_allclose(ops.attention_term_magnitudes(np.abs(d), q, k, v, S, H, Dh, 0.5)[3], dv_pos,
+                               rtol=1e-13)

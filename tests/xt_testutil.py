@@ -9,6 +9,11 @@ Comparison rules (written out so a reader can check them against the tests):
         below f32 resolution.
   bf16: |gpu - ref| <= 2e-2 * |ref| + 1e-2 * rms(ref) per element (a pure
         relative bound is undefined at 0, hence the floor).
+  f32 through a composed graph (gradients that pass through tens of ops on
+        the tape, where no per-element term magnitude is at hand):
+        |gpu - ref| <= 1e-6 + 1e-5 * (|ref| + rms(ref)) per element, the f32
+        rule with the bf16 rule's kind of floor; the share of elements that
+        also meet the literal 1e-6 + 1e-5 * |ref| is printed beside it.
   masks, int32 indexing: bit-exact.
 """
 from __future__ import annotations
@@ -72,6 +77,8 @@ def close_f32(gpu, ref, scale=None, what=""):
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     mag = np.abs(ref) if scale is None else np.maximum(np.abs(ref), scale)
     bad = np.abs(gpu - ref) > 1e-6 + 1e-5 * mag
+    if scale is not None:
+        print(f"[f32 sum] {what}: literal 1e-5/1e-6 bar met by {100 * literal_rate(gpu, ref):.3f}% of {ref.size}")
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} f32 elements off; first at {tuple(i)}: "
@@ -88,6 +95,32 @@ def close_bf16(gpu, ref, what=""):
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} bf16 elements off; first at {tuple(i)}: "
                              f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r}")
+
+
+def literal_rate(gpu, ref) -> float:
+    """Share of elements within the literal f32 bar 1e-6 + 1e-5 * |ref|."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 1.0
+    return float(np.mean(np.abs(gpu - ref) <= 1e-6 + 1e-5 * np.abs(ref)))
+
+
+def close_chain_f32(gpu, ref, what=""):
+    """Per-element f32 bar for outputs of a composed graph (see the module
+    docstring); prints the literal-bar pass rate beside it."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    err = np.abs(gpu - ref)
+    bad = err > 1e-6 + 1e-5 * (np.abs(ref) + rms)
+    print(f"[f32 chain] {what}: literal 1e-5/1e-6 bar met by {100 * literal_rate(gpu, ref):.3f}% of {ref.size}; "
+          f"max |err|/rms {float(err.max() / rms) if ref.size and rms > 0 else 0.0:.2e}")
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} f32 elements off; first at {tuple(i)}: "
+                             f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r} rms={rms!r}")
 
 
 def close(gpu, ref, dtype: str, scale=None, what=""):
