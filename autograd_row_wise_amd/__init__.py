@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "XtError", "Tensor", "Params", "OP", "DT", "lib", "view", "params",
-    "xt_op_fwd", "xt_op_bwd", "xt_grad_accumulate", "xt_dropout_mask", "xt_workspace_bytes",
+    "xt_op_fwd", "xt_op_bwd", "xt_op_bwd_noalloc", "xt_grad_accumulate", "xt_dropout_mask", "xt_workspace_bytes",
     "xt_status_str", "xt_last_error", "xt_abi_version", "Tape", "LIB_PATH",
 ]
 
@@ -79,6 +79,9 @@ lib.xt_op_fwd.argtypes = [C.c_int, C.POINTER(Params), _TP, C.c_int, _TP, C.c_int
 lib.xt_op_bwd.restype = C.c_int
 lib.xt_op_bwd.argtypes = [C.c_int, C.POINTER(Params), _TP, _TP, C.c_int, _TP, C.c_int,
                           _TP, C.c_int, C.c_uint32, C.c_void_p, C.c_size_t, C.c_void_p]
+lib.xt_op_bwd_noalloc.restype = C.c_int
+lib.xt_op_bwd_noalloc.argtypes = [C.c_int, C.POINTER(Params), _TP, _TP, C.c_int, _TP, C.c_int,
+                                  _TP, C.c_int, C.c_uint32, C.c_void_p]
 lib.xt_grad_accumulate.restype = C.c_int
 lib.xt_grad_accumulate.argtypes = [_TP, _TP, C.c_void_p]
 lib.xt_dropout_mask.restype = C.c_int
@@ -227,6 +230,14 @@ def xt_op_bwd(op: int, prm: Params, dout: Tensor, ins, saved, din, accumulate=0,
     d, nd = _arr(din)
     _check(lib.xt_op_bwd(op, C.byref(prm), C.byref(dout), a, n, s, ns, d, nd, accumulate, ws,
                          ws_bytes, _stream(stream)), "xt_op_bwd")
+
+
+def xt_op_bwd_noalloc(op: int, prm: Params, dout: Tensor, ins, saved, din, accumulate=0, stream=None) -> None:
+    a, n = _arr(ins)
+    s, ns = _arr(saved)
+    d, nd = _arr(din)
+    _check(lib.xt_op_bwd_noalloc(op, C.byref(prm), C.byref(dout), a, n, s, ns, d, nd, accumulate,
+                                 _stream(stream)), "xt_op_bwd_noalloc")
 
 
 def xt_grad_accumulate(dst: Tensor, src: Tensor, stream=None) -> None:

@@ -174,6 +174,18 @@ size_t matmul_ws(const xt_params* prm, const xt_tensor* in, int n_in, int is_bwd
 
 }  // namespace
 
+namespace xt {
+xt_status set_error(xt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+}  // namespace xt
+
 extern "C" {
 
 const char* xt_status_str(xt_status s) {

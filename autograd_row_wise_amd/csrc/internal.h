@@ -12,6 +12,10 @@
 
 namespace xt {
 
+// Sets the thread-local text xt_last_error() returns (printf format) and
+// returns `s`.
+xt_status set_error(xt_status s, const char* fmt, ...);
+
 // --- row-wise reductions (rowwise.hip) ---------------------------------
 // Plan of a row-resident launch: RW waves share one row, each thread keeps
 // NV 16-byte packs of it in registers; rows longer than the register

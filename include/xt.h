@@ -210,6 +210,34 @@ xt_status xt_op_bwd(xt_op op, const xt_params* prm, const xt_tensor* dout,
                     const xt_tensor* din, int n_din, uint32_t accumulate,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the static device array xt_op_bwd_noalloc takes its workspace
+ * from: 32 MiB, held on every GPU the library runs on until the process
+ * ends. */
+#define XT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * xt_op_bwd with the same arguments and results, its workspace taken from a
+ * static device array of XT_NOALLOC_SCRATCH_BYTES inside the library
+ * instead of from the caller.  Calls no hipMalloc / hipFree.
+ *   - Inputs, outputs and gradients are caller-owned device buffers, as for
+ *     xt_op_bwd.
+ *   - A backward whose workspace (xt_workspace_bytes) exceeds the array is
+ *     rejected with XT_ERR_WORKSPACE before anything is launched; MATMUL
+ *     instead splits its contraction less so as to fit.
+ *   - The first call on a device resolves that device's copy of the array
+ *     (hipGetSymbolAddress, with the device current); the array is then
+ *     kept until the process ends.
+ *   - Every call on one GPU uses that GPU's one array: calls whose kernels
+ *     overlap on a GPU (other streams, other host threads) race.  Nothing in
+ *     the array needs to start at zero, and its contents after a call are
+ *     unspecified. */
+xt_status xt_op_bwd_noalloc(xt_op op, const xt_params* prm, const xt_tensor* dout,
+                            const xt_tensor* in, int n_in,
+                            const xt_tensor* saved, int n_saved,
+                            const xt_tensor* din, int n_din, uint32_t accumulate,
+                            void* stream);
+
 /* dst += src elementwise, in place (f32 arithmetic, one rounding into dst's
  * dtype).  dst and src have the same shape; dtypes may differ.
  * [AE] "梯度累加（扇出求和）": the accumulate of push_grad. */
