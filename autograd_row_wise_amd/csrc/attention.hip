@@ -132,17 +132,10 @@ __device__ __forceinline__ void mul_rows(const float (&a)[16], const T* x, const
   }
 }
 
-// Max / sum over the 32 lanes of a lane half (one accumulator row).
-__device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// Max / sum over the 32 lanes of a lane half (one accumulator row), on the
+// DPP paths (common.h half_reduce).
+__device__ __forceinline__ float half_max(float v) { return half_reduce(v, OpMax{}); }
+__device__ __forceinline__ float half_sum(float v) { return half_reduce(v, OpAdd{}); }
 
 template <typename T, int DH>
 __global__ __launch_bounds__(WAVE) void attn_fwd_k(const T* __restrict__ q, const T* __restrict__ k,
@@ -567,7 +560,7 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl;
+      mx = xor32_reduce(mx, OpMax{}) * sl;
       // The reference point m only moves when some row's maximum exceeds it
       // by more than 8 (log2 units): exponentials stay below 2^8, and the
       // final division by the row sum cancels the choice of m exactly.
@@ -608,7 +601,7 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
     if (j + 1 < nt) st.load(k, v, g, base, (int64_t)(j + 1) * BK, tid);
     stage_next(j);
   }
-  const float tot = ls + __shfl_xor(ls, 32);
+  const float tot = xor32_reduce(ls, OpAdd{});
   if (qme < g.S) {
     const float inv = 1.f / tot;
     bf16_t* orow = out + (b * g.S + qme) * g.ld + hd * DH;
@@ -670,7 +663,7 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
     for (int kk = 0; kk < DH / 16; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)df[kk][e] * (float)of[kk][e];
-    Dq = acc + __shfl_xor(acc, 32);
+    Dq = xor32_reduce(acc, OpAdd{});
     if (qok && h == 0) dd[(b * g.S + qme) * g.H + hd] = Dq;
   }
   if (!dq) return;

@@ -172,18 +172,93 @@ __device__ __forceinline__ void store_pack_acc(T* row, I c0, I n, float* f, bool
 }
 
 // --------------------------------------------------------------- reductions
-// Butterfly over the 64 lanes: every lane ends with the same bits (each level
-// adds the same two operands in both lanes), so the result is deterministic.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Wave reductions run on the VALU's cross-lane operand paths, not through
+// LDS: DPP (data-parallel primitives) hands an instruction the operand of
+// another lane of the same 16-lane row (quad_perm, row_half_mirror,
+// row_mirror) or the last lane of a row to the next rows (row_bcast15,
+// row_bcast31); one readlane then makes the wave's result uniform.
+namespace dpp {
+constexpr int XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int HALF_MIRROR = 0x141;  // lane i of each 8 <- lane 7 - i
+constexpr int MIRROR = 0x140;       // lane i of each 16 <- lane 15 - i
+constexpr int BCAST15 = 0x142;      // lane 15 of row r -> row r + 1
+constexpr int BCAST31 = 0x143;      // lane 31 -> rows 2 and 3
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                               false));
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// op over each 16-lane row: after the four steps every lane of a row holds
+// the row's result, with the same bits in every lane (each step combines
+// the same two values in both lanes of a pair, and op is commutative).
+template <class Op>
+__device__ __forceinline__ float row16_reduce(float v, Op op) {
+  v = op(v, dpp_f<dpp::XOR1>(v));
+  v = op(v, dpp_f<dpp::XOR2>(v));
+  v = op(v, dpp_f<dpp::HALF_MIRROR>(v));
+  v = op(v, dpp_f<dpp::MIRROR>(v));
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+// op over the 64 lanes, result uniform (one readlane): rows, then rows 1
+// and 3 take rows 0 and 2, then rows 2 and 3 take lane 31; lane 63 ends
+// with op((r2 op r3), (r0 op r1)).  A fixed order: deterministic.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = row16_reduce(v, op);
+  const int lane = __lane_id();
+  const float a = op(v, dpp_f<dpp::BCAST15, 0xa>(v));
+  v = (lane & 16) ? a : v;
+  const float b = op(v, dpp_f<dpp::BCAST31, 0xc>(v));
+  v = (lane & 32) ? b : v;
+  return readlane_f(v, 63);
+}
+
+// op over each 32-lane half of the wave; every lane gets its half's result.
+template <class Op>
+__device__ __forceinline__ float half_reduce(float v, Op op) {
+  v = row16_reduce(v, op);
+  const float a = op(v, dpp_f<dpp::BCAST15, 0xa>(v));   // lanes 31 and 63: their half's result
+  const float lo = readlane_f(a, 31), hi = readlane_f(a, 63);
+  return __lane_id() < 32 ? lo : hi;
+}
+
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd{}); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
+
+// The value of lane l ^ 32 (v_permlane32_swap: the two halves of two
+// registers trade places).  The compiler's builtin for this instruction
+// loses its second result, so it is written out; the s_nop gives the swap
+// the two wait states it needs after a VALU write of its operands.
+__device__ __forceinline__ void swap_halves(float& lo_out, float& hi_out, float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo_out = __uint_as_float(a);     // every lane: v of lane (l mod 32)
+  hi_out = __uint_as_float(b);     // every lane: v of lane (l mod 32) + 32
+}
+
+// op(v of lane l mod 32, v of lane l mod 32 + 32): the same two operands,
+// in the same order, in lanes l and l ^ 32.
+template <class Op>
+__device__ __forceinline__ float xor32_reduce(float v, Op op) {
+  float lo, hi;
+  swap_halves(lo, hi, v);
+  return op(lo, hi);
 }
 
 // Sum over a group of RW consecutive waves of the block (one row per group).

@@ -80,12 +80,36 @@ __device__ __forceinline__ void st_el(const Unit& u, int64_t c, float v) {
   else reinterpret_cast<float*>(u.row)[c] = v;
 }
 
-// Block sum of one double per thread in a fixed order: xor-shuffle tree in
-// each wave, then the four wave sums in wave order.
+// A double from lane `CTRL` (DPP control) away: its two halves moved alike.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int2 h = __builtin_bit_cast(int2, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, h.x, CTRL, ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, h.y, CTRL, ROW_MASK, 0xf, false);
+  return __builtin_bit_cast(double, make_int2(lo, hi));
+}
+
+// Wave sum of doubles in the order of wave_reduce (common.h): rows by DPP
+// steps, rows 1, 3 add rows 0, 2, rows 2, 3 add lane 31, lane 63 read.
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<dpp::XOR1>(v);
+  v += dpp_d<dpp::XOR2>(v);
+  v += dpp_d<dpp::HALF_MIRROR>(v);
+  v += dpp_d<dpp::MIRROR>(v);
+  const int lane = __lane_id();
+  const double a = v + dpp_d<dpp::BCAST15, 0xa>(v);
+  v = (lane & 16) ? a : v;
+  const double b = v + dpp_d<dpp::BCAST31, 0xc>(v);
+  v = (lane & 32) ? b : v;
+  const int2 h = __builtin_bit_cast(int2, v);
+  return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(h.x, 63), __builtin_amdgcn_readlane(h.y, 63)));
+}
+
+// Block sum of one double per thread in a fixed order: the DPP wave sum,
+// then the four wave sums in wave order.
 __device__ __forceinline__ double block_sum(double v) {
   __shared__ double ws[GB / WAVE];
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum_d(v);
   if (threadIdx.x % WAVE == 0) ws[threadIdx.x / WAVE] = v;
   __syncthreads();
   double s = 0.0;
