@@ -86,10 +86,12 @@ def dropout_mask(shape, p: float, seed: int, index_offset: int = 0) -> np.ndarra
     return keep.reshape(shape).astype(np.uint8)
 
 
-def dropout(x, p: float, seed: int):
-    """Returns (y, mask).  y = x*s where kept, +0 where dropped."""
+def dropout(x, p: float, seed: int, index_offset: int = 0):
+    """Returns (y, mask).  y = x*s where kept, +0 where dropped.  Element i
+    of x uses counter index_offset + i (a block of rows of a larger tensor
+    passes the flat index of its first element)."""
     X = np.asarray(x, dtype=np.float64)
-    mask = dropout_mask(X.shape, p, seed)
+    mask = dropout_mask(X.shape, p, seed, index_offset)
     s = keep_scale(p)
     return np.where(mask == 1, X * s, 0.0), mask
 
