@@ -261,61 +261,72 @@ __device__ __forceinline__ float xor32_reduce(float v, Op op) {
   return op(lo, hi);
 }
 
-// Sum over a group of RW consecutive waves of the block (one row per group).
-// Every thread of the block must call it (it contains barriers when RW > 1).
-// `lds` holds one float per wave of the block.
+// Reductions over a group of RW consecutive waves of the block (one row per
+// group).  Every thread of the block must make the same sequence of calls
+// (they contain barriers when RW > 1).  `lds` holds 4 floats per wave of
+// the block: two slot sets of up to two values per wave.  Successive calls
+// alternate between the sets (`ph`, a per-thread counter starting at 0), so
+// a set is written again only after the next call's barrier, by which time
+// every wave has read it: one barrier per reduction.  The waves' results are
+// combined in wave order, so the result is deterministic.
 template <int RW>
-__device__ __forceinline__ float group_sum(float v, float* lds) {
+__device__ __forceinline__ float* group_slot(float* lds, int& ph) {
+  float* slot = lds + ph * 2 * (int)(blockDim.x / WAVE);
+  ph ^= 1;
+  return slot;
+}
+
+template <int RW>
+__device__ __forceinline__ float group_sum(float v, float* lds, int& ph) {
   v = wave_sum(v);
   if constexpr (RW == 1) {
     return v;
   } else {
     const int w = threadIdx.x / WAVE;
     const int g0 = (w / RW) * RW;
+    float* slot = group_slot<RW>(lds, ph);
+    if ((threadIdx.x % WAVE) == 0) slot[w] = v;
     __syncthreads();
-    if ((threadIdx.x % WAVE) == 0) lds[w] = v;
-    __syncthreads();
-    float s = lds[g0];
+    float s = slot[g0];
 #pragma unroll
-    for (int i = 1; i < RW; ++i) s += lds[g0 + i];
+    for (int i = 1; i < RW; ++i) s += slot[g0 + i];
     return s;
   }
 }
 
 template <int RW>
-__device__ __forceinline__ float group_max(float v, float* lds) {
+__device__ __forceinline__ float group_max(float v, float* lds, int& ph) {
   v = wave_max(v);
   if constexpr (RW == 1) {
     return v;
   } else {
     const int w = threadIdx.x / WAVE;
     const int g0 = (w / RW) * RW;
+    float* slot = group_slot<RW>(lds, ph);
+    if ((threadIdx.x % WAVE) == 0) slot[w] = v;
     __syncthreads();
-    if ((threadIdx.x % WAVE) == 0) lds[w] = v;
-    __syncthreads();
-    float s = lds[g0];
+    float s = slot[g0];
 #pragma unroll
-    for (int i = 1; i < RW; ++i) s = fmaxf(s, lds[g0 + i]);
+    for (int i = 1; i < RW; ++i) s = fmaxf(s, slot[g0 + i]);
     return s;
   }
 }
 
-// Two sums over the group with one pair of barriers.  `lds` holds two
-// floats per wave of the block.
+// Two sums over the group with one barrier.
 template <int RW>
-__device__ __forceinline__ void group_sum2(float& a, float& b, float* lds) {
+__device__ __forceinline__ void group_sum2(float& a, float& b, float* lds, int& ph) {
   a = wave_sum(a);
   b = wave_sum(b);
   if constexpr (RW > 1) {
     const int w = threadIdx.x / WAVE;
     const int g0 = (w / RW) * RW;
+    float* slot = group_slot<RW>(lds, ph);
+    if ((threadIdx.x % WAVE) == 0) { slot[2 * w] = a; slot[2 * w + 1] = b; }
     __syncthreads();
-    if ((threadIdx.x % WAVE) == 0) { lds[2 * w] = a; lds[2 * w + 1] = b; }
-    __syncthreads();
-    a = lds[2 * g0];
-    b = lds[2 * g0 + 1];
+    a = slot[2 * g0];
+    b = slot[2 * g0 + 1];
 #pragma unroll
-    for (int i = 1; i < RW; ++i) { a += lds[2 * (g0 + i)]; b += lds[2 * (g0 + i) + 1]; }
+    for (int i = 1; i < RW; ++i) { a += slot[2 * (g0 + i)]; b += slot[2 * (g0 + i) + 1]; }
   }
 }
 

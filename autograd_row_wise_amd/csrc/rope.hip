@@ -12,6 +12,7 @@
 // row's heads as 16-byte packs: each thread reads the pack of x_i and the
 // pack of x_{i+h} and writes both rotated packs.
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 #include "internal.h"
@@ -20,6 +21,46 @@ namespace xt {
 namespace {
 
 constexpr int RB = 256;
+
+// cos and sin of th (0 <= th < 2^30) rounded once to f32.  The argument is
+// reduced by pi/2 in f64 with a two-part constant (Cody and Waite, "Software
+// Manual for the Elementary Functions", 1980): k = nearest integer to
+// th * 2/pi; pi/2 = P1 + P2 with P1 holding 33 significant bits, so k * P1
+// is exact for k < 2^20 and r = (th - k P1) - k P2 lies in [-pi/4, pi/4]
+// within ~1e-16 k.  sin r and cos r are Taylor polynomials in f64 through
+// r^13 and r^16 (truncation below 3e-14 on |r| <= pi/4), and the quadrant
+// k mod 4 picks and signs them.  The f64 result is within ~1e-13 of the
+// exact value before its one rounding to f32; about 25 f64 operations
+// instead of a general library sincos.
+__device__ __forceinline__ void sincos_f32(double th, float& c, float& s) {
+  const double INV_PIO2 = 0.63661977236758138;        // 2/pi
+  const double P1 = 1.5707963267341256;               // pi/2, first 33 bits
+  const double P2 = 6.077100506506192e-11;            // pi/2 - P1
+  const double k = __builtin_rint(th * INV_PIO2);
+  const double r = __builtin_fma(-k, P2, __builtin_fma(-k, P1, th));
+  const double r2 = r * r;
+  double sp = 1.0 / 6227020800.0;                      // 1/13!
+  sp = __builtin_fma(sp, r2, -1.0 / 39916800.0);       // 1/11!
+  sp = __builtin_fma(sp, r2, 1.0 / 362880.0);          // 1/9!
+  sp = __builtin_fma(sp, r2, -1.0 / 5040.0);
+  sp = __builtin_fma(sp, r2, 1.0 / 120.0);
+  sp = __builtin_fma(sp, r2, -1.0 / 6.0);
+  const double sn = __builtin_fma(sp * r2, r, r);
+  double cp = 1.0 / 20922789888000.0;                  // 1/16!
+  cp = __builtin_fma(cp, r2, -1.0 / 87178291200.0);    // 1/14!
+  cp = __builtin_fma(cp, r2, 1.0 / 479001600.0);       // 1/12!
+  cp = __builtin_fma(cp, r2, -1.0 / 3628800.0);
+  cp = __builtin_fma(cp, r2, 1.0 / 40320.0);
+  cp = __builtin_fma(cp, r2, -1.0 / 720.0);
+  cp = __builtin_fma(cp, r2, 1.0 / 24.0);
+  cp = __builtin_fma(cp, r2, -0.5);
+  const double cn = __builtin_fma(cp, r2, 1.0);
+  const int q = (int)((long long)k & 3);
+  const double cq = q == 0 ? cn : q == 1 ? -sn : q == 2 ? -cn : sn;
+  const double sq = q == 0 ? sn : q == 1 ? cn : q == 2 ? -sn : -cn;
+  c = (float)cq;
+  s = (float)sq;
+}
 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t ldx,
@@ -37,10 +78,10 @@ __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t
     __syncthreads();
     for (int i = threadIdx.x; i < half; i += RB) {
       const double th = pos * pow(base, -2.0 * (double)i / (double)head_dim);
-      double sn, cn;
-      sincos(th, &sn, &cn);
-      cs[i] = (float)cn;
-      cs[half + i] = sign * (float)sn;
+      float cn, sn;
+      sincos_f32(th, cn, sn);
+      cs[i] = cn;
+      cs[half + i] = sign * sn;
     }
     __syncthreads();
     const T* xr = reinterpret_cast<const T*>(x) + r * ldx;
@@ -101,19 +142,28 @@ __global__ __launch_bounds__(RB) void rope_k(const void* __restrict__ x, int64_t
 // computed once per block (f64, LDS); per tile, the angles pos * freq are
 // formed in f64 and their cos/sin rounded to f32 into one of two LDS
 // buffers, while the block's next tile's packs (if it has more than one
-// tile) are already being fetched: one barrier per tile.
+// tile) are already being fetched: one barrier per tile.  With one tile
+// per block, the frequencies come from the host-computed table in the
+// kernel arguments (wider heads compute them with pow).
+// The frequencies base^(-2i/head_dim) of heads up to 128 wide, computed once
+// on the host (f64) and passed in the kernel arguments.
+constexpr int FREQ_MAX = 64;
+struct FreqTable {
+  double f[FREQ_MAX];
+};
+
 template <typename T>
 __global__ __launch_bounds__(RB) void rope_pipe_k(const void* __restrict__ x, int64_t ldx,
                                                   void* __restrict__ y, int64_t ldy, int acc,
                                                   int64_t R, int head_dim, double base, int seq_len,
-                                                  float sign, int items, int rpi) {
+                                                  float sign, int items, int rpi, FreqTable ft) {
   constexpr int V = io<T>::VEC, NIT = 2;
   extern __shared__ double rsh[];                 // freq[half] (f64), then cs[2][rpi][2*half] (f32)
   const int half = head_dim / 2, per_head = half / V;
   double* freq = rsh;
   float* cs = reinterpret_cast<float*>(rsh + half);
   const int tid = threadIdx.x;
-  for (int i = tid; i < half; i += RB) freq[i] = pow(base, -2.0 * (double)i / (double)head_dim);
+  for (int i = tid; i < half; i += RB) freq[i] = half <= FREQ_MAX ? ft.f[i] : pow(base, -2.0 * (double)i / (double)head_dim);
 
   int srow[NIT], scol[NIT], sv[NIT];
   bool sok[NIT];
@@ -150,10 +200,10 @@ __global__ __launch_bounds__(RB) void rope_pipe_k(const void* __restrict__ x, in
       const int rr = idx / half, i = idx % half;
       const int64_t r = t * rpi + rr;
       const double th = (double)(r % seq_len) * freq[i];
-      double sn, cn;
-      sincos(th, &sn, &cn);
-      cb_[rr * 2 * half + i] = (float)cn;
-      cb_[rr * 2 * half + half + i] = sign * (float)sn;
+      float cn, sn;
+      sincos_f32(th, cn, sn);
+      cb_[rr * 2 * half + i] = cn;
+      cb_[rr * 2 * half + half + i] = sign * sn;
     }
     const int64_t tn = t + gridDim.x;
     if (tn < tiles) fetch(tn, na, nb);
@@ -211,12 +261,15 @@ hipError_t launch_rope(const xt_tensor& x, const xt_tensor& y, bool acc, int hea
     // tensors than 2048 resident blocks looping over tiles
     const unsigned g = (unsigned)std::min<int64_t>(tiles, INT32_MAX);
     const size_t sh = (size_t)half * sizeof(double) + (size_t)2 * rpi * 2 * half * sizeof(float);
+    FreqTable ft{};
+    if (half <= FREQ_MAX)
+      for (int i = 0; i < half; ++i) ft.f[i] = std::pow((double)base, -2.0 * (double)i / (double)head_dim);
     if (x.dtype == XT_F32)
       rope_pipe_k<float><<<g, RB, sh, s>>>(x.data, x.ld, y.data, y.ld, acc, R, head_dim, base, seq_len, sign,
-                                           (int)items, rpi);
+                                           (int)items, rpi, ft);
     else
       rope_pipe_k<bf16_t><<<g, RB, sh, s>>>(x.data, x.ld, y.data, y.ld, acc, R, head_dim, base, seq_len, sign,
-                                            (int)items, rpi);
+                                            (int)items, rpi, ft);
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)std::min<int64_t>(R, 8192);

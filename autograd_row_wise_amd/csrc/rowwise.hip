@@ -94,7 +94,8 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
     void* __restrict__ y, int64_t ldy, float* __restrict__ ir, int64_t ldir,
     int64_t R, int64_t C, float eps, float invC) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
-  __shared__ float lds[BLOCK / WAVE];
+  __shared__ float lds[4 * BLOCK / WAVE];
+  int ph = 0;
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
   const int64_t stride = (int64_t)gridDim.x * NG;
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(BLOCK) void rms_fwd_fast(
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) ss += v[j][k] * v[j][k];
-    ss = group_sum<RW>(ss, lds);
+    ss = group_sum<RW>(ss, lds, ph);
     const float irv = rsqrtf(ss * invC + eps);
     if (active) {
       T* yr = row_ptr_w<T>(y, r, ldy);
@@ -172,7 +173,8 @@ __global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && NV <= 2 ? 4 : 1) void 
     int64_t R, int64_t C, float invC) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BWD_BLOCK / G;
   extern __shared__ float red[];               // C floats
-  __shared__ float lds[BWD_BLOCK / WAVE];
+  __shared__ float lds[4 * BWD_BLOCK / WAVE];
+  int ph = 0;
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
   float gam[NV][V], pp[1][NV][V];
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && NV <= 2 ? 4 : 1) void 
 #pragma unroll
       for (int k = 0; k < V; ++k) dot += dv[k] * gam[j][k] * xv[k];
     }
-    dot = group_sum<RW>(dot, lds);
+    dot = group_sum<RW>(dot, lds, ph);
     keep_raw(cd);
     keep_raw(cx);
     if (active) {
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
     float* __restrict__ mean, int64_t ldm, float* __restrict__ rstd, int64_t ldr,
     int64_t R, int64_t C, float eps, float invC) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
-  __shared__ float lds[BLOCK / WAVE];
+  __shared__ float lds[4 * BLOCK / WAVE];
+  int ph = 0;
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
   const int64_t stride = (int64_t)gridDim.x * NG;
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) s += v[j][k];
-    const float mu = group_sum<RW>(s, lds) * invC;
+    const float mu = group_sum<RW>(s, lds, ph) * invC;
     float q = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
         const float t = v[j][k] - mu;
         if (pack_col<NV, V>(j, gl) + k < Ci) q += t * t;
       }
-    const float var = group_sum<RW>(q, lds) * invC;
+    const float var = group_sum<RW>(q, lds, ph) * invC;
     const float rs = rsqrtf(var + eps);
     if (active) {
       T* yr = row_ptr_w<T>(y, r, ldy);
@@ -315,23 +318,49 @@ __global__ __launch_bounds__(BLOCK) void ln_fwd_fast(
 }
 
 template <typename T, int RW, int NV>
-__global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
+__global__ __launch_bounds__(BWD_BLOCK, sizeof(T) == 2 && RW == 1 && NV <= 2 ? 4 : 1) void ln_bwd_fast(
     const void* __restrict__ d, int64_t ldd, const void* __restrict__ x, int64_t ldx,
     const float* __restrict__ gamma, const float* __restrict__ mean, int64_t ldm,
     const float* __restrict__ rstd, int64_t ldr, void* __restrict__ dx, int64_t lddx,
     int acc_dx, float* __restrict__ part, int64_t R, int64_t C, float invC) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BWD_BLOCK / G;
-  extern __shared__ float red[];               // 2C floats
-  __shared__ float lds[2 * BWD_BLOCK / WAVE];
+  // bf16 rows held by one wave keep gamma in LDS (read where used) rather
+  // than in registers, so the raw-pack form below fits four waves per SIMD
+  // (measured at d = 768: 634 -> 573 us over 1 GiB).  Rows of several waves
+  // keep the unpacked ring with gamma in registers (two waves per SIMD),
+  // measured faster for them (d = 3072: 602 vs 660 us; 4096: 527 vs 584 us).
+  constexpr bool GLDS = sizeof(T) == 2 && RW == 1;
+  constexpr int NVG = GLDS ? 1 : NV;
+  extern __shared__ float red[];               // 2C floats (partials fold); bf16: gamma in the first C
+  __shared__ float lds[4 * BWD_BLOCK / WAVE];
+  int ph = 0;
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
-  float gam[NV][V], pp[2][NV][V];
+  float gam[NVG][V], pp[2][NV][V];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
+    if constexpr (!GLDS) load_f32s<V, int>(gamma, pack_col<NV, V>(j, gl), Ci, gam[j]);
 #pragma unroll
     for (int k = 0; k < V; ++k) { pp[0][j][k] = 0.f; pp[1][j][k] = 0.f; }
   }
+  if constexpr (GLDS) {
+    for (int c = threadIdx.x; c < Ci; c += BWD_BLOCK) red[c] = gamma[c];
+    __syncthreads();
+  }
+  // gamma of elements k of pack j of this lane (bf16: from LDS)
+  auto gam_of = [&](int j, float (&gv)[V]) {
+    if constexpr (GLDS) {
+      const float4* p = reinterpret_cast<const float4*>(red + pack_col<NV, V>(j, gl));
+#pragma unroll
+      for (int k = 0; k < V; k += 4) {
+        const float4 q = p[k / 4];
+        gv[k] = q.x; gv[k + 1] = q.y; gv[k + 2] = q.z; gv[k + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) gv[k] = gam[j < NVG ? j : 0][k];
+    }
+  };
   // rows interleaved over the blocks: step k of group g is row
   // blockIdx.x NG + g + k gridDim.x NG, so the rows in flight across the
   // chip at any time form one contiguous window of the tensor
@@ -366,12 +395,12 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
       for (int k = 0; k < V; ++k) {
         const bool ok = c0 + k < Ci;
         xh[j][k] = ok ? (xh[j][k] - mu) * rs : 0.f;
-        const float gv = dv[j][k] * gam[j][k];
+        const float gv = dv[j][k] * gam[j < NVG ? j : 0][k];
         s1 += gv;
         s2 += gv * xh[j][k];
       }
     }
-    group_sum2<RW>(s1, s2, lds);
+    group_sum2<RW>(s1, s2, lds, ph);
     if (active) {
       const float a = s1 * invC, b = s2 * invC;
       T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
@@ -382,7 +411,7 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
           float o[V];
 #pragma unroll
           for (int k = 0; k < V; ++k) {
-            o[k] = rs * (dv[j][k] * gam[j][k] - a - xh[j][k] * b);
+            o[k] = rs * (dv[j][k] * gam[j < NVG ? j : 0][k] - a - xh[j][k] * b);
             pp[0][j][k] += dv[j][k] * xh[j][k];
             pp[1][j][k] += dv[j][k];
           }
@@ -391,10 +420,69 @@ __global__ __launch_bounds__(BWD_BLOCK) void ln_bwd_fast(
       }
     }
   };
+  // bf16: only raw packs stay live across the reduction (unpacked where
+  // used, as in the rms_norm backward), and a ring set is refilled once its
+  // row is written; the unpacked f32 ring needs 171-176 VGPRs at two packs
+  // per lane (two waves per SIMD), the raw one fits four.
+  auto step_raw = [&](RowPacks<T, NV, G>& cd, RowPacks<T, NV, G>& cx, int64_t base) {
+    const int64_t r = base + g, rn = base + 2 * stride + g;
+    const bool active = r < end;
+    const float mu = active ? mean[r * ldm] : 0.f;
+    const float rs = active ? rstd[r * ldr] : 0.f;
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float dv[V], xv[V], gm[V];
+      io<T>::unpack(cd.q[j], dv);
+      io<T>::unpack(cx.q[j], xv);
+      gam_of(j, gm);
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float gv = dv[k] * gm[k];      // 0 past the row: those packs load as 0
+        s1 += gv;
+        s2 += gv * ((xv[k] - mu) * rs);
+      }
+    }
+    group_sum2<RW>(s1, s2, lds, ph);
+    keep_raw(cd);
+    keep_raw(cx);
+    if (active) {
+      const float a = s1 * invC, b = s2 * invC;
+      T* dxr = dx ? row_ptr_w<T>(dx, r, lddx) : nullptr;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int c0 = pack_col<NV, V>(j, gl);
+        if (c0 < Ci) {
+          float dv[V], xv[V], gm[V], o[V];
+          io<T>::unpack(cd.q[j], dv);
+          io<T>::unpack(cx.q[j], xv);
+          gam_of(j, gm);
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const float xh = (xv[k] - mu) * rs;
+            o[k] = rs * (dv[k] * gm[k] - a - xh * b);
+            pp[0][j][k] += dv[k] * xh;
+            pp[1][j][k] += dv[k];
+          }
+          if (dxr) store_full<T>(dxr + c0, o, acc_dx != 0);
+        }
+      }
+    }
+    if (base + 2 * stride < end) {
+      cd.load(row_ptr<T>(d, rn < end ? rn : 0, ldd), gl, Ci, rn < end);
+      cx.load(row_ptr<T>(x, rn < end ? rn : 0, ldx), gl, Ci, rn < end);
+    }
+  };
   for (int64_t base = first; base < end; base += 2 * stride) {
-    step(d0, x0, base);
-    if (base + stride < end) step(d1, x1, base + stride);
+    if constexpr (GLDS) {
+      step_raw(d0, x0, base);
+      if (base + stride < end) step_raw(d1, x1, base + stride);
+    } else {
+      step(d0, x0, base);
+      if (base + stride < end) step(d1, x1, base + stride);
+    }
   }
+  if constexpr (GLDS) __syncthreads();         // every group is done with gamma before the fold reuses red
   if (part) fold_partials<NV, V, G, NG, 2, BWD_BLOCK>(pp, red, part, C);
 }
 
@@ -407,7 +495,8 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
     const void* __restrict__ x, int64_t ldx, void* __restrict__ y, int64_t ldy,
     int64_t R, int64_t C, float alpha, int seq_len) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
-  __shared__ float lds[BLOCK / WAVE];
+  __shared__ float lds[4 * BLOCK / WAVE];
+  int ph = 0;
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
   const float NEG_INF = -__builtin_inff();
@@ -436,7 +525,7 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
         m = fmaxf(m, v[j][k]);
       }
     }
-    m = group_max<RW>(m, lds);
+    m = group_max<RW>(m, lds, ph);
     if (bs + 2 * stride < R) cur.load(row_ptr<T>(x, rn < R ? rn : 0, ldx), gl, Ci, rn < R);
     float s = 0.f;
 #pragma unroll
@@ -446,7 +535,7 @@ __global__ __launch_bounds__(BLOCK) void sm_fwd_fast(
         v[j][k] = fast_exp(v[j][k] - m);
         s += v[j][k];
       }
-    s = group_sum<RW>(s, lds);
+    s = group_sum<RW>(s, lds, ph);
     const float inv = 1.0f / s;
     if (active) {
       T* yr = row_ptr_w<T>(y, r, ldy);
@@ -473,7 +562,8 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
     const void* __restrict__ d, int64_t ldd, const void* __restrict__ y, int64_t ldy,
     void* __restrict__ dx, int64_t lddx, int acc, int64_t R, int64_t C, float alpha) {
   constexpr int V = io<T>::VEC, G = WAVE * RW, NG = BLOCK / G;
-  __shared__ float lds[BLOCK / WAVE];
+  __shared__ float lds[4 * BLOCK / WAVE];
+  int ph = 0;
   const int g = threadIdx.x / G, gl = threadIdx.x % G;
   const int Ci = (int)C;
   const int64_t stride = (int64_t)gridDim.x * NG;
@@ -499,7 +589,7 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int k = 0; k < V; ++k) dot += dv[j][k] * yv[j][k];
-    dot = group_sum<RW>(dot, lds);
+    dot = group_sum<RW>(dot, lds, ph);
     if (active) {
       T* dxr = row_ptr_w<T>(dx, r, lddx);
 #pragma unroll
@@ -532,11 +622,12 @@ template <typename T>
 __global__ __launch_bounds__(GEN_BLOCK) void rms_fwd_gen(
     const void* x, int64_t ldx, const float* gamma, void* y, int64_t ldy, float* ir, int64_t ldir,
     int64_t R, int64_t C, float eps, float invC) {
-  __shared__ float lds[GEN_BLOCK / WAVE];
+  __shared__ float lds[4 * GEN_BLOCK / WAVE];
+  int ph = 0;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     float ss = 0.f;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) { const float v = gl1<T>(x, r, ldx, c); ss += v * v; }
-    ss = group_sum<GEN_BLOCK / WAVE>(ss, lds);
+    ss = group_sum<GEN_BLOCK / WAVE>(ss, lds, ph);
     const float irv = rsqrtf(ss * invC + eps);
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) gs1<T>(y, r, ldy, c, gl1<T>(x, r, ldx, c) * irv * gamma[c], false);
     if (threadIdx.x == 0) ir[r * ldir] = irv;
@@ -547,11 +638,12 @@ template <typename T>
 __global__ __launch_bounds__(GEN_BLOCK) void rms_bwd_gen(
     const void* d, int64_t ldd, const void* x, int64_t ldx, const float* gamma, const float* ir,
     int64_t ldir, void* dx, int64_t lddx, int acc, int64_t R, int64_t C, float invC) {
-  __shared__ float lds[GEN_BLOCK / WAVE];
+  __shared__ float lds[4 * GEN_BLOCK / WAVE];
+  int ph = 0;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     float dot = 0.f;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) dot += gl1<T>(d, r, ldd, c) * gamma[c] * gl1<T>(x, r, ldx, c);
-    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds);
+    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds, ph);
     const float irv = ir[r * ldir];
     const float c1 = irv * irv * irv * invC * dot;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
@@ -563,14 +655,15 @@ template <typename T>
 __global__ __launch_bounds__(GEN_BLOCK) void ln_fwd_gen(
     const void* x, int64_t ldx, const float* gamma, const float* beta, void* y, int64_t ldy,
     float* mean, int64_t ldm, float* rstd, int64_t ldr, int64_t R, int64_t C, float eps, float invC) {
-  __shared__ float lds[GEN_BLOCK / WAVE];
+  __shared__ float lds[4 * GEN_BLOCK / WAVE];
+  int ph = 0;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     float s = 0.f;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) s += gl1<T>(x, r, ldx, c);
-    const float mu = group_sum<GEN_BLOCK / WAVE>(s, lds) * invC;
+    const float mu = group_sum<GEN_BLOCK / WAVE>(s, lds, ph) * invC;
     float q = 0.f;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) { const float t = gl1<T>(x, r, ldx, c) - mu; q += t * t; }
-    const float rs = rsqrtf(group_sum<GEN_BLOCK / WAVE>(q, lds) * invC + eps);
+    const float rs = rsqrtf(group_sum<GEN_BLOCK / WAVE>(q, lds, ph) * invC + eps);
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
       gs1<T>(y, r, ldy, c, (gl1<T>(x, r, ldx, c) - mu) * rs * gamma[c] + beta[c], false);
     if (threadIdx.x == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
@@ -582,7 +675,8 @@ __global__ __launch_bounds__(GEN_BLOCK) void ln_bwd_gen(
     const void* d, int64_t ldd, const void* x, int64_t ldx, const float* gamma, const float* mean,
     int64_t ldm, const float* rstd, int64_t ldr, void* dx, int64_t lddx, int acc, int64_t R,
     int64_t C, float invC) {
-  __shared__ float lds[2 * GEN_BLOCK / WAVE];
+  __shared__ float lds[4 * GEN_BLOCK / WAVE];
+  int ph = 0;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const float mu = mean[r * ldm], rs = rstd[r * ldr];
     float s1 = 0.f, s2 = 0.f;
@@ -591,7 +685,7 @@ __global__ __launch_bounds__(GEN_BLOCK) void ln_bwd_gen(
       s1 += gv;
       s2 += gv * (gl1<T>(x, r, ldx, c) - mu) * rs;
     }
-    group_sum2<GEN_BLOCK / WAVE>(s1, s2, lds);
+    group_sum2<GEN_BLOCK / WAVE>(s1, s2, lds, ph);
     const float a = s1 * invC, b = s2 * invC;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
       const float xh = (gl1<T>(x, r, ldx, c) - mu) * rs;
@@ -626,16 +720,17 @@ template <typename T>
 __global__ __launch_bounds__(GEN_BLOCK) void sm_fwd_gen(
     const void* x, int64_t ldx, void* y, int64_t ldy, int64_t R, int64_t C, float alpha,
     int causal, int seq_len) {
-  __shared__ float lds[GEN_BLOCK / WAVE];
+  __shared__ float lds[4 * GEN_BLOCK / WAVE];
+  int ph = 0;
   const float NEG_INF = -__builtin_inff();
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;
     float m = NEG_INF;
     for (int64_t c = threadIdx.x; c < lim; c += GEN_BLOCK) m = fmaxf(m, alpha * gl1<T>(x, r, ldx, c));
-    m = group_max<GEN_BLOCK / WAVE>(m, lds);
+    m = group_max<GEN_BLOCK / WAVE>(m, lds, ph);
     float s = 0.f;
     for (int64_t c = threadIdx.x; c < lim; c += GEN_BLOCK) s += fast_exp(alpha * gl1<T>(x, r, ldx, c) - m);
-    const float inv = 1.0f / group_sum<GEN_BLOCK / WAVE>(s, lds);
+    const float inv = 1.0f / group_sum<GEN_BLOCK / WAVE>(s, lds, ph);
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
       gs1<T>(y, r, ldy, c, c < lim ? fast_exp(alpha * gl1<T>(x, r, ldx, c) - m) * inv : 0.f, false);
   }
@@ -645,11 +740,12 @@ template <typename T>
 __global__ __launch_bounds__(GEN_BLOCK) void sm_bwd_gen(
     const void* d, int64_t ldd, const void* y, int64_t ldy, void* dx, int64_t lddx, int acc,
     int64_t R, int64_t C, float alpha) {
-  __shared__ float lds[GEN_BLOCK / WAVE];
+  __shared__ float lds[4 * GEN_BLOCK / WAVE];
+  int ph = 0;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     float dot = 0.f;
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) dot += gl1<T>(d, r, ldd, c) * gl1<T>(y, r, ldy, c);
-    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds);
+    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds, ph);
     for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
       const float yv = gl1<T>(y, r, ldy, c);
       gs1<T>(dx, r, lddx, c, alpha * yv * (gl1<T>(d, r, ldd, c) - dot), acc != 0);
@@ -659,41 +755,44 @@ __global__ __launch_bounds__(GEN_BLOCK) void sm_bwd_gen(
 
 // ============================================================ column sums
 // Second pass: column c of the partial rows, summed over b = 0..P-1 in a
-// fixed order (wave w takes b = w, w+16, ..., then the 16 wave sums are
-// added in wave order), goes to out0[c] for c < n0 and to out1[c - n0]
-// otherwise (the two parameter gradients of layer_norm in one launch), each
-// stored or added (acc0 / acc1).  64 columns per block.
-__global__ __launch_bounds__(1024) void fold_columns(const float* __restrict__ part, int64_t P,
-                                                    int64_t stride, int64_t C, float* __restrict__ out0,
-                                                    int acc0, int64_t n0, float* __restrict__ out1,
-                                                    int acc1) {
-  __shared__ float lds[16][64];
-  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
-  const int64_t c = (int64_t)blockIdx.x * 64 + l;
+// fixed order, goes to out0[c] for c < n0 and to out1[c - n0] otherwise
+// (the two parameter gradients of layer_norm in one launch), each stored or
+// added (acc0 / acc1).  A 512-thread block takes 32 columns (one 128-byte
+// segment of each partial row): thread t sums column t % 32 over the
+// partial rows b = p, p + 16, ... of its phase p = t / 32 (FOLD_U rows'
+// loads in flight, added in b order), then the 16 phase sums are added in
+// phase order.  Against 64 columns per block this spreads the pass over
+// twice the blocks (a 4096-wide gradient: 128); 16 columns per block
+// (64-byte segments) measured twice the fetched bytes and was slower.
+constexpr int FOLD_T = 512, FOLD_W = 32, FOLD_PH = FOLD_T / FOLD_W, FOLD_U = 32;
+
+__global__ __launch_bounds__(FOLD_T) void fold_columns(const float* __restrict__ part, int64_t P,
+                                                      int64_t stride, int64_t C, float* __restrict__ out0,
+                                                      int acc0, int64_t n0, float* __restrict__ out1,
+                                                      int acc1) {
+  __shared__ float lds[FOLD_PH][FOLD_W];
+  const int ph = threadIdx.x / FOLD_W, cl = threadIdx.x % FOLD_W;
+  const int64_t c = (int64_t)blockIdx.x * FOLD_W + cl;
   float s = 0.f;
   if (c < C) {
-    // 32 partial rows per wave in flight before the first add (the adds
-    // stay in b order); the partials sit in cache, so latency, not
-    // bandwidth, bounds this pass
-    constexpr int U = 32;
-    for (int64_t b0 = w; b0 < P; b0 += 16 * U) {
-      float v[U];
+    for (int64_t b0 = ph; b0 < P; b0 += FOLD_PH * FOLD_U) {
+      float v[FOLD_U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t b = b0 + 16 * u;
+      for (int u = 0; u < FOLD_U; ++u) {
+        const int64_t b = b0 + FOLD_PH * u;
         v[u] = b < P ? part[b * stride + c] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (b0 + 16 * u < P) s += v[u];
+      for (int u = 0; u < FOLD_U; ++u)
+        if (b0 + FOLD_PH * u < P) s += v[u];
     }
   }
-  lds[w][l] = s;
+  lds[ph][cl] = s;
   __syncthreads();
-  if (w == 0 && c < C) {
-    float t = lds[0][l];
+  if (ph == 0 && c < C) {
+    float t = lds[0][cl];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) t += lds[i][l];
+    for (int i = 1; i < FOLD_PH; ++i) t += lds[i][cl];
     float* o = c < n0 ? out0 + c : out1 + (c - n0);
     *o = (c < n0 ? acc0 : acc1) ? acc_add(*o, t) : t;
   }
@@ -786,8 +885,13 @@ int row_shapes(RowKind k, const RowShape** out) {
   static const RowShape fwd[] = {{1, 256, 8, 4}, {4, 256, 8, 4}, {8, 512, 8, 8}};
   static const RowShape lnf[] = {{1, 256, 8, 4}, {4, 256, 8, 4}, {8, 512, 8, 4}};
   static const RowShape smb[] = {{1, 256, 8, 4}, {4, 256, 8, 4}, {16, 1024, 4, 4}};
+  // bf16 rms_norm rows of up to 4 packs per lane stay on one wave (d = 2048
+  // over 1 GiB: 622 -> 610 us); layer_norm keeps them on 4 waves (562 vs
+  // 638 us), its backward holding more per lane
+  static const RowShape rmsb[] = {{1, BWD_BLOCK, 4, 4}, {4, BWD_BLOCK, 4, 2}, {8, BWD_BLOCK, 4, 2}};
   static const RowShape bwd[] = {{1, BWD_BLOCK, 4, 2}, {4, BWD_BLOCK, 4, 2}, {8, BWD_BLOCK, 4, 2}};
   if (k == RK_SM_BWD) *out = smb;
+  else if (k == RK_RMS_BWD) *out = rmsb;
   else if (is_bwd(k)) *out = bwd;
   else if (k == RK_LN_FWD) *out = lnf;
   else *out = fwd;
@@ -957,7 +1061,7 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
     if (dgamma)
       norm_partials_gen<T, 0><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)ir.data, ir.ld, nullptr, 0, part, R, C, rpb);
   }
-  if (dgamma) fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, C, C, dgamma, acc_dg, C, nullptr, 0);
+  if (dgamma) fold_columns<<<(unsigned)cdiv(C, FOLD_W), FOLD_T, 0, s>>>(part, p.grid, C, C, dgamma, acc_dg, C, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1010,7 +1114,8 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
   if (p.grid < 1) return hipErrorInvalidValue;
   float* part = want_p ? (float*)ws : nullptr;
   if (p.fast) {
-    const size_t shm = want_p ? (size_t)2 * C * sizeof(float) : 0;
+    // partial-row fold: 2C floats; one-wave bf16 rows also stage gamma (C floats) there
+    const size_t shm = (want_p ? (size_t)2 * C : sizeof(T) == 2 && p.rw == 1 ? (size_t)C : 0) * sizeof(float);
     XT_ROW_SWITCH_BWD(
       auto kf = ln_bwd_fast<T, RW, NV>;
       p.grid = fit_grid((const void*)kf, BWD_BLOCK, shm, p.grid);
@@ -1027,11 +1132,11 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
                                                            (const float*)rstd.data, rstd.ld, part, R, C, rpb);
   }
   if (dgamma && dbeta)        // partial rows are [dgamma | dbeta]: one fold over 2C columns
-    fold_columns<<<(unsigned)cdiv(2 * C, 64), 1024, 0, s>>>(part, p.grid, 2 * C, 2 * C, dgamma, acc_dg, C, dbeta, acc_db);
+    fold_columns<<<(unsigned)cdiv(2 * C, FOLD_W), FOLD_T, 0, s>>>(part, p.grid, 2 * C, 2 * C, dgamma, acc_dg, C, dbeta, acc_db);
   else if (dgamma)
-    fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.grid, 2 * C, C, dgamma, acc_dg, C, nullptr, 0);
+    fold_columns<<<(unsigned)cdiv(C, FOLD_W), FOLD_T, 0, s>>>(part, p.grid, 2 * C, C, dgamma, acc_dg, C, nullptr, 0);
   else if (dbeta)
-    fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part + C, p.grid, 2 * C, C, dbeta, acc_db, C, nullptr, 0);
+    fold_columns<<<(unsigned)cdiv(C, FOLD_W), FOLD_T, 0, s>>>(part + C, p.grid, 2 * C, C, dbeta, acc_db, C, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1142,7 +1247,7 @@ hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, siz
     else
       colsum_partials_gen<bf16_t><<<dim3(1, p.gy), GEN_BLOCK, 0, s>>>(d.data, d.ld, R, C, p.rpb, part);
   }
-  fold_columns<<<(unsigned)cdiv(C, 64), 1024, 0, s>>>(part, p.gy, C, C, out, acc, C, nullptr, 0);
+  fold_columns<<<(unsigned)cdiv(C, FOLD_W), FOLD_T, 0, s>>>(part, p.gy, C, C, out, acc, C, nullptr, 0);
   return hipGetLastError();
 }
 
