@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libxt.so")
-SOURCES = ["abi.cpp", "tape.cpp", "rowwise.hip", "ce.hip", "elementwise.hip", "rope.hip", "gemm.hip", "gradbuf.hip", "embed.hip", "attention.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "tape.cpp", "rowwise.hip", "rowstream.hip", "ce.hip", "elementwise.hip", "rope.hip", "gemm.hip", "gradbuf.hip", "embed.hip", "attention.hip", "noalloc.hip"]
 ARCH = os.environ.get("XT_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -261,6 +261,39 @@ __device__ __forceinline__ float xor32_reduce(float v, Op op) {
   return op(lo, hi);
 }
 
+// Online (max, sum of exp) state, in base-2 units: value = s * 2^(m) with
+// m = max * log2(e).
+struct MS { float m, s; };
+
+__device__ __forceinline__ MS ms_merge(MS a, MS b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -__builtin_inff()) return {m, 0.f};
+  return {m, a.s * __builtin_amdgcn_exp2f(a.m - m) + b.s * __builtin_amdgcn_exp2f(b.m - m)};
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ MS dpp_ms(MS a) {
+  return {dpp_f<CTRL, ROW_MASK>(a.m), dpp_f<CTRL, ROW_MASK>(a.s)};
+}
+
+// ms_merge over the 64 lanes in the order of wave_reduce (above): the 16
+// lanes of a row by DPP steps, then rows 1, 3 take rows 0, 2 and rows 2, 3
+// take lane 31; the wave's state is read from lane 63.  ms_merge combines
+// its two arguments symmetrically, so both lanes of a pair hold the same
+// bits after each step.
+__device__ __forceinline__ MS wave_merge(MS st) {
+  st = ms_merge(st, dpp_ms<dpp::XOR1>(st));
+  st = ms_merge(st, dpp_ms<dpp::XOR2>(st));
+  st = ms_merge(st, dpp_ms<dpp::HALF_MIRROR>(st));
+  st = ms_merge(st, dpp_ms<dpp::MIRROR>(st));
+  const int lane = __lane_id();
+  const MS a = ms_merge(st, dpp_ms<dpp::BCAST15, 0xa>(st));
+  if (lane & 16) st = a;
+  const MS b = ms_merge(st, dpp_ms<dpp::BCAST31, 0xc>(st));
+  if (lane & 32) st = b;
+  return {readlane_f(st.m, 63), readlane_f(st.s, 63)};
+}
+
 // Reductions over a group of RW consecutive waves of the block (one row per
 // group).  Every thread of the block must make the same sequence of calls
 // (they contain barriers when RW > 1).  `lds` holds 4 floats per wave of

@@ -53,6 +53,28 @@ hipError_t launch_softmax_fwd(const xt_tensor& x, const xt_tensor& y, float alph
 hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx,
                               bool acc, float alpha, hipStream_t s);
 
+// Streaming row kernels (rowstream.hip) for rows the register-resident
+// kernels do not take: one 1024-thread block per row step, `grid` blocks.
+// The backward launchers write `part` (one partial row of the parameter
+// gradients per block) only where every row starts 16-byte aligned and
+// stream_owns_partials holds; `part` = nullptr skips them.
+constexpr int STREAM_BWD_GRID = 256;
+int stream_bwd_grid(int64_t R);
+bool stream_owns_partials(int dtype, int64_t C, const xt_tensor& d, const xt_tensor& x, const xt_tensor* dx);
+hipError_t launch_sm_fwd_stream(const xt_tensor& x, const xt_tensor& y, float alpha, int causal, int seq_len,
+                                int grid, hipStream_t s);
+hipError_t launch_sm_bwd_stream(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx, bool acc, float alpha,
+                                int grid, hipStream_t s);
+hipError_t launch_rms_fwd_stream(const xt_tensor& x, const float* gamma, const xt_tensor& y, const xt_tensor& ir,
+                                 float eps, int grid, hipStream_t s);
+hipError_t launch_ln_fwd_stream(const xt_tensor& x, const float* gamma, const float* beta, const xt_tensor& y,
+                                const xt_tensor& mean, const xt_tensor& rstd, float eps, int grid, hipStream_t s);
+hipError_t launch_rms_bwd_stream(const xt_tensor& d, const xt_tensor& x, const float* gamma, const xt_tensor& ir,
+                                 const xt_tensor* dx, bool acc_dx, float* part, int grid, hipStream_t s);
+hipError_t launch_ln_bwd_stream(const xt_tensor& d, const xt_tensor& x, const float* gamma, const xt_tensor& mean,
+                                const xt_tensor& rstd, const xt_tensor* dx, bool acc_dx, float* part, int grid,
+                                hipStream_t s);
+
 // Column sums: out[c] (+)= sum_r d[r, c]  (add_bias backward).
 size_t colsum_workspace(int dtype, int64_t R, int64_t C);
 hipError_t launch_colsum(const xt_tensor& d, float* out, bool acc, void* ws, size_t ws_bytes, hipStream_t s);

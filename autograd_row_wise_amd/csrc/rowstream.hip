@@ -1,0 +1,967 @@
+// Row-wise reductions on the rows the register-resident kernels of
+// rowwise.hip do not take: rows longer than a row group's registers hold
+// (f32 softmax rows past 16384 columns, layer_norm backward rows whose
+// parameter partials would not fit the block's LDS fold), and rows that are
+// not a whole number of 16-byte packs or do not start on a 16-byte boundary
+// (a 50257-wide vocabulary row).
+//
+// [AE] "RMSNorm" paragraph and the op-backward rows "softmax" / "Softmax
+// 反向推导"; [BP] k_layernorm_fwd / k_layernorm_bwd, "Sparade tensorer",
+// "En baklängeskärnas uppgift" -- the same mathematics as the register
+// kernels, with the same saved statistics and outputs.
+//
+// One 1024-thread block per row (blocks loop over rows).  Each row is split
+// at 16-byte boundaries into a scalar head (elements before the first
+// boundary), a body of 16-byte packs and a scalar tail; every tensor the op
+// touches is split the same way when their rows start at the same offset
+// modulo 16 bytes (else the whole row goes element by element).  A row is
+// traversed twice (three times for the layer_norm forward, whose variance is
+// taken about the mean): a reduction pass with ordinary loads, so the row's
+// lines stay in the L2 and the Infinity Cache, then the pass that writes,
+// whose re-read is served from there -- HBM sees the algorithmic bytes once.
+// Block reductions are DPP wave reductions plus a fixed-order LDS combine:
+// deterministic.
+//
+// Parameter gradients (rms_norm dgamma, layer_norm dgamma | dbeta): when
+// every row has the same split (row starts 16-byte aligned), thread t owns
+// the same columns in every row -- packs t, t + 1024, ... and tail element
+// t -- and keeps their partial sums in registers over the block's rows; at
+// the end it writes them to the block's partial row (no LDS).  The fixed-
+// order column fold of rowwise.hip then sums the partial rows.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace xt {
+namespace {
+
+constexpr int ST = 1024, SW = ST / WAVE;    // threads and waves per block
+constexpr int SU = 8;                       // packs per thread in flight (forward)
+constexpr int SUB = 2;                      // (backward, three tensors)
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct Split {
+  int64_t head, packs;   // elements before the first 16-byte boundary; whole packs after them
+};
+
+template <typename T>
+__device__ __forceinline__ Split split_of(const void* p, int64_t C) {
+  constexpr int V = io<T>::VEC;
+  const uintptr_t a = (uintptr_t)p;
+  int64_t h = (int64_t)(((16 - (a & 15)) & 15) / sizeof(T));
+  if (h > C) h = C;
+  return {h, (C - h) / V};
+}
+
+__device__ __forceinline__ bool same16(const void* a, const void* b) {
+  return !b || ((((uintptr_t)a) ^ ((uintptr_t)b)) & 15) == 0;
+}
+
+template <typename T> __device__ __forceinline__ const T* crow(const void* p, int64_t r, int64_t ld) {
+  return reinterpret_cast<const T*>(p) + r * ld;
+}
+template <typename T> __device__ __forceinline__ T* wrow(void* p, int64_t r, int64_t ld) {
+  return reinterpret_cast<T*>(p) + r * ld;
+}
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (NT) return ld_nt(p);
+  else return *reinterpret_cast<const uint4*>(p);
+}
+
+// One pass over a row of NTS tensors: fs(c) for every head / tail element,
+// fp(c0, q) for every body pack (q[t] the raw pack of tensor t at column
+// c0), U packs' loads in flight per thread.  NT: nontemporal loads (the
+// last pass over the row).
+template <typename T, int NTS, int U, bool NT, class FS, class FP>
+__device__ __forceinline__ void row_pass(const T* const (&src)[NTS], const Split& sp, int64_t C, FS fs, FP fp) {
+  constexpr int V = io<T>::VEC;
+  const int tid = threadIdx.x;
+  for (int64_t c = tid; c < sp.head; c += ST) fs(c);
+  for (int64_t p0 = tid; p0 < sp.packs; p0 += (int64_t)ST * U) {
+    uint4 q[U][NTS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = p0 + (int64_t)u * ST;
+      if (p < sp.packs)
+#pragma unroll
+        for (int t = 0; t < NTS; ++t) q[u][t] = ld16<NT>(src[t] + sp.head + p * V);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = p0 + (int64_t)u * ST;
+      if (p < sp.packs) fp(sp.head + p * V, q[u]);
+    }
+  }
+  for (int64_t c = sp.head + sp.packs * V + tid; c < C; c += ST) fs(c);
+}
+
+// Block-wide (max, sum) merge: wave_merge, then the waves in order.  `ms`
+// holds two sets of SW states; consecutive calls alternate between them.
+template <int NW = SW>
+__device__ __forceinline__ MS block_merge(MS st, float (*ms)[2][NW], int& ph) {
+  st = wave_merge(st);
+  const int w = threadIdx.x / WAVE;
+  if ((threadIdx.x % WAVE) == 0) { ms[ph][0][w] = st.m; ms[ph][1][w] = st.s; }
+  __syncthreads();
+  MS tot{ms[ph][0][0], ms[ph][1][0]};
+#pragma unroll
+  for (int i = 1; i < NW; ++i) tot = ms_merge(tot, MS{ms[ph][0][i], ms[ph][1][i]});
+  ph ^= 1;
+  return tot;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_acc1(T* p, float v, bool acc) {
+  io<T>::st(p, acc ? acc_add(io<T>::ld(p), v) : v);
+}
+
+// V consecutive f32 of a parameter vector from column c0 (c0 + V <= C).  A
+// row's packs start at c0 = head + p*V, so their 4-float phase
+// (g + c0) mod 16 bytes is the same for the whole row: the covering span is
+// read with aligned 16-byte loads and the V values taken out with a
+// row-uniform select; a span that would reach past C goes element by element.
+template <int V>
+__device__ __forceinline__ void load_par(const float* __restrict__ g, int64_t c0, int64_t C, float* out) {
+  const int mis = (int)((((uintptr_t)(g + c0)) >> 2) & 3);
+  if (mis == 0) {
+#pragma unroll
+    for (int k = 0; k < V; k += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(g + c0 + k);
+      out[k] = q.x; out[k + 1] = q.y; out[k + 2] = q.z; out[k + 3] = q.w;
+    }
+    return;
+  }
+  constexpr int NQ = V / 4 + 1;
+  if (c0 - mis + 4 * NQ > C) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) out[k] = g[c0 + k];
+    return;
+  }
+  const float* base = g + c0 - mis;
+  float w[4 * NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const float4 q = *reinterpret_cast<const float4*>(base + 4 * i);
+    w[4 * i] = q.x; w[4 * i + 1] = q.y; w[4 * i + 2] = q.z; w[4 * i + 3] = q.w;
+  }
+  if (mis == 1) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) out[k] = w[k + 1];
+  } else if (mis == 2) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) out[k] = w[k + 2];
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) out[k] = w[k + 3];
+  }
+}
+
+// ================================================================ softmax
+template <typename T>
+__global__ __launch_bounds__(ST) void sm_fwd_stream(const void* __restrict__ x, int64_t ldx, void* __restrict__ y,
+                                                    int64_t ldy, int64_t R, int64_t C, float alpha, int causal,
+                                                    int seq_len) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float ms[2][2][SW];
+  int ph = 0;
+  const float sl = alpha * LOG2E;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* xr = crow<T>(x, r, ldx);
+    T* yr = wrow<T>(y, r, ldy);
+    const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;
+    const Split sp = same16(xr, yr) ? split_of<T>(xr, C) : Split{C, 0};
+    float m = -__builtin_inff(), s = 0.f;     // base-2 online state of this thread
+    const T* src[1] = {xr};
+    row_pass<T, 1, SU, false>(src, sp, C,
+        [&](int64_t c) {
+          if (c < lim) {
+            const float t = io<T>::ld(xr + c) * sl;
+            if (t > m) { s = s * __builtin_amdgcn_exp2f(m - t) + 1.f; m = t; }
+            else s += __builtin_amdgcn_exp2f(t - m);
+          }
+        },
+        [&](int64_t c0, const uint4 (&q)[1]) {
+          float v[V];
+          io<T>::unpack(q[0], v);
+          float pm = -__builtin_inff();
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            v[k] = c0 + k < lim ? v[k] * sl : -__builtin_inff();
+            pm = fmaxf(pm, v[k]);
+          }
+          if (pm == -__builtin_inff()) return;      // the whole pack is past the causal limit
+          if (pm > m) { s *= __builtin_amdgcn_exp2f(m - pm); m = pm; }
+          float a = 0.f;
+#pragma unroll
+          for (int k = 0; k < V; ++k) a += __builtin_amdgcn_exp2f(v[k] - m);
+          s += a;
+        });
+    const MS tot = block_merge(MS{m, s}, ms, ph);
+    const float inv = 1.f / tot.s, mm = tot.m;
+    row_pass<T, 1, SU, true>(src, sp, C,
+        [&](int64_t c) { io<T>::st(yr + c, c < lim ? __builtin_amdgcn_exp2f(io<T>::ld(xr + c) * sl - mm) * inv : 0.f); },
+        [&](int64_t c0, const uint4 (&q)[1]) {
+          float v[V];
+          io<T>::unpack(q[0], v);
+#pragma unroll
+          for (int k = 0; k < V; ++k) v[k] = c0 + k < lim ? __builtin_amdgcn_exp2f(v[k] * sl - mm) * inv : 0.f;
+          st_nt(yr + c0, io<T>::pack(v));
+        });
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(ST) void sm_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ y,
+                                                    int64_t ldy, void* __restrict__ dx, int64_t lddx, int acc,
+                                                    int64_t R, int64_t C, float alpha) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* dr = crow<T>(d, r, ldd);
+    const T* yr = crow<T>(y, r, ldy);
+    T* xr = wrow<T>(dx, r, lddx);
+    const Split sp = same16(dr, yr) && same16(dr, xr) ? split_of<T>(dr, C) : Split{C, 0};
+    const T* src[2] = {dr, yr};
+    float dot = 0.f;
+    row_pass<T, 2, SUB, false>(src, sp, C, [&](int64_t c) { dot += io<T>::ld(dr + c) * io<T>::ld(yr + c); },
+        [&](int64_t, const uint4 (&q)[2]) {
+          float a[V], b[V];
+          io<T>::unpack(q[0], a);
+          io<T>::unpack(q[1], b);
+#pragma unroll
+          for (int k = 0; k < V; ++k) dot += a[k] * b[k];
+        });
+    dot = group_sum<SW>(dot, lds, ph);
+    row_pass<T, 2, SUB, true>(src, sp, C,
+        [&](int64_t c) { store_acc1<T>(xr + c, alpha * io<T>::ld(yr + c) * (io<T>::ld(dr + c) - dot), acc != 0); },
+        [&](int64_t c0, const uint4 (&q)[2]) {
+          float a[V], b[V], o[V];
+          io<T>::unpack(q[0], a);
+          io<T>::unpack(q[1], b);
+#pragma unroll
+          for (int k = 0; k < V; ++k) o[k] = alpha * b[k] * (a[k] - dot);
+          if (acc) {
+            float old[V];
+            io<T>::unpack(ld_nt(xr + c0), old);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = acc_add(old[k], o[k]);
+          }
+          st_nt(xr + c0, io<T>::pack(o));
+        });
+  }
+}
+
+// =============================================================== rms_norm
+template <typename T>
+__global__ __launch_bounds__(ST) void rms_fwd_stream(const void* __restrict__ x, int64_t ldx,
+                                                     const float* __restrict__ gamma, void* __restrict__ y,
+                                                     int64_t ldy, float* __restrict__ ir, int64_t ldir, int64_t R,
+                                                     int64_t C, float eps, float invC) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* xr = crow<T>(x, r, ldx);
+    T* yr = wrow<T>(y, r, ldy);
+    const Split sp = same16(xr, yr) ? split_of<T>(xr, C) : Split{C, 0};
+    const T* src[1] = {xr};
+    float ss = 0.f;
+    row_pass<T, 1, SU, false>(src, sp, C, [&](int64_t c) { const float v = io<T>::ld(xr + c); ss += v * v; },
+        [&](int64_t, const uint4 (&q)[1]) {
+          float v[V];
+          io<T>::unpack(q[0], v);
+#pragma unroll
+          for (int k = 0; k < V; ++k) ss += v[k] * v[k];
+        });
+    ss = group_sum<SW>(ss, lds, ph);
+    const float irv = rsqrtf(ss * invC + eps);
+    if (threadIdx.x == 0) ir[r * ldir] = irv;
+    row_pass<T, 1, SU, true>(src, sp, C, [&](int64_t c) { io<T>::st(yr + c, io<T>::ld(xr + c) * irv * gamma[c]); },
+        [&](int64_t c0, const uint4 (&q)[1]) {
+          float v[V], g[V];
+          io<T>::unpack(q[0], v);
+          load_par<V>(gamma, c0, C, g);
+#pragma unroll
+          for (int k = 0; k < V; ++k) v[k] = v[k] * irv * g[k];
+          st_nt(yr + c0, io<T>::pack(v));
+        });
+  }
+}
+
+// Columns owned by this thread when every row has the same split with no
+// head: packs tid + k*ST (k < PK) and tail element tid.  Partial sums of
+// NP per-column terms are kept for them over the block's rows.
+template <int NP, int PK, int V>
+struct OwnedPartials {
+  float pk[NP][PK][V];
+  float tl[NP];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      tl[q] = 0.f;
+#pragma unroll
+      for (int k = 0; k < PK; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) pk[q][k][e] = 0.f;
+    }
+  }
+  // writes this thread's columns of the block's partial row (NP vectors of C)
+  __device__ __forceinline__ void write(float* part, int64_t packs, int64_t C) const {
+    float* out = part + (int64_t)blockIdx.x * NP * C;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+#pragma unroll
+      for (int k = 0; k < PK; ++k) {
+        const int64_t p = tid + (int64_t)k * ST;
+        if (p < packs)
+#pragma unroll
+          for (int e = 0; e < V; ++e) out[q * C + p * V + e] = pk[q][k][e];
+      }
+      const int64_t c = packs * V + tid;
+      if (c < C) out[q * C + c] = tl[q];
+    }
+  }
+};
+
+// rms_norm backward, fixed split (PK > 0: owned partials of dgamma) or any
+// split (PK == 0: dx only; the partials come from a separate column pass).
+template <typename T, int PK>
+__global__ __launch_bounds__(ST) void rms_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
+                                                     int64_t ldx, const float* __restrict__ gamma,
+                                                     const float* __restrict__ ir, int64_t ldir, void* __restrict__ dx,
+                                                     int64_t lddx, int acc, float* __restrict__ part, int64_t R,
+                                                     int64_t C, float invC) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  OwnedPartials<1, PK ? PK : 1, V> pp;
+  pp.zero();
+  const int tid = threadIdx.x;
+  int64_t packs_fixed = 0;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* dr = crow<T>(d, r, ldd);
+    const T* xr = crow<T>(x, r, ldx);
+    T* or_ = dx ? wrow<T>(dx, r, lddx) : nullptr;
+    const Split sp = same16(dr, xr) && same16(dr, or_) ? split_of<T>(dr, C) : Split{C, 0};
+    const float irv = ir[r * ldir];
+    const T* src[2] = {dr, xr};
+    float dot = 0.f;
+    row_pass<T, 2, SUB, false>(src, sp, C, [&](int64_t c) { dot += io<T>::ld(dr + c) * gamma[c] * io<T>::ld(xr + c); },
+        [&](int64_t c0, const uint4 (&q)[2]) {
+          float a[V], b[V], g[V];
+          io<T>::unpack(q[0], a);
+          io<T>::unpack(q[1], b);
+          load_par<V>(gamma, c0, C, g);
+#pragma unroll
+          for (int k = 0; k < V; ++k) dot += a[k] * g[k] * b[k];
+        });
+    dot = group_sum<SW>(dot, lds, ph);
+    const float c1 = irv * irv * irv * invC * dot;
+    if constexpr (PK > 0) {
+      // fixed split (head 0): pack tid + k*ST of every row is this thread's
+      packs_fixed = sp.packs;
+#pragma unroll
+      for (int k0 = 0; k0 < PK; k0 += SUB) {
+        uint4 q[SUB][2];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          const int64_t p = tid + (int64_t)(k0 + u) * ST;
+          if (p < sp.packs) { q[u][0] = ld_nt(dr + p * V); q[u][1] = ld_nt(xr + p * V); }
+        }
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          const int64_t p = tid + (int64_t)(k0 + u) * ST;
+          if (p >= sp.packs) continue;
+          float a[V], b[V], g[V], o[V];
+          io<T>::unpack(q[u][0], a);
+          io<T>::unpack(q[u][1], b);
+          load_par<V>(gamma, p * V, C, g);
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            o[k] = irv * (a[k] * g[k]) - b[k] * c1;
+            pp.pk[0][k0 + u][k] += a[k] * b[k] * irv;
+          }
+          if (or_) {
+            if (acc) {
+              float old[V];
+              io<T>::unpack(ld_nt(or_ + p * V), old);
+#pragma unroll
+              for (int k = 0; k < V; ++k) o[k] = acc_add(old[k], o[k]);
+            }
+            st_nt(or_ + p * V, io<T>::pack(o));
+          }
+        }
+      }
+      const int64_t c = sp.packs * V + tid;
+      if (c < C) {
+        const float a = io<T>::ld(dr + c), b = io<T>::ld(xr + c);
+        pp.tl[0] += a * b * irv;
+        if (or_) store_acc1<T>(or_ + c, irv * (a * gamma[c]) - b * c1, acc != 0);
+      }
+    } else if (or_) {
+      row_pass<T, 2, SUB, true>(src, sp, C,
+          [&](int64_t c) { store_acc1<T>(or_ + c, irv * (io<T>::ld(dr + c) * gamma[c]) - io<T>::ld(xr + c) * c1, acc != 0); },
+          [&](int64_t c0, const uint4 (&q)[2]) {
+            float a[V], b[V], g[V], o[V];
+            io<T>::unpack(q[0], a);
+            io<T>::unpack(q[1], b);
+            load_par<V>(gamma, c0, C, g);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = irv * (a[k] * g[k]) - b[k] * c1;
+            if (acc) {
+              float old[V];
+              io<T>::unpack(ld_nt(or_ + c0), old);
+#pragma unroll
+              for (int k = 0; k < V; ++k) o[k] = acc_add(old[k], o[k]);
+            }
+            st_nt(or_ + c0, io<T>::pack(o));
+          });
+    }
+  }
+  if constexpr (PK > 0)
+    if (part) pp.write(part, packs_fixed, C);
+}
+
+// ============================================================= layer_norm
+template <typename T>
+__global__ __launch_bounds__(ST) void ln_fwd_stream(const void* __restrict__ x, int64_t ldx,
+                                                    const float* __restrict__ gamma, const float* __restrict__ beta,
+                                                    void* __restrict__ y, int64_t ldy, float* __restrict__ mean,
+                                                    int64_t ldm, float* __restrict__ rstd, int64_t ldr, int64_t R,
+                                                    int64_t C, float eps, float invC) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* xr = crow<T>(x, r, ldx);
+    T* yr = wrow<T>(y, r, ldy);
+    const Split sp = same16(xr, yr) ? split_of<T>(xr, C) : Split{C, 0};
+    const T* src[1] = {xr};
+    float s = 0.f;
+    row_pass<T, 1, SU, false>(src, sp, C, [&](int64_t c) { s += io<T>::ld(xr + c); },
+        [&](int64_t, const uint4 (&q)[1]) {
+          float v[V];
+          io<T>::unpack(q[0], v);
+#pragma unroll
+          for (int k = 0; k < V; ++k) s += v[k];
+        });
+    const float mu = group_sum<SW>(s, lds, ph) * invC;
+    float qv = 0.f;        // sum of squared deviations about the mean (a second pass)
+    row_pass<T, 1, SU, false>(src, sp, C, [&](int64_t c) { const float t = io<T>::ld(xr + c) - mu; qv += t * t; },
+        [&](int64_t, const uint4 (&q)[1]) {
+          float v[V];
+          io<T>::unpack(q[0], v);
+#pragma unroll
+          for (int k = 0; k < V; ++k) { const float t = v[k] - mu; qv += t * t; }
+        });
+    const float rs = rsqrtf(group_sum<SW>(qv, lds, ph) * invC + eps);
+    if (threadIdx.x == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
+    row_pass<T, 1, SU, true>(src, sp, C,
+        [&](int64_t c) { io<T>::st(yr + c, (io<T>::ld(xr + c) - mu) * rs * gamma[c] + beta[c]); },
+        [&](int64_t c0, const uint4 (&q)[1]) {
+          float v[V], g[V], b[V];
+          io<T>::unpack(q[0], v);
+          load_par<V>(gamma, c0, C, g);
+          load_par<V>(beta, c0, C, b);
+#pragma unroll
+          for (int k = 0; k < V; ++k) v[k] = (v[k] - mu) * rs * g[k] + b[k];
+          st_nt(yr + c0, io<T>::pack(v));
+        });
+  }
+}
+
+template <typename T, int PK>
+__global__ __launch_bounds__(ST) void ln_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
+                                                    int64_t ldx, const float* __restrict__ gamma,
+                                                    const float* __restrict__ mean, int64_t ldm,
+                                                    const float* __restrict__ rstd, int64_t ldr,
+                                                    void* __restrict__ dx, int64_t lddx, int acc,
+                                                    float* __restrict__ part, int64_t R, int64_t C, float invC) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  OwnedPartials<2, PK ? PK : 1, V> pp;
+  pp.zero();
+  const int tid = threadIdx.x;
+  int64_t packs_fixed = 0;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* dr = crow<T>(d, r, ldd);
+    const T* xr = crow<T>(x, r, ldx);
+    T* or_ = dx ? wrow<T>(dx, r, lddx) : nullptr;
+    const Split sp = same16(dr, xr) && same16(dr, or_) ? split_of<T>(dr, C) : Split{C, 0};
+    const float mu = mean[r * ldm], rs = rstd[r * ldr];
+    const T* src[2] = {dr, xr};
+    float s1 = 0.f, s2 = 0.f;
+    row_pass<T, 2, SUB, false>(src, sp, C,
+        [&](int64_t c) {
+          const float gv = io<T>::ld(dr + c) * gamma[c];
+          s1 += gv;
+          s2 += gv * ((io<T>::ld(xr + c) - mu) * rs);
+        },
+        [&](int64_t c0, const uint4 (&q)[2]) {
+          float a[V], b[V], g[V];
+          io<T>::unpack(q[0], a);
+          io<T>::unpack(q[1], b);
+          load_par<V>(gamma, c0, C, g);
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const float gv = a[k] * g[k];
+            s1 += gv;
+            s2 += gv * ((b[k] - mu) * rs);
+          }
+        });
+    group_sum2<SW>(s1, s2, lds, ph);
+    const float a1 = s1 * invC, b1 = s2 * invC;
+    auto dxv = [&](float dv, float gv, float xv) { return rs * (dv * gv - a1 - ((xv - mu) * rs) * b1); };
+    if constexpr (PK > 0) {
+      packs_fixed = sp.packs;
+#pragma unroll
+      for (int k0 = 0; k0 < PK; k0 += SUB) {
+        uint4 q[SUB][2];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          const int64_t p = tid + (int64_t)(k0 + u) * ST;
+          if (p < sp.packs) { q[u][0] = ld_nt(dr + p * V); q[u][1] = ld_nt(xr + p * V); }
+        }
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          const int64_t p = tid + (int64_t)(k0 + u) * ST;
+          if (p >= sp.packs) continue;
+          float a[V], b[V], g[V], o[V];
+          io<T>::unpack(q[u][0], a);
+          io<T>::unpack(q[u][1], b);
+          load_par<V>(gamma, p * V, C, g);
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            o[k] = dxv(a[k], g[k], b[k]);
+            pp.pk[0][k0 + u][k] += a[k] * ((b[k] - mu) * rs);
+            pp.pk[1][k0 + u][k] += a[k];
+          }
+          if (or_) {
+            if (acc) {
+              float old[V];
+              io<T>::unpack(ld_nt(or_ + p * V), old);
+#pragma unroll
+              for (int k = 0; k < V; ++k) o[k] = acc_add(old[k], o[k]);
+            }
+            st_nt(or_ + p * V, io<T>::pack(o));
+          }
+        }
+      }
+      const int64_t c = sp.packs * V + tid;
+      if (c < C) {
+        const float a = io<T>::ld(dr + c), b = io<T>::ld(xr + c);
+        pp.tl[0] += a * ((b - mu) * rs);
+        pp.tl[1] += a;
+        if (or_) store_acc1<T>(or_ + c, dxv(a, gamma[c], b), acc != 0);
+      }
+    } else if (or_) {
+      row_pass<T, 2, SUB, true>(src, sp, C,
+          [&](int64_t c) { store_acc1<T>(or_ + c, dxv(io<T>::ld(dr + c), gamma[c], io<T>::ld(xr + c)), acc != 0); },
+          [&](int64_t c0, const uint4 (&q)[2]) {
+            float a[V], b[V], g[V], o[V];
+            io<T>::unpack(q[0], a);
+            io<T>::unpack(q[1], b);
+            load_par<V>(gamma, c0, C, g);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = dxv(a[k], g[k], b[k]);
+            if (acc) {
+              float old[V];
+              io<T>::unpack(ld_nt(or_ + c0), old);
+#pragma unroll
+              for (int k = 0; k < V; ++k) o[k] = acc_add(old[k], o[k]);
+            }
+            st_nt(or_ + c0, io<T>::pack(o));
+          });
+    }
+  }
+  if constexpr (PK > 0)
+    if (part) pp.write(part, packs_fixed, C);
+}
+
+// ======================================================= register rows
+// Rows of at most NPR packs per thread are loaded once into registers: thread
+// t holds packs t + k*ST (k < NPR) of each tensor, and at most one head and
+// one tail element (both are shorter than a pack).  Both passes then run on
+// the registers: HBM sees each byte once, no second read.  The tensors'
+// rows must start at the same offset modulo 16 bytes (checked on the host).
+
+template <typename T, int NTS, int NPR, int BT = ST>
+struct RegRow {
+  static constexpr int V = io<T>::VEC;
+  uint4 q[NPR][NTS];
+  float h[NTS], t[NTS];     // this thread's head element (column tid) and tail element
+  int64_t tc;                // column of the tail element
+  bool hv, tv;
+  __device__ __forceinline__ void load(const T* const (&src)[NTS], const Split& sp, int64_t C) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      const int64_t p = tid + (int64_t)k * BT;
+#pragma unroll
+      for (int i = 0; i < NTS; ++i) q[k][i] = p < sp.packs ? ld_nt(src[i] + sp.head + p * V) : make_uint4(0, 0, 0, 0);
+    }
+    hv = tid < sp.head;
+    tc = sp.head + sp.packs * V + tid;
+    tv = tc < C;
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) {
+      h[i] = hv ? io<T>::ld(src[i] + tid) : 0.f;
+      t[i] = tv ? io<T>::ld(src[i] + tc) : 0.f;
+    }
+  }
+  // An empty asm that claims to rewrite the raw packs: values unpacked
+  // from them before it cannot be kept past it, so only the raw packs stay
+  // live across a block reduction (half the registers of bf16 values as
+  // f32) and each pass unpacks again where it uses them.
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int k = 0; k < NPR; ++k)
+#pragma unroll
+      for (int i = 0; i < NTS; ++i) asm volatile("" : "+v"(q[k][i].x), "+v"(q[k][i].y), "+v"(q[k][i].z), "+v"(q[k][i].w));
+  }
+  __device__ __forceinline__ bool has(const Split& sp, int k) const { return threadIdx.x + (int64_t)k * BT < sp.packs; }
+  __device__ __forceinline__ int64_t col(const Split& sp, int k) const {
+    return sp.head + (threadIdx.x + (int64_t)k * BT) * V;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void store_pack_acc_full(T* p, float* o, bool acc) {
+  constexpr int V = io<T>::VEC;
+  if (acc) {
+    float old[V];
+    io<T>::unpack(ld_nt(p), old);
+#pragma unroll
+    for (int k = 0; k < V; ++k) o[k] = acc_add(old[k], o[k]);
+  }
+  st_nt(p, io<T>::pack(o));
+}
+
+template <typename T, int NPR>
+__global__ __launch_bounds__(ST) void sm_bwd_reg(const void* __restrict__ d, int64_t ldd, const void* __restrict__ y,
+                                                 int64_t ldy, void* __restrict__ dx, int64_t lddx, int acc, int64_t R,
+                                                 int64_t C, float alpha) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* dr = crow<T>(d, r, ldd);
+    const T* yr = crow<T>(y, r, ldy);
+    T* xr = wrow<T>(dx, r, lddx);
+    const Split sp = split_of<T>(dr, C);
+    const T* src[2] = {dr, yr};
+    RegRow<T, 2, NPR> rr;
+    rr.load(src, sp, C);
+    float dot = rr.h[0] * rr.h[1] + rr.t[0] * rr.t[1];
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float a[V], b[V];
+      io<T>::unpack(rr.q[k][0], a);
+      io<T>::unpack(rr.q[k][1], b);
+#pragma unroll
+      for (int e = 0; e < V; ++e) dot += a[e] * b[e];
+    }
+    dot = group_sum<SW>(dot, lds, ph);
+    rr.pin();
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float a[V], b[V], o[V];
+      io<T>::unpack(rr.q[k][0], a);
+      io<T>::unpack(rr.q[k][1], b);
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = alpha * b[e] * (a[e] - dot);
+      store_pack_acc_full<T>(xr + rr.col(sp, k), o, acc != 0);
+    }
+    if (rr.hv) store_acc1<T>(xr + threadIdx.x, alpha * rr.h[1] * (rr.h[0] - dot), acc != 0);
+    if (rr.tv) store_acc1<T>(xr + rr.tc, alpha * rr.t[1] * (rr.t[0] - dot), acc != 0);
+  }
+}
+
+// rms_norm / layer_norm backward on register rows (LN = false: rms_norm).
+// OWN: every row starts 16-byte aligned (no head), so thread t's columns
+// are the same in every row and it keeps their parameter-gradient partial
+// sums; otherwise dx only (the partials come from the column pass).
+template <typename T, int NPR, bool LN, bool OWN>
+__global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
+                                                   int64_t ldx, const float* __restrict__ gamma,
+                                                   const float* __restrict__ st0, int64_t ld0,
+                                                   const float* __restrict__ st1, int64_t ld1, void* __restrict__ dx,
+                                                   int64_t lddx, int acc, float* __restrict__ part, int64_t R,
+                                                   int64_t C, float invC) {
+  constexpr int V = io<T>::VEC, NP = LN ? 2 : 1;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  OwnedPartials<NP, OWN ? NPR : 1, V> pp;
+  pp.zero();
+  int64_t packs_fixed = 0;
+  const int tid = threadIdx.x;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* dr = crow<T>(d, r, ldd);
+    const T* xr = crow<T>(x, r, ldx);
+    T* orr = dx ? wrow<T>(dx, r, lddx) : nullptr;
+    const Split sp = split_of<T>(dr, C);
+    packs_fixed = sp.packs;
+    const T* src[2] = {dr, xr};
+    RegRow<T, 2, NPR> rr;
+    rr.load(src, sp, C);
+    // rms_norm: st0 = inv_rms; layer_norm: st0 = mean, st1 = rstd
+    const float s0 = st0[r * ld0], s1v = LN ? st1[r * ld1] : 0.f;
+    auto xhat = [&](float xv) { return LN ? (xv - s0) * s1v : xv; };
+    const float gh = rr.hv ? gamma[tid] : 0.f, gt = rr.tv ? gamma[rr.tc] : 0.f;
+    float a1 = rr.h[0] * gh + rr.t[0] * gt;                                   // layer_norm: sum d*gamma
+    float a2 = rr.h[0] * gh * xhat(rr.h[1]) + rr.t[0] * gt * xhat(rr.t[1]);   // sum d*gamma*xhat (rms: *x)
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float a[V], b[V], g[V];
+      io<T>::unpack(rr.q[k][0], a);
+      io<T>::unpack(rr.q[k][1], b);
+      load_par<V>(gamma, rr.col(sp, k), C, g);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float gv = a[e] * g[e];
+        a1 += gv;
+        a2 += gv * xhat(b[e]);
+      }
+    }
+    float c1, mg, mgx;
+    if constexpr (LN) {
+      group_sum2<SW>(a1, a2, lds, ph);
+      mg = a1 * invC;
+      mgx = a2 * invC;
+      c1 = 0.f;
+    } else {
+      a2 = group_sum<SW>(a2, lds, ph);
+      c1 = s0 * s0 * s0 * invC * a2;
+      mg = mgx = 0.f;
+    }
+    rr.pin();
+    auto dxv = [&](float dv, float gv, float xv) {
+      return LN ? s1v * (dv * gv - mg - xhat(xv) * mgx) : s0 * (dv * gv) - xv * c1;
+    };
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float a[V], b[V], g[V], o[V];
+      io<T>::unpack(rr.q[k][0], a);
+      io<T>::unpack(rr.q[k][1], b);
+      const int64_t c0 = rr.col(sp, k);
+      load_par<V>(gamma, c0, C, g);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        o[e] = dxv(a[e], g[e], b[e]);
+        if constexpr (OWN) {
+          pp.pk[0][k][e] += LN ? a[e] * xhat(b[e]) : a[e] * b[e] * s0;
+          if constexpr (LN) pp.pk[NP - 1][k][e] += a[e];
+        }
+      }
+      if (orr) store_pack_acc_full<T>(orr + c0, o, acc != 0);
+    }
+    if (rr.hv && orr) store_acc1<T>(orr + tid, dxv(rr.h[0], gh, rr.h[1]), acc != 0);
+    if (rr.tv) {
+      if (orr) store_acc1<T>(orr + rr.tc, dxv(rr.t[0], gt, rr.t[1]), acc != 0);
+      if constexpr (OWN) {
+        pp.tl[0] += LN ? rr.t[0] * xhat(rr.t[1]) : rr.t[0] * rr.t[1] * s0;
+        if constexpr (LN) pp.tl[NP - 1] += rr.t[0];
+      }
+    }
+  }
+  if constexpr (OWN)
+    if (part) pp.write(part, packs_fixed, C);
+}
+
+bool al16(const xt_tensor* t) {
+  if (!t) return true;
+  const int es = t->dtype == XT_F32 ? 4 : 2;
+  return (((uintptr_t)t->data) & 15) == 0 && ((t->ld * es) & 15) == 0;
+}
+
+// Every row of a and of b starts at the same offset modulo 16 bytes.
+bool same_phase(const xt_tensor& a, const xt_tensor* b) {
+  if (!b) return true;
+  const int es = a.dtype == XT_F32 ? 4 : 2;
+  return ((((uintptr_t)a.data) - ((uintptr_t)b->data)) & 15) == 0 && (((a.ld - b->ld) * es) & 15) == 0;
+}
+
+// Packs per thread a register row needs (the head takes at most V - 1 more
+// elements, which never add a pack): 1, 2, 4, 8 or 16; 0 past `cap`.
+int reg_npr(int dtype, int64_t C, int cap, int bt = ST) {
+  const int V = dtype == XT_F32 ? 4 : 8;
+  const int64_t per = (C / V + bt - 1) / bt;
+  int n = 1;
+  while (n < per) n *= 2;
+  return n <= cap ? n : 0;
+}
+
+// Packs per thread when every row starts 16-byte aligned and has at most
+// 4 (f32) / 2 (bf16) packs per thread, i.e. up to 16384 columns; 0
+// otherwise (no owned partials).  More packs per thread spill registers.
+int owned_pk(int dtype, int64_t C, bool fixed) {
+  const int V = dtype == XT_F32 ? 4 : 8;
+  if (!fixed) return 0;
+  const int64_t per = (C / V + ST - 1) / ST;
+  const int cap = dtype == XT_F32 ? 4 : 2;
+  if (per > cap) return 0;
+  return per <= 2 ? 2 : 4;
+}
+
+#define XT_NPR_CASES(NPRV, MAXN, ...)                                               \
+  do {                                                                             \
+    if (NPRV == 1) { constexpr int NPR = 1; __VA_ARGS__; }                         \
+    else if (NPRV == 2) { constexpr int NPR = 2; __VA_ARGS__; }                    \
+    else if (NPRV == 4) { constexpr int NPR = 4; __VA_ARGS__; }                    \
+    else if (NPRV == 8 && MAXN >= 8) { constexpr int NPR = (MAXN >= 8 ? 8 : 1); __VA_ARGS__; } \
+    else if (MAXN >= 16) { constexpr int NPR = (MAXN >= 16 ? 16 : 1); __VA_ARGS__; } \
+  } while (0)
+
+}  // namespace
+
+int stream_bwd_grid(int64_t R) { return (int)std::max<int64_t>(1, std::min<int64_t>(R, STREAM_BWD_GRID)); }
+
+bool stream_owns_partials(int dtype, int64_t C, const xt_tensor& d, const xt_tensor& x, const xt_tensor* dx) {
+  return owned_pk(dtype, C, al16(&d) && al16(&x) && al16(dx)) > 0;
+}
+
+hipError_t launch_sm_fwd_stream(const xt_tensor& x, const xt_tensor& y, float alpha, int causal, int seq_len,
+                                int grid, hipStream_t s) {
+  if (x.dtype == XT_F32)
+    sm_fwd_stream<float><<<grid, ST, 0, s>>>(x.data, x.ld, y.data, y.ld, x.rows, x.cols, alpha, causal, seq_len);
+  else
+    sm_fwd_stream<bf16_t><<<grid, ST, 0, s>>>(x.data, x.ld, y.data, y.ld, x.rows, x.cols, alpha, causal, seq_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_sm_bwd_stream(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx, bool acc, float alpha,
+                                int grid, hipStream_t s) {
+  const int npr = same_phase(d, &y) && same_phase(d, &dx) ? reg_npr(d.dtype, d.cols, 8) : 0;
+  if (npr) {
+    if (d.dtype == XT_F32)
+      XT_NPR_CASES(npr, 8, sm_bwd_reg<float, NPR><<<grid, ST, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc,
+                                                                      d.rows, d.cols, alpha));
+    else
+      XT_NPR_CASES(npr, 8, sm_bwd_reg<bf16_t, NPR><<<grid, ST, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc,
+                                                                       d.rows, d.cols, alpha));
+    return hipGetLastError();
+  }
+  if (d.dtype == XT_F32)
+    sm_bwd_stream<float><<<grid, ST, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, d.rows, d.cols, alpha);
+  else
+    sm_bwd_stream<bf16_t><<<grid, ST, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, d.rows, d.cols, alpha);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_fwd_stream(const xt_tensor& x, const float* gamma, const xt_tensor& y, const xt_tensor& ir,
+                                 float eps, int grid, hipStream_t s) {
+  const float invC = 1.0f / (float)x.cols;
+  if (x.dtype == XT_F32)
+    rms_fwd_stream<float><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, x.rows,
+                                              x.cols, eps, invC);
+  else
+    rms_fwd_stream<bf16_t><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, x.rows,
+                                               x.cols, eps, invC);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_fwd_stream(const xt_tensor& x, const float* gamma, const float* beta, const xt_tensor& y,
+                                const xt_tensor& mean, const xt_tensor& rstd, float eps, int grid, hipStream_t s) {
+  const float invC = 1.0f / (float)x.cols;
+  if (x.dtype == XT_F32)
+    ln_fwd_stream<float><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld,
+                                             (float*)rstd.data, rstd.ld, x.rows, x.cols, eps, invC);
+  else
+    ln_fwd_stream<bf16_t><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld,
+                                              (float*)rstd.data, rstd.ld, x.rows, x.cols, eps, invC);
+  return hipGetLastError();
+}
+
+// part: the block partial rows of dgamma when the split is fixed (owned
+// partials); otherwise the caller computes them with a column pass.
+#define XT_STREAM_PK(DT, PKV, ...)                                                   \
+  do {                                                                              \
+    if (DT == XT_F32) {                                                             \
+      using T = float;                                                              \
+      if (PKV == 0) { constexpr int PK = 0; __VA_ARGS__; }                          \
+      else if (PKV == 2) { constexpr int PK = 2; __VA_ARGS__; }                     \
+      else { constexpr int PK = 4; __VA_ARGS__; }                                   \
+    } else {                                                                        \
+      using T = bf16_t;                                                             \
+      if (PKV == 0) { constexpr int PK = 0; __VA_ARGS__; }                          \
+      else { constexpr int PK = 2; __VA_ARGS__; }                                   \
+    }                                                                               \
+  } while (0)
+
+namespace {
+// Launches the register-row backward when the rows fit (up to 8 packs per
+// thread; with owned partials, the owned_pk sizes); returns false to leave
+// the row to the two-pass kernels.  part != nullptr only with owned
+// partials (pk > 0).
+template <bool LN>
+bool norm_bwd_reg_launch(const xt_tensor& d, const xt_tensor& x, const float* gamma, const float* st0, int64_t ld0,
+                         const float* st1, int64_t ld1, const xt_tensor* dx, bool acc, float* part, int pk, int grid,
+                         hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  if (!same_phase(d, &x) || !same_phase(d, dx)) return false;
+  const float invC = 1.0f / (float)C;
+  void* dxp = dx ? dx->data : nullptr;
+  const int64_t lddx = dx ? dx->ld : 0;
+  if (part) {
+    // owned partials: NPR = pk packs per thread
+    if (d.dtype == XT_F32) {
+      if (pk == 2) norm_bwd_reg<float, 2, LN, true><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, st0, ld0, st1, ld1, dxp, lddx, acc, part, R, C, invC);
+      else norm_bwd_reg<float, 4, LN, true><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, st0, ld0, st1, ld1, dxp, lddx, acc, part, R, C, invC);
+    } else {
+      norm_bwd_reg<bf16_t, 2, LN, true><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, st0, ld0, st1, ld1, dxp, lddx, acc, part, R, C, invC);
+    }
+    return true;
+  }
+  if (!dx) return true;                 // no dx and no owned partials: nothing for this kernel
+  const int npr = reg_npr(d.dtype, C, 8);
+  if (!npr) return false;
+  if (d.dtype == XT_F32)
+    XT_NPR_CASES(npr, 8, norm_bwd_reg<float, NPR, LN, false><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, st0, ld0, st1, ld1, dxp, lddx, acc, nullptr, R, C, invC));
+  else
+    XT_NPR_CASES(npr, 8, norm_bwd_reg<bf16_t, NPR, LN, false><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, st0, ld0, st1, ld1, dxp, lddx, acc, nullptr, R, C, invC));
+  return true;
+}
+}  // namespace
+
+hipError_t launch_rms_bwd_stream(const xt_tensor& d, const xt_tensor& x, const float* gamma, const xt_tensor& ir,
+                                 const xt_tensor* dx, bool acc_dx, float* part, int grid, hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  const float invC = 1.0f / (float)C;
+  const int pk = part ? owned_pk(d.dtype, C, al16(&d) && al16(&x) && al16(dx)) : 0;
+  if (norm_bwd_reg_launch<false>(d, x, gamma, (const float*)ir.data, ir.ld, nullptr, 0, dx, acc_dx, pk ? part : nullptr,
+                                 pk, grid, s))
+    return hipGetLastError();
+  XT_STREAM_PK(d.dtype, pk,
+      rms_bwd_stream<T, PK><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
+                                                dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, pk ? part : nullptr,
+                                                R, C, invC));
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_bwd_stream(const xt_tensor& d, const xt_tensor& x, const float* gamma, const xt_tensor& mean,
+                                const xt_tensor& rstd, const xt_tensor* dx, bool acc_dx, float* part, int grid,
+                                hipStream_t s) {
+  const int64_t R = d.rows, C = d.cols;
+  const float invC = 1.0f / (float)C;
+  const int pk = part ? owned_pk(d.dtype, C, al16(&d) && al16(&x) && al16(dx)) : 0;
+  if (norm_bwd_reg_launch<true>(d, x, gamma, (const float*)mean.data, mean.ld, (const float*)rstd.data, rstd.ld, dx,
+                                acc_dx, pk ? part : nullptr, pk, grid, s))
+    return hipGetLastError();
+  XT_STREAM_PK(d.dtype, pk,
+      ln_bwd_stream<T, PK><<<grid, ST, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
+                                               (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr,
+                                               dx ? dx->ld : 0, acc_dx, pk ? part : nullptr, R, C, invC));
+  return hipGetLastError();
+}
+
+}  // namespace xt

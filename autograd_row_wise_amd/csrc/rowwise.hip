@@ -609,148 +609,47 @@ __global__ __launch_bounds__(BLOCK) void sm_bwd_fast(
 }
 
 // =============================================================== generic path
-// One 256-thread block per row, element-wise loads, several passes.
+// Rows the register-resident kernels do not take go to the streaming
+// kernels of rowstream.hip.  What remains here: the parameter-gradient
+// partials of rows whose starts are not 16-byte aligned (the streaming
+// backward then keeps no per-thread column partials), by columns.
 template <typename T> __device__ __forceinline__ float gl1(const void* p, int64_t r, int64_t ld, int64_t c) {
   return io<T>::ld(reinterpret_cast<const T*>(p) + r * ld + c);
 }
-template <typename T> __device__ __forceinline__ void gs1(void* p, int64_t r, int64_t ld, int64_t c, float v, bool acc) {
-  T* q = reinterpret_cast<T*>(p) + r * ld + c;
-  io<T>::st(q, acc ? acc_add(io<T>::ld(q), v) : v);
-}
 
-template <typename T>
-__global__ __launch_bounds__(GEN_BLOCK) void rms_fwd_gen(
-    const void* x, int64_t ldx, const float* gamma, void* y, int64_t ldy, float* ir, int64_t ldir,
-    int64_t R, int64_t C, float eps, float invC) {
-  __shared__ float lds[4 * GEN_BLOCK / WAVE];
-  int ph = 0;
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-    float ss = 0.f;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) { const float v = gl1<T>(x, r, ldx, c); ss += v * v; }
-    ss = group_sum<GEN_BLOCK / WAVE>(ss, lds, ph);
-    const float irv = rsqrtf(ss * invC + eps);
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) gs1<T>(y, r, ldy, c, gl1<T>(x, r, ldx, c) * irv * gamma[c], false);
-    if (threadIdx.x == 0) ir[r * ldir] = irv;
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(GEN_BLOCK) void rms_bwd_gen(
-    const void* d, int64_t ldd, const void* x, int64_t ldx, const float* gamma, const float* ir,
-    int64_t ldir, void* dx, int64_t lddx, int acc, int64_t R, int64_t C, float invC) {
-  __shared__ float lds[4 * GEN_BLOCK / WAVE];
-  int ph = 0;
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-    float dot = 0.f;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) dot += gl1<T>(d, r, ldd, c) * gamma[c] * gl1<T>(x, r, ldx, c);
-    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds, ph);
-    const float irv = ir[r * ldir];
-    const float c1 = irv * irv * irv * invC * dot;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
-      gs1<T>(dx, r, lddx, c, irv * (gl1<T>(d, r, ldd, c) * gamma[c]) - gl1<T>(x, r, ldx, c) * c1, acc != 0);
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(GEN_BLOCK) void ln_fwd_gen(
-    const void* x, int64_t ldx, const float* gamma, const float* beta, void* y, int64_t ldy,
-    float* mean, int64_t ldm, float* rstd, int64_t ldr, int64_t R, int64_t C, float eps, float invC) {
-  __shared__ float lds[4 * GEN_BLOCK / WAVE];
-  int ph = 0;
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-    float s = 0.f;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) s += gl1<T>(x, r, ldx, c);
-    const float mu = group_sum<GEN_BLOCK / WAVE>(s, lds, ph) * invC;
-    float q = 0.f;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) { const float t = gl1<T>(x, r, ldx, c) - mu; q += t * t; }
-    const float rs = rsqrtf(group_sum<GEN_BLOCK / WAVE>(q, lds, ph) * invC + eps);
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
-      gs1<T>(y, r, ldy, c, (gl1<T>(x, r, ldx, c) - mu) * rs * gamma[c] + beta[c], false);
-    if (threadIdx.x == 0) { mean[r * ldm] = mu; rstd[r * ldr] = rs; }
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(GEN_BLOCK) void ln_bwd_gen(
-    const void* d, int64_t ldd, const void* x, int64_t ldx, const float* gamma, const float* mean,
-    int64_t ldm, const float* rstd, int64_t ldr, void* dx, int64_t lddx, int acc, int64_t R,
-    int64_t C, float invC) {
-  __shared__ float lds[4 * GEN_BLOCK / WAVE];
-  int ph = 0;
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-    const float mu = mean[r * ldm], rs = rstd[r * ldr];
-    float s1 = 0.f, s2 = 0.f;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
-      const float gv = gl1<T>(d, r, ldd, c) * gamma[c];
-      s1 += gv;
-      s2 += gv * (gl1<T>(x, r, ldx, c) - mu) * rs;
-    }
-    group_sum2<GEN_BLOCK / WAVE>(s1, s2, lds, ph);
-    const float a = s1 * invC, b = s2 * invC;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
-      const float xh = (gl1<T>(x, r, ldx, c) - mu) * rs;
-      gs1<T>(dx, r, lddx, c, rs * (gl1<T>(d, r, ldd, c) * gamma[c] - a - xh * b), acc != 0);
-    }
-  }
-}
-
-// Parameter-gradient partials of the generic path: block b sums its row
-// chunk for each column (threads stride over columns).  kind 0: d*x*ir
-// (rms_norm dgamma); kind 1: d*xhat and d (layer_norm dgamma, dbeta).
+// Parameter-gradient partials of rows whose starts are not 16-byte aligned:
+// block (bx, by) sums rows [by*rpb, (by+1)*rpb) of columns bx*256 + t, one
+// column per thread, eight rows' loads in flight, added in row order; one
+// partial row (NP vectors of C) per block row by.  kind 0: d*x*ir (rms_norm
+// dgamma); kind 1: d*xhat and d (layer_norm dgamma, dbeta).
 template <typename T, int KIND>
 __global__ __launch_bounds__(GEN_BLOCK) void norm_partials_gen(
     const void* d, int64_t ldd, const void* x, int64_t ldx, const float* st0, int64_t ld0,
     const float* st1, int64_t ld1, float* part, int64_t R, int64_t C, int64_t rpb) {
-  const int64_t start = (int64_t)blockIdx.x * rpb, end = min(R, start + rpb);
-  constexpr int NP = KIND == 0 ? 1 : 2;
-  float* out = part + (int64_t)blockIdx.x * NP * C;
-  for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
-    float a = 0.f, b = 0.f;
-    for (int64_t r = start; r < end; ++r) {
-      const float dv = gl1<T>(d, r, ldd, c), xv = gl1<T>(x, r, ldx, c);
-      if (KIND == 0) a += dv * xv * st0[r * ld0];
-      else { a += dv * (xv - st0[r * ld0]) * st1[r * ld1]; b += dv; }
-    }
-    out[c] = a;
-    if (KIND == 1) out[C + c] = b;
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(GEN_BLOCK) void sm_fwd_gen(
-    const void* x, int64_t ldx, void* y, int64_t ldy, int64_t R, int64_t C, float alpha,
-    int causal, int seq_len) {
-  __shared__ float lds[4 * GEN_BLOCK / WAVE];
-  int ph = 0;
-  const float NEG_INF = -__builtin_inff();
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-    const int64_t lim = causal ? min(C, (int64_t)(r % seq_len) + 1) : C;
-    float m = NEG_INF;
-    for (int64_t c = threadIdx.x; c < lim; c += GEN_BLOCK) m = fmaxf(m, alpha * gl1<T>(x, r, ldx, c));
-    m = group_max<GEN_BLOCK / WAVE>(m, lds, ph);
-    float s = 0.f;
-    for (int64_t c = threadIdx.x; c < lim; c += GEN_BLOCK) s += fast_exp(alpha * gl1<T>(x, r, ldx, c) - m);
-    const float inv = 1.0f / group_sum<GEN_BLOCK / WAVE>(s, lds, ph);
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK)
-      gs1<T>(y, r, ldy, c, c < lim ? fast_exp(alpha * gl1<T>(x, r, ldx, c) - m) * inv : 0.f, false);
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(GEN_BLOCK) void sm_bwd_gen(
-    const void* d, int64_t ldd, const void* y, int64_t ldy, void* dx, int64_t lddx, int acc,
-    int64_t R, int64_t C, float alpha) {
-  __shared__ float lds[4 * GEN_BLOCK / WAVE];
-  int ph = 0;
-  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-    float dot = 0.f;
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) dot += gl1<T>(d, r, ldd, c) * gl1<T>(y, r, ldy, c);
-    dot = group_sum<GEN_BLOCK / WAVE>(dot, lds, ph);
-    for (int64_t c = threadIdx.x; c < C; c += GEN_BLOCK) {
-      const float yv = gl1<T>(y, r, ldy, c);
-      gs1<T>(dx, r, lddx, c, alpha * yv * (gl1<T>(d, r, ldd, c) - dot), acc != 0);
+  constexpr int NP = KIND == 0 ? 1 : 2, U = 8;
+  const int64_t start = (int64_t)blockIdx.y * rpb, end = min(R, start + rpb);
+  const int64_t c = (int64_t)blockIdx.x * GEN_BLOCK + threadIdx.x;
+  if (c >= C) return;
+  float a = 0.f, b = 0.f;
+  int64_t r = start;
+  for (; r + U <= end; r += U) {
+    float dv[U], xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { dv[u] = gl1<T>(d, r + u, ldd, c); xv[u] = gl1<T>(x, r + u, ldx, c); }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (KIND == 0) a += dv[u] * xv[u] * st0[(r + u) * ld0];
+      else { a += dv[u] * (xv[u] - st0[(r + u) * ld0]) * st1[(r + u) * ld1]; b += dv[u]; }
     }
   }
+  for (; r < end; ++r) {
+    const float dv = gl1<T>(d, r, ldd, c), xv = gl1<T>(x, r, ldx, c);
+    if (KIND == 0) a += dv * xv * st0[r * ld0];
+    else { a += dv * (xv - st0[r * ld0]) * st1[r * ld1]; b += dv; }
+  }
+  float* out = part + (int64_t)blockIdx.y * NP * C;
+  out[c] = a;
+  if (KIND == 1) out[C + c] = b;
 }
 
 // ============================================================ column sums
@@ -938,8 +837,10 @@ RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
                        : std::min<int64_t>(cdiv(R, p.groups), kind == RK_SM_BWD ? 2 * LONG_ROW_GRID : LONG_ROW_GRID);
     p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(g, INT32_MAX));
   } else {
-    p.rw = 4; p.nv = 0; p.block = GEN_BLOCK; p.groups = 1;
-    p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(R, is_bwd(kind) ? BWD_GRID_MAX : LONG_ROW_GRID));
+    // streaming kernels: one row per 1024-thread block step; a backward's
+    // blocks each write one partial row of the parameter gradients
+    p.rw = 16; p.nv = 0; p.block = 1024; p.groups = 1;
+    p.grid = is_bwd(kind) ? stream_bwd_grid(R) : (int)std::max<int64_t>(1, std::min<int64_t>(R, LONG_ROW_GRID));
   }
   return p;
 }
@@ -1016,10 +917,9 @@ static hipError_t rms_fwd_t(const xt_tensor& x, const float* gamma, const xt_ten
     XT_ROW_SWITCH_FWD(
         auto kf = rms_fwd_fast<T, RW, NV, BLOCK>;
         kf<<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC));
-  } else {
-    rms_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, R, C, eps, invC);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return launch_rms_fwd_stream(x, gamma, y, ir, eps, p.grid, s);
 }
 
 hipError_t launch_rms_fwd(const xt_tensor& x, const float* gamma, const xt_tensor& y,
@@ -1055,11 +955,15 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
       kf<<<p.grid, BWD_BLOCK, shm, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld,
                                         dx ? dx->data : nullptr, dx ? dx->ld : 0, acc_dx, part, R, C, invC));
   } else {
-    const int64_t rpb = cdiv(R, p.grid);
-    if (dx)
-      rms_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)ir.data, ir.ld, dx->data, dx->ld, acc_dx, R, C, invC);
-    if (dgamma)
-      norm_partials_gen<T, 0><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)ir.data, ir.ld, nullptr, 0, part, R, C, rpb);
+    // streaming rows: dgamma partials in registers when every row starts
+    // 16-byte aligned, else by a column pass
+    const bool own = dgamma && stream_owns_partials(d.dtype, C, d, x, dx);
+    hipError_t e = hipSuccess;
+    if (dx || own) e = launch_rms_bwd_stream(d, x, gamma, ir, dx, acc_dx, own ? part : nullptr, p.grid, s);
+    if (e != hipSuccess) return e;
+    if (dgamma && !own)
+      norm_partials_gen<T, 0><<<dim3((unsigned)cdiv(C, GEN_BLOCK), p.grid), GEN_BLOCK, 0, s>>>(
+          d.data, d.ld, x.data, x.ld, (const float*)ir.data, ir.ld, nullptr, 0, part, R, C, cdiv(R, p.grid));
   }
   if (dgamma) fold_columns<<<(unsigned)cdiv(C, FOLD_W), FOLD_T, 0, s>>>(part, p.grid, C, C, dgamma, acc_dg, C, nullptr, 0);
   return hipGetLastError();
@@ -1087,10 +991,9 @@ static hipError_t ln_fwd_t(const xt_tensor& x, const float* gamma, const float* 
     XT_ROW_SWITCH_FWD(
         auto kf = ln_fwd_fast<T, RW, NV, BLOCK>;
         kf<<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC));
-  } else {
-    ln_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, R, C, eps, invC);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return launch_ln_fwd_stream(x, gamma, beta, y, mean, rstd, eps, p.grid, s);
 }
 
 hipError_t launch_ln_fwd(const xt_tensor& x, const float* gamma, const float* beta,
@@ -1123,13 +1026,14 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
                                         (const float*)rstd.data, rstd.ld, dx ? dx->data : nullptr, dx ? dx->ld : 0,
                                         acc_dx, part, R, C, invC));
   } else {
-    const int64_t rpb = cdiv(R, p.grid);
-    if (dx)
-      ln_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, gamma, (const float*)mean.data, mean.ld,
-                                                 (const float*)rstd.data, rstd.ld, dx->data, dx->ld, acc_dx, R, C, invC);
-    if (want_p)
-      norm_partials_gen<T, 1><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, x.data, x.ld, (const float*)mean.data, mean.ld,
-                                                           (const float*)rstd.data, rstd.ld, part, R, C, rpb);
+    const bool own = want_p && stream_owns_partials(d.dtype, C, d, x, dx);
+    hipError_t e = hipSuccess;
+    if (dx || own) e = launch_ln_bwd_stream(d, x, gamma, mean, rstd, dx, acc_dx, own ? part : nullptr, p.grid, s);
+    if (e != hipSuccess) return e;
+    if (want_p && !own)
+      norm_partials_gen<T, 1><<<dim3((unsigned)cdiv(C, GEN_BLOCK), p.grid), GEN_BLOCK, 0, s>>>(
+          d.data, d.ld, x.data, x.ld, (const float*)mean.data, mean.ld, (const float*)rstd.data, rstd.ld, part, R, C,
+          cdiv(R, p.grid));
   }
   if (dgamma && dbeta)        // partial rows are [dgamma | dbeta]: one fold over 2C columns
     fold_columns<<<(unsigned)cdiv(2 * C, FOLD_W), FOLD_T, 0, s>>>(part, p.grid, 2 * C, 2 * C, dgamma, acc_dg, C, dbeta, acc_db);
@@ -1164,10 +1068,9 @@ static hipError_t sm_fwd_t(const xt_tensor& x, const xt_tensor& y, float alpha, 
     XT_ROW_SWITCH_FWD(
         auto kf = causal ? sm_fwd_fast<T, RW, NV, BLOCK, true> : sm_fwd_fast<T, RW, NV, BLOCK, false>;
         kf<<<p.grid, BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, seq_len));
-  } else {
-    sm_fwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(x.data, x.ld, y.data, y.ld, R, C, alpha, causal, seq_len);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return launch_sm_fwd_stream(x, y, alpha, causal, seq_len, p.grid, s);
 }
 
 hipError_t launch_softmax_fwd(const xt_tensor& x, const xt_tensor& y, float alpha,
@@ -1185,10 +1088,9 @@ static hipError_t sm_bwd_t(const xt_tensor& d, const xt_tensor& y, const xt_tens
   if (p.fast) {
     XT_ROW_SWITCH_SMB(
         sm_bwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha));
-  } else {
-    sm_bwd_gen<T><<<p.grid, GEN_BLOCK, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return launch_sm_bwd_stream(d, y, dx, acc, alpha, p.grid, s);
 }
 
 hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx,

@@ -547,6 +547,75 @@ def sweep(steps, warmup):
     return res
 
 
+LONG_ROWS = (("softmax", "f32", 32768), ("softmax", "f32", 50257), ("softmax", "bf16", 50257),
+             ("layer_norm", "f32", 16384), ("rms_norm", "f32", 16384), ("layer_norm", "bf16", 50257))
+
+
+def long_rows(steps, warmup):
+    """Rows the register-resident kernels do not take (the streaming path):
+    each op fwd and bwd at 1 GiB per activation tensor, R = 2^30 / (s*d)
+    contiguous rows (a 50257-wide row starts 16-byte aligned only every
+    16 / gcd(16, s*50257) rows); timed like the sweep."""
+    import torch
+    import autograd_row_wise_amd as xt
+    from synth import device_normal
+
+    V, P = xt.view, xt.params
+    big = 1 << 30
+    res = []
+    for name, dt, d in LONG_ROWS:
+        s_ = 4 if dt == "f32" else 2
+        R = big // (s_ * d)
+        N = R * d
+        x = device_normal((R, d), 8, "x", dtype=dt)
+        dd = device_normal((R, d), 8, "dout", dtype=dt)
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        a, b = (torch.empty((R, 1), dtype=torch.float32, device="cuda") for _ in range(2))
+        g = torch.ones((1, d), dtype=torch.float32, device="cuda")
+        bt = torch.zeros((1, d), dtype=torch.float32, device="cuda")
+        gg, gb = torch.empty_like(g), torch.empty_like(g)
+        pe = P(eps=1e-5)
+        if name == "softmax":
+            f = lambda: xt.xt_op_fwd(xt.OP.SOFTMAX, P(), [V(x)], [V(y)])  # noqa: E731
+            bw = lambda: xt.xt_op_bwd(xt.OP.SOFTMAX, P(), V(dd), [V(x)], [V(y)], [V(dx)])  # noqa: E731
+            bf, bb = 2 * s_ * N, 3 * s_ * N
+        elif name == "rms_norm":
+            n = xt.xt_workspace_bytes(xt.OP.RMS_NORM, 1, pe, [V(x), V(g)])
+            w = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+            f = lambda: xt.xt_op_fwd(xt.OP.RMS_NORM, pe, [V(x), V(g)], [V(y), V(a)])  # noqa: E731
+            bw = lambda: xt.xt_op_bwd(xt.OP.RMS_NORM, pe, V(dd), [V(x), V(g)], [V(a)], [V(dx), V(gg)], 0,  # noqa: E731
+                                      w.data_ptr(), n)
+            bf, bb = 2 * s_ * N + 4 * R, 3 * s_ * N + 4 * R
+        else:
+            n = xt.xt_workspace_bytes(xt.OP.LAYER_NORM, 1, pe, [V(x), V(g), V(bt)])
+            w = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+            f = lambda: xt.xt_op_fwd(xt.OP.LAYER_NORM, pe, [V(x), V(g), V(bt)], [V(y), V(a), V(b)])  # noqa: E731
+            bw = lambda: xt.xt_op_bwd(xt.OP.LAYER_NORM, pe, V(dd), [V(x), V(g), V(bt)], [V(a), V(b)],  # noqa: E731
+                                      [V(dx), V(gg), V(gb)], 0, w.data_ptr(), n)
+            bf, bb = 2 * s_ * N + 8 * R, 3 * s_ * N + 8 * R
+        stream = torch.cuda.current_stream()
+        ms = []
+        for fn in (f, bw):
+            for _ in range(warmup):
+                fn()
+            ev = []
+            for _ in range(steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            ms.append(med([e0.elapsed_time(e1) for e0, e1 in ev]))
+        gbps = (bf + bb) / ((ms[0] + ms[1]) * 1e-3) / 1e9
+        res.append({"op": name, "dtype": dt, "d": d, "rows": R, "fwd_ms": round(ms[0], 4), "bwd_ms": round(ms[1], 4),
+                    "fwd_GBps": round(bf / (ms[0] * 1e-3) / 1e9, 1), "bwd_GBps": round(bb / (ms[1] * 1e-3) / 1e9, 1),
+                    "fwdbwd_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        del x, dd, y, dx
+        torch.cuda.empty_cache()
+    return res
+
+
 # --------------------------------------------------------------------------
 def c1_latency(steps, warmup, reps=50):
     """Every op of the 8 x 64 f32 workload, forward and backward, as the
@@ -951,6 +1020,9 @@ def main():
     if not args.no_sweep and not args.only:
         out["sweep"] = {"what": "fwd and bwd of each row-wise op at 1 GiB per activation tensor, R = 2^30/(s*d)",
                         "entries": sweep(args.steps, args.warmup)}
+    if not args.no_sweep and (not args.only or "long" in args.only):
+        out["long_rows"] = {"what": "rows the register-resident kernels do not take (streaming kernels), "
+                                    "1 GiB per activation tensor", "entries": long_rows(args.steps, args.warmup)}
     if not args.only:
         out["c1_latency"] = c1_latency(args.steps, args.warmup)
     if not args.no_cpu_baseline:

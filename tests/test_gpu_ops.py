@@ -25,8 +25,11 @@ DTYPES = ["f32", "bf16"]
 # (rows, cols, ld): ld None = contiguous
 LAYOUTS = [(8, 64, None), (37, 1000, None), (37, 1000, 1008), (37, 1001, None), (37, 1001, 1008),
            (5, 3001, 3008), (3, 20000, None), (130, 256, None), (9, 32768, None),
-           # wider than any register-resident row: the general kernels, ragged and strided
-           (3, 40000, None), (2, 65601, 65608)]
+           # wider than any register-resident row: the streaming kernels, ragged and strided
+           (3, 40000, None), (2, 65601, 65608),
+           # aligned rows past the register kernels' reach whose parameter partials the
+           # streaming backward keeps per thread (f32 up to 4 packs, bf16 up to 2 per thread)
+           (33, 16384, None), (20, 12288, None), (17, 16000, 16004)]
 
 
 def put(a_f32: np.ndarray, dtype: str, ld=None):
@@ -451,3 +454,53 @@ def test_matmul_split_k(dtype, M, N, K, ta, tb, batch, ws_frac):
     else:
         close(host(dA).reshape(dA_ref.shape), k * dA_ref, "bf16", what="dA")
     close_f32(host(dB).reshape(dB_ref.shape), k * dB_ref, k * sum_scale(sB, M), what="dB")
+
+
+# ----------------------------------------------- accumulating row backwards
+ACC_LAYOUTS = [(130, 256, None), (37, 1001, None), (33, 16384, None), (3, 40000, None), (5, 3001, 3008)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("R,C,ld", ACC_LAYOUTS)
+@pytest.mark.parametrize("op", ["rms_norm", "layer_norm", "softmax"])
+def test_row_backward_accumulate(op, dtype, R, C, ld):
+    """A second backward with every accumulate bit set adds onto the first:
+    f32 gradients become exactly twice the first pass (one rounding of g + g),
+    bf16 dx twice the oracle within the bf16 bar; register-resident,
+    streaming, owned-partial and column-pass layouts."""
+    x, xv = put(normal((R, C), 6, "x"), dtype, ld)
+    d, dv = put(normal((R, C), 6, "dout"), dtype, ld)
+    g = dev(normal((C,), 6, "gamma", 1.0, 0.1))
+    b = dev(normal((C,), 6, "beta", 0.0, 0.1))
+    if op == "rms_norm":
+        opc, prm, ins = xt.OP.RMS_NORM, xt.params(eps=1e-5), [x, g]
+        saved = [empty((R, 1), "f32")]
+        nparam = 1
+    elif op == "layer_norm":
+        opc, prm, ins = xt.OP.LAYER_NORM, xt.params(eps=1e-5), [x, g, b]
+        saved = [empty((R, 1), "f32"), empty((R, 1), "f32")]
+        nparam = 2
+    else:
+        opc, prm, ins = xt.OP.SOFTMAX, xt.params(), [x]
+        saved = []
+        nparam = 0
+    y = out_like(R, C, dtype, ld)
+    fwd(opc, prm, ins, [y] + saved)
+    if op == "softmax":
+        saved = [y]
+    grads = [out_like(R, C, dtype, ld)] + [empty((C,), "f32") for _ in range(nparam)]
+    bwd(opc, prm, d, ins, saved, grads)
+    first = [host(t) for t in grads]
+    bwd(opc, prm, d, ins, saved, grads, acc=(1 << len(grads)) - 1)
+    for k, (t, f0) in enumerate(zip(grads, first)):
+        if dtype == "f32" or k > 0:
+            assert np.array_equal(host(t), 2.0 * f0), (op, k)
+    if dtype == "bf16":
+        if op == "rms_norm":
+            ref = ops.rms_norm_bwd(dv, xv, host(g), ops.rms_norm(xv, host(g), 1e-5)[1])[0]
+        elif op == "layer_norm":
+            _, mu, rs = ops.layer_norm(xv, host(g), host(b), 1e-5)
+            ref = ops.layer_norm_bwd(dv, xv, host(g), mu, rs)[0]
+        else:
+            ref = ops.softmax_bwd(dv, round_bf16(ops.softmax(xv)))
+        close(host(grads[0]), 2.0 * ref, dtype, what="accumulated dx")

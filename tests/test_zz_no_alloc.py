@@ -118,8 +118,9 @@ def test_attention_bf16():
 
 
 def test_oversized_workspace_is_rejected():
-    # 512 rows of 16384 f32: 512 partial rows of dgamma | dbeta = 64 MiB > 32 MiB
-    R, C = 512, 16384
+    # 512 rows of 32768 f32 on the streaming backward: 256 partial rows of
+    # dgamma | dbeta = 64 MiB > 32 MiB
+    R, C = 512, 32768
     x, d, dx = (torch.zeros((R, C), device="cuda") for _ in range(3))
     g, b, dg, db = (torch.zeros((C,), device="cuda") for _ in range(4))
     mu, rs = torch.zeros((R, 1), device="cuda"), torch.ones((R, 1), device="cuda")
