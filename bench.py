@@ -351,12 +351,37 @@ def build_entries(only):
                                 checkpoint=ckpt, fused_attention=fused)
                 t.backward(loss)
                 holder[key] = t
+            def graph_block(key, fused=False):
+                """The block recorded and run backward on a tape inside a HIP
+                graph capture (after one eager warm-up on a side stream); the
+                returned call replays it.  The tape stays alive with the graph."""
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    run_block(False, key + "_warm", fused)
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    t = xt.Tape()
+                    w = xb.leaves(t, Wt)
+                    loss = xb.block(t, w, t.leaf(V(bx2)), t.leaf(V(bt2), requires_grad=False), shp, xt.DT.F32,
+                                    fused_attention=fused)
+                    t.backward(loss)
+                torch.cuda.synchronize()
+                holder[key] = (t, g)
+                return g.replay
+
             # GEMM flops of one fwd+bwd (for the record; the block is launch/cache bound)
             T, D = shp.B * shp.S, shp.D
             fl = 2 * T * D * D * 4 + 2 * T * D * shp.hidden * 3 + 2 * T * D * shp.vocab \
                 + 2 * 2 * shp.B * shp.H * shp.S * shp.S * shp.Dh
             E.append(Entry("c2.block.fwdbwd", "tiny block 4x256x256 f32", "f32", "block", run_block, 0, 3 * fl,
                            shp.B * shp.S))
+            # the same fwd+bwd replayed from a captured graph: device time
+            # without the tape's host work and Python launch path
+            E.append(Entry("c2.block.fwdbwd_graph", "tiny block 4x256x256 f32", "f32", "blockgraph",
+                           graph_block("tape_graph"), 0, 3 * fl, shp.B * shp.S))
             # the same block as one recompute segment: the layer's forward runs
             # twice (the GEMM flops of the record count it once)
             E.append(Entry("f4.block.fwdbwd_recompute", "tiny block 4x256x256 f32", "f32", "block",
@@ -364,6 +389,8 @@ def build_entries(only):
             # the same block with the fused attention op
             E.append(Entry("f1.block.fwdbwd_fused_attention", "tiny block 4x256x256 f32", "f32", "block",
                            lambda: run_block(False, "tape_fused", True), 0, 3 * fl, shp.B * shp.S))
+            E.append(Entry("f1.block.fwdbwd_fused_attention_graph", "tiny block 4x256x256 f32", "f32", "blockgraph",
+                           graph_block("tape_fused_graph", True), 0, 3 * fl, shp.B * shp.S))
     def f3():
         nonlocal keep
         if not want("f3"):
@@ -886,8 +913,10 @@ def time_step_graph(entries, stream, steps, warmup):
     block runs eagerly after it): wall-clock ms per step, synchronised on
     both sides of the K timed steps."""
     import torch
-    cap = [e for e in entries if e.kind != "block"]
-    eager = [e for e in entries if e.kind == "block"]
+    # tape-driven blocks run eagerly after the graph (a block replayed from
+    # its own graph cannot be launched inside another capture)
+    cap = [e for e in entries if e.kind not in ("block", "blockgraph")]
+    eager = [e for e in entries if e.kind in ("block", "blockgraph")]
     g = capture([e.fn for e in cap]) if cap else None
     for _ in range(warmup):
         if g is not None:
@@ -928,7 +957,10 @@ def op_record(e):
         rec.update(flops=e.flops, TFLOPs=round(tf, 2), frac=round(tf / MFMA_PEAK_TFLOPS[e.dtype], 4),
                    bytes=e.bytes)
     else:
-        rec.update(flops=e.flops, TFLOPs=round(e.flops / (ms * 1e-3) / 1e12, 3), note="tape-driven, cache-resident")
+        rec.update(flops=e.flops, TFLOPs=round(e.flops / (ms * 1e-3) / 1e12, 3),
+                   note="tape-driven, cache-resident" + (", replayed from a captured HIP graph (device time)"
+                                                         if e.kind == "blockgraph" else ", eager (host tape work and "
+                                                         "Python launch path included)"))
     return rec
 
 
@@ -959,8 +991,8 @@ def main():
         wall_ms = time_step_graph(main, stream, args.steps, args.warmup)
         hbm_wall_ms = time_step_graph([e for e in main if e.kind == "hbm"], stream, args.steps, args.warmup)
         for group in (main, extra):
-            time_graphs([e for e in group if e.kind != "block"], stream, args.steps, args.warmup)
-            time_steps([e for e in group if e.kind == "block"], stream, args.steps, args.warmup)
+            time_graphs([e for e in group if e.kind not in ("block", "blockgraph")], stream, args.steps, args.warmup)
+            time_steps([e for e in group if e.kind in ("block", "blockgraph")], stream, args.steps, args.warmup)
 
     ops_out = [op_record(e) for e in main]
     extra_out = [op_record(e) for e in extra]

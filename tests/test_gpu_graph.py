@@ -169,3 +169,62 @@ def test_graph_replays_reproduce_eager_results():
                                ref.view(torch.uint8) if ref.dtype != torch.uint8 else ref), (rep, i)
         del scratch
     del g, keep
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_tape_block_replays_from_a_graph(fused):
+    """The tiny transformer block (batch 4, seq 256, d 256, 4 x 64 heads, f32)
+    recorded and run backward on a tape inside a graph capture: every
+    replay (three, with eager work and synchronisations between them and the
+    gradients overwritten with NaN before each) reproduces the eager tape's
+    loss and weight gradients bit for bit."""
+    from autograd_row_wise_amd import block as xb
+    shp = xb.BlockShape(B=4, S=256, H=4, Dh=64, hidden=688, vocab=4096)
+    W = {}
+    for k, s in xb.WEIGHT_SHAPES(shp).items():
+        W[k] = torch.ones(s, device="cuda") if k.startswith("g") else synth.device_normal(s, 31, k, 0.0, 0.02)
+    x = synth.device_normal((shp.B * shp.S, shp.D), 31, "x")
+    tg = synth.device_uniform_int((shp.B * shp.S, 1), 0, shp.vocab, 31, "targets")
+
+    def record():
+        t = xt.Tape()
+        w = xb.leaves(t, W)
+        loss = xb.block(t, w, t.leaf(xt.view(x)), t.leaf(xt.view(tg), requires_grad=False), shp, xt.DT.F32,
+                        fused_attention=fused)
+        t.backward(loss)
+        return t, w, loss
+
+    te, we, le = record()
+    torch.cuda.synchronize()
+    ref = {k: xt.to_torch(te.grad(v)).clone() for k, v in we.items()}
+    ref_loss = xt.to_torch(te.value(le)).clone()
+    te.close()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on a side stream, as torch asks before a capture
+        tw, _, _ = record()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    tw.close()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tc, wc, lc = record()
+    torch.cuda.synchronize()
+    grads = {k: xt.to_torch(tc.grad(v)) for k, v in wc.items()}       # copies: re-read after each replay
+    for rep in range(3):
+        for k, v in wc.items():
+            view = tc.grad(v)                                             # overwrite every gradient with NaN
+            nb = ((view.rows - 1) * view.ld + view.cols) * 4
+            xt._raw_cuda_tensor(view.data, nb).view(torch.float32).fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()                  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in wc.items():
+            got = xt.to_torch(tc.grad(v))
+            assert torch.equal(got, ref[k]), (fused, rep, k)
+        assert torch.equal(xt.to_torch(tc.value(lc)), ref_loss)
+        del junk
+    del grads
+    tc.close()
+    del g
