@@ -438,10 +438,14 @@ __global__ __launch_bounds__(NT) void gemm_big_k(
 // as [row][k]; one stored transposed lands as [k][row] and is turned into
 // MFMA fragments by the transposing LDS read (ds_read_b64_tr_b16), so all
 // four layouts (d B^T, A^T d, ...) share the kernel and no transpose copy
-// exists.  K tiles are 32 deep in a ring of four 32 KB stages.  Step kt
-// multiplies tile kt while tile kt+3 is requested, and reads the first
-// fragments of tile kt+1 before its closing barrier, so MFMAs restart right
-// after it; tile kt+2 must have landed by then.
+// exists.  K tiles are 64 deep in two 64 KB stages (schedule below).
+//
+// Measured alternatives that ran slower on this product (8192 x 4096 x
+// 4096): 32-deep tiles in four stages (each k-contiguous 128-byte line then
+// reaches L2 as two 64-byte requests); two 4-wave groups alternating load
+// and MFMA phases with a barrier per phase; 4 waves of 128 x 128 (one wave
+// per SIMD, with 32- or 64-deep tiles), whose LDS reads per MFMA are fewer
+// but whose stalls no second wave covers.
 //
 // Tile order: blocks are dealt to the 8 XCDs round-robin; XCD x takes the
 // contiguous tile range x * tiles / 8 .., walked in groups of four tile rows
@@ -460,77 +464,31 @@ __device__ __forceinline__ void tile_of(int tt, int tiles_m, int tiles_n, int64_
   m0 = (int64_t)(first + r % gm) * bm; n0 = (int64_t)(r / gm) * bn;
 }
 
-namespace b8d {
-constexpr int BK = 32, NS = 4;
-constexpr int TILE = 256 * BK;                       // elements of one operand tile
-}  // namespace b8d
-
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-__device__ __forceinline__ int swz4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
-
-// One operand tile (256 rows x 32 k) into LDS: two 1 KB transfers per wave.
-// k-contiguous operands land as [row][k] (64-byte rows, chunk c of row r at
-// c ^ ((r >> 2) & 3)); the others as [k][row] (512-byte k-rows, chunk c of
-// k-row kr at c ^ 4 (kr & 3)).
-template <bool KCONTIG>
-__device__ __forceinline__ void b8d_dma_tile(const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
-                                             bf16_t* __restrict__ lds_tile, int w, int l) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int blk = w * 2 + j;                       // LDS slots 64 blk .. 64 blk + 63
-    const bf16_t* src;
-    if constexpr (KCONTIG) {                         // rows 16 blk .. +15, 4 chunks each
-      const int row = blk * 16 + l / 4;
-      const int c = (l % 4) ^ ((row >> 2) & 3);
-      src = g + (row0 + row) * ld + k0 + c * 8;
-    } else {                                         // k-rows 2 blk, 2 blk + 1, 32 chunks each
-      const int kr = blk * 2 + l / 32;
-      const int c = (l % 32) ^ (4 * (kr & 3));
-      src = g + (k0 + kr) * ld + row0 + c * 8;
-    }
-    __builtin_amdgcn_global_load_lds(src, lds_tile + blk * 64 * 8, 16, 0, 0);
-  }
-}
-
 // MFMA operand of fragment rows f0 .. f0+31, k 16 s .. 16 s + 15 (lane l:
-// row f0 + l % 32, k 16 s + 8 (l / 32) .. +7).  From a [k][row] tile it takes
-// two transposing reads (ds_read_b64_tr_b16: within each group of 16 lanes,
-// lane j receives element j % 4 of the 8-byte rows that lanes 4 v + j / 4
+// row f0 + l % 32, k 16 s + 8 (l / 32) .. +7) from a [k][row] tile: two
+// transposing reads (ds_read_b64_tr_b16: within each group of 16 lanes, lane
+// j receives element j % 4 of the 8-byte rows that lanes 4 v + j / 4
 // address, v = 0..3).
-template <bool KCONTIG>
-__device__ __forceinline__ bf16x8_t b8d_frag(const bf16_t* __restrict__ tile, int f0, int s, int l) {
-  if constexpr (KCONTIG) {
-    const u32x4_t* L = reinterpret_cast<const u32x4_t*>(tile);
-    return __builtin_bit_cast(bf16x8_t, L[swz4(f0 + l % 32, 2 * s + l / 32)]);
-  } else {
-    const int g = l / 16, q = l % 16;                // source role of this lane within its group
-    const int row = f0 + 16 * (g & 1) + 4 * (q & 3); // 4 consecutive rows from here
-    const int c = row / 8, half = (row / 4) & 1;
-    s16x4_t v[2];
+__device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* __restrict__ tile, int f0, int s, int l) {
+  const int g = l / 16, q = l % 16;                  // source role of this lane within its group
+  const int row = f0 + 16 * (g & 1) + 4 * (q & 3);   // 4 consecutive rows from here
+  const int c = row / 8, half = (row / 4) & 1;
+  s16x4_t v[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kr = 16 * s + 8 * (g >> 1) + 4 * h + q / 4;
-      const bf16_t* p = tile + kr * 256 + ((c ^ (4 * (kr & 3))) * 8) + half * 4;
-      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-    }
-    const short __attribute__((ext_vector_type(8))) w8 = {v[0][0], v[0][1], v[0][2], v[0][3],
-                                                          v[1][0], v[1][1], v[1][2], v[1][3]};
-    return __builtin_bit_cast(bf16x8_t, w8);
+  for (int h = 0; h < 2; ++h) {
+    const int kr = 16 * s + 8 * (g >> 1) + 4 * h + q / 4;
+    const bf16_t* p = tile + kr * 256 + ((c ^ (4 * (kr & 3))) * 8) + half * 4;
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
   }
+  const short __attribute__((ext_vector_type(8))) w8 = {v[0][0], v[0][1], v[0][2], v[0][3],
+                                                        v[1][0], v[1][1], v[1][2], v[1][3]};
+  return __builtin_bit_cast(bf16x8_t, w8);
 }
 
 struct b8d_frags { bf16x8_t a[4], b[2]; };
-
-// Fragments of k substep s of the stage at `st` ([A tile, B tile]).
-template <bool KA, bool KB>
-__device__ __forceinline__ void b8d_read(const bf16_t* __restrict__ st, int s, b8d_frags& f, int wm, int wn, int l) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = b8d_frag<KA>(st, wm + i * 32, s, l);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) f.b[j] = b8d_frag<KB>(st + b8d::TILE, wn + j * 32, s, l);
-}
 
 __device__ __forceinline__ void b8d_mfma(const b8d_frags& f, f32x16_t (&acc)[4][2]) {
 #pragma unroll
@@ -573,45 +531,108 @@ __device__ __forceinline__ void b8d_sched_half() {
   }
 }
 
-// One K tile kt: multiply substep 0 (fragments already in f0) while substep
-// 1 of tile kt is read from `cur`; request tile kt+NS-1 into `dst`; multiply
-// substep 1 while substep 0 of tile kt+1 is read from `ahead`.  Three
-// restrict pointers: the compiler sees that neither read depends on the
-// transfer, and inserts no wait for it.
-template <bool KA, bool KB>
-__device__ __forceinline__ void b8d_step(const bf16_t* __restrict__ cur, const bf16_t* __restrict__ ahead,
-                                         bf16_t* __restrict__ dst, const bf16_t* A, int64_t lda, int64_t m0,
-                                         const bf16_t* B, int64_t ldb, int64_t n0, int64_t k0, b8d_frags& f0,
-                                         b8d_frags& f1, f32x16_t (&acc)[4][2], int w, int l, int wm, int wn) {
-  b8d_frags f2;
-  b8d_read<KA, KB>(cur, 1, f1, wm, wn, l);
-  b8d_mfma(f0, acc);
-  b8d_dma_tile<KA>(A, lda, m0, k0, dst, w, l);
-  b8d_dma_tile<KB>(B, ldb, n0, k0, dst + b8d::TILE, w, l);
-  b8d_read<KA, KB>(ahead, 0, f2, wm, wn, l);
-  b8d_mfma(f1, acc);
-  f0 = f2;
-  constexpr int NR = (KA ? 4 : 8) + (KB ? 2 : 4);
-  b8d_sched_half<NR>();
-  __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
-  b8d_sched_half<NR>();
+// K tiles are 64 deep in two 64 KB stages.  A k-contiguous operand row is
+// then 128 bytes per tile: each transfer reads whole cache lines (with
+// 32-deep tiles every line is fetched as two 64-byte halves, one tile apart,
+// which doubles the requests to L2), and there is one barrier per 64 k.
+//
+// Step kt multiplies the four 16-deep substeps of tile kt (stage kt % 2),
+// each while the next substep's fragments are read.  After the third
+// substep's MFMAs are issued, a wave waits until its transfers of tile kt+1
+// have landed and its reads of stage kt % 2 are complete, then the block
+// barrier; after it, every wave requests its share of tile kt+2 into stage
+// kt % 2 and reads substep 0 of tile kt+1 during substep 3's MFMAs.  A
+// transfer thus has one whole step (the 32 MFMAs of each wave) to land.
+namespace k64 {
+constexpr int BK = 64, TILE = 256 * BK;              // elements of one operand tile
+}  // namespace k64
+
+// k-contiguous tiles: [row][64 k] (128-byte rows, 16-byte chunk c of row r
+// at c ^ ((r >> 1) & 7): the 16 rows one ds_read_b128 phase touches fall in
+// 16 different bank groups).  Others: [k][row] (512-byte k-rows, chunk c of
+// k-row kr at c ^ 4 (kr & 3), read by tr_frag).  32 transfers of 1 KB per
+// tile, NB per wave: transfer b covers rows 8 b .. 8 b + 7 (or k-rows 2 b,
+// 2 b + 1).
+template <bool KCONTIG, int NB = 4>
+__device__ __forceinline__ void k64_dma_tile(const bf16_t* g, int64_t ld, int64_t row0, int64_t k0,
+                                             bf16_t* __restrict__ lds_tile, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int blk = w * NB + j;
+    const bf16_t* src;
+    if constexpr (KCONTIG) {
+      const int row = blk * 8 + l / 8;
+      const int c = (l % 8) ^ ((row >> 1) & 7);
+      src = g + (row0 + row) * ld + k0 + c * 8;
+    } else {
+      const int kr = blk * 2 + l / 32;
+      const int c = (l % 32) ^ (4 * (kr & 3));
+      src = g + (k0 + kr) * ld + row0 + c * 8;
+    }
+    __builtin_amdgcn_global_load_lds(src, lds_tile + blk * 64 * 8, 16, 0, 0);
+  }
 }
 
-// bf16 products of 256 x 256 tiles, 8 waves (2 per SIMD, 2 (m) x 4 (n), 128 x
-// 64 each as 4 x 2 MFMA 32x32x16 accumulators).  Operands reach LDS through
-// global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
-// destination + 16 lane, with no staging registers and no ds_write.  K tiles
-// are 32 deep in a ring of NS = 4 stages of 32 KB; tile kt+3 is requested in
-// the middle of step kt and must have landed by the end of step kt+1.
+template <bool KCONTIG>
+__device__ __forceinline__ bf16x8_t k64_frag(const bf16_t* __restrict__ tile, int f0, int s, int l) {
+  if constexpr (KCONTIG) {
+    const u32x4_t* L = reinterpret_cast<const u32x4_t*>(tile);
+    const int row = f0 + l % 32, c = 2 * s + l / 32;
+    return __builtin_bit_cast(bf16x8_t, L[row * 8 + (c ^ ((row >> 1) & 7))]);
+  } else {
+    return tr_frag(tile, f0, s, l);
+  }
+}
+
+template <bool KA, bool KB>
+__device__ __forceinline__ void k64_read(const bf16_t* __restrict__ st, int s, b8d_frags& f, int wm, int wn, int l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = k64_frag<KA>(st, wm + i * 32, s, l);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f.b[j] = k64_frag<KB>(st + k64::TILE, wn + j * 32, s, l);
+}
+
+// Substeps 0..2 of a step: MFMAs of `cur` substep s while substep s+1 is
+// read (restrict: the reads do not wait for the transfers in flight).
+template <bool KA, bool KB>
+__device__ __forceinline__ void k64_sub(const bf16_t* __restrict__ st, int s, const b8d_frags& fc, b8d_frags& fn,
+                                        f32x16_t (&acc)[4][2], int wm, int wn, int l) {
+  k64_read<KA, KB>(st, s + 1, fn, wm, wn, l);
+  b8d_mfma(fc, acc);
+  b8d_sched_half<(KA ? 4 : 8) + (KB ? 2 : 4)>();
+}
+
+// After the barrier: request tile kn into `dst` (the stage just released),
+// then substep 3's MFMAs while substep 0 of the next tile is read from `nxt`.
+template <bool KA, bool KB>
+__device__ __forceinline__ void k64_last(const bf16_t* __restrict__ nxt, bf16_t* __restrict__ dst,
+                                         const bf16_t* A, int64_t lda, int64_t m0, const bf16_t* B, int64_t ldb,
+                                         int64_t n0, int64_t k0, const b8d_frags& fc, b8d_frags& fn,
+                                         f32x16_t (&acc)[4][2], int w, int l, int wm, int wn, bool more) {
+  if (more) {
+    k64_dma_tile<KA>(A, lda, m0, k0, dst, w, l);
+    k64_dma_tile<KB>(B, ldb, n0, k0, dst + k64::TILE, w, l);
+  }
+  k64_read<KA, KB>(nxt, 0, fn, wm, wn, l);
+  b8d_mfma(fc, acc);
+  b8d_sched_half<(KA ? 4 : 8) + (KB ? 2 : 4)>();
+}
+
+__device__ __forceinline__ void k64_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename TC, bool KA, bool KB>
-__global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
+__global__ __launch_bounds__(b8::NT) void gemm_k64_k(
     const bf16_t* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
     const bf16_t* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
     TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
     int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
     int64_t kchunk, int64_t nbatch, int64_t scs) {
-  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = b8d::BK, TILE = b8d::TILE, NS = b8d::NS;
-  __shared__ __align__(16) bf16_t lds[NS][2 * TILE];       // [stage][A tile, B tile]
+  constexpr int BM8 = b8::BM, BN8 = b8::BN, BK = k64::BK, TILE = k64::TILE;
+  __shared__ __align__(16) bf16_t lds[2][2 * TILE];        // [stage][A tile, B tile]
 
   const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
   const int64_t kb0 = split * kchunk;
@@ -627,7 +648,7 @@ __global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
   int64_t m0, n0;
   tile_of(tt, (int)(M / BM8), tiles_n, m0, n0, BM8, BN8);
 
-  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), l = threadIdx.x % WAVE;
   const int wm = (w / 4) * 128, wn = (w % 4) * 64;
   f32x16_t acc[4][2];
 #pragma unroll
@@ -638,36 +659,31 @@ __global__ __launch_bounds__(b8::NT) void gemm_b8dma_k(
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   const int nk = (int)(K / BK);
-  // prologue: tiles 0 .. NS-2 requested and landed, substep 0 of tile 0 read
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nk) {
-      b8d_dma_tile<KA>(A, lda, m0, (int64_t)p * BK, lds[p], w, l);
-      b8d_dma_tile<KB>(B, ldb, n0, (int64_t)p * BK, lds[p] + TILE, w, l);
-    }
+  // prologue: tile 0 landed and substep 0 read; tile 1 requested
+  k64_dma_tile<KA>(A, lda, m0, 0, lds[0], w, l);
+  k64_dma_tile<KB>(B, ldb, n0, 0, lds[0] + TILE, w, l);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  b8d_frags f0, f1;
-  b8d_read<KA, KB>(lds[0], 0, f0, wm, wn, l);
-  for (int kt = 0; kt < nk; ++kt) {
-    // past the last tile the transfers re-read the last tile into a stage
-    // that is never read again, so every step issues the same four
-    const int kn = kt + NS - 1 < nk ? kt + NS - 1 : nk - 1;
-    b8d_step<KA, KB>(lds[kt % NS], lds[(kt + 1) % NS], lds[(kt + NS - 1) % NS], A, lda, m0, B, ldb, n0,
-                     (int64_t)kn * BK, f0, f1, acc, w, l, wm, wn);
-    // Tile kt+2 must have landed before the barrier publishes it (the next
-    // step reads its substep 0 ahead); only the four transfers of the one
-    // newer tile (kt+3) may stay in flight: vmcnt(4).  lgkmcnt(0): this
-    // wave's reads of stage kt are complete before anyone refills it.  A
-    // bare s_barrier: a __syncthreads() fence would wait for every transfer
-    // in flight.  The empty asm statements keep the compiler from moving
-    // LDS accesses across it.
-    __builtin_amdgcn_s_waitcnt(0x074);                       // vmcnt(4) expcnt(7) lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+  if (nk > 1) {
+    k64_dma_tile<KA>(A, lda, m0, BK, lds[1], w, l);
+    k64_dma_tile<KB>(B, ldb, n0, BK, lds[1] + TILE, w, l);
   }
-  __builtin_amdgcn_s_waitcnt(0);                             // the re-read transfers have landed
+  b8d_frags f0, f1;
+  k64_read<KA, KB>(lds[0], 0, f0, wm, wn, l);
+  for (int kt = 0; kt < nk; ++kt) {
+    const bf16_t* cur = lds[kt & 1];
+    k64_sub<KA, KB>(cur, 0, f0, f1, acc, wm, wn, l);
+    k64_sub<KA, KB>(cur, 1, f1, f0, acc, wm, wn, l);
+    k64_sub<KA, KB>(cur, 2, f0, f1, acc, wm, wn, l);
+    // this wave's transfers of tile kt+1 landed, its reads of stage kt done
+    __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) expcnt(7) lgkmcnt(0)
+    k64_barrier();
+    // the last step reads stage kt+1 % 2 too: never written past the end,
+    // its substep-0 fragments are simply not used
+    k64_last<KA, KB>(lds[(kt + 1) & 1], lds[kt & 1], A, lda, m0, B, ldb, n0, (int64_t)(kt + 2) * BK, f1, f0,
+                     acc, w, l, wm, wn, kt + 2 < nk);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -812,7 +828,7 @@ hipError_t gemm_run(bool bigk, bool small, const xt_tensor& A, bool ta, const xt
     const bf16_t* a8 = (const bf16_t*)A.data;
     const bf16_t* b8p = (const bf16_t*)B.data;
 #define XT_B8D(KA_, KB_)                                                                                   \
-    gemm_b8dma_k<TC, KA_, KB_><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0], B.sb[1], c, \
+    gemm_k64_k<TC, KA_, KB_><<<grid, b8::NT, 0, s>>>(a8, A.ld, A.sb[0], A.sb[1], b8p, B.ld, B.sb[0], B.sb[1], c, \
                                                        ldc, sc0, sc1, M, N, K, nb1, alpha, acc ? 1 : 0, kchunk,  \
                                                        nbatch, scs)
     if (!ta && tb) XT_B8D(true, true);

@@ -344,9 +344,10 @@ MM_CASES = [  # (M, N, K, ta, tb, batch)
     (8, 64, 64, 0, 0, (1, 1)), (200, 130, 70, 0, 0, (1, 1)), (200, 130, 70, 0, 1, (1, 1)),
     (200, 130, 70, 1, 0, (1, 1)), (200, 130, 70, 1, 1, (1, 1)), (256, 256, 64, 0, 1, (2, 3)),
     (129, 257, 300, 0, 0, (1, 1)), (512, 384, 256, 0, 0, (1, 1)),
-    # whole-tile shapes: the large-tile kernel (256 x 256 x 64 bf16, 128 x 128 x 32 f32)
+    # whole-tile shapes: the large-tile kernels (256 x 256 x 32 bf16, 128 x 128 x 32 f32)
     (512, 256, 192, 0, 0, (1, 1)), (512, 256, 192, 0, 1, (1, 1)), (512, 256, 192, 1, 0, (1, 1)),
     (512, 256, 192, 1, 1, (1, 1)), (256, 512, 128, 0, 1, (2, 2)), (256, 256, 64, 1, 0, (1, 3)),
+    (256, 256, 32, 1, 1, (1, 1)), (768, 512, 416, 0, 1, (1, 1)),
 ]
 
 
