@@ -302,6 +302,19 @@ __device__ __forceinline__ MS wave_merge(MS st) {
 // a set is written again only after the next call's barrier, by which time
 // every wave has read it: one barrier per reduction.  The waves' results are
 // combined in wave order, so the result is deterministic.
+// Block barrier for LDS traffic: this wave's LDS accesses complete, then
+// s_barrier.  Unlike __syncthreads() it does not wait for the wave's global
+// memory operations in flight (loads, stores, transfers into LDS issued by
+// global_load_lds), so a reduction does not stall on a prefetch or on the
+// previous row's stores.  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int RW>
 __device__ __forceinline__ float* group_slot(float* lds, int& ph) {
   float* slot = lds + ph * 2 * (int)(blockDim.x / WAVE);
@@ -319,7 +332,7 @@ __device__ __forceinline__ float group_sum(float v, float* lds, int& ph) {
     const int g0 = (w / RW) * RW;
     float* slot = group_slot<RW>(lds, ph);
     if ((threadIdx.x % WAVE) == 0) slot[w] = v;
-    __syncthreads();
+    lds_barrier();
     float s = slot[g0];
 #pragma unroll
     for (int i = 1; i < RW; ++i) s += slot[g0 + i];
@@ -337,7 +350,7 @@ __device__ __forceinline__ float group_max(float v, float* lds, int& ph) {
     const int g0 = (w / RW) * RW;
     float* slot = group_slot<RW>(lds, ph);
     if ((threadIdx.x % WAVE) == 0) slot[w] = v;
-    __syncthreads();
+    lds_barrier();
     float s = slot[g0];
 #pragma unroll
     for (int i = 1; i < RW; ++i) s = fmaxf(s, slot[g0 + i]);
@@ -355,7 +368,7 @@ __device__ __forceinline__ void group_sum2(float& a, float& b, float* lds, int& 
     const int g0 = (w / RW) * RW;
     float* slot = group_slot<RW>(lds, ph);
     if ((threadIdx.x % WAVE) == 0) { slot[2 * w] = a; slot[2 * w + 1] = b; }
-    __syncthreads();
+    lds_barrier();
     a = slot[2 * g0];
     b = slot[2 * g0 + 1];
 #pragma unroll

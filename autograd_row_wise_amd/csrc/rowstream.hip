@@ -105,7 +105,7 @@ __device__ __forceinline__ MS block_merge(MS st, float (*ms)[2][NW], int& ph) {
   st = wave_merge(st);
   const int w = threadIdx.x / WAVE;
   if ((threadIdx.x % WAVE) == 0) { ms[ph][0][w] = st.m; ms[ph][1][w] = st.s; }
-  __syncthreads();
+  lds_barrier();
   MS tot{ms[ph][0][0], ms[ph][1][0]};
 #pragma unroll
   for (int i = 1; i < NW; ++i) tot = ms_merge(tot, MS{ms[ph][0][i], ms[ph][1][i]});
@@ -625,6 +625,27 @@ struct RegRow {
 #pragma unroll
       for (int i = 0; i < NTS; ++i) asm volatile("" : "+v"(q[k][i].x), "+v"(q[k][i].y), "+v"(q[k][i].z), "+v"(q[k][i].w));
   }
+  // The packs from an LDS copy ([tensor][k][thread], 16 bytes each), the
+  // head and tail elements from global memory.
+  __device__ __forceinline__ void load_lds(const unsigned* bufw, const T* const (&src)[NTS], const Split& sp,
+                                           int64_t C) {
+    const uint4* buf = reinterpret_cast<const uint4*>(bufw);
+    const int tid = threadIdx.x;
+    // every slot is read (a pack past the row is read but never used), so
+    // the reads are all in flight at once
+#pragma unroll
+    for (int k = 0; k < NPR; ++k)
+#pragma unroll
+      for (int i = 0; i < NTS; ++i) q[k][i] = buf[(i * NPR + k) * BT + tid];
+    hv = tid < sp.head;
+    tc = sp.head + sp.packs * V + tid;
+    tv = tc < C;
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) {
+      h[i] = hv ? io<T>::ld(src[i] + tid) : 0.f;
+      t[i] = tv ? io<T>::ld(src[i] + tc) : 0.f;
+    }
+  }
   __device__ __forceinline__ bool has(const Split& sp, int k) const { return threadIdx.x + (int64_t)k * BT < sp.packs; }
   __device__ __forceinline__ int64_t col(const Split& sp, int k) const {
     return sp.head + (threadIdx.x + (int64_t)k * BT) * V;
@@ -685,10 +706,38 @@ __global__ __launch_bounds__(ST) void sm_bwd_reg(const void* __restrict__ d, int
   }
 }
 
+// f32 row r's packs of d and x into the LDS copy [tensor][k][thread] (16-byte
+// packs, NPR <= 4 per thread) by global_load_lds: 16 bytes per lane, no
+// registers held.
+__device__ __forceinline__ void reg_row_dma_f32(const float* dr, const float* xr, int64_t packs, int npr,
+                                                unsigned* __restrict__ buf) {
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // uniform base of the k-th run of ST packs, plus one lane offset shared by all k
+    const float* dk = dr + k * ST * 4;
+    const float* xk = xr + k * ST * 4;
+    if (k < npr && tid + k * ST < packs) {
+      __builtin_amdgcn_global_load_lds(dk + tid * 4, buf + 4 * (k * ST + w * WAVE), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(xk + tid * 4, buf + 4 * ((npr + k) * ST + w * WAVE), 16, 0, 0);
+    }
+  }
+}
+
 // rms_norm / layer_norm backward on register rows (LN = false: rms_norm).
 // OWN: every row starts 16-byte aligned (no head), so thread t's columns
 // are the same in every row and it keeps their parameter-gradient partial
 // sums; otherwise dx only (the partials come from the column pass).
+//
+// f32 rows with owned partials (every row 16-byte aligned, so the split is
+// the same for every row) are prefetched (PF): while a block works on row r
+// from registers, the packs of its next row travel into an LDS copy (2 NPR
+// 16-byte packs per thread: at most 128 KB), so a CU always has a row's
+// loads in flight.  vmcnt counts loads in issue order, so every other load
+// of row r is made before the next row's transfers are issued: gamma is
+// requested with the wait for the row, the first pass adds this row's
+// parameter-gradient terms and replaces d by d * gamma in the registers,
+// and the second pass needs no load.
 template <typename T, int NPR, bool LN, bool OWN>
 __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
                                                    int64_t ldx, const float* __restrict__ gamma,
@@ -697,12 +746,18 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
                                                    int64_t lddx, int acc, float* __restrict__ part, int64_t R,
                                                    int64_t C, float invC) {
   constexpr int V = io<T>::VEC, NP = LN ? 2 : 1;
+  constexpr bool PF = OWN && sizeof(T) == 4;
   __shared__ float lds[4 * SW];
+  __shared__ __align__(16) unsigned buf[(PF ? 2 * NPR : 1) * ST * 4];   // [tensor][k][thread] packs
   int ph = 0;
   OwnedPartials<NP, OWN ? NPR : 1, V> pp;
   pp.zero();
   int64_t packs_fixed = 0;
   const int tid = threadIdx.x;
+  if constexpr (PF)
+    if (blockIdx.x < R)
+      reg_row_dma_f32(crow<float>(d, blockIdx.x, ldd), crow<float>(x, blockIdx.x, ldx),
+                      split_of<T>(crow<T>(d, blockIdx.x, ldd), C).packs, NPR, buf);
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const T* dr = crow<T>(d, r, ldd);
     const T* xr = crow<T>(x, r, ldx);
@@ -711,7 +766,30 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
     packs_fixed = sp.packs;
     const T* src[2] = {dr, xr};
     RegRow<T, 2, NPR> rr;
-    rr.load(src, sp, C);
+    // PF: this thread's gamma packs, requested before the wait for the row
+    // so the two latencies overlap (a 16-byte aligned gamma: one load each)
+    float gk[PF ? NPR : 1][V];
+    if constexpr (PF) {
+      const bool ga = (((uintptr_t)gamma) & 15) == 0;
+#pragma unroll
+      for (int k = 0; k < NPR; ++k) {
+        const int c0 = (int)sp.head + (tid + k * ST) * V;   // < 2^31: OWN rows are at most 16384 wide
+        if (c0 + V > C) continue;
+        if (ga) {
+          const float4 g4 = *reinterpret_cast<const float4*>(gamma + c0);
+          gk[k][0] = g4.x; gk[k][1] = g4.y; gk[k][2] = g4.z; gk[k][3] = g4.w;
+        } else {
+          load_par<V>(gamma, c0, C, gk[k]);
+        }
+      }
+    }
+    if constexpr (PF) {
+      __builtin_amdgcn_s_waitcnt(0);    // this thread's transfers, gamma loads (and earlier stores) complete
+      __syncthreads();                  // every thread's transfers of row r have landed
+      rr.load_lds(buf, src, sp, C);
+    } else {
+      rr.load(src, sp, C);
+    }
     // rms_norm: st0 = inv_rms; layer_norm: st0 = mean, st1 = rstd
     const float s0 = st0[r * ld0], s1v = LN ? st1[r * ld1] : 0.f;
     auto xhat = [&](float xv) { return LN ? (xv - s0) * s1v : xv; };
@@ -724,13 +802,29 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
       float a[V], b[V], g[V];
       io<T>::unpack(rr.q[k][0], a);
       io<T>::unpack(rr.q[k][1], b);
-      load_par<V>(gamma, rr.col(sp, k), C, g);
+      if constexpr (PF) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) g[e] = gk[k][e];
+      } else {
+        load_par<V>(gamma, rr.col(sp, k), C, g);
+      }
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float gv = a[e] * g[e];
         a1 += gv;
         a2 += gv * xhat(b[e]);
+        if constexpr (PF) {
+          pp.pk[0][k][e] += LN ? a[e] * xhat(b[e]) : a[e] * b[e] * s0;
+          if constexpr (LN) pp.pk[NP - 1][k][e] += a[e];
+          a[e] = gv;
+        }
       }
+      if constexpr (PF) rr.q[k][0] = io<T>::pack(a);       // d * gamma from here on
+    }
+    if constexpr (PF) {
+      lds_barrier();                    // every thread's reads of buf complete before anyone refills it
+      const int64_t rn = r + gridDim.x;
+      if (rn < R) reg_row_dma_f32(crow<float>(d, rn, ldd), crow<float>(x, rn, ldx), sp.packs, NPR, buf);
     }
     float c1, mg, mgx;
     if constexpr (LN) {
@@ -744,30 +838,36 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
       mg = mgx = 0.f;
     }
     rr.pin();
-    auto dxv = [&](float dv, float gv, float xv) {
-      return LN ? s1v * (dv * gv - mg - xhat(xv) * mgx) : s0 * (dv * gv) - xv * c1;
-    };
+    // dx from d * gamma (dg) and x
+    auto dxg = [&](float dg, float xv) { return LN ? s1v * (dg - mg - xhat(xv) * mgx) : s0 * dg - xv * c1; };
 #pragma unroll
     for (int k = 0; k < NPR; ++k) {
       if (!rr.has(sp, k)) continue;
-      float a[V], b[V], g[V], o[V];
+      float a[V], b[V], o[V];
       io<T>::unpack(rr.q[k][0], a);
       io<T>::unpack(rr.q[k][1], b);
-      const int64_t c0 = rr.col(sp, k);
-      load_par<V>(gamma, c0, C, g);
+      // PF rows are at most 16384 wide: a 32-bit offset from the row start
+      const int64_t c0 = PF ? (int64_t)(int)rr.col(sp, k) : rr.col(sp, k);
+      if constexpr (PF) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        o[e] = dxv(a[e], g[e], b[e]);
-        if constexpr (OWN) {
-          pp.pk[0][k][e] += LN ? a[e] * xhat(b[e]) : a[e] * b[e] * s0;
-          if constexpr (LN) pp.pk[NP - 1][k][e] += a[e];
+        for (int e = 0; e < V; ++e) o[e] = dxg(a[e], b[e]);
+      } else {
+        float g[V];
+        load_par<V>(gamma, c0, C, g);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          o[e] = dxg(a[e] * g[e], b[e]);
+          if constexpr (OWN) {
+            pp.pk[0][k][e] += LN ? a[e] * xhat(b[e]) : a[e] * b[e] * s0;
+            if constexpr (LN) pp.pk[NP - 1][k][e] += a[e];
+          }
         }
       }
       if (orr) store_pack_acc_full<T>(orr + c0, o, acc != 0);
     }
-    if (rr.hv && orr) store_acc1<T>(orr + tid, dxv(rr.h[0], gh, rr.h[1]), acc != 0);
+    if (rr.hv && orr) store_acc1<T>(orr + tid, dxg(rr.h[0] * gh, rr.h[1]), acc != 0);
     if (rr.tv) {
-      if (orr) store_acc1<T>(orr + rr.tc, dxv(rr.t[0], gt, rr.t[1]), acc != 0);
+      if (orr) store_acc1<T>(orr + rr.tc, dxg(rr.t[0] * gt, rr.t[1]), acc != 0);
       if constexpr (OWN) {
         pp.tl[0] += LN ? rr.t[0] * xhat(rr.t[1]) : rr.t[0] * rr.t[1] * s0;
         if constexpr (LN) pp.tl[NP - 1] += rr.t[0];
