@@ -10,7 +10,10 @@
 // "En baklängeskärnas uppgift" -- the same mathematics as the register
 // kernels, with the same saved statistics and outputs.
 //
-// One 1024-thread block per row (blocks loop over rows).  Each row is split
+// One 1024-thread block per row (blocks loop over rows).  The kernels that
+// fit 64 registers without spilling and write no partial rows (f32 softmax
+// forward, softmax backward, f32 rms_norm dx) are held to 64, so two blocks
+// (two rows' loads in flight) share a CU.  Each row is split
 // at 16-byte boundaries into a scalar head (elements before the first
 // boundary), a body of 16-byte packs and a scalar tail; every tensor the op
 // touches is split the same way when their rows start at the same offset
@@ -161,7 +164,7 @@ __device__ __forceinline__ void load_par(const float* __restrict__ g, int64_t c0
 
 // ================================================================ softmax
 template <typename T>
-__global__ __launch_bounds__(ST) void sm_fwd_stream(const void* __restrict__ x, int64_t ldx, void* __restrict__ y,
+__global__ __launch_bounds__(ST, sizeof(T) == 4 ? 8 : 1) void sm_fwd_stream(const void* __restrict__ x, int64_t ldx, void* __restrict__ y,
                                                     int64_t ldy, int64_t R, int64_t C, float alpha, int causal,
                                                     int seq_len) {
   constexpr int V = io<T>::VEC;
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(ST) void sm_fwd_stream(const void* __restrict__ x, 
 }
 
 template <typename T>
-__global__ __launch_bounds__(ST) void sm_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ y,
+__global__ __launch_bounds__(ST, 8) void sm_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ y,
                                                     int64_t ldy, void* __restrict__ dx, int64_t lddx, int acc,
                                                     int64_t R, int64_t C, float alpha) {
   constexpr int V = io<T>::VEC;
@@ -331,7 +334,7 @@ struct OwnedPartials {
 // rms_norm backward, fixed split (PK > 0: owned partials of dgamma) or any
 // split (PK == 0: dx only; the partials come from a separate column pass).
 template <typename T, int PK>
-__global__ __launch_bounds__(ST) void rms_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
+__global__ __launch_bounds__(ST, PK == 0 && sizeof(T) == 4 ? 8 : 1) void rms_bwd_stream(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
                                                      int64_t ldx, const float* __restrict__ gamma,
                                                      const float* __restrict__ ir, int64_t ldir, void* __restrict__ dx,
                                                      int64_t lddx, int acc, float* __restrict__ part, int64_t R,

@@ -845,6 +845,10 @@ RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
   return p;
 }
 
+// Grid of a streaming backward that writes no parameter-gradient partial
+// rows: one 1024-thread block per row step, up to LONG_ROW_GRID blocks.
+static int dx_grid(int64_t R) { return (int)std::max<int64_t>(1, std::min<int64_t>(R, LONG_ROW_GRID)); }
+
 size_t row_bwd_workspace(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
   if (R <= 0 || C <= 0) return 0;
   const RowPlan p = plan_rows(kind, dtype, R, C, aligned);
@@ -959,7 +963,9 @@ static hipError_t rms_bwd_t(const xt_tensor& d, const xt_tensor& x, const float*
     // 16-byte aligned, else by a column pass
     const bool own = dgamma && stream_owns_partials(d.dtype, C, d, x, dx);
     hipError_t e = hipSuccess;
-    if (dx || own) e = launch_rms_bwd_stream(d, x, gamma, ir, dx, acc_dx, own ? part : nullptr, p.grid, s);
+    // without owned partials the dx kernel writes no partial rows: it takes
+    // as many blocks as the rows allow, several resident per CU
+    if (dx || own) e = launch_rms_bwd_stream(d, x, gamma, ir, dx, acc_dx, own ? part : nullptr, own ? p.grid : dx_grid(R), s);
     if (e != hipSuccess) return e;
     if (dgamma && !own)
       norm_partials_gen<T, 0><<<dim3((unsigned)cdiv(C, GEN_BLOCK), p.grid), GEN_BLOCK, 0, s>>>(
@@ -1028,7 +1034,7 @@ static hipError_t ln_bwd_t(const xt_tensor& d, const xt_tensor& x, const float* 
   } else {
     const bool own = want_p && stream_owns_partials(d.dtype, C, d, x, dx);
     hipError_t e = hipSuccess;
-    if (dx || own) e = launch_ln_bwd_stream(d, x, gamma, mean, rstd, dx, acc_dx, own ? part : nullptr, p.grid, s);
+    if (dx || own) e = launch_ln_bwd_stream(d, x, gamma, mean, rstd, dx, acc_dx, own ? part : nullptr, own ? p.grid : dx_grid(R), s);
     if (e != hipSuccess) return e;
     if (want_p && !own)
       norm_partials_gen<T, 1><<<dim3((unsigned)cdiv(C, GEN_BLOCK), p.grid), GEN_BLOCK, 0, s>>>(
@@ -1090,7 +1096,7 @@ static hipError_t sm_bwd_t(const xt_tensor& d, const xt_tensor& y, const xt_tens
         sm_bwd_fast<T, RW, NV, BLOCK><<<p.grid, BLOCK, 0, s>>>(d.data, d.ld, y.data, y.ld, dx.data, dx.ld, acc, R, C, alpha));
     return hipGetLastError();
   }
-  return launch_sm_bwd_stream(d, y, dx, acc, alpha, p.grid, s);
+  return launch_sm_bwd_stream(d, y, dx, acc, alpha, dx_grid(R), s);   // no partial rows: as for the forward
 }
 
 hipError_t launch_softmax_bwd(const xt_tensor& d, const xt_tensor& y, const xt_tensor& dx,
