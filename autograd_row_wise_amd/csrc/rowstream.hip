@@ -709,6 +709,180 @@ __global__ __launch_bounds__(ST) void sm_bwd_reg(const void* __restrict__ d, int
   }
 }
 
+// Forwards on register rows of at most 8 packs per thread (f32 rows up to
+// 32768 columns, bf16 up to 65536): the row is read from HBM once and both
+// passes (statistics, then the output) run on the registers.  At most 32
+// registers of packs, so the softmax (and the narrower norms) are held to
+// 64 registers and two blocks share a CU: one block's loads are in flight
+// while the other reduces and writes.  Addresses are a row-uniform base per pack slot plus
+// one 32-bit lane offset (the rows are at most 65536 wide).
+template <typename T, int NPR>
+struct FwdRow {
+  static constexpr int V = io<T>::VEC;
+  uint4 q[NPR];
+  float h, t;         // head element (column tid) and tail element (column tc)
+  int tc;
+  bool hv, tv;
+  __device__ __forceinline__ void load(const T* xr, const Split& sp, int C) {
+    const int tid = threadIdx.x, lo = tid * V;
+    const T* xb = xr + sp.head;
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) q[k] = has(sp, k) ? ld_nt(xb + k * ST * V + lo) : make_uint4(0, 0, 0, 0);
+    hv = tid < sp.head;
+    tc = (int)(sp.head + sp.packs * V) + tid;
+    tv = tc < C;
+    h = hv ? io<T>::ld(xr + tid) : 0.f;
+    t = tv ? io<T>::ld(xr + tc) : 0.f;
+  }
+  __device__ __forceinline__ bool has(const Split& sp, int k) const { return (int)threadIdx.x + k * ST < (int)sp.packs; }
+  // the same empty-asm barrier as RegRow::pin
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) asm volatile("" : "+v"(q[k].x), "+v"(q[k].y), "+v"(q[k].z), "+v"(q[k].w));
+  }
+};
+
+template <typename T, int NPR, bool CAUSAL>
+__global__ __launch_bounds__(ST, 8) void sm_fwd_reg(const void* __restrict__ x, int64_t ldx, void* __restrict__ y,
+                                                    int64_t ldy, int64_t R, int64_t C, float alpha, int causal,
+                                                    int seq_len) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float ms[2][2][SW];
+  int ph = 0;
+  const float sl = alpha * LOG2E;
+  const int tid = threadIdx.x, lo = tid * V, Ci = (int)C;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* xr = crow<T>(x, r, ldx);
+    T* yr = wrow<T>(y, r, ldy);
+    const int lim = CAUSAL ? min(Ci, (int)(r % seq_len) + 1) : Ci;
+    const Split sp = split_of<T>(xr, C);
+    FwdRow<T, NPR> rr;
+    rr.load(xr, sp, Ci);
+    // base-2 scaled scores; columns at or past the causal limit are -inf.
+    // Pack slot k holds columns head + k*ST*V + lo + e: its limit relative
+    // to the lane offset is row-uniform.
+    auto lim_k = [&](int k) { return lim - (int)sp.head - k * ST * V; };
+    auto sc = [&](float v, int c, int l) { return !CAUSAL || c < l ? v * sl : -__builtin_inff(); };
+    // this thread's online (max, sum) state, one pack at a time
+    float m = fmaxf(rr.hv ? sc(rr.h, tid, lim) : -__builtin_inff(), rr.tv ? sc(rr.t, rr.tc, lim) : -__builtin_inff());
+    float s = (rr.hv && (!CAUSAL || tid < lim) ? __builtin_amdgcn_exp2f(rr.h * sl - m) : 0.f) +
+              (rr.tv && (!CAUSAL || rr.tc < lim) ? __builtin_amdgcn_exp2f(rr.t * sl - m) : 0.f);
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float v[V];
+      io<T>::unpack(rr.q[k], v);
+      const int l = lim_k(k);
+      float pm = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        v[e] = sc(v[e], lo + e, l);
+        pm = fmaxf(pm, v[e]);
+      }
+      if (CAUSAL && pm == -__builtin_inff()) continue;    // the whole pack is past the causal limit
+      if (pm > m) { s *= __builtin_amdgcn_exp2f(m - pm); m = pm; }
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) a += __builtin_amdgcn_exp2f(v[e] - m);
+      s += a;
+    }
+    rr.pin();
+    const MS tot = block_merge(MS{m, s}, ms, ph);
+    const float inv = 1.f / tot.s, mm = tot.m;
+    auto out = [&](float v, int c, int l) { return !CAUSAL || c < l ? __builtin_amdgcn_exp2f(fmaf(v, sl, -mm)) * inv : 0.f; };
+    T* yb = yr + sp.head;
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float v[V];
+      io<T>::unpack(rr.q[k], v);
+      const int l = lim_k(k);
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] = out(v[e], lo + e, l);
+      st_nt(yb + k * ST * V + lo, io<T>::pack(v));
+    }
+    if (rr.hv) io<T>::st(yr + tid, out(rr.h, tid, lim));
+    if (rr.tv) io<T>::st(yr + rr.tc, out(rr.t, rr.tc, lim));
+  }
+}
+
+// The norm forwards on register rows fit 64 registers without spilling
+// (two blocks per CU) up to these packs per thread (es: element bytes);
+// wider rows take the streaming kernels, which measured faster there than
+// a register row at one block per CU (bf16 layer_norm, 50257 columns:
+// 0.70 vs 0.76 ms).
+__host__ __device__ constexpr bool norm_fwd_fits(int es, int npr, bool ln) {
+  return ln ? (es == 4 ? npr <= 2 : npr <= 1) : npr <= 4;
+}
+
+// rms_norm (LN = false; st0 = inv_rms) or layer_norm (st0 = mean, st1 =
+// rstd; the variance about the mean, a second pass over the registers).
+template <typename T, int NPR, bool LN>
+__global__ __launch_bounds__(ST, 8) void norm_fwd_reg(const void* __restrict__ x, int64_t ldx,
+                                                      const float* __restrict__ gamma, const float* __restrict__ beta,
+                                                      void* __restrict__ y, int64_t ldy, float* __restrict__ st0,
+                                                      int64_t ld0, float* __restrict__ st1, int64_t ld1, int64_t R,
+                                                      int64_t C, float eps, float invC) {
+  constexpr int V = io<T>::VEC;
+  __shared__ float lds[4 * SW];
+  int ph = 0;
+  const int tid = threadIdx.x, lo = tid * V, Ci = (int)C;
+  for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+    const T* xr = crow<T>(x, r, ldx);
+    T* yr = wrow<T>(y, r, ldy);
+    const Split sp = split_of<T>(xr, C);
+    FwdRow<T, NPR> rr;
+    rr.load(xr, sp, Ci);
+    // layer_norm: the mean first (empty slots hold 0 and add nothing)
+    float mu = 0.f;
+    if constexpr (LN) {
+      float a = rr.h + rr.t;
+#pragma unroll
+      for (int k = 0; k < NPR; ++k) {
+        float v[V];
+        io<T>::unpack(rr.q[k], v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) a += v[e];
+      }
+      rr.pin();
+      mu = group_sum<SW>(a, lds, ph) * invC;
+    }
+    // sum of squares (rms_norm) or of squared deviations about the mean
+    auto dev = [&](float v) { return LN ? v - mu : v; };
+    float q2 = (rr.hv ? dev(rr.h) * dev(rr.h) : 0.f) + (rr.tv ? dev(rr.t) * dev(rr.t) : 0.f);
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float v[V];
+      io<T>::unpack(rr.q[k], v);
+#pragma unroll
+      for (int e = 0; e < V; ++e) q2 += dev(v[e]) * dev(v[e]);
+    }
+    rr.pin();
+    const float rs = rsqrtf(group_sum<SW>(q2, lds, ph) * invC + eps);
+    if (tid == 0) {
+      if constexpr (LN) { st0[r * ld0] = mu; st1[r * ld1] = rs; }
+      else st0[r * ld0] = rs;
+    }
+    T* yb = yr + sp.head;
+    const float* gb = gamma + sp.head;
+    const float* bb = LN ? beta + sp.head : nullptr;
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      if (!rr.has(sp, k)) continue;
+      float v[V], g[V], b[V];
+      io<T>::unpack(rr.q[k], v);
+      load_par<V>(gb + k * ST * V, lo, (int64_t)(Ci - (int)sp.head - k * ST * V), g);
+      if constexpr (LN) load_par<V>(bb + k * ST * V, lo, (int64_t)(Ci - (int)sp.head - k * ST * V), b);
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] = LN ? dev(v[e]) * rs * g[e] + b[e] : v[e] * rs * g[e];
+      st_nt(yb + k * ST * V + lo, io<T>::pack(v));
+    }
+    if (rr.hv) io<T>::st(yr + tid, LN ? dev(rr.h) * rs * gamma[tid] + beta[tid] : rr.h * rs * gamma[tid]);
+    if (rr.tv) io<T>::st(yr + rr.tc, LN ? dev(rr.t) * rs * gamma[rr.tc] + beta[rr.tc] : rr.t * rs * gamma[rr.tc]);
+  }
+}
+
 // f32 row r's packs of d and x into the LDS copy [tensor][k][thread] (16-byte
 // packs, NPR <= 4 per thread) by global_load_lds: 16 bytes per lane, no
 // registers held.
@@ -935,6 +1109,20 @@ bool stream_owns_partials(int dtype, int64_t C, const xt_tensor& d, const xt_ten
 
 hipError_t launch_sm_fwd_stream(const xt_tensor& x, const xt_tensor& y, float alpha, int causal, int seq_len,
                                 int grid, hipStream_t s) {
+  const int npr = same_phase(x, &y) ? reg_npr(x.dtype, x.cols, 8) : 0;
+  if (npr) {
+    if (x.dtype == XT_F32)
+      XT_NPR_CASES(npr, 8, {
+        auto kf = causal ? sm_fwd_reg<float, NPR, true> : sm_fwd_reg<float, NPR, false>;
+        kf<<<grid, ST, 0, s>>>(x.data, x.ld, y.data, y.ld, x.rows, x.cols, alpha, causal, seq_len);
+      });
+    else
+      XT_NPR_CASES(npr, 8, {
+        auto kf = causal ? sm_fwd_reg<bf16_t, NPR, true> : sm_fwd_reg<bf16_t, NPR, false>;
+        kf<<<grid, ST, 0, s>>>(x.data, x.ld, y.data, y.ld, x.rows, x.cols, alpha, causal, seq_len);
+      });
+    return hipGetLastError();
+  }
   if (x.dtype == XT_F32)
     sm_fwd_stream<float><<<grid, ST, 0, s>>>(x.data, x.ld, y.data, y.ld, x.rows, x.cols, alpha, causal, seq_len);
   else
@@ -964,6 +1152,16 @@ hipError_t launch_sm_bwd_stream(const xt_tensor& d, const xt_tensor& y, const xt
 hipError_t launch_rms_fwd_stream(const xt_tensor& x, const float* gamma, const xt_tensor& y, const xt_tensor& ir,
                                  float eps, int grid, hipStream_t s) {
   const float invC = 1.0f / (float)x.cols;
+  const int npr = same_phase(x, &y) ? reg_npr(x.dtype, x.cols, 8) : 0;
+  if (npr && norm_fwd_fits(x.dtype == XT_F32 ? 4 : 2, npr, false)) {
+    if (x.dtype == XT_F32)
+      XT_NPR_CASES(npr, 4, norm_fwd_reg<float, NPR, false><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, nullptr, y.data, y.ld,
+          (float*)ir.data, ir.ld, nullptr, 0, x.rows, x.cols, eps, invC));
+    else
+      XT_NPR_CASES(npr, 4, norm_fwd_reg<bf16_t, NPR, false><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, nullptr, y.data, y.ld,
+          (float*)ir.data, ir.ld, nullptr, 0, x.rows, x.cols, eps, invC));
+    return hipGetLastError();
+  }
   if (x.dtype == XT_F32)
     rms_fwd_stream<float><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, y.data, y.ld, (float*)ir.data, ir.ld, x.rows,
                                               x.cols, eps, invC);
@@ -976,6 +1174,16 @@ hipError_t launch_rms_fwd_stream(const xt_tensor& x, const float* gamma, const x
 hipError_t launch_ln_fwd_stream(const xt_tensor& x, const float* gamma, const float* beta, const xt_tensor& y,
                                 const xt_tensor& mean, const xt_tensor& rstd, float eps, int grid, hipStream_t s) {
   const float invC = 1.0f / (float)x.cols;
+  const int npr = same_phase(x, &y) ? reg_npr(x.dtype, x.cols, 8) : 0;
+  if (npr && norm_fwd_fits(x.dtype == XT_F32 ? 4 : 2, npr, true)) {
+    if (x.dtype == XT_F32)
+      XT_NPR_CASES(npr, 4, norm_fwd_reg<float, NPR, true><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld,
+          (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, x.rows, x.cols, eps, invC));
+    else
+      XT_NPR_CASES(npr, 4, norm_fwd_reg<bf16_t, NPR, true><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld,
+          (float*)mean.data, mean.ld, (float*)rstd.data, rstd.ld, x.rows, x.cols, eps, invC));
+    return hipGetLastError();
+  }
   if (x.dtype == XT_F32)
     ln_fwd_stream<float><<<grid, ST, 0, s>>>(x.data, x.ld, gamma, beta, y.data, y.ld, (float*)mean.data, mean.ld,
                                              (float*)rstd.data, rstd.ld, x.rows, x.cols, eps, invC);

@@ -27,6 +27,8 @@ LAYOUTS = [(8, 64, None), (37, 1000, None), (37, 1000, 1008), (37, 1001, None), 
            (5, 3001, 3008), (3, 20000, None), (130, 256, None), (9, 32768, None),
            # wider than any register-resident row: the streaming kernels, ragged and strided
            (3, 40000, None), (2, 65601, 65608),
+           # a vocabulary-wide row: every row starts at another offset modulo 16 bytes
+           (9, 50257, None),
            # aligned rows past the register kernels' reach whose parameter partials the
            # streaming backward keeps per thread (f32 up to 4 packs, bf16 up to 2 per thread)
            (33, 16384, None), (20, 12288, None), (17, 16000, 16004)]
