@@ -315,6 +315,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Waits until at most n of the wave's vector memory operations are
+// outstanding (n clamped to 15).  vmcnt retires them in issue order, so
+// every operation issued before the last n has completed.  n may differ
+// between lanes: the wave then waits for the smallest, which is stronger.
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  asm volatile("" ::: "memory");
+  // s_waitcnt immediate: vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 at
+  // their maxima (not waited for)
+#define XT_VMW(N) case N: __builtin_amdgcn_s_waitcnt(0x0F70 | N); break;
+  switch (n < 15 ? (n < 0 ? 0 : n) : 15) {
+    XT_VMW(0) XT_VMW(1) XT_VMW(2) XT_VMW(3) XT_VMW(4) XT_VMW(5) XT_VMW(6) XT_VMW(7)
+    XT_VMW(8) XT_VMW(9) XT_VMW(10) XT_VMW(11) XT_VMW(12) XT_VMW(13) XT_VMW(14)
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+  }
+#undef XT_VMW
+  asm volatile("" ::: "memory");
+}
+
 template <int RW>
 __device__ __forceinline__ float* group_slot(float* lds, int& ph) {
   float* slot = lds + ph * 2 * (int)(blockDim.x / WAVE);

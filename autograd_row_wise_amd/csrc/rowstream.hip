@@ -649,6 +649,64 @@ struct RegRow {
       t[i] = tv ? io<T>::ld(src[i] + tc) : 0.f;
     }
   }
+  // load_lds for f32 rows with no head (16-byte aligned starts) whose tail
+  // elements are in the copy too (after the packs), with the LDS reads
+  // written out and waited for in one asm statement: the compiler then sees
+  // no read of the copy that a pending global-to-LDS transfer may write, so
+  // it adds no wait for every outstanding vector memory operation in front
+  // of them, and the row needs no global load; the caller has already
+  // waited for the transfers that wrote the copy.  (Reads and wait share
+  // one statement so no output is used before its data has arrived.)
+  // Slot J = i*NPR + k (tensor i, pack k) is 16 bytes at J*BT*16 + 16*tid.
+  __device__ __forceinline__ void load_lds_direct(const unsigned* bufw, const Split& sp, int64_t C) {
+    static_assert(BT == 1024 && NTS == 2 && (NPR == 2 || NPR == 4) && sizeof(T) == 4, "prefetched f32 rows");
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const unsigned base = (unsigned)(uintptr_t)bufw;
+    const unsigned a0 = base + threadIdx.x * 16;
+    const unsigned at = base + NTS * NPR * BT * 16 + (threadIdx.x & 3) * 4;   // tail words 4 i + tid (tid < 4)
+    u32x4 v[2 * NPR];
+    unsigned tw0, tw1;
+    if constexpr (NPR == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %6 offset:0\n\t"
+          "ds_read_b128 %1, %6 offset:16384\n\t"
+          "ds_read_b128 %2, %6 offset:32768\n\t"
+          "ds_read_b128 %3, %6 offset:49152\n\t"
+          "ds_read_b32 %4, %7 offset:0\n\t"
+          "ds_read_b32 %5, %7 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(tw0), "=&v"(tw1)
+          : "v"(a0), "v"(at)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %10 offset:0\n\t"
+          "ds_read_b128 %1, %10 offset:16384\n\t"
+          "ds_read_b128 %2, %10 offset:32768\n\t"
+          "ds_read_b128 %3, %10 offset:49152\n\t"
+          "ds_read_b128 %4, %11 offset:0\n\t"
+          "ds_read_b128 %5, %11 offset:16384\n\t"
+          "ds_read_b128 %6, %11 offset:32768\n\t"
+          "ds_read_b128 %7, %11 offset:49152\n\t"
+          "ds_read_b32 %8, %12 offset:0\n\t"
+          "ds_read_b32 %9, %12 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+            "=&v"(v[7]), "=&v"(tw0), "=&v"(tw1)
+          : "v"(a0), "v"(a0 + 65536u), "v"(at)
+          : "memory");
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * NPR; ++j) q[j % NPR][j / NPR] = make_uint4(v[j].x, v[j].y, v[j].z, v[j].w);
+    // rows of at most 2^31 elements: 32-bit offsets from the row starts
+    const int tci = (int)(sp.packs * V) + threadIdx.x;
+    hv = false;
+    tc = tci;
+    tv = tci < C;
+    h[0] = h[1] = 0.f;
+    t[0] = tv ? __uint_as_float(tw0) : 0.f;
+    t[1] = tv ? __uint_as_float(tw1) : 0.f;
+  }
   __device__ __forceinline__ bool has(const Split& sp, int k) const { return threadIdx.x + (int64_t)k * BT < sp.packs; }
   __device__ __forceinline__ int64_t col(const Split& sp, int k) const {
     return sp.head + (threadIdx.x + (int64_t)k * BT) * V;
@@ -885,8 +943,9 @@ __global__ __launch_bounds__(ST, 8) void norm_fwd_reg(const void* __restrict__ x
 
 // f32 row r's packs of d and x into the LDS copy [tensor][k][thread] (16-byte
 // packs, NPR <= 4 per thread) by global_load_lds: 16 bytes per lane, no
-// registers held.
-__device__ __forceinline__ void reg_row_dma_f32(const float* dr, const float* xr, int64_t packs, int npr,
+// registers held.  The row's tail elements (C - 4*packs < 4 of each tensor)
+// follow the packs: d's at word 8*npr*ST, x's 4 words on.
+__device__ __forceinline__ void reg_row_dma_f32(const float* dr, const float* xr, int64_t packs, int npr, int64_t C,
                                                 unsigned* __restrict__ buf) {
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / WAVE);
 #pragma unroll
@@ -899,6 +958,11 @@ __device__ __forceinline__ void reg_row_dma_f32(const float* dr, const float* xr
       __builtin_amdgcn_global_load_lds(xk + tid * 4, buf + 4 * ((npr + k) * ST + w * WAVE), 16, 0, 0);
     }
   }
+  // 4 bytes per lane: lane l of wave 0 writes word l of the tail region
+  if (tid < C - packs * 4) {
+    __builtin_amdgcn_global_load_lds(dr + packs * 4 + tid, buf + 8 * npr * ST, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(xr + packs * 4 + tid, buf + 8 * npr * ST + 4, 4, 0, 0);
+  }
 }
 
 // rms_norm / layer_norm backward on register rows (LN = false: rms_norm).
@@ -907,14 +971,14 @@ __device__ __forceinline__ void reg_row_dma_f32(const float* dr, const float* xr
 // sums; otherwise dx only (the partials come from the column pass).
 //
 // f32 rows with owned partials (every row 16-byte aligned, so the split is
-// the same for every row) are prefetched (PF): while a block works on row r
-// from registers, the packs of its next row travel into an LDS copy (2 NPR
-// 16-byte packs per thread: at most 128 KB), so a CU always has a row's
-// loads in flight.  vmcnt counts loads in issue order, so every other load
-// of row r is made before the next row's transfers are issued: gamma is
-// requested with the wait for the row, the first pass adds this row's
-// parameter-gradient terms and replaces d by d * gamma in the registers,
-// and the second pass needs no load.
+// the same for every row) are prefetched (PF): a block copies row r (packs
+// and tail elements) from its LDS copy into registers and at once sends its
+// next row into the LDS copy (2 NPR 16-byte packs per thread: at most
+// 128 KB), so that transfer runs under row r's first pass.  The row then
+// needs no global load: gamma is the same for every row of a thread and is
+// loaded once.  vmcnt counts the vector memory operations in issue order,
+// so the wait at the top of a row leaves the previous row's stores (issued
+// after the transfer, counted in nvm) in flight.
 template <typename T, int NPR, bool LN, bool OWN>
 __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, int64_t ldd, const void* __restrict__ x,
                                                    int64_t ldx, const float* __restrict__ gamma,
@@ -925,16 +989,35 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
   constexpr int V = io<T>::VEC, NP = LN ? 2 : 1;
   constexpr bool PF = OWN && sizeof(T) == 4;
   __shared__ float lds[4 * SW];
-  __shared__ __align__(16) unsigned buf[(PF ? 2 * NPR : 1) * ST * 4];   // [tensor][k][thread] packs
+  __shared__ __align__(16) unsigned buf[PF ? 2 * NPR * ST * 4 + 8 : ST * 4];   // [tensor][k][thread] packs, tails
   int ph = 0;
   OwnedPartials<NP, OWN ? NPR : 1, V> pp;
   pp.zero();
   int64_t packs_fixed = 0;
   const int tid = threadIdx.x;
-  if constexpr (PF)
+  // PF: this thread's gamma packs (columns (tid + k*ST)*V of every row)
+  float gk[PF ? NPR : 1][V];
+  int nvm = 0;                          // PF: vector memory operations since the last transfer
+  float gtf = 0.f;                      // PF: gamma at this thread's tail column
+  if constexpr (PF) {
+    const int64_t tcf = C / V * V + tid;
+    if (tcf < C) gtf = gamma[tcf];
+    const bool ga = (((uintptr_t)gamma) & 15) == 0;
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
+      const int c0 = (tid + k * ST) * V;   // < 2^31: OWN rows are at most 16384 wide
+      if (c0 + V > C) continue;
+      if (ga) {
+        const float4 g4 = *reinterpret_cast<const float4*>(gamma + c0);
+        gk[k][0] = g4.x; gk[k][1] = g4.y; gk[k][2] = g4.z; gk[k][3] = g4.w;
+      } else {
+        load_par<V>(gamma, c0, C, gk[k]);
+      }
+    }
     if (blockIdx.x < R)
       reg_row_dma_f32(crow<float>(d, blockIdx.x, ldd), crow<float>(x, blockIdx.x, ldx),
-                      split_of<T>(crow<T>(d, blockIdx.x, ldd), C).packs, NPR, buf);
+                      split_of<T>(crow<T>(d, blockIdx.x, ldd), C).packs, NPR, C, buf);
+  }
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const T* dr = crow<T>(d, r, ldd);
     const T* xr = crow<T>(x, r, ldx);
@@ -943,34 +1026,23 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
     packs_fixed = sp.packs;
     const T* src[2] = {dr, xr};
     RegRow<T, 2, NPR> rr;
-    // PF: this thread's gamma packs, requested before the wait for the row
-    // so the two latencies overlap (a 16-byte aligned gamma: one load each)
-    float gk[PF ? NPR : 1][V];
     if constexpr (PF) {
-      const bool ga = (((uintptr_t)gamma) & 15) == 0;
-#pragma unroll
-      for (int k = 0; k < NPR; ++k) {
-        const int c0 = (int)sp.head + (tid + k * ST) * V;   // < 2^31: OWN rows are at most 16384 wide
-        if (c0 + V > C) continue;
-        if (ga) {
-          const float4 g4 = *reinterpret_cast<const float4*>(gamma + c0);
-          gk[k][0] = g4.x; gk[k][1] = g4.y; gk[k][2] = g4.z; gk[k][3] = g4.w;
-        } else {
-          load_par<V>(gamma, c0, C, gk[k]);
-        }
-      }
-    }
-    if constexpr (PF) {
-      __builtin_amdgcn_s_waitcnt(0);    // this thread's transfers, gamma loads (and earlier stores) complete
-      __syncthreads();                  // every thread's transfers of row r have landed
-      rr.load_lds(buf, src, sp, C);
+      wait_vmcnt_at_most(nvm);          // this thread's transfers of row r have landed
+      lds_barrier();                    // ... and every other thread's
+      rr.load_lds_direct(buf, sp, C);
     } else {
       rr.load(src, sp, C);
     }
     // rms_norm: st0 = inv_rms; layer_norm: st0 = mean, st1 = rstd
     const float s0 = st0[r * ld0], s1v = LN ? st1[r * ld1] : 0.f;
     auto xhat = [&](float xv) { return LN ? (xv - s0) * s1v : xv; };
-    const float gh = rr.hv ? gamma[tid] : 0.f, gt = rr.tv ? gamma[rr.tc] : 0.f;
+    const float gh = !PF && rr.hv ? gamma[tid] : 0.f, gt = PF ? gtf : rr.tv ? gamma[rr.tc] : 0.f;
+    if constexpr (PF) {
+      lds_barrier();                    // every thread's reads of buf complete before anyone refills it
+      const int64_t rn = r + gridDim.x;
+      if (rn < R) reg_row_dma_f32(crow<float>(d, rn, ldd), crow<float>(x, rn, ldx), sp.packs, NPR, C, buf);
+      nvm = 0;
+    }
     float a1 = rr.h[0] * gh + rr.t[0] * gt;                                   // layer_norm: sum d*gamma
     float a2 = rr.h[0] * gh * xhat(rr.h[1]) + rr.t[0] * gt * xhat(rr.t[1]);   // sum d*gamma*xhat (rms: *x)
 #pragma unroll
@@ -998,11 +1070,10 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
       }
       if constexpr (PF) rr.q[k][0] = io<T>::pack(a);       // d * gamma from here on
     }
-    if constexpr (PF) {
-      lds_barrier();                    // every thread's reads of buf complete before anyone refills it
-      const int64_t rn = r + gridDim.x;
-      if (rn < R) reg_row_dma_f32(crow<float>(d, rn, ldd), crow<float>(x, rn, ldx), sp.packs, NPR, buf);
-    }
+    // the next row's transfer is waited for before the reduction: letting it
+    // run on under the reduction and this row's stores measured slower
+    // (16384-wide f32 rows: 625 -> 615 us)
+    if constexpr (PF) wait_vmcnt_at_most(0);
     float c1, mg, mgx;
     if constexpr (LN) {
       group_sum2<SW>(a1, a2, lds, ph);
@@ -1040,11 +1111,20 @@ __global__ __launch_bounds__(ST) void norm_bwd_reg(const void* __restrict__ d, i
           }
         }
       }
-      if (orr) store_pack_acc_full<T>(orr + c0, o, acc != 0);
+      if (orr) {
+        store_pack_acc_full<T>(orr + c0, o, acc != 0);
+        nvm += acc ? 2 : 1;
+      }
     }
-    if (rr.hv && orr) store_acc1<T>(orr + tid, dxg(rr.h[0] * gh, rr.h[1]), acc != 0);
+    if (!PF && rr.hv && orr) {
+      store_acc1<T>(orr + tid, dxg(rr.h[0] * gh, rr.h[1]), acc != 0);
+      nvm += acc ? 2 : 1;
+    }
     if (rr.tv) {
-      if (orr) store_acc1<T>(orr + rr.tc, dxg(rr.t[0] * gt, rr.t[1]), acc != 0);
+      if (orr) {
+        store_acc1<T>(orr + rr.tc, dxg(rr.t[0] * gt, rr.t[1]), acc != 0);
+        nvm += acc ? 2 : 1;
+      }
       if constexpr (OWN) {
         pp.tl[0] += LN ? rr.t[0] * xhat(rr.t[1]) : rr.t[0] * rr.t[1] * s0;
         if constexpr (LN) pp.tl[NP - 1] += rr.t[0];

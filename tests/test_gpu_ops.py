@@ -31,7 +31,9 @@ LAYOUTS = [(8, 64, None), (37, 1000, None), (37, 1000, 1008), (37, 1001, None), 
            (9, 50257, None),
            # aligned rows past the register kernels' reach whose parameter partials the
            # streaming backward keeps per thread (f32 up to 4 packs, bf16 up to 2 per thread)
-           (33, 16384, None), (20, 12288, None), (17, 16000, 16004)]
+           (33, 16384, None), (20, 12288, None), (17, 16000, 16004),
+           # ... with a tail of 3 elements after the last whole f32 pack
+           (6, 15999, 16004)]
 
 
 def put(a_f32: np.ndarray, dtype: str, ld=None):
