@@ -10,9 +10,10 @@
 //
 // Layout: q, k, v and out are [B*S, H*Dh] (row b*S + s, head h in columns
 // h*Dh ..); L is [B*S, H] f32.  Two kernel families:
-//   - f32 storage, and bf16 rows that are not 16-byte aligned: one wave per
-//     32 query rows (forward, dQ) or 32 key rows (dK, dV) of one (sequence,
-//     head); products are v_mfma_f32_32x32x2f32 in f32 (bf16 widened on
+//   - f32 storage, and bf16 rows that are not 16-byte aligned: one block of
+//     four waves per 32 query rows (forward, dQ) or 32 key rows (dK, dV) of
+//     one (sequence, head), the waves splitting the loop over the other
+//     operand's tiles; products are v_mfma_f32_32x32x2f32 in f32 (bf16 widened on
 //     load): for a contraction of length n, MFMA j takes index h*(n/2) + j
 //     from lane half h for both operands (a fixed permutation of the
 //     summation order).  A probability tile leaves the MFMA in the
@@ -137,12 +138,22 @@ __device__ __forceinline__ void mul_rows(const float (&a)[16], const T* x, const
 __device__ __forceinline__ float half_max(float v) { return half_reduce(v, OpMax{}); }
 __device__ __forceinline__ float half_sum(float v) { return half_reduce(v, OpAdd{}); }
 
-template <typename T, int DH>
-__global__ __launch_bounds__(WAVE) void attn_fwd_k(const T* __restrict__ q, const T* __restrict__ k,
-                                                   const T* __restrict__ v, T* __restrict__ out,
-                                                   float* __restrict__ lse, Geo g, float alpha, int causal) {
-  __shared__ float tile[32 * 33];
-  const int l = threadIdx.x;
+// Blocks of KW waves share one 32-row tile: wave w takes the loop's tiles
+// w, w + KW, ... (the key tiles of a query tile, or the query tiles of a
+// key tile) with its own online state or partial sums, and wave 0 merges
+// the waves' states in wave order (fixed: bitwise reproducible) and writes
+// the result.  KW > 1 shortens the serial loop of each block KW-fold where
+// the (sequence, head, tile) grid alone is too small to fill the chip.
+constexpr int AKW = 4;
+
+template <typename T, int DH, int KW>
+__global__ __launch_bounds__(WAVE * KW) void attn_fwd_k(const T* __restrict__ q, const T* __restrict__ k,
+                                                        const T* __restrict__ v, T* __restrict__ out,
+                                                        float* __restrict__ lse, Geo g, float alpha, int causal) {
+  __shared__ float tiles[KW][32 * 33];
+  __shared__ float mrg[KW > 1 ? KW - 1 : 1][2 + DH / 32][16][WAVE];   // m, s, o per register and lane
+  const int l = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+  float* tile = tiles[w];
   const int64_t q0 = (int64_t)blockIdx.x * 32, hd = blockIdx.y, b = blockIdx.z;
   float qf[DH / 2];
   frag_dh<T, DH>(q, g, b, hd, q0, l, qf);
@@ -155,7 +166,9 @@ __global__ __launch_bounds__(WAVE) void attn_fwd_k(const T* __restrict__ q, cons
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
   const int64_t kend = causal ? (q0 + 32 < g.S ? q0 + 32 : g.S) : g.S;
-  for (int64_t k0 = 0; k0 < kend; k0 += 32) {
+  // every tile a wave takes keeps at least one key of each row (causal:
+  // k0 <= q0 <= the row), so m is finite after a wave's first tile
+  for (int64_t k0 = (int64_t)w * 32; k0 < kend; k0 += 32 * KW) {
     float kf[DH / 2];
     frag_dh<T, DH>(k, g, b, hd, k0, l, kf);
     f32x16_t z = dot_tile<DH>(qf, kf);
@@ -180,6 +193,31 @@ __global__ __launch_bounds__(WAVE) void attn_fwd_k(const T* __restrict__ q, cons
     float pa[16];
     c_to_a(pc, tile, l, pa);
     mul_rows<T, DH>(pa, v, g, b, hd, k0, l, o);
+  }
+  if constexpr (KW > 1) {
+    if (w > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        mrg[w - 1][0][i][l] = m[i];
+        mrg[w - 1][1][i][l] = s[i];
+#pragma unroll
+        for (int t = 0; t < DH / 32; ++t) mrg[w - 1][2 + t][i][l] = o[t][i];
+      }
+    }
+    __syncthreads();
+    if (w > 0) return;
+    // a wave with no tile holds m = -inf, s = 0, o = 0 and adds nothing
+    for (int u = 1; u < KW; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float mu = mrg[u - 1][0][i][l];
+        const float mn = fmaxf(m[i], mu);
+        const float ca = m[i] == -INFINITY ? 0.f : ex(m[i] - mn), cb = mu == -INFINITY ? 0.f : ex(mu - mn);
+        s[i] = s[i] * ca + mrg[u - 1][1][i][l] * cb;
+#pragma unroll
+        for (int t = 0; t < DH / 32; ++t) o[t][i] = o[t][i] * ca + mrg[u - 1][2 + t][i][l] * cb;
+        m[i] = mn;
+      }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -209,14 +247,16 @@ __global__ __launch_bounds__(256) void attn_bwd_d_k(const T* __restrict__ dout, 
 
 // dQ of 32 query rows: over key tiles, P = exp(alpha S - L), dP = dO V^T,
 // dS = P (dP - D), dQ += alpha dS K.
-template <typename T, int DH>
-__global__ __launch_bounds__(WAVE) void attn_bwd_dq_k(const T* __restrict__ q, const T* __restrict__ k,
-                                                      const T* __restrict__ v, const T* __restrict__ dout,
-                                                      const float* __restrict__ lse, const float* __restrict__ dd,
-                                                      T* __restrict__ dq, int acc_dq, Geo g, float alpha,
-                                                      int causal) {
-  __shared__ float tile[32 * 33];
-  const int l = threadIdx.x;
+template <typename T, int DH, int KW>
+__global__ __launch_bounds__(WAVE * KW) void attn_bwd_dq_k(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ v, const T* __restrict__ dout,
+                                                           const float* __restrict__ lse, const float* __restrict__ dd,
+                                                           T* __restrict__ dq, int acc_dq, Geo g, float alpha,
+                                                           int causal) {
+  __shared__ float tiles[KW][32 * 33];
+  __shared__ float mrg[KW > 1 ? KW - 1 : 1][DH / 32][16][WAVE];
+  const int l = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+  float* tile = tiles[w];
   const int64_t q0 = (int64_t)blockIdx.x * 32, hd = blockIdx.y, b = blockIdx.z;
   float qf[DH / 2], df[DH / 2];
   frag_dh<T, DH>(q, g, b, hd, q0, l, qf);
@@ -234,7 +274,7 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dq_k(const T* __restrict__ q, c
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
   const int64_t kend = causal ? (q0 + 32 < g.S ? q0 + 32 : g.S) : g.S;
-  for (int64_t k0 = 0; k0 < kend; k0 += 32) {
+  for (int64_t k0 = (int64_t)w * 32; k0 < kend; k0 += 32 * KW) {
     float kf[DH / 2], vf[DH / 2];
     frag_dh<T, DH>(k, g, b, hd, k0, l, kf);
     frag_dh<T, DH>(v, g, b, hd, k0, l, vf);
@@ -253,6 +293,21 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dq_k(const T* __restrict__ q, c
     c_to_a(ds, tile, l, da);
     mul_rows<T, DH>(da, k, g, b, hd, k0, l, acc);
   }
+  if constexpr (KW > 1) {
+    if (w > 0) {
+#pragma unroll
+      for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mrg[w - 1][t][i][l] = acc[t][i];
+    }
+    __syncthreads();
+    if (w > 0) return;
+    for (int u = 1; u < KW; ++u)
+#pragma unroll
+      for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] += mrg[u - 1][t][i][l];
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t qr = q0 + crow(i, l);
@@ -270,14 +325,16 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dq_k(const T* __restrict__ q, c
 // dK, dV of 32 key rows: over query tiles, with rows = keys:
 // P^T = exp(alpha K Q^T - L), dV += P^T dO, dP^T = V dO^T,
 // dS^T = P^T (dP^T - D), dK += alpha dS^T Q.
-template <typename T, int DH>
-__global__ __launch_bounds__(WAVE) void attn_bwd_dkv_k(const T* __restrict__ q, const T* __restrict__ k,
-                                                       const T* __restrict__ v, const T* __restrict__ dout,
-                                                       const float* __restrict__ lse, const float* __restrict__ dd,
-                                                       T* __restrict__ dk, int acc_dk, T* __restrict__ dv,
-                                                       int acc_dv, Geo g, float alpha, int causal) {
-  __shared__ float tile[32 * 33];
-  const int l = threadIdx.x;
+template <typename T, int DH, int KW>
+__global__ __launch_bounds__(WAVE * KW) void attn_bwd_dkv_k(const T* __restrict__ q, const T* __restrict__ k,
+                                                            const T* __restrict__ v, const T* __restrict__ dout,
+                                                            const float* __restrict__ lse, const float* __restrict__ dd,
+                                                            T* __restrict__ dk, int acc_dk, T* __restrict__ dv,
+                                                            int acc_dv, Geo g, float alpha, int causal) {
+  __shared__ float tiles[KW][32 * 33];
+  __shared__ float mrg[KW > 1 ? KW - 1 : 1][2 * (DH / 32)][16][WAVE];
+  const int l = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+  float* tile = tiles[w];
   const int64_t k0 = (int64_t)blockIdx.x * 32, hd = blockIdx.y, b = blockIdx.z;
   float kf[DH / 2], vf[DH / 2];
   frag_dh<T, DH>(k, g, b, hd, k0, l, kf);
@@ -287,7 +344,7 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dkv_k(const T* __restrict__ q, 
   for (int t = 0; t < DH / 32; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { ak[t][i] = 0.f; av[t][i] = 0.f; }
-  for (int64_t q0 = causal ? k0 : 0; q0 < g.S; q0 += 32) {
+  for (int64_t q0 = (causal ? k0 : 0) + (int64_t)w * 32; q0 < g.S; q0 += 32 * KW) {
     float qf[DH / 2], df[DH / 2];
     frag_dh<T, DH>(q, g, b, hd, q0, l, qf);
     frag_dh<T, DH>(dout, g, b, hd, q0, l, df);
@@ -309,6 +366,27 @@ __global__ __launch_bounds__(WAVE) void attn_bwd_dkv_k(const T* __restrict__ q, 
     mul_rows<T, DH>(pa, dout, g, b, hd, q0, l, av);
     c_to_a(dst, tile, l, sa);
     mul_rows<T, DH>(sa, q, g, b, hd, q0, l, ak);
+  }
+  if constexpr (KW > 1) {
+    if (w > 0) {
+#pragma unroll
+      for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          mrg[w - 1][t][i][l] = ak[t][i];
+          mrg[w - 1][DH / 32 + t][i][l] = av[t][i];
+        }
+    }
+    __syncthreads();
+    if (w > 0) return;
+    for (int u = 1; u < KW; ++u)
+#pragma unroll
+      for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          ak[t][i] += mrg[u - 1][t][i][l];
+          av[t][i] += mrg[u - 1][DH / 32 + t][i][l];
+        }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -982,7 +1060,7 @@ template <typename T, int DH>
 hipError_t fwd_dh(const AttnArgs& a, hipStream_t s) {
   const Geo g{a.S, a.H, a.ld, a.ldl};
   const dim3 grid((unsigned)((a.S + 31) / 32), (unsigned)a.H, (unsigned)a.B);
-  attn_fwd_k<T, DH><<<grid, WAVE, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, g,
+  attn_fwd_k<T, DH, AKW><<<grid, WAVE * AKW, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, g,
                                           a.alpha, a.causal);
   return hipGetLastError();
 }
@@ -997,13 +1075,13 @@ hipError_t bwd_dh(const AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.S + 31) / 32), (unsigned)a.H, (unsigned)a.B);
   if (a.dq) {
-    attn_bwd_dq_k<T, DH><<<grid, WAVE, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+    attn_bwd_dq_k<T, DH, AKW><<<grid, WAVE * AKW, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                                                a.lse, a.dd, (T*)a.dq, a.acc_dq, g, a.alpha, a.causal);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.dk || a.dv) {
-    attn_bwd_dkv_k<T, DH><<<grid, WAVE, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+    attn_bwd_dkv_k<T, DH, AKW><<<grid, WAVE * AKW, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                                                 a.lse, a.dd, (T*)a.dk, a.acc_dk, (T*)a.dv, a.acc_dv, g, a.alpha,
                                                 a.causal);
     e = hipGetLastError();
