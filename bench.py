@@ -68,9 +68,9 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # measured on: the fingerprint of those files is checked at run time and the
 # figure is dropped (traffic = null) once they have changed.
 MEASURED_TRAFFIC = {
-    "c5.ce.bwd": {"bytes": 16817462997, "sources": ["autograd_row_wise_amd/csrc/ce.hip",
+    "c5.ce.bwd": {"bytes": 16817274163, "sources": ["autograd_row_wise_amd/csrc/ce.hip",
                                                     "autograd_row_wise_amd/csrc/common.h"],
-                  "sha256_16": "0cbd8a05f92b83ee", "profile": "profiles/ce_bwd_bf16_32768x128256.md"},
+                  "sha256_16": "648fd5858341e740", "profile": "profiles/ce_bwd_bf16_32768x128256.md"},
 }
 
 
@@ -936,6 +936,39 @@ def time_step_graph(entries, stream, steps, warmup):
     return (t1 - t0) * 1e3 / max(steps, 1)
 
 
+def copy_floor(ops_out, steps, warmup, below=0.72):
+    """For every memory-bound op of the step under `below` of the HBM peak:
+    the same algorithmic bytes moved by a plain streaming kernel (the
+    library's SCALE by 1: one 16-byte load and one store per pack, nothing
+    else), on f32 rows of the op's width, timed the same way as the op (a
+    graph of repeated launches over independent buffer copies).  At these
+    sizes a launch's ramp-up and drain are a large part of its time; the
+    copy's fraction is the floor such a launch reaches."""
+    import torch
+    import autograd_row_wise_amd as xt
+    picked = [o for o in ops_out if "GBps" in o and o["frac"] < below]
+    res = []
+    for o in picked:
+        n = o["bytes"] // 8                                  # f32 elements read (and as many written)
+        cols = 768 if n % 768 == 0 else 4096 if n % 4096 == 0 else 1
+        rows = n // cols
+        k = min(MAX_COPIES, max(1, -(-ROTATE_BYTES // o["bytes"])))
+        bufs = [(torch.ones((rows, cols), dtype=torch.float32, device="cuda"),
+                 torch.empty((rows, cols), dtype=torch.float32, device="cuda")) for _ in range(k)]
+        prm = xt.params(alpha=1.0)
+        e = Entry("floor." + o["op"], "copy of the same bytes", "f32", "hbm",
+                  lambda a=bufs[0]: xt.xt_op_fwd(xt.OP.SCALE, prm, [xt.view(a[0])], [xt.view(a[1])]), 8 * n, rows=rows)
+        e.fns = [(lambda a=a: xt.xt_op_fwd(xt.OP.SCALE, prm, [xt.view(a[0])], [xt.view(a[1])])) for a in bufs]
+        time_graphs([e], torch.cuda.current_stream(), steps, warmup)
+        ms = med(e.times_ms)
+        gbps = e.bytes / (ms * 1e-3) / 1e9
+        res.append({"op": o["op"], "op_frac": o["frac"], "bytes": e.bytes, "copy_ms": round(ms, 5),
+                    "copy_GBps": round(gbps, 1), "copy_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                    "op_vs_copy": round(o["GBps"] / gbps, 4)})
+        del bufs
+    return res
+
+
 def med(xs):
     """Median of the timed repetitions (robust to a stray slow launch)."""
     v = sorted(xs)
@@ -1057,6 +1090,10 @@ def main():
                                     "1 GiB per activation tensor", "entries": long_rows(args.steps, args.warmup)}
     if not args.only:
         out["c1_latency"] = c1_latency(args.steps, args.warmup)
+    if not args.only or "floor" in args.only:
+        out["copy_floor"] = {"what": "each memory-bound op under 72% of HBM peak beside a plain streaming copy "
+                                     "(SCALE by 1, f32) of the same algorithmic bytes, timed the same way",
+                             "entries": copy_floor(ops_out, args.steps, args.warmup)}
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline()
