@@ -827,6 +827,12 @@ RowPlan plan_rows(RowKind kind, int dtype, int64_t R, int64_t C, bool aligned) {
     // backward folds parameter partials in LDS: keep them within 64 KiB
     const int np = kind == RK_LN_BWD ? 2 : 1;
     if (is_bwd(kind) && (int64_t)np * C * 4 > 65536) p.fast = false;
+    // f32 rms_norm rows past 8192 columns: the register-row forward of
+    // rowstream.hip (one row per 1024-thread block, two blocks per CU) is
+    // faster than a multi-wave row group here (16384 columns, 1 GiB:
+    // 410 -> 381 us); the layer_norm forward does not fit its registers
+    // (426 vs 394 us) and keeps this kernel
+    if (kind == RK_RMS_FWD && dtype == XT_F32 && C > 8192) p.fast = false;
   }
   if (p.fast) {
     p.groups = p.block / (WAVE * p.rw);
