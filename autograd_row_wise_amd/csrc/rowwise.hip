@@ -716,18 +716,39 @@ __global__ __launch_bounds__(1024) void colsum_partials(
   for (int k = 0; k < V; ++k) a[k] = 0.f;
   if (c0 < C) {
     int64_t r = (int64_t)blockIdx.y * nph + ph;
-    // eight rows' packs in flight per thread, added in row order
+    // eight rows' packs per group, added in row order; the next group's
+    // loads are issued before the current group is added, so a thread
+    // always has a group in flight
     constexpr int U = 8;
-    for (; r + (U - 1) * rstep < end; r += U * rstep) {
-      uint4 q[U];
+    auto load8 = [&](uint4 (&q)[U], int64_t r0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) q[u] = load_raw<T>(row_ptr<T>(d, r + u * rstep, ldd), c0, C);
+      for (int u = 0; u < U; ++u) q[u] = load_raw<T>(row_ptr<T>(d, r0 + u * rstep, ldd), c0, C);
+    };
+    auto add8 = [&](const uint4 (&q)[U]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float v[V];
         io<T>::unpack(q[u], v);
 #pragma unroll
         for (int k = 0; k < V; ++k) a[k] += v[k];
+      }
+    };
+    if (r + (U - 1) * rstep < end) {
+      uint4 qa[U], qb[U];
+      load8(qa, r);
+      for (;;) {
+        const int64_t r2 = r + U * rstep;
+        const bool m2 = r2 + (U - 1) * rstep < end;
+        if (m2) load8(qb, r2);
+        add8(qa);
+        r = r2;
+        if (!m2) break;
+        const int64_t r3 = r + U * rstep;
+        const bool m3 = r3 + (U - 1) * rstep < end;
+        if (m3) load8(qa, r3);
+        add8(qb);
+        r = r3;
+        if (!m3) break;
       }
     }
     for (; r < end; r += rstep) {
