@@ -725,45 +725,68 @@ __device__ __forceinline__ void store_pack_acc_full(T* p, float* o, bool acc) {
   st_nt(p, io<T>::pack(o));
 }
 
+// softmax backward on register rows: d and y of a row read once (thread t:
+// packs t + 1024 k, at most one head and one tail element each), the dot
+// product and dx from the registers.  Addresses are a row-uniform base per
+// pack slot plus one 32-bit lane offset (rows of at most 65536 elements).
+// Up to 4 packs per thread the kernel is held to 64 registers, so two rows
+// share a CU.
 template <typename T, int NPR>
-__global__ __launch_bounds__(ST) void sm_bwd_reg(const void* __restrict__ d, int64_t ldd, const void* __restrict__ y,
-                                                 int64_t ldy, void* __restrict__ dx, int64_t lddx, int acc, int64_t R,
-                                                 int64_t C, float alpha) {
+__global__ __launch_bounds__(ST, NPR <= 4 ? 8 : 1) void sm_bwd_reg(const void* __restrict__ d, int64_t ldd,
+                                                                  const void* __restrict__ y, int64_t ldy,
+                                                                  void* __restrict__ dx, int64_t lddx, int acc,
+                                                                  int64_t R, int64_t C, float alpha) {
   constexpr int V = io<T>::VEC;
   __shared__ float lds[4 * SW];
   int ph = 0;
+  const int tid = threadIdx.x, lo = tid * V, Ci = (int)C;
   for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
     const T* dr = crow<T>(d, r, ldd);
     const T* yr = crow<T>(y, r, ldy);
     T* xr = wrow<T>(dx, r, lddx);
     const Split sp = split_of<T>(dr, C);
-    const T* src[2] = {dr, yr};
-    RegRow<T, 2, NPR> rr;
-    rr.load(src, sp, C);
-    float dot = rr.h[0] * rr.h[1] + rr.t[0] * rr.t[1];
+    const int head = (int)sp.head, packs = (int)sp.packs;
+    const T* db = dr + head;
+    const T* yb = yr + head;
+    uint4 qd[NPR], qy[NPR];
 #pragma unroll
     for (int k = 0; k < NPR; ++k) {
-      if (!rr.has(sp, k)) continue;
+      const bool ok = tid + k * ST < packs;
+      qd[k] = ok ? ld_nt(db + k * ST * V + lo) : make_uint4(0, 0, 0, 0);
+      qy[k] = ok ? ld_nt(yb + k * ST * V + lo) : make_uint4(0, 0, 0, 0);
+    }
+    const bool hv = tid < head;
+    const int tc = head + packs * V + tid;
+    const bool tv = tc < Ci;
+    const float hd = hv ? io<T>::ld(dr + tid) : 0.f, hy = hv ? io<T>::ld(yr + tid) : 0.f;
+    const float td = tv ? io<T>::ld(dr + tc) : 0.f, ty = tv ? io<T>::ld(yr + tc) : 0.f;
+    float dot = hd * hy + td * ty;
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) {
       float a[V], b[V];
-      io<T>::unpack(rr.q[k][0], a);
-      io<T>::unpack(rr.q[k][1], b);
+      io<T>::unpack(qd[k], a);
+      io<T>::unpack(qy[k], b);
 #pragma unroll
       for (int e = 0; e < V; ++e) dot += a[e] * b[e];
     }
     dot = group_sum<SW>(dot, lds, ph);
-    rr.pin();
+    // only the raw packs stay live across the reduction (as RegRow::pin)
+#pragma unroll
+    for (int k = 0; k < NPR; ++k) asm volatile("" : "+v"(qd[k].x), "+v"(qd[k].y), "+v"(qd[k].z), "+v"(qd[k].w),
+                                                    "+v"(qy[k].x), "+v"(qy[k].y), "+v"(qy[k].z), "+v"(qy[k].w));
+    T* xb = xr + head;
 #pragma unroll
     for (int k = 0; k < NPR; ++k) {
-      if (!rr.has(sp, k)) continue;
+      if (tid + k * ST >= packs) continue;
       float a[V], b[V], o[V];
-      io<T>::unpack(rr.q[k][0], a);
-      io<T>::unpack(rr.q[k][1], b);
+      io<T>::unpack(qd[k], a);
+      io<T>::unpack(qy[k], b);
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = alpha * b[e] * (a[e] - dot);
-      store_pack_acc_full<T>(xr + rr.col(sp, k), o, acc != 0);
+      store_pack_acc_full<T>(xb + k * ST * V + lo, o, acc != 0);
     }
-    if (rr.hv) store_acc1<T>(xr + threadIdx.x, alpha * rr.h[1] * (rr.h[0] - dot), acc != 0);
-    if (rr.tv) store_acc1<T>(xr + rr.tc, alpha * rr.t[1] * (rr.t[0] - dot), acc != 0);
+    if (hv) store_acc1<T>(xr + tid, alpha * hy * (hd - dot), acc != 0);
+    if (tv) store_acc1<T>(xr + tc, alpha * ty * (td - dot), acc != 0);
   }
 }
 
