@@ -24,6 +24,9 @@ ARCH = os.environ.get("XT_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
+# Per-source additions.  attention.hip: matrix-core accumulators in ordinary
+# VGPRs, so the softmax of a score tile reads them without AGPR copies.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:
@@ -34,7 +37,7 @@ def _hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *FLAGS]
+    cmd = [_hipcc(), *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", src, "-o", obj]

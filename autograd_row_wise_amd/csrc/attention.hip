@@ -481,14 +481,33 @@ __device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* tile, int r0, int col0
 struct Split8 {
   bf16x8_t hi, lo;
 };
-__device__ __forceinline__ Split8 split8(const f32x16_t& c, int m) {
+// x - hi is formed as a two-term bf16 dot product of the packed hi pair
+// with (-1, 0) or (0, -1), accumulated onto x: one instruction per element,
+// exact like the subtraction (both products are exact and the sum is an f32
+// value).  With sum given, the hi and lo parts are added to it pairwise by
+// the same dot product with (1, 1): the row sum of exactly the operand
+// values that enter the product.
+// The three packed constants are passed in scalar registers: the compiler
+// would encode the pair (-1, 0) as the inline constant -1.0, which the
+// instruction does not read as that bf16 pair.
+__device__ __forceinline__ Split8 split8(const f32x16_t& c, int m, float* sum = nullptr) {
+  uint32_t kl = 0x0000BF80u, kh = 0xBF800000u, k1 = 0x3F803F80u;
+  asm("" : "+s"(kl), "+s"(kh), "+s"(k1));
+  const bf16x2_t neg_lo = __builtin_bit_cast(bf16x2_t, kl), neg_hi = __builtin_bit_cast(bf16x2_t, kh);
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, k1);
   uint32_t h[4], r[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float a = c[8 * m + 2 * q], b = c[8 * m + 2 * q + 1];
     const uint32_t u = f2bf2(a, b);
     h[q] = u;
-    r[q] = f2bf2(a - __uint_as_float(u << 16), b - __uint_as_float(u & 0xffff0000u));
+    const bf16x2_t hp = __builtin_bit_cast(bf16x2_t, u);
+    r[q] = f2bf2(__builtin_amdgcn_fdot2_f32_bf16(hp, neg_lo, a, false),
+                 __builtin_amdgcn_fdot2_f32_bf16(hp, neg_hi, b, false));
+    if (sum) {
+      *sum = __builtin_amdgcn_fdot2_f32_bf16(hp, ones, *sum, false);
+      *sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r[q]), ones, *sum, false);
+    }
   }
   const u32x4_t uh = {h[0], h[1], h[2], h[3]}, ur = {r[0], r[1], r[2], r[3]};
   return Split8{__builtin_bit_cast(bf16x8_t, uh), __builtin_bit_cast(bf16x8_t, ur)};
@@ -525,20 +544,39 @@ __device__ __forceinline__ void row_frags(const bf16_t* x, const Geo& g, int64_t
 }
 
 // Staging of an R-row tile of two tensors (rows clamped to the sequence):
-// thread t moves 16-byte chunks t, t + 256, ...
+// thread t moves 16-byte chunks t, t + 256, ...  Addresses are a
+// tile-uniform base (row r0) plus 32-bit lane offsets (R ld < 2^31 elements,
+// which fa_aligned guarantees), fixed for every tile that lies inside the
+// sequence; only a tile that reaches past its end clamps rows per lane.
 template <int DH, int R>
 struct Stage2 {
   static constexpr int CPR = DH / 8, NC = R * CPR, N = (NC + fa::NT - 1) / fa::NT;   // chunks per row, tile, thread
   u32x4_t a[N], b[N];
   __device__ __forceinline__ void load(const bf16_t* xa, const bf16_t* xb, const Geo& g, int64_t base, int64_t r0,
                                        int tid) {
+    const bf16_t* pa = xa + base + r0 * g.ld;
+    const bf16_t* pb = xb + base + r0 * g.ld;
+    const int ld = (int)g.ld;
+    if (r0 + R <= g.S) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + fa::NT * i, row = c / CPR, col = c % CPR;
-      if (NC % fa::NT == 0 || c < NC) {
-        const int64_t r = r0 + row < g.S ? r0 + row : g.S - 1;
-        a[i] = *reinterpret_cast<const u32x4_t*>(xa + base + r * g.ld + col * 8);
-        b[i] = *reinterpret_cast<const u32x4_t*>(xb + base + r * g.ld + col * 8);
+      for (int i = 0; i < N; ++i) {
+        const int c = tid + fa::NT * i, row = c / CPR, col = c % CPR;
+        if (NC % fa::NT == 0 || c < NC) {
+          const uint32_t off = (uint32_t)(row * ld + col * 8);
+          a[i] = *reinterpret_cast<const u32x4_t*>(pa + off);
+          b[i] = *reinterpret_cast<const u32x4_t*>(pb + off);
+        }
+      }
+    } else {
+      const int last = (int)(g.S - 1 - r0);   // < R - 1 here
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int c = tid + fa::NT * i, row = c / CPR, col = c % CPR;
+        if (NC % fa::NT == 0 || c < NC) {
+          const uint32_t off = (uint32_t)((row < last ? row : last) * ld + col * 8);
+          a[i] = *reinterpret_cast<const u32x4_t*>(pa + off);
+          b[i] = *reinterpret_cast<const u32x4_t*>(pb + off);
+        }
       }
     }
   }
@@ -612,24 +650,29 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
     const bf16_t* Kt = lds + (j & 1) * ST;
     const bf16_t* Vt = Kt + KT;
     {
+      // the two 32-key halves' products alternate: consecutive MFMAs are
+      // independent
       f32x16_t s[2];
+      zero(s[0]);
+      zero(s[1]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        zero(s[t]);
-#pragma unroll
-        for (int kk = 0; kk < DH / 16; ++kk) s[t] = mfma16(lds8(Kt + (32 * t + c) * KS + 16 * kk + 8 * h), qf[kk], s[t]);
+      for (int kk = 0; kk < DH / 16; ++kk) {
+        const bf16x8_t k0f = lds8(Kt + c * KS + 16 * kk + 8 * h), k1f = lds8(Kt + (32 + c) * KS + 16 * kk + 8 * h);
+        s[0] = mfma16(k0f, qf[kk], s[0]);
+        s[1] = mfma16(k1f, qf[kk], s[1]);
       }
       // Row maximum of the raw scores (alpha > 0, so the order is that of
       // alpha S); masked keys become -inf.
       const bool edge = k0 + BK > g.S || (causal && k0 + BK - 1 > qw);
       float mx = -INFINITY;
       if (edge) {                       // keys past klim are masked
-        const int kl = klim - (int)k0;
+        // arow(i, h) = arow(i, 0) + 4 h: compare immediates with a shifted limit
+        const int kl = klim - (int)k0 - 4 * h;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            s[t][i] = 32 * t + arow(i, h) <= kl ? s[t][i] : -INFINITY;
+            s[t][i] = 32 * t + arow(i, 0) <= kl ? s[t][i] : -INFINITY;
             mx = fmaxf(mx, s[t][i]);
           }
       } else {
@@ -655,22 +698,19 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_fwd_k(const bf16_t* __restrict__
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], sl, -m));
-          s[t][i] = p;
-          ls += p;
-        }
+        for (int i = 0; i < 16; ++i) s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], sl, -m));
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const Split8 pf = split8(s[t], mm);
+          const Split8 pf = split8(s[t], mm, &ls);
+          bf16x8_t vf[DH / 32];
 #pragma unroll
-          for (int bb = 0; bb < DH / 32; ++bb) {
-            const bf16x8_t vf = tr_frag<VS>(Vt, 32 * t + 16 * mm, 32 * bb, l);
-            o[bb] = mfma16(vf, pf.lo, o[bb]);
-            o[bb] = mfma16(vf, pf.hi, o[bb]);
-          }
+          for (int bb = 0; bb < DH / 32; ++bb) vf[bb] = tr_frag<VS>(Vt, 32 * t + 16 * mm, 32 * bb, l);
+#pragma unroll
+          for (int bb = 0; bb < DH / 32; ++bb) o[bb] = mfma16(vf[bb], pf.lo, o[bb]);
+#pragma unroll
+          for (int bb = 0; bb < DH / 32; ++bb) o[bb] = mfma16(vf[bb], pf.hi, o[bb]);
         }
     }
     stage_next(j);
@@ -781,10 +821,10 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
       }
       const bool edge = k0 + BK > g.S || (causal && k0 + BK - 1 > qw);
       if (edge) {
-        const int kl = klim - (int)k0;
+        const int kl = klim - (int)k0 - 4 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = arow(i, h) <= kl ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -L2)) : 0.f;
+          const float p = arow(i, 0) <= kl ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -L2)) : 0.f;
           s[i] = p * (dp[i] - Dq);
         }
       } else {
@@ -794,12 +834,13 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const Split8 sf = split8(s, mm);
+        bf16x8_t kf[DH / 32];
 #pragma unroll
-        for (int bb = 0; bb < DH / 32; ++bb) {
-          const bf16x8_t kf = tr_frag<KS>(Kt, 16 * mm, 32 * bb, l);
-          acc[bb] = mfma16(kf, sf.lo, acc[bb]);
-          acc[bb] = mfma16(kf, sf.hi, acc[bb]);
-        }
+        for (int bb = 0; bb < DH / 32; ++bb) kf[bb] = tr_frag<KS>(Kt, 16 * mm, 32 * bb, l);
+#pragma unroll
+        for (int bb = 0; bb < DH / 32; ++bb) acc[bb] = mfma16(kf[bb], sf.lo, acc[bb]);
+#pragma unroll
+        for (int bb = 0; bb < DH / 32; ++bb) acc[bb] = mfma16(kf[bb], sf.hi, acc[bb]);
       }
     }
     stage_next(j);
@@ -943,11 +984,11 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
       }
       if (edge) {
         // visible rows of the tile: qlo .. qhi (none for a key past the sequence)
-        const int qlo = causal ? (int)(kme - q0) : 0;
-        const int qhi = kok ? (int)(g.S - 1 - q0) : -1;
+        const int qlo = (causal ? (int)(kme - q0) : 0) - 4 * h;
+        const int qhi = (kok ? (int)(g.S - 1 - q0) : -1) - 4 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = arow(i, h);
+          const int r = arow(i, 0);
           const float p = r >= qlo && r <= qhi ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -Lv[i])) : 0.f;
           s[i] = p;
           dp[i] = p * (dp[i] - Dv[i]);
@@ -967,8 +1008,8 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
         for (int bb = 0; bb < DH / 32; ++bb) {
           const bf16x8_t df = tr_frag<QS>(Dt, 16 * mm, 32 * bb, l), qf = tr_frag<QS>(Qt, 16 * mm, 32 * bb, l);
           av[bb] = mfma16(pf.lo, df, av[bb]);
-          av[bb] = mfma16(pf.hi, df, av[bb]);
           ak[bb] = mfma16(sf.lo, qf, ak[bb]);
+          av[bb] = mfma16(pf.hi, df, av[bb]);
           ak[bb] = mfma16(sf.hi, qf, ak[bb]);
         }
       }
@@ -1050,6 +1091,7 @@ hipError_t fa_bwd(const AttnArgs& a, hipStream_t s) {
 // row stride that keeps rows aligned; and they take alpha > 0.
 bool fa_aligned(const AttnArgs& a) {
   if (a.ld % 8 || !(a.alpha > 0.f)) return false;   // the forward orders scores by the raw products
+  if (a.ld >= (int64_t)1 << 23) return false;        // tile offsets are 32-bit (128 rows of ld elements)
   const void* p[] = {a.q, a.k, a.v, a.out, a.dout, a.dq, a.dk, a.dv};
   for (const void* x : p)
     if (x && ((uintptr_t)x & 15u)) return false;
