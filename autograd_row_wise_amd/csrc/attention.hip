@@ -896,14 +896,14 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ dd,
                                                       bf16_t* __restrict__ dk, int acc_dk, bf16_t* __restrict__ dv,
-                                                      int acc_dv, Geo g, float alpha, int causal, int nkb) {
+                                                      int acc_dv, Geo g, float alpha, int causal, int nkb, int pair) {
   constexpr int BQ = 32, QS = fa::RS<DH>, QT = BQ * QS, ST = 2 * QT + 4 * BQ;   // + L2 and D: 2 BQ f32
   constexpr int KV = 128 * QS;                        // the block's K (then V) rows
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST + 2 * KV];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
-  int kb;
   int64_t hb;
-  fa_block(nkb, causal ? -1 : 0, kb, hb);
+  // one key block of (sequence, head) hb
+  auto run = [&](int kb) {
   const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
   const int64_t k0 = (int64_t)kb * 128, kw = k0 + 32 * w, kme = kw + c;
   const bool kok = kme < g.S;
@@ -1035,6 +1035,22 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
       }
     }
   }
+  };
+  if (pair) {
+    // causal pairs: the heaviest key block of the pair (the first keys see
+    // every query), then the lightest, so every block carries the same work
+    const int np = (nkb + 1) / 2, HB = gridDim.x / np, r = blockIdx.x / HB;
+    hb = blockIdx.x % HB;
+    run(r);
+    if (r != nkb - 1 - r) {
+      __syncthreads();
+      run(nkb - 1 - r);
+    }
+  } else {
+    int kb;
+    fa_block(nkb, causal ? -1 : 0, kb, hb);
+    run(kb);
+  }
 }
 
 // Compute units of the current device (0 if unknown).
@@ -1081,9 +1097,15 @@ hipError_t fa_bwd(const AttnArgs& a, hipStream_t s) {
                                     a.acc_dq, g, a.alpha, a.causal, nb, pair);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (!a.dk && !a.dv)) return e;
-  fa_dkv_k<DH><<<grid, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
-                                       (const bf16_t*)a.dout, a.lse, a.dd, (bf16_t*)a.dk, a.acc_dk, (bf16_t*)a.dv,
-                                       a.acc_dv, g, a.alpha, a.causal, nb);
+  // dK / dV run one block per CU: key blocks pair up once the pairs alone
+  // fill every CU
+  const int cus = device_cus();
+  const int64_t npair = (int64_t)((nb + 1) / 2) * a.H * a.B;
+  const int kpair = a.causal && nb > 1 && cus > 0 && npair >= (int64_t)cus ? 1 : 0;
+  const unsigned gk = kpair ? (unsigned)npair : grid;
+  fa_dkv_k<DH><<<gk, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+                                     (const bf16_t*)a.dout, a.lse, a.dd, (bf16_t*)a.dk, a.acc_dk, (bf16_t*)a.dv,
+                                     a.acc_dv, g, a.alpha, a.causal, nb, kpair);
   return hipGetLastError();
 }
 

@@ -196,9 +196,11 @@ def test_attention_bf16_unaligned_rows():
 
 
 def test_attention_bench_shape_two_heads():
-    """The 2 x 2048 tokens, 16 heads x 128, causal, bf16 workload run whole;
-    heads (sequence 0, head 3) and (sequence 1, head 12) checked in full
-    against the oracle on those heads alone."""
+    """The 2 x 2048 tokens, 16 heads x 128, causal, bf16 workload run whole
+    (its 256 (heaviest, lightest) pairs of 128-key blocks fill a 256-CU
+    MI355X, so the dK / dV pass runs its paired grid); heads (sequence 0,
+    head 3) and (sequence 1, head 12) checked in full against the oracle on
+    those heads alone."""
     B, S, H, Dh = 2, 2048, 16, 128
     R, C = B * S, H * Dh
     alpha = 1.0 / math.sqrt(Dh)
@@ -224,7 +226,7 @@ def test_attention_bench_shape_two_heads():
 def test_attention_causal_paired_query_blocks():
     """2 x 4096 tokens, 16 heads x 128, causal, bf16: 512 (heaviest,
     lightest) pairs of 128-query blocks, two per CU on a 256-CU MI355X, so
-    the forward and the dQ pass run their paired grids.  Heads (sequence 0,
+    the forward, the dQ pass and the dK / dV pass run their paired grids.  Heads (sequence 0,
     head 5) and (sequence 1, head 14) checked in full against the oracle:
     output, log-sum-exp and the three gradients."""
     B, S, H, Dh = 2, 4096, 16, 128
