@@ -700,6 +700,148 @@ __global__ __launch_bounds__(b8::NT) void gemm_k64_k(
       }
 }
 
+// ==========================================================================
+// Small f32 products (at most 256 tiles of 64 x 64 of C): one block of 16
+// waves per tile, in four groups of four.  Group q sums k over its quarter
+// of K (whole 16-deep K tiles) into its own 2 x 2 waves of 32 x 32
+// accumulators, through its own double-buffered LDS tiles, with the next
+// SK_PD K tiles of its quarter already requested into registers; the four
+// partial tiles are then added in group order (fixed: bitwise reproducible)
+// and written once.  A 1024 x 256 x 256 product then runs 16-deep MFMA
+// chains of 64 in k per wave instead of 256, with four K tiles of loads in
+// flight instead of one.
+// ==========================================================================
+namespace sk {
+constexpr int G = 4, GT = NT, NTB = G * GT, TB = 64, BK = 16, LDK = BK + 4, PD = 4;
+}
+
+// One thread's 16-byte share of a 64 x 16 f32 operand tile (256 threads of
+// a group): k-contiguous storage ([rows][K]) moves rows t / 4, k (t % 4) * 4;
+// transposed storage ([K][rows]) moves k row t / 16, rows (t % 16) * 4.
+template <bool KCONTIG>
+__device__ __forceinline__ uint4 sk_load(const float* g, int64_t ld, int64_t row0, int64_t rows_total, int64_t k0,
+                                         int64_t kend, bool full, int t) {
+  const int row = KCONTIG ? t / 4 : (t % 16) * 4, kk = KCONTIG ? (t % 4) * 4 : t / 16;
+  const int64_t gr = row0 + row, gk = k0 + kk;
+  if (full) return *reinterpret_cast<const uint4*>(KCONTIG ? g + gr * ld + gk : g + gk * ld + gr);
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t rr = KCONTIG ? gr : gr + j, kq = KCONTIG ? gk + j : gk;
+    v[j] = (rr < rows_total && kq < kend) ? g[KCONTIG ? rr * ld + kq : kq * ld + rr] : 0.f;
+  }
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+
+template <bool KCONTIG>
+__device__ __forceinline__ void sk_store(float* lds, uint4 r, int t) {
+  if constexpr (KCONTIG) {
+    *reinterpret_cast<uint4*>(lds + (t / 4) * sk::LDK + (t % 4) * 4) = r;
+  } else {
+    const int kk = t / 16, row = (t % 16) * 4;
+    lds[(row + 0) * sk::LDK + kk] = __uint_as_float(r.x);
+    lds[(row + 1) * sk::LDK + kk] = __uint_as_float(r.y);
+    lds[(row + 2) * sk::LDK + kk] = __uint_as_float(r.z);
+    lds[(row + 3) * sk::LDK + kk] = __uint_as_float(r.w);
+  }
+}
+
+template <typename TC, bool TRANS_A, bool TRANS_B>
+__global__ __launch_bounds__(sk::NTB) void gemm_sk_k(
+    const float* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
+    const float* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
+    TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
+    int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
+    int64_t kchunk, int64_t nbatch, int64_t scs) {
+  constexpr int TB = sk::TB, BK = sk::BK, LDK = sk::LDK, PD = sk::PD;
+  __shared__ __align__(16) float lds[sk::G][2][2][TB * LDK];   // [group][stage][A, B]
+
+  const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
+  const int64_t kb = split * kchunk;
+  A += b0 * sa0 + b1 * sa1 + (TRANS_A ? kb * lda : kb);
+  B += b0 * sb0 + b1 * sb1 + (TRANS_B ? kb : kb * ldb);
+  C += b0 * sc0 + b1 * sc1 + split * scs;
+  K = K - kb < kchunk ? K - kb : kchunk;
+  const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const int q = w / 4, t = threadIdx.x % sk::GT;               // group, thread within the group
+  const int wm = ((w % 4) / 2) * 32, wn = (w % 2) * 32;
+  // this group's k range: whole 16-deep tiles, quarters as equal as they come
+  const int64_t ntk = (K + BK - 1) / BK, per = (ntk + sk::G - 1) / sk::G;
+  const int64_t kt0 = q * per, kt1 = kt0 + per < ntk ? kt0 + per : ntk;
+  const int nkt = kt1 > kt0 ? (int)(kt1 - kt0) : 0;
+  const bool fullMN = (m0 + TB <= M) && (n0 + TB <= N);
+  const bool alA = (((uintptr_t)A) & 15) == 0 && ((lda * 4) & 15) == 0;
+  const bool alB = (((uintptr_t)B) & 15) == 0 && ((ldb * 4) & 15) == 0;
+  auto fetch = [&](int i, uint4& ra, uint4& rb) {
+    const int64_t k0 = (kt0 + i) * BK;
+    const bool full = fullMN && alA && alB && k0 + BK <= K;
+    ra = sk_load<!TRANS_A>(A, lda, m0, M, k0, K, full, t);
+    rb = sk_load<TRANS_B>(B, ldb, n0, N, k0, K, full, t);
+  };
+
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  uint4 ra[PD], rb[PD];
+#pragma unroll
+  for (int u = 0; u < PD; ++u)
+    if (u < nkt) fetch(u, ra[u], rb[u]);
+  // Every group runs the same number of rounds (the barriers are the
+  // block's); a group past its own tiles only passes the barriers.
+  const int rounds = (int)per;
+  const int lr = l % 32, lk = (l / 32) * 8;
+  for (int i0 = 0; i0 < rounds; i0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int i = i0 + u;
+      if (i >= rounds) break;
+      float* As = lds[q][i & 1][0];
+      float* Bs = lds[q][i & 1][1];
+      if (i < nkt) {
+        sk_store<!TRANS_A>(As, ra[u], t);
+        sk_store<TRANS_B>(Bs, rb[u], t);
+      }
+      __syncthreads();
+      if (i + PD < nkt) fetch(i + PD, ra[u], rb[u]);
+      if (i < nkt) {
+        const float4* pa = reinterpret_cast<const float4*>(As + (wm + lr) * LDK + lk);
+        const float4* pb = reinterpret_cast<const float4*>(Bs + (wn + lr) * LDK + lk);
+        const float4 a0 = pa[0], a1 = pa[1], b0v = pb[0], b1v = pb[1];
+        const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float b[8] = {b0v.x, b0v.y, b0v.z, b0v.w, b1v.x, b1v.y, b1v.z, b1v.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[k], b[k], acc, 0, 0, 0);
+      }
+    }
+  }
+  // partial tiles of groups 1..3 through LDS, added by group 0 in group order
+  __syncthreads();
+  float* red = &lds[0][0][0][0];                               // [group - 1][wave in group][16][64]
+  if (q > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[(((q - 1) * 4 + w % 4) * 16 + i) * WAVE + l] = acc[i];
+  }
+  __syncthreads();
+  if (q == 0) {
+#pragma unroll
+    for (int g = 1; g < sk::G; ++g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = acc_add(acc[i], red[(((g - 1) * 4 + w) * 16 + i) * WAVE + l]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t row = m0 + wm + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
+      const int64_t col = n0 + wn + (l % 32);
+      if (row < M && col < N) {
+        TC* p = C + row * ldc + col;
+        float v = alpha * acc[i];
+        if (acc_c) v = acc_add(io<TC>::ld(p), v);
+        io<TC>::st(p, v);
+      }
+    }
+  }
+}
+
 // f32 products with at most 256 tiles of 64 x 64 (one per CU) run those
 // tiles: a product of a few hundred rows (the tiny block's projections and
 // attention scores) then spreads over four times the CUs of its 128 x 128
@@ -854,8 +996,17 @@ hipError_t gemm_run(bool bigk, bool small, const xt_tensor& A, bool ta, const xt
   {
     const int tbs = small ? 64 : BM;
     dim3 grid((unsigned)((N + tbs - 1) / tbs), (unsigned)((M + tbs - 1) / tbs), (unsigned)(S * nbatch));
+    // small f32 products on the 16-wave K-split tiles (the tiny block's
+    // fwd+bwd: 645 -> 607 us; keeping the 4-wave tiles for K < 128 or more
+    // than 128 tiles measured 623 us)
+    const bool ksplit = small && sizeof(TA) == 4;
 #define XT_GEMM_LAUNCH(TA_, TB_)                                                                        \
-    if (small)                                                                                          \
+    if (ksplit)                                                                                         \
+      gemm_sk_k<TC, TA_, TB_><<<grid, sk::NTB, 0, s>>>((const float*)a, A.ld, A.sb[0], A.sb[1],          \
+                                                      (const float*)b, B.ld, B.sb[0], B.sb[1], c, ldc,   \
+                                                      sc0, sc1, M, N, K, nb1, alpha, acc ? 1 : 0,        \
+                                                      kchunk, nbatch, scs);                              \
+    else if (small)                                                                                     \
       gemm_k<TA, TC, TA_, TB_, 64><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0],    \
                                                        B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1, alpha, \
                                                        acc ? 1 : 0, kchunk, nbatch, scs);              \
