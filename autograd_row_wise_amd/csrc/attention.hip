@@ -885,55 +885,66 @@ __global__ __launch_bounds__(fa::NT, 2) void fa_dq_k(const bf16_t* __restrict__ 
   }
 }
 
-// Backward, dK and dV: 128 keys per block (32 per wave), Q / dO tiles of 32
-// queries, with their L and D.  Scores are not transposed here: S = Q K^T
-// has the wave's key per lane (column) and the queries in registers, which
-// is the A-operand order of P^T and dS^T for dV += P^T dO, dK += dS^T Q.
-// The block's K and V rows stay in LDS for the whole kernel (registers go to
-// the two 32 x Dh accumulators).
+// Backward, dK and dV: 128 keys per block, in two groups of four waves
+// (32 keys per wave); Q / dO tiles of 32 queries, with their L and D.
+// Group gq takes the query tiles gq, gq + 2, ... of the block's range, so
+// each SIMD holds two waves working on the block's K and V (one from each
+// group), and group 1's dK, dV are added to group 0's through LDS at the
+// end (fixed order: bitwise reproducible).  Scores are not transposed here:
+// S = Q K^T has the wave's key per lane (column) and the queries in
+// registers, which is the A-operand order of P^T and dS^T for dV += P^T dO,
+// dK += dS^T Q.  The block's K and V rows stay in LDS for the whole kernel
+// (registers go to the two 32 x Dh accumulators).
 template <int DH>
-__global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                                                      const float* __restrict__ lse, const float* __restrict__ dd,
-                                                      bf16_t* __restrict__ dk, int acc_dk, bf16_t* __restrict__ dv,
-                                                      int acc_dv, Geo g, float alpha, int causal, int nkb, int pair) {
+__global__ __launch_bounds__(2 * fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                          const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse, const float* __restrict__ dd,
+                                                          bf16_t* __restrict__ dk, int acc_dk, bf16_t* __restrict__ dv,
+                                                          int acc_dv, Geo g, float alpha, int causal, int nkb, int pair) {
   constexpr int BQ = 32, QS = fa::RS<DH>, QT = BQ * QS, ST = 2 * QT + 4 * BQ;   // + L2 and D: 2 BQ f32
   constexpr int KV = 128 * QS;                        // the block's K (then V) rows
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * ST + 2 * KV];
-  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
+  constexpr int NACC = 2 * (DH / 32) * 16;            // accumulator registers per lane (dK, dV)
+  static_assert((size_t)4 * WAVE * NACC * sizeof(float) <= (4 * ST + 2 * KV) * sizeof(bf16_t),
+                "group 1's accumulators fit the block's LDS");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * ST + 2 * KV];   // [group][stage] tiles, then K, V
+  const int tid = threadIdx.x, gq = tid / fa::NT, gt = tid % fa::NT;
+  const int w = gt / WAVE, l = tid % WAVE, h = l / 32, c = l % 32;
   int64_t hb;
   // one key block of (sequence, head) hb
   auto run = [&](int kb) {
   const int64_t b = hb / g.H, hd = hb % g.H, base = b * g.S * g.ld + hd * DH;
   const int64_t k0 = (int64_t)kb * 128, kw = k0 + 32 * w, kme = kw + c;
   const bool kok = kme < g.S;
-  bf16_t* const Kb = lds + 2 * ST;                    // rows k0 .. k0 + 127 (clamped)
+  bf16_t* const Kb = lds + 4 * ST;                    // rows k0 .. k0 + 127 (clamped)
   bf16_t* const Vb = Kb + KV;
-  {
+  if (gq == 0) {
     Stage2<DH, 128> kv;
-    kv.load(k, v, g, base, k0, tid);
-    kv.template store<QS, QS>(Kb, Vb, tid);
+    kv.load(k, v, g, base, k0, gt);
+    kv.template store<QS, QS>(Kb, Vb, gt);
   }
   const bf16_t* const Kw = Kb + 32 * w * QS + c * QS + 8 * h;   // this lane's key row, piece kk at + 16 kk
   const bf16_t* const Vw = Vb + 32 * w * QS + c * QS + 8 * h;
   const float sl = alpha * LOG2E;
   const int64_t qbeg = causal ? k0 / BQ : 0;          // first query tile
   const int nt = (int)((g.S + BQ - 1) / BQ - qbeg);
+  bf16_t* const G = lds + gq * 2 * ST;                // this group's two stages
   Stage2<DH, BQ> st;
   float lq = 0.f;                                     // this thread's L2 or D entry of the staged tile
   auto load_ld = [&](int64_t r0) {
-    if (tid < 2 * BQ) {
-      const int64_t r = r0 + tid % BQ < g.S ? r0 + tid % BQ : g.S - 1;
-      lq = tid < BQ ? lse[(b * g.S + r) * g.ldl + hd] * LOG2E : dd[(b * g.S + r) * g.H + hd];
+    if (gt < 2 * BQ) {
+      const int64_t r = r0 + gt % BQ < g.S ? r0 + gt % BQ : g.S - 1;
+      lq = gt < BQ ? lse[(b * g.S + r) * g.ldl + hd] * LOG2E : dd[(b * g.S + r) * g.H + hd];
     }
   };
   auto store_ld = [&](bf16_t* t) {
-    if (tid < 2 * BQ) reinterpret_cast<float*>(t + 2 * QT)[tid] = lq;
+    if (gt < 2 * BQ) reinterpret_cast<float*>(t + 2 * QT)[gt] = lq;
   };
-  st.load(q, dout, g, base, qbeg * BQ, tid);
-  load_ld(qbeg * BQ);
-  st.template store<QS, QS>(lds, lds + QT, tid);
-  store_ld(lds);
+  if (gq < nt) {
+    st.load(q, dout, g, base, (qbeg + gq) * BQ, gt);
+    load_ld((qbeg + gq) * BQ);
+    st.template store<QS, QS>(G, G + QT, gt);
+    store_ld(G);
+  }
   __syncthreads();
   f32x16_t ak[DH / 32], av[DH / 32];   // rows = the wave's keys, column = head dimension
 #pragma unroll
@@ -945,23 +956,14 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
     const int64_t f = (kw - BQ + 1 + BQ - 1) / BQ - qbeg;   // first tile with q0 + BQ - 1 >= kw
     jfirst = f < 0 ? 0 : f > nt ? nt : (int)f;
   }
-  auto stage_next = [&](int j) {
-    if (j + 1 < nt) {
-      bf16_t* nx = lds + ((j + 1) & 1) * ST;
-      st.template store<QS, QS>(nx, nx + QT, tid);
-      store_ld(nx);
-    }
-    __syncthreads();
-  };
-  int j = 0;
-  for (; j < jfirst; ++j) {
-    if (j + 1 < nt) { st.load(q, dout, g, base, (qbeg + j + 1) * BQ, tid); load_ld((qbeg + j + 1) * BQ); }
-    stage_next(j);
-  }
-  for (; j < nt; ++j) {
+  // both groups run the same rounds (the barriers are the block's)
+  const int rounds = (nt + 1) / 2;
+  for (int jj = 0; jj < rounds; ++jj) {
+    const int j = 2 * jj + gq;
     const int64_t q0 = (qbeg + j) * BQ;
-    if (j + 1 < nt) { st.load(q, dout, g, base, q0 + BQ, tid); load_ld(q0 + BQ); }
-    const bf16_t* Qt = lds + (j & 1) * ST;
+    if (j + 2 < nt) { st.load(q, dout, g, base, q0 + 2 * BQ, gt); load_ld(q0 + 2 * BQ); }
+    if (j < nt && j >= jfirst) {
+    const bf16_t* Qt = G + (jj & 1) * ST;
     const bf16_t* Dt = Qt + QT;
     const float* LD = reinterpret_cast<const float*>(Qt + 2 * QT);   // [0, BQ): L2, [BQ, 2 BQ): D
     {
@@ -1014,24 +1016,51 @@ __global__ __launch_bounds__(fa::NT, 1) void fa_dkv_k(const bf16_t* __restrict__
         }
       }
     }
-    stage_next(j);
+    }
+    if (j + 2 < nt) {
+      bf16_t* nx = G + ((jj + 1) & 1) * ST;
+      st.template store<QS, QS>(nx, nx + QT, gt);
+      store_ld(nx);
+    }
+    __syncthreads();
   }
+  // group 1's sums through LDS (every wave is past its last LDS read)
+  float* red = reinterpret_cast<float*>(lds) + (size_t)w * NACC * WAVE;
+  if (gq == 1) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t key = kw + arow(i, h);
-    if (key >= g.S) continue;
-    const int64_t off = (b * g.S + key) * g.ld + hd * DH + c;
+    for (int bb = 0; bb < DH / 32; ++bb)
 #pragma unroll
-    for (int bb = 0; bb < DH / 32; ++bb) {
-      if (dk) {
-        float val = alpha * ak[bb][i];
-        if (acc_dk) val = acc_add(bf2f(dk[off + 32 * bb]), val);
-        dk[off + 32 * bb] = (bf16_t)f2bf(val);
+      for (int i = 0; i < 16; ++i) {
+        red[(bb * 16 + i) * WAVE + l] = ak[bb][i];
+        red[((DH / 32 + bb) * 16 + i) * WAVE + l] = av[bb][i];
       }
-      if (dv) {
-        float val = av[bb][i];
-        if (acc_dv) val = acc_add(bf2f(dv[off + 32 * bb]), val);
-        dv[off + 32 * bb] = (bf16_t)f2bf(val);
+  }
+  __syncthreads();
+  if (gq == 0) {
+#pragma unroll
+    for (int bb = 0; bb < DH / 32; ++bb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        ak[bb][i] = acc_add(ak[bb][i], red[(bb * 16 + i) * WAVE + l]);
+        av[bb][i] = acc_add(av[bb][i], red[((DH / 32 + bb) * 16 + i) * WAVE + l]);
+      }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t key = kw + arow(i, h);
+      if (key >= g.S) continue;
+      const int64_t off = (b * g.S + key) * g.ld + hd * DH + c;
+#pragma unroll
+      for (int bb = 0; bb < DH / 32; ++bb) {
+        if (dk) {
+          float val = alpha * ak[bb][i];
+          if (acc_dk) val = acc_add(bf2f(dk[off + 32 * bb]), val);
+          dk[off + 32 * bb] = (bf16_t)f2bf(val);
+        }
+        if (dv) {
+          float val = av[bb][i];
+          if (acc_dv) val = acc_add(bf2f(dv[off + 32 * bb]), val);
+          dv[off + 32 * bb] = (bf16_t)f2bf(val);
+        }
       }
     }
   }
@@ -1103,7 +1132,7 @@ hipError_t fa_bwd(const AttnArgs& a, hipStream_t s) {
   const int64_t npair = (int64_t)((nb + 1) / 2) * a.H * a.B;
   const int kpair = a.causal && nb > 1 && cus > 0 && npair >= (int64_t)cus ? 1 : 0;
   const unsigned gk = kpair ? (unsigned)npair : grid;
-  fa_dkv_k<DH><<<gk, fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+  fa_dkv_k<DH><<<gk, 2 * fa::NT, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                                      (const bf16_t*)a.dout, a.lse, a.dd, (bf16_t*)a.dk, a.acc_dk, (bf16_t*)a.dv,
                                      a.acc_dv, g, a.alpha, a.causal, nb, kpair);
   return hipGetLastError();
