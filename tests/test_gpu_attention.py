@@ -223,6 +223,35 @@ def test_attention_bench_shape_two_heads():
     del w
 
 
+def test_attention_causal_paired_key_blocks_odd_ragged():
+    """2 x 1900 tokens, 16 heads x 128, causal, bf16: 15 key blocks per
+    (sequence, head), the last one ragged (108 keys).  Their 8 pairs per
+    (sequence, head), 256 in all, fill a 256-CU MI355X, so the dK / dV pass
+    runs its paired grid, the middle block of each head on its own; the dQ
+    pass keeps its unpaired grid.  Heads (sequence 0, head 2) and
+    (sequence 1, head 9) checked in full against the oracle."""
+    B, S, H, Dh = 2, 1900, 16, 128
+    R, C = B * S, H * Dh
+    alpha = 1.0 / math.sqrt(Dh)
+    x = {n: synth.device_normal((R, C), 16, n, dtype="bf16") for n in ("q", "k", "v", "dout")}
+    prm = xt.params(alpha=alpha, causal=1, seq_len=S, head_dim=Dh)
+    out = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    ins = [xt.view(x["q"]), xt.view(x["k"]), xt.view(x["v"])]
+    xt.xt_op_fwd(xt.OP.ATTENTION, prm, ins, [xt.view(out), xt.view(lse)])
+    grads = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    w, wp, wb = xt.workspace(xt.OP.ATTENTION, 1, prm, ins)
+    xt.xt_op_bwd(xt.OP.ATTENTION, prm, xt.view(x["dout"]), ins, [xt.view(out), xt.view(lse)],
+                 [xt.view(g) for g in grads], 0, wp, wb)
+    torch.cuda.synchronize()
+    for b, hd in ((0, 2), (1, 9)):
+        rows, cols = slice(b * S, (b + 1) * S), slice(hd * Dh, (hd + 1) * Dh)
+        sl = {n: host(t[rows, cols]) for n, t in x.items()}
+        check_all(out[rows, cols], lse[rows, hd:hd + 1], [host(g[rows, cols]) for g in grads], sl["q"], sl["k"],
+                  sl["v"], sl["dout"], S, 1, Dh, alpha, True, "bf16", (b, hd))
+    del w
+
+
 def test_attention_causal_paired_query_blocks():
     """2 x 4096 tokens, 16 heads x 128, causal, bf16: 512 (heaviest,
     lightest) pairs of 128-query blocks, two per CU on a 256-CU MI355X, so
