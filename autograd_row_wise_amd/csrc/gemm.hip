@@ -701,44 +701,70 @@ __global__ __launch_bounds__(b8::NT) void gemm_k64_k(
 }
 
 // ==========================================================================
-// Small f32 products (at most 256 tiles of 64 x 64 of C): one block of 16
-// waves per tile, in four groups of four.  Group q sums k over its quarter
-// of K (whole 16-deep K tiles) into its own 2 x 2 waves of 32 x 32
-// accumulators, through its own double-buffered LDS tiles, with the next
-// SK_PD K tiles of its quarter already requested into registers; the four
-// partial tiles are then added in group order (fixed: bitwise reproducible)
-// and written once.  A 1024 x 256 x 256 product then runs 16-deep MFMA
-// chains of 64 in k per wave instead of 256, with four K tiles of loads in
-// flight instead of one.
+// Small f32 products (at most 256 tiles of 64 x 64 of C): one block per
+// tile of TB x TB (TB = 64: 16 waves; TB = 32: 4 waves), in four groups.
+// Group q sums k over its quarter of K (whole 16-deep K tiles) into its own
+// 32 x 32 accumulators (2 x 2 waves, or one wave), through its own
+// double-buffered LDS tiles, with the next PD K tiles of its quarter already
+// requested into registers; the four partial tiles are then added in group
+// order (fixed: bitwise reproducible) and written once.
+//
+// The four groups share one CU's matrix cores, so a block's time is bounded
+// by its MFMA work (64 x 64 x 256 in f32: about 4 us); products with few
+// tiles therefore take the 32 x 32 tiles, a quarter of that work per block
+// on four times the CUs.  Operand tiles move as 16-byte chunks whose loads
+// are the same in every step (no branch around them, out-of-range chunks
+// read a block of zeros): the compiler then waits for exactly the tile a
+// step stores, not for every load in flight.
 // ==========================================================================
 namespace sk {
-constexpr int G = 4, GT = NT, NTB = G * GT, TB = 64, BK = 16, LDK = BK + 4, PD = 4;
+constexpr int G = 4, BK = 16, LDK = BK + 4, PD = 4;
+// Per tile edge TB (64 or 32): threads of a group (2 x 2 waves of 32 x 32
+// accumulators, or one wave), of the block, and 16-byte chunks each thread
+// moves per operand tile (TB x 16 floats).
+template <int TB> struct cfg {
+  static constexpr int GT = TB == 64 ? 256 : 64, NTB = G * GT, CH = TB * BK / 4 / GT;
+};
 }
 
-// One thread's 16-byte share of a 64 x 16 f32 operand tile (256 threads of
-// a group): k-contiguous storage ([rows][K]) moves rows t / 4, k (t % 4) * 4;
-// transposed storage ([K][rows]) moves k row t / 16, rows (t % 16) * 4.
-template <bool KCONTIG>
+// Never written: the source of out-of-range chunks.
+__device__ __align__(16) float sk_zeros[4] = {0.f, 0.f, 0.f, 0.f};
+
+// Chunk j of thread t in a TB x 16 operand tile: k-contiguous storage
+// ([rows][K]) moves row c / 4, k (c % 4) * 4; transposed storage ([K][rows])
+// moves k row c / (TB / 4), rows (c % (TB / 4)) * 4, with c = t + j * GT.
+template <int TB, bool KCONTIG>
+__device__ __forceinline__ void sk_pos(int c, int& row, int& kk) {
+  row = KCONTIG ? c / 4 : (c % (TB / 4)) * 4;
+  kk = KCONTIG ? (c % 4) * 4 : c / (TB / 4);
+}
+
+// Every lane loads, a chunk out of range from a 16-byte block of zeros, so
+// each step issues the same loads and nothing is left to do on their data
+// (the host guarantees no chunk straddles the end of its range).
+template <int TB, bool KCONTIG>
 __device__ __forceinline__ uint4 sk_load(const float* g, int64_t ld, int64_t row0, int64_t rows_total, int64_t k0,
-                                         int64_t kend, bool full, int t) {
-  const int row = KCONTIG ? t / 4 : (t % 16) * 4, kk = KCONTIG ? (t % 4) * 4 : t / 16;
+                                         int64_t kend, int c) {
+  int row, kk;
+  sk_pos<TB, KCONTIG>(c, row, kk);
   const int64_t gr = row0 + row, gk = k0 + kk;
-  if (full) return *reinterpret_cast<const uint4*>(KCONTIG ? g + gr * ld + gk : g + gk * ld + gr);
-  float v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t rr = KCONTIG ? gr : gr + j, kq = KCONTIG ? gk + j : gk;
-    v[j] = (rr < rows_total && kq < kend) ? g[KCONTIG ? rr * ld + kq : kq * ld + rr] : 0.f;
-  }
-  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  const bool ok = gr < rows_total && gk < kend;
+  typedef __attribute__((address_space(1))) const float gf;
+  typedef __attribute__((address_space(1))) const u32x4_t gu4;
+  gf* z = (gf*)sk_zeros;
+  asm("" : "+s"(z));
+  gf* p = ok ? (gf*)(KCONTIG ? g + gr * ld + gk : g + gk * ld + gr) : z;
+  const u32x4_t v = *(gu4*)p;
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-template <bool KCONTIG>
-__device__ __forceinline__ void sk_store(float* lds, uint4 r, int t) {
+template <int TB, bool KCONTIG>
+__device__ __forceinline__ void sk_store(float* lds, uint4 r, int c) {
+  int row, kk;
+  sk_pos<TB, KCONTIG>(c, row, kk);
   if constexpr (KCONTIG) {
-    *reinterpret_cast<uint4*>(lds + (t / 4) * sk::LDK + (t % 4) * 4) = r;
+    *reinterpret_cast<uint4*>(lds + row * sk::LDK + kk) = r;
   } else {
-    const int kk = t / 16, row = (t % 16) * 4;
     lds[(row + 0) * sk::LDK + kk] = __uint_as_float(r.x);
     lds[(row + 1) * sk::LDK + kk] = __uint_as_float(r.y);
     lds[(row + 2) * sk::LDK + kk] = __uint_as_float(r.z);
@@ -746,14 +772,15 @@ __device__ __forceinline__ void sk_store(float* lds, uint4 r, int t) {
   }
 }
 
-template <typename TC, bool TRANS_A, bool TRANS_B>
-__global__ __launch_bounds__(sk::NTB) void gemm_sk_k(
+template <typename TC, bool TRANS_A, bool TRANS_B, int TB>
+__global__ __launch_bounds__(sk::cfg<TB>::NTB) void gemm_sk_k(
     const float* __restrict__ A, int64_t lda, int64_t sa0, int64_t sa1,
     const float* __restrict__ B, int64_t ldb, int64_t sb0, int64_t sb1,
     TC* __restrict__ C, int64_t ldc, int64_t sc0, int64_t sc1,
     int64_t M, int64_t N, int64_t K, int64_t nb1, float alpha, int acc_c,
     int64_t kchunk, int64_t nbatch, int64_t scs) {
-  constexpr int TB = sk::TB, BK = sk::BK, LDK = sk::LDK, PD = sk::PD;
+  constexpr int BK = sk::BK, LDK = sk::LDK, PD = sk::PD, GT = sk::cfg<TB>::GT, CH = sk::cfg<TB>::CH;
+  constexpr int WG = GT / WAVE;                                // waves per group
   __shared__ __align__(16) float lds[sk::G][2][2][TB * LDK];   // [group][stage][A, B]
 
   const int64_t z = blockIdx.z, split = z / nbatch, bz = z % nbatch, b0 = bz / nb1, b1 = bz % nb1;
@@ -764,29 +791,27 @@ __global__ __launch_bounds__(sk::NTB) void gemm_sk_k(
   K = K - kb < kchunk ? K - kb : kchunk;
   const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
-  const int q = w / 4, t = threadIdx.x % sk::GT;               // group, thread within the group
-  const int wm = ((w % 4) / 2) * 32, wn = (w % 2) * 32;
+  const int q = w / WG, t = threadIdx.x % GT, wg = w % WG;     // group, thread and wave within the group
+  const int wm = TB == 64 ? (wg / 2) * 32 : 0, wn = TB == 64 ? (wg % 2) * 32 : 0;
   // this group's k range: whole 16-deep tiles, quarters as equal as they come
   const int64_t ntk = (K + BK - 1) / BK, per = (ntk + sk::G - 1) / sk::G;
   const int64_t kt0 = q * per, kt1 = kt0 + per < ntk ? kt0 + per : ntk;
   const int nkt = kt1 > kt0 ? (int)(kt1 - kt0) : 0;
-  const bool fullMN = (m0 + TB <= M) && (n0 + TB <= N);
-  const bool alA = (((uintptr_t)A) & 15) == 0 && ((lda * 4) & 15) == 0;
-  const bool alB = (((uintptr_t)B) & 15) == 0 && ((ldb * 4) & 15) == 0;
-  auto fetch = [&](int i, uint4& ra, uint4& rb) {
+  auto fetch = [&](int i, uint4 (&ra)[CH], uint4 (&rb)[CH]) {
     const int64_t k0 = (kt0 + i) * BK;
-    const bool full = fullMN && alA && alB && k0 + BK <= K;
-    ra = sk_load<!TRANS_A>(A, lda, m0, M, k0, K, full, t);
-    rb = sk_load<TRANS_B>(B, ldb, n0, N, k0, K, full, t);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      ra[j] = sk_load<TB, !TRANS_A>(A, lda, m0, M, k0, K, t + j * GT);
+      rb[j] = sk_load<TB, TRANS_B>(B, ldb, n0, N, k0, K, t + j * GT);
+    }
   };
 
   f32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  uint4 ra[PD], rb[PD];
+  uint4 ra[PD][CH], rb[PD][CH];
 #pragma unroll
-  for (int u = 0; u < PD; ++u)
-    if (u < nkt) fetch(u, ra[u], rb[u]);
+  for (int u = 0; u < PD; ++u) fetch(u, ra[u], rb[u]);
   // Every group runs the same number of rounds (the barriers are the
   // block's); a group past its own tiles only passes the barriers.
   const int rounds = (int)per;
@@ -799,11 +824,14 @@ __global__ __launch_bounds__(sk::NTB) void gemm_sk_k(
       float* As = lds[q][i & 1][0];
       float* Bs = lds[q][i & 1][1];
       if (i < nkt) {
-        sk_store<!TRANS_A>(As, ra[u], t);
-        sk_store<TRANS_B>(Bs, rb[u], t);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          sk_store<TB, !TRANS_A>(As, ra[u][j], t + j * GT);
+          sk_store<TB, TRANS_B>(Bs, rb[u][j], t + j * GT);
+        }
       }
       __syncthreads();
-      if (i + PD < nkt) fetch(i + PD, ra[u], rb[u]);
+      fetch(i + PD, ra[u], rb[u]);
       if (i < nkt) {
         const float4* pa = reinterpret_cast<const float4*>(As + (wm + lr) * LDK + lk);
         const float4* pb = reinterpret_cast<const float4*>(Bs + (wn + lr) * LDK + lk);
@@ -820,14 +848,14 @@ __global__ __launch_bounds__(sk::NTB) void gemm_sk_k(
   float* red = &lds[0][0][0][0];                               // [group - 1][wave in group][16][64]
   if (q > 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[(((q - 1) * 4 + w % 4) * 16 + i) * WAVE + l] = acc[i];
+    for (int i = 0; i < 16; ++i) red[(((q - 1) * WG + wg) * 16 + i) * WAVE + l] = acc[i];
   }
   __syncthreads();
   if (q == 0) {
 #pragma unroll
     for (int g = 1; g < sk::G; ++g)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = acc_add(acc[i], red[(((g - 1) * 4 + w) * 16 + i) * WAVE + l]);
+      for (int i = 0; i < 16; ++i) acc[i] = acc_add(acc[i], red[(((g - 1) * WG + wg) * 16 + i) * WAVE + l]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t row = m0 + wm + 8 * (i / 4) + 4 * (l / 32) + (i % 4);
@@ -877,18 +905,24 @@ bool big_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_t
 // slices, and never more slices than the workspace can hold.
 struct SplitPlan { int64_t S, kchunk; };
 
+// Kernel choice for a small f32 product (sk_kind, below).
+enum { SK_NONE = 0, SK_32 = 1, SK_64 = 2, SK_GEN = 3 };
+
 // Blocks resident on the 256 CUs at once (a SIMD holds 512 registers per
 // lane; each block puts one wave on each SIMD): the f32 large-tile kernel
 // uses 152 (3 per CU), the bf16 one 512 (1 per CU), the 128 x 128 kernel
 // 172 (2 per CU).
-SplitPlan split_plan(bool bf16, bool bigk, bool small, int64_t M, int64_t N, int64_t K, int64_t nbatch,
+SplitPlan split_plan(bool bf16, bool bigk, int sk, int64_t M, int64_t N, int64_t K, int64_t nbatch,
                      size_t ws_bytes) {
-  const int64_t tb = small ? 64 : BM;
+  const bool small = sk != SK_NONE;
+  const int64_t tb = sk == SK_32 ? 32 : small ? 64 : BM;
   const int64_t bm = bigk ? (bf16 ? 256 : 128) : tb, bn = bigk ? (bf16 ? 256 : 128) : tb;
   const int64_t bk = bigk ? (bf16 ? big<bf16_t>::BK : big<float>::BK) : (bf16 ? gcfg<bf16_t>::BK : gcfg<float>::BK);
-  // blocks the split aims at: what the chip holds at once; for the small
-  // 64 x 64 tiles (20 KB of LDS, 42 VGPRs) four per CU
-  const int64_t resident = bigk ? (bf16 ? 256 : 768) : (small ? 1024 : 512);
+  // blocks the split aims at: what the chip holds at once (the generic
+  // kernel on 64 x 64 tiles: 20 KB of LDS, four per CU); for the K-split
+  // small kernels two 32 x 32 blocks or one 64 x 64 block per CU, since a
+  // block already keeps its CU's matrix cores busy
+  const int64_t resident = bigk ? (bf16 ? 256 : 768) : sk == SK_32 ? 512 : sk == SK_64 ? 256 : sk == SK_GEN ? 1024 : 512;
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * nbatch;
   const int64_t nk = (K + bk - 1) / bk;
   const int64_t per = nbatch * M * N * (int64_t)sizeof(float);
@@ -956,8 +990,31 @@ hipError_t splitk_sum(const float* P, int64_t S, int64_t scs, const xt_tensor& C
 // One launch of either kernel family: C (+)= alpha op(A) op(B) over k slices
 // of kchunk (kchunk = K: no split), writing through C's own strides, or
 // (split) into partial slices `scs` elements apart.
+// Operands the small-product kernel moves as 16-byte chunks: aligned, and no
+// chunk (4 consecutive k of a k-contiguous operand, 4 consecutive rows of a
+// transposed one) straddles the end of its range.
+bool sk_vec_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, int64_t M, int64_t N, int64_t K) {
+  auto al = [](const xt_tensor& t) {
+    return (((uintptr_t)t.data) & 15) == 0 && t.ld % 4 == 0 && t.sb[0] % 4 == 0 && t.sb[1] % 4 == 0;
+  };
+  return al(A) && al(B) && (ta ? M % 4 == 0 : K % 4 == 0) && (tb ? K % 4 == 0 : N % 4 == 0);
+}
+
+// Kernel for a small f32 product: none (not small), the 16-byte-chunk
+// kernel on 32 x 32 or 64 x 64 tiles, or the generic kernel on 64 x 64 tiles
+// for operands it cannot move in chunks.  Products of at most 128 tiles of
+// 64 x 64 take the 32 x 32 tiles: four times the CUs, each with a quarter of
+// the MFMA work (1024 x 256 x 256: 11.1 -> 6.5 us); from about 200 tiles of
+// 64 x 64 up the larger tiles are faster (1024 x 1024 x 256: 11.9 vs 14.3 us).
+int sk_kind(bool small, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C, int64_t K) {
+  if (!small) return SK_NONE;
+  if (!sk_vec_ok(A, ta, B, tb, C.rows, C.cols, K)) return SK_GEN;
+  const int64_t t64 = ((C.rows + 63) / 64) * ((C.cols + 63) / 64) * C.nb[0] * C.nb[1];
+  return t64 <= 128 ? SK_32 : SK_64;
+}
+
 template <typename TA, typename TC>
-hipError_t gemm_run(bool bigk, bool small, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
+hipError_t gemm_run(bool bigk, int sk, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb,
                     TC* c, int64_t ldc, int64_t sc0, int64_t sc1, int64_t M, int64_t N, int64_t K,
                     int64_t nb0, int64_t nb1, float alpha, bool acc, int64_t S, int64_t kchunk, int64_t scs,
                     hipStream_t s) {
@@ -994,19 +1051,22 @@ hipError_t gemm_run(bool bigk, bool small, const xt_tensor& A, bool ta, const xt
     return hipGetLastError();
   }
   {
-    const int tbs = small ? 64 : BM;
+    const int tbs = sk == SK_32 ? 32 : sk != SK_NONE ? 64 : BM;
     dim3 grid((unsigned)((N + tbs - 1) / tbs), (unsigned)((M + tbs - 1) / tbs), (unsigned)(S * nbatch));
     // small f32 products on the 16-wave K-split tiles (the tiny block's
     // fwd+bwd: 645 -> 607 us; keeping the 4-wave tiles for K < 128 or more
     // than 128 tiles measured 623 us)
-    const bool ksplit = small && sizeof(TA) == 4;
+#define XT_SK(TA_, TB_, T)                                                                              \
+      gemm_sk_k<TC, TA_, TB_, T><<<grid, sk::cfg<T>::NTB, 0, s>>>((const float*)a, A.ld, A.sb[0], A.sb[1], \
+                                                                  (const float*)b, B.ld, B.sb[0], B.sb[1], \
+                                                                  c, ldc, sc0, sc1, M, N, K, nb1, alpha,   \
+                                                                  acc ? 1 : 0, kchunk, nbatch, scs)
 #define XT_GEMM_LAUNCH(TA_, TB_)                                                                        \
-    if (ksplit)                                                                                         \
-      gemm_sk_k<TC, TA_, TB_><<<grid, sk::NTB, 0, s>>>((const float*)a, A.ld, A.sb[0], A.sb[1],          \
-                                                      (const float*)b, B.ld, B.sb[0], B.sb[1], c, ldc,   \
-                                                      sc0, sc1, M, N, K, nb1, alpha, acc ? 1 : 0,        \
-                                                      kchunk, nbatch, scs);                              \
-    else if (small)                                                                                     \
+    if (sk == SK_32)                                                                                    \
+      XT_SK(TA_, TB_, 32);                                                                              \
+    else if (sk == SK_64)                                                                               \
+      XT_SK(TA_, TB_, 64);                                                                              \
+    else if (sk == SK_GEN)                                                                              \
       gemm_k<TA, TC, TA_, TB_, 64><<<grid, NT, 0, s>>>(a, A.ld, A.sb[0], A.sb[1], b, B.ld, B.sb[0],    \
                                                        B.sb[1], c, ldc, sc0, sc1, M, N, K, nb1, alpha, \
                                                        acc ? 1 : 0, kchunk, nbatch, scs);              \
@@ -1019,6 +1079,7 @@ hipError_t gemm_run(bool bigk, bool small, const xt_tensor& A, bool ta, const xt
     else if (ta && !tb) XT_GEMM_LAUNCH(true, false);
     else XT_GEMM_LAUNCH(true, true);
 #undef XT_GEMM_LAUNCH
+#undef XT_SK
   }
   return hipGetLastError();
 }
@@ -1031,13 +1092,14 @@ hipError_t gemm_go(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, con
   if (M == 0 || N == 0 || nbatch == 0) return hipSuccess;
   const bool small = small_tiles<TA>(A, ta, B, tb, C);
   const bool bigk = !small && big_ok<TA>(A, ta, B, tb, C);
-  const SplitPlan sp = split_plan(sizeof(TA) == 2, bigk, small, M, N, K, nbatch, ws ? ws_bytes : 0);
+  const int sk = sk_kind(small, A, ta, B, tb, C, K);
+  const SplitPlan sp = split_plan(sizeof(TA) == 2, bigk, sk, M, N, K, nbatch, ws ? ws_bytes : 0);
   if (sp.S == 1)
-    return gemm_run<TA, TC>(bigk, small, A, ta, B, tb, (TC*)C.data, C.ld, C.sb[0], C.sb[1], M, N, K, nb0, nb1,
+    return gemm_run<TA, TC>(bigk, sk, A, ta, B, tb, (TC*)C.data, C.ld, C.sb[0], C.sb[1], M, N, K, nb0, nb1,
                             alpha, acc, 1, K, 0, s);
   float* P = (float*)ws;
   const int64_t scs = nbatch * M * N;
-  hipError_t e = gemm_run<TA, float>(bigk, small, A, ta, B, tb, P, N, nb1 * M * N, M * N, M, N, K, nb0, nb1,
+  hipError_t e = gemm_run<TA, float>(bigk, sk, A, ta, B, tb, P, N, nb1 * M * N, M * N, M, N, K, nb0, nb1,
                                      1.f, false, sp.S, sp.kchunk, scs, s);
   if (e != hipSuccess) return e;
   return splitk_sum<TC>(P, sp.S, scs, C, nbatch, alpha, acc, s);
@@ -1078,9 +1140,9 @@ size_t gemm_workspace(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, 
   const bool small = bf ? small_tiles<bf16_t>(A, ta, B, tb, C) : small_tiles<float>(A, ta, B, tb, C);
   if (small) cand[0] = cand[1] = false;
   size_t best = 0;
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < 5; ++k) {
     if (k < 2 ? !cand[k] : !small) continue;
-    const SplitPlan sp = split_plan(bf, k == 1, k == 2, M, N, K, nbatch, SIZE_MAX);
+    const SplitPlan sp = split_plan(bf, k == 1, k < 2 ? SK_NONE : k - 1, M, N, K, nbatch, SIZE_MAX);
     if (sp.S > 1) best = std::max(best, (size_t)sp.S * (size_t)(nbatch * M * N) * sizeof(float));
   }
   return best;
