@@ -920,9 +920,10 @@ SplitPlan split_plan(bool bf16, bool bigk, int sk, int64_t M, int64_t N, int64_t
   const int64_t bk = bigk ? (bf16 ? big<bf16_t>::BK : big<float>::BK) : (bf16 ? gcfg<bf16_t>::BK : gcfg<float>::BK);
   // blocks the split aims at: what the chip holds at once (the generic
   // kernel on 64 x 64 tiles: 20 KB of LDS, four per CU); for the K-split
-  // small kernels two 32 x 32 blocks or one 64 x 64 block per CU, since a
-  // block already keeps its CU's matrix cores busy
-  const int64_t resident = bigk ? (bf16 ? 256 : 768) : sk == SK_32 ? 512 : sk == SK_64 ? 256 : sk == SK_GEN ? 1024 : 512;
+  // small kernels one block per CU, since a block already keeps its CU's
+  // matrix cores busy (two 32 x 32 blocks per CU and a second summing pass
+  // measured slower: tiny block 471 vs 479 us)
+  const int64_t resident = bigk ? (bf16 ? 256 : 768) : sk == SK_32 ? 256 : sk == SK_64 ? 256 : sk == SK_GEN ? 1024 : 512;
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * nbatch;
   const int64_t nk = (K + bk - 1) / bk;
   const int64_t per = nbatch * M * N * (int64_t)sizeof(float);
