@@ -17,17 +17,20 @@
 //     load): for a contraction of length n, MFMA j takes index h*(n/2) + j
 //     from lane half h for both operands (a fixed permutation of the
 //     summation order).  A probability tile leaves the MFMA in the
-//     accumulator layout (row by register, column by lane); it goes through
-//     a per-wave 32 x 33 LDS tile to become the A operand of the next
-//     product.
+//     accumulator layout (row by register, column by lane).  The forward
+//     forms its scores transposed (one query per lane column), so the
+//     softmax needs no cross-lane reduction beyond one exchange and P^T is
+//     the B operand of O^T += V^T P^T as it stands; the backward passes
+//     take a tile through a per-wave 32 x 33 LDS tile to make it the A
+//     operand of the next product.
 //   - aligned bf16 storage: blocks of four waves on the bf16 matrix cores
 //     (v_mfma_f32_32x32x16_bf16, f32 accumulation), with the f32
 //     probabilities split into two bf16 parts so every product keeps f32
 //     accuracy (see the section below).
 //
-// The backward is three launches with no atomics: D = rowsum(dO * O) per
-// (row, head); dQ per query tile over its key tiles; dK and dV per key tile
-// over its query tiles.  Results are bitwise reproducible.
+// The backward is two launches with no atomics: D = rowsum(dO * O) per
+// (row, head) and dQ per query tile over its key tiles; dK and dV per key
+// tile over its query tiles.  Results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -133,10 +136,51 @@ __device__ __forceinline__ void mul_rows(const float (&a)[16], const T* x, const
   }
 }
 
-// Max / sum over the 32 lanes of a lane half (one accumulator row), on the
-// DPP paths (common.h half_reduce).
-__device__ __forceinline__ float half_max(float v) { return half_reduce(v, OpMax{}); }
-__device__ __forceinline__ float half_sum(float v) { return half_reduce(v, OpAdd{}); }
+// Operand fragment of a contraction over 32 rows of x (keys or queries) taken
+// in an accumulator's row order: lane l, MFMA j: x[row0 + arow(j, l)][col0 +
+// l % 32] (0 past the sequence end), arow(j, l) = 8 (j / 4) + 4 (l / 32) +
+// j % 4.  Register j of an accumulator tile whose rows are those 32 rows is
+// then the other operand of MFMA j as it is: the tile needs no transpose.
+template <typename T, int DH>
+__device__ __forceinline__ void frag_acc_rows(const T* x, const Geo& g, int64_t b, int64_t hd, int64_t row0,
+                                              int col0, int l, float (&f)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t r = row0 + crow(j, l);
+    const float u = ldv<T>(rowp(x, g, b, hd, r < g.S ? r : g.S - 1, DH) + col0 + l % 32);
+    f[j] = r < g.S ? u : 0.f;
+  }
+}
+
+// acc[t] (rows: head dimension t*32 .., columns: the tile's 32 columns) +=
+// X^T C, the contraction over the 32 rows of the accumulator tile C, with
+// X^T's fragments from frag_acc_rows.
+template <int DH>
+__device__ __forceinline__ void mul_acc(const float (&x)[DH / 32][16], const f32x16_t& c, f32x16_t (&acc)[DH / 32]) {
+#pragma unroll
+  for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(x[t][j], c[j], acc[t], 0, 0, 0);
+}
+
+// Store an accumulator tile whose rows are the head dimension and whose
+// column l % 32 is token `row` (when inside the sequence): register 4a + c
+// holds dimension 8a + 4 (l / 32) + c, four consecutive values.
+template <typename T, int DH>
+__device__ __forceinline__ void store_dh(T* dst, const Geo& g, int64_t b, int64_t hd, int64_t row, int l,
+                                         const f32x16_t (&acc)[DH / 32], float scale, int accumulate) {
+  if (row >= g.S) return;
+  T* p = dst + (b * g.S + row) * g.ld + hd * DH + 4 * (l / 32);
+#pragma unroll
+  for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      T* q = p + t * 32 + 8 * (i / 4) + (i % 4);
+      float v = scale * acc[t][i];
+      if (accumulate) v = acc_add(ldv<T>(q), v);
+      stv<T>(q, v);
+    }
+}
 
 // Blocks of KW waves share one 32-row tile: wave w takes the loop's tiles
 // w, w + KW, ... (the key tiles of a query tile, or the query tiles of a
@@ -146,113 +190,115 @@ __device__ __forceinline__ float half_sum(float v) { return half_reduce(v, OpAdd
 // the (sequence, head, tile) grid alone is too small to fill the chip.
 constexpr int AKW = 4;
 
+// Forward, scores transposed: S^T = K Q^T puts this lane's query (column
+// l % 32) against the tile's keys in its 16 registers and the other lane
+// half, so the row maximum and sum are in-lane plus one exchange with lane
+// l ^ 32, and the probability tile P^T is directly the B operand of
+// O^T += V^T P^T.
 template <typename T, int DH, int KW>
 __global__ __launch_bounds__(WAVE * KW) void attn_fwd_k(const T* __restrict__ q, const T* __restrict__ k,
                                                         const T* __restrict__ v, T* __restrict__ out,
                                                         float* __restrict__ lse, Geo g, float alpha, int causal) {
-  __shared__ float tiles[KW][32 * 33];
-  __shared__ float mrg[KW > 1 ? KW - 1 : 1][2 + DH / 32][16][WAVE];   // m, s, o per register and lane
+  __shared__ float mrg[KW > 1 ? KW - 1 : 1][2 + 16 * (DH / 32)][WAVE];   // m, s, O^T per register and lane
   const int l = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
-  float* tile = tiles[w];
-  const int64_t q0 = (int64_t)blockIdx.x * 32, hd = blockIdx.y, b = blockIdx.z;
+  const int64_t q0 = (int64_t)blockIdx.x * 32, hd = blockIdx.y, b = blockIdx.z, qme = q0 + l % 32;
   float qf[DH / 2];
   frag_dh<T, DH>(q, g, b, hd, q0, l, qf);
-  float m[16], s[16];
+  float m = -INFINITY, s = 0.f;
   f32x16_t o[DH / 32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) { m[i] = -INFINITY; s[i] = 0.f; }
 #pragma unroll
   for (int t = 0; t < DH / 32; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
   const int64_t kend = causal ? (q0 + 32 < g.S ? q0 + 32 : g.S) : g.S;
-  // every tile a wave takes keeps at least one key of each row (causal:
-  // k0 <= q0 <= the row), so m is finite after a wave's first tile
+  // every tile a wave takes keeps at least one key of each query (causal:
+  // k0 <= q0 <= the query), so m is finite after a wave's first tile
   for (int64_t k0 = (int64_t)w * 32; k0 < kend; k0 += 32 * KW) {
-    float kf[DH / 2];
+    // V^T fragments are loaded with K's, or (head size 128, where they
+    // would not fit the registers) one 32-wide slice at a time before its
+    // products
+    constexpr bool EARLY = DH <= 64;
+    float kf[DH / 2], vt[DH / 32][16];
     frag_dh<T, DH>(k, g, b, hd, k0, l, kf);
-    f32x16_t z = dot_tile<DH>(qf, kf);
-    const int64_t key = k0 + l % 32;
-    float p[16];
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int t = 0; t < DH / 32; ++t) frag_acc_rows<T, DH>(v, g, b, hd, k0, t * 32, l, vt[t]);
+    }
+    const f32x16_t z = dot_tile<DH>(kf, qf);
+    float zs[16], mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int64_t qr = q0 + crow(i, l);
-      const bool keep = key < g.S && (!causal || key <= qr);
-      const float zi = keep ? alpha * z[i] : -INFINITY;
-      const float mn = fmaxf(m[i], half_max(zi));
-      const float sc = ex(m[i] - mn);                     // 0 on the first tile (m = -inf)
-      p[i] = keep ? ex(zi - mn) : 0.f;
-      s[i] = s[i] * sc + half_sum(p[i]);
-      m[i] = mn;
-#pragma unroll
-      for (int t = 0; t < DH / 32; ++t) o[t][i] *= sc;
+      const int64_t key = k0 + crow(i, l);
+      const bool keep = key < g.S && (!causal || key <= qme);
+      zs[i] = keep ? alpha * z[i] : -INFINITY;
+      mx = fmaxf(mx, zs[i]);
     }
-    f32x16_t pc;
+    const float mn = fmaxf(m, xor32_reduce(mx, OpMax{}));
+    const float sc = ex(m - mn);                     // 0 on the first tile (m = -inf)
+    f32x16_t p;
+    float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pc[i] = p[i];
-    float pa[16];
-    c_to_a(pc, tile, l, pa);
-    mul_rows<T, DH>(pa, v, g, b, hd, k0, l, o);
+    for (int i = 0; i < 16; ++i) {
+      p[i] = zs[i] == -INFINITY ? 0.f : ex(zs[i] - mn);
+      ps += p[i];
+    }
+    s = s * sc + xor32_reduce(ps, OpAdd{});
+    m = mn;
+#pragma unroll
+    for (int t = 0; t < DH / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] *= sc;
+    if constexpr (EARLY) {
+      mul_acc<DH>(vt, p, o);
+    } else {
+#pragma unroll
+      for (int t = 0; t < DH / 32; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        frag_acc_rows<T, DH>(v, g, b, hd, k0, t * 32, l, vt[0]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[0][j], p[j], o[t], 0, 0, 0);
+      }
+    }
   }
   if constexpr (KW > 1) {
     if (w > 0) {
+      mrg[w - 1][0][l] = m;
+      mrg[w - 1][1][l] = s;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        mrg[w - 1][0][i][l] = m[i];
-        mrg[w - 1][1][i][l] = s[i];
+      for (int t = 0; t < DH / 32; ++t)
 #pragma unroll
-        for (int t = 0; t < DH / 32; ++t) mrg[w - 1][2 + t][i][l] = o[t][i];
-      }
+        for (int i = 0; i < 16; ++i) mrg[w - 1][2 + 16 * t + i][l] = o[t][i];
     }
     __syncthreads();
     if (w > 0) return;
     // a wave with no tile holds m = -inf, s = 0, o = 0 and adds nothing
-    for (int u = 1; u < KW; ++u)
+    for (int u = 1; u < KW; ++u) {
+      const float mu = mrg[u - 1][0][l];
+      const float mn = fmaxf(m, mu);
+      const float ca = m == -INFINITY ? 0.f : ex(m - mn), cb = mu == -INFINITY ? 0.f : ex(mu - mn);
+      s = s * ca + mrg[u - 1][1][l] * cb;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float mu = mrg[u - 1][0][i][l];
-        const float mn = fmaxf(m[i], mu);
-        const float ca = m[i] == -INFINITY ? 0.f : ex(m[i] - mn), cb = mu == -INFINITY ? 0.f : ex(mu - mn);
-        s[i] = s[i] * ca + mrg[u - 1][1][i][l] * cb;
+      for (int t = 0; t < DH / 32; ++t)
 #pragma unroll
-        for (int t = 0; t < DH / 32; ++t) o[t][i] = o[t][i] * ca + mrg[u - 1][2 + t][i][l] * cb;
-        m[i] = mn;
-      }
+        for (int i = 0; i < 16; ++i) o[t][i] = o[t][i] * ca + mrg[u - 1][2 + 16 * t + i][l] * cb;
+      m = mn;
+    }
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t qr = q0 + crow(i, l);
-    if (qr >= g.S) continue;
-    const float inv = 1.f / s[i];
-    T* orow = out + (b * g.S + qr) * g.ld + hd * DH;
-#pragma unroll
-    for (int t = 0; t < DH / 32; ++t) stv<T>(orow + t * 32 + l % 32, o[t][i] * inv);
-    if (l % 32 == 0) lse[(b * g.S + qr) * g.ldl + hd] = m[i] + logf(s[i]);
-  }
-}
-
-// D[row, h] = sum over the head dimension of dO * O (f32).
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_bwd_d_k(const T* __restrict__ dout, const T* __restrict__ out,
-                                                    float* __restrict__ dd, Geo g, int64_t rows) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (row, head)
-  if (idx >= rows * g.H) return;
-  const int64_t r = idx / g.H, hd = idx % g.H;
-  const T* a = dout + r * g.ld + hd * DH;
-  const T* o = out + r * g.ld + hd * DH;
-  float acc = 0.f;
-  for (int j = 0; j < DH; ++j) acc += ldv<T>(a + j) * ldv<T>(o + j);
-  dd[idx] = acc;
+  store_dh<T, DH>(out, g, b, hd, qme, l, o, 1.f / s, 0);
+  if (qme < g.S && l < 32) lse[(b * g.S + qme) * g.ldl + hd] = m + logf(s);
 }
 
 // dQ of 32 query rows: over key tiles, P = exp(alpha S - L), dP = dO V^T,
-// dS = P (dP - D), dQ += alpha dS K.
+// dS = P (dP - D), dQ += alpha dS K.  D = rowsum(dO * O) of the block's
+// rows is formed here (each lane half sums its half of the head dimension,
+// the halves are then added) and stored for the dK / dV pass; with
+// dq == nullptr only D is produced.
 template <typename T, int DH, int KW>
 __global__ __launch_bounds__(WAVE * KW) void attn_bwd_dq_k(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const T* __restrict__ dout,
-                                                           const float* __restrict__ lse, const float* __restrict__ dd,
-                                                           T* __restrict__ dq, int acc_dq, Geo g, float alpha,
-                                                           int causal) {
+                                                           const T* __restrict__ out, const float* __restrict__ lse,
+                                                           float* __restrict__ dd, T* __restrict__ dq, int acc_dq,
+                                                           Geo g, float alpha, int causal) {
   __shared__ float tiles[KW][32 * 33];
   __shared__ float mrg[KW > 1 ? KW - 1 : 1][DH / 32][16][WAVE];
   const int l = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
@@ -261,12 +307,22 @@ __global__ __launch_bounds__(WAVE * KW) void attn_bwd_dq_k(const T* __restrict__
   float qf[DH / 2], df[DH / 2];
   frag_dh<T, DH>(q, g, b, hd, q0, l, qf);
   frag_dh<T, DH>(dout, g, b, hd, q0, l, df);
+  float Dme;                                       // D of row q0 + l % 32 (0 past the end)
+  {
+    float of[DH / 2], part = 0.f;
+    frag_dh<T, DH>(out, g, b, hd, q0, l, of);
+#pragma unroll
+    for (int j = 0; j < DH / 2; ++j) part += df[j] * of[j];
+    Dme = xor32_reduce(part, OpAdd{});
+  }
+  if (w == 0 && l < 32 && q0 + l < g.S) dd[(b * g.S + q0 + l) * g.H + hd] = Dme;
+  if (dq == nullptr) return;
   float Lr[16], Dr[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t qr = q0 + crow(i, l);
     Lr[i] = qr < g.S ? lse[(b * g.S + qr) * g.ldl + hd] : 0.f;
-    Dr[i] = qr < g.S ? dd[(b * g.S + qr) * g.H + hd] : 0.f;
+    Dr[i] = __shfl(Dme, crow(i, l));
   }
   f32x16_t acc[DH / 32];
 #pragma unroll
@@ -1161,18 +1217,13 @@ hipError_t fwd_dh(const AttnArgs& a, hipStream_t s) {
 template <typename T, int DH>
 hipError_t bwd_dh(const AttnArgs& a, hipStream_t s) {
   const Geo g{a.S, a.H, a.ld, a.ldl};
-  const int64_t rows = a.B * a.S;
-  attn_bwd_d_k<T, DH><<<(unsigned)((rows * a.H + 255) / 256), 256, 0, s>>>((const T*)a.dout, (const T*)a.out,
-                                                                          a.dd, g, rows);
+  const dim3 grid((unsigned)((a.S + 31) / 32), (unsigned)a.H, (unsigned)a.B);
+  // D for every row, and dQ when asked for
+  attn_bwd_dq_k<T, DH, AKW><<<grid, WAVE * AKW, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                                                         (const T*)a.out, a.lse, a.dd, (T*)a.dq, a.acc_dq, g, a.alpha,
+                                                         a.causal);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((a.S + 31) / 32), (unsigned)a.H, (unsigned)a.B);
-  if (a.dq) {
-    attn_bwd_dq_k<T, DH, AKW><<<grid, WAVE * AKW, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                                               a.lse, a.dd, (T*)a.dq, a.acc_dq, g, a.alpha, a.causal);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (a.dk || a.dv) {
     attn_bwd_dkv_k<T, DH, AKW><<<grid, WAVE * AKW, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                                                 a.lse, a.dd, (T*)a.dk, a.acc_dk, (T*)a.dv, a.acc_dv, g, a.alpha,
