@@ -352,6 +352,10 @@ MM_CASES = [  # (M, N, K, ta, tb, batch)
     (512, 256, 192, 0, 0, (1, 1)), (512, 256, 192, 0, 1, (1, 1)), (512, 256, 192, 1, 0, (1, 1)),
     (512, 256, 192, 1, 1, (1, 1)), (256, 512, 128, 0, 1, (2, 2)), (256, 256, 64, 1, 0, (1, 3)),
     (256, 256, 32, 1, 1, (1, 1)), (768, 512, 416, 0, 1, (1, 1)),
+    # small f32 products on 16-byte chunks: 32 x 32 tiles with edge tiles in
+    # both dimensions, and 64 x 64 tiles (more than 128 of them) with edges
+    (200, 132, 72, 0, 0, (1, 1)), (196, 132, 72, 1, 1, (1, 1)),
+    (1000, 700, 96, 0, 1, (1, 1)), (1000, 700, 96, 1, 0, (1, 1)),
 ]
 
 
