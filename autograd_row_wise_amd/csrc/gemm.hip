@@ -830,7 +830,10 @@ __global__ __launch_bounds__(sk::cfg<TB>::NTB) void gemm_sk_k(
           sk_store<TB, TRANS_B>(Bs, rb[u][j], t + j * GT);
         }
       }
-      __syncthreads();
+      // a group of one wave (32 x 32 tiles) reads only what it wrote: its
+      // stores complete before its reads, no block barrier
+      if constexpr (WG == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      else __syncthreads();
       fetch(i + PD, ra[u], rb[u]);
       if (i < nkt) {
         const float4* pa = reinterpret_cast<const float4*>(As + (wm + lr) * LDK + lk);
