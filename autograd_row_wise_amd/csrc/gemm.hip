@@ -1006,15 +1006,16 @@ bool sk_vec_ok(const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, int64_t
 
 // Kernel for a small f32 product: none (not small), the 16-byte-chunk
 // kernel on 32 x 32 or 64 x 64 tiles, or the generic kernel on 64 x 64 tiles
-// for operands it cannot move in chunks.  Products of at most 128 tiles of
+// for operands it cannot move in chunks.  Products of at most 192 tiles of
 // 64 x 64 take the 32 x 32 tiles: four times the CUs, each with a quarter of
-// the MFMA work (1024 x 256 x 256: 11.1 -> 6.5 us); from about 200 tiles of
-// 64 x 64 up the larger tiles are faster (1024 x 1024 x 256: 11.9 vs 14.3 us).
+// the MFMA work (1024 x 256 x 256: 11.1 -> 6.5 us; 1024 x 688 x 256: 11.7 ->
+// 11.5 us); at 256 tiles the larger tiles are faster (1024 x 1024 x 256:
+// 12.0 vs 15.6 us).
 int sk_kind(bool small, const xt_tensor& A, bool ta, const xt_tensor& B, bool tb, const xt_tensor& C, int64_t K) {
   if (!small) return SK_NONE;
   if (!sk_vec_ok(A, ta, B, tb, C.rows, C.cols, K)) return SK_GEN;
   const int64_t t64 = ((C.rows + 63) / 64) * ((C.cols + 63) / 64) * C.nb[0] * C.nb[1];
-  return t64 <= 128 ? SK_32 : SK_64;
+  return t64 <= 192 ? SK_32 : SK_64;
 }
 
 template <typename TA, typename TC>
